@@ -1,0 +1,295 @@
+#!/usr/bin/env python3
+"""Benchmark of the KVarN hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input:
+  for every layer: quantize K and V (all 128-token chunks), append one new
+  token to each, and run one decode-attention step over the 2-bit cache.
+(The Llama-3-8B-shaped workload quantizes its cache once, before timing, and
+its step is append + decode per layer: steady-state decoding.)
+
+Default workload: Qwen3-4B-shaped full cache (36 layers, batch 8, 8 kv-heads
+x 128, 32768 tokens, 32 query heads), the largest of the workloads and the
+one that does not fit in the 256 MB last-level cache.
+
+Prints ONE JSON line. Per-kernel durations come from HIP events recorded on
+the launch stream around every launch in the timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import threading
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "quantize GB/s (bf16 in) + 2-bit decode-attn tokens/s; % of HBM peak"
+HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E, published
+D, CHUNK = 128, 128
+# algorithmic bytes per element of one quantize launch: 2 B bf16 in, 0.25 B
+# codes, 4 B row scale per 128 channels, 4 B column scale per 128 tokens
+QUANT_BYTES_PER_ELT_BF16 = 2.0 + 0.25 + 4.0 / 128 + 4.0 / 128
+# algorithmic bytes per cached token per kv-head read by decode: 64 B codes
+# (K and V), 8 B row scales, 8 B column scales amortized over the chunk
+DECODE_BYTES_PER_TOKEN = 80.0
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--workload", type=int, default=2,
+                   help="index into kvgen.WORKLOADS (1..4; 2 = default)")
+    p.add_argument("--iters", type=int, default=4)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-slices", type=int, default=0,
+                   help="oracle slices for the CPU baseline (0 = 2 per thread)")
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path "
+              "shards by sequence or kv-head with no exchange, so per-GPU throughput is "
+              "the single-GPU figure. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import kv_cache_bit_kvarn_amd as kv
+    import kvgen
+
+    kv.load()
+    wl = kvgen.WORKLOADS[args.workload]
+    if args.workload == 0:
+        sys.exit("workload 0 is the oracle-sized parity case, not a benchmark")
+    steady = args.workload == 3           # cache built once; step = append + decode
+    dev = torch.device("cuda:0")
+    L, B, Hkv, Hq, T = wl.layers, wl.batch, wl.kv_heads, wl.q_heads, wl.tokens
+    cap = T + CHUNK
+    if steady and args.steps + args.warmup > CHUNK:
+        sys.exit("steady-state workload: steps + warmup must be <= 128")
+
+    log(f"[bench] workload {wl.name}: generating inputs on {dev} ...")
+    t0 = time.time()
+    xs, news, qs, caches = [], [], [], []
+    for layer in range(L):
+        xk = kvgen.kv_tensor(wl.seed, layer, kvgen.K, B, Hkv, T, wl.sigma, device=dev)
+        xv = kvgen.kv_tensor(wl.seed, layer, kvgen.V, B, Hkv, T, wl.sigma, device=dev)
+        xs.append((xk, xv))
+        news.append((kvgen.new_tokens(wl.seed, layer, kvgen.K, B, Hkv, wl.sigma, device=dev),
+                     kvgen.new_tokens(wl.seed, layer, kvgen.V, B, Hkv, wl.sigma, device=dev)))
+        qs.append(kvgen.queries(wl.seed, layer, B, Hq, device=dev))
+        caches.append((kv.Cache.empty(B, Hkv, cap, kv.K, device=dev),
+                       kv.Cache.empty(B, Hkv, cap, kv.V, device=dev)))
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    ws = kv.decode_workspace(B, Hq, cap, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs ready in {time.time() - t0:.1f}s "
+        f"({sum(x.numel() * 2 for p in xs for x in p) / 1e9:.2f} GB bf16 K/V)")
+
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    if steady:
+        for layer in range(L):
+            kv.quantize(xs[layer][0], caches[layer][0], iters=args.iters)
+            kv.quantize(xs[layer][1], caches[layer][1], iters=args.iters)
+        torch.cuda.synchronize()
+
+    def step(i: int, rec: dict | None):
+        p = (T + i) if steady else T
+        pos = torch.full((B,), p, dtype=torch.int32, device=dev)
+        lens = torch.full((B,), p + 1, dtype=torch.int32, device=dev)
+        for layer in range(L):
+            kc, vc = caches[layer]
+            if not steady:
+                for x, c in ((xs[layer][0], kc), (xs[layer][1], vc)):
+                    if rec is not None:
+                        a, b_ = ev(), ev()
+                        a.record(stream)
+                        kv.quantize(x, c, iters=args.iters, stream=stream)
+                        b_.record(stream)
+                        rec["quantize"].append((a, b_))
+                    else:
+                        kv.quantize(x, c, iters=args.iters, stream=stream)
+            for n, c in ((news[layer][0], kc), (news[layer][1], vc)):
+                if rec is not None:
+                    a, b_ = ev(), ev()
+                    a.record(stream)
+                    kv.append(n, pos, c, stream=stream)
+                    b_.record(stream)
+                    rec["append"].append((a, b_))
+                else:
+                    kv.append(n, pos, c, stream=stream)
+            if rec is not None:
+                a, b_ = ev(), ev()
+                a.record(stream)
+            kv.decode_attn(qs[layer], kc, vc, lens, out=out, workspace=ws, stream=stream)
+            if rec is not None:
+                b_.record(stream)
+                rec["decode"].append((a, b_))
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i, None)
+    torch.cuda.synchronize()
+
+    rec = {"quantize": [], "append": [], "decode": []}
+    log(f"[bench] timing {args.steps} steps")
+    start, end = ev(), ev()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, rec)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+
+    def avg_us(name):
+        v = [a.elapsed_time(b_) * 1e3 for a, b_ in rec[name]]
+        return (sum(v) / len(v)) if v else None
+
+    q_us, a_us, d_us = avg_us("quantize"), avg_us("append"), avg_us("decode")
+    elts_per_quant = B * Hkv * T * D
+    q_launches = 0 if steady else 2 * L
+    bf16_bytes_step = q_launches * elts_per_quant * 2
+    dec_tokens = (T + args.warmup + args.steps // 2 + 1) if steady else (T + 1)
+    dec_bytes = DECODE_BYTES_PER_TOKEN * dec_tokens * B * Hkv + B * Hq * D * (2 + 4)
+    decode_ms_step = L * d_us / 1e3
+
+    res = {
+        "metric": METRIC,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "layers": L, "batch": B, "kv_heads": Hkv,
+                   "q_heads": Hq, "head_dim": D, "tokens": T, "chunk": CHUNK,
+                   "balancing_iters": args.iters, "input_dtype": "bf16",
+                   "token_scale_sigma": wl.sigma,
+                   "step": "append+decode per layer" if steady else
+                           "quantize K,V + append + decode per layer"},
+    }
+    dec = {"tokens_per_s": round(B / (decode_ms_step / 1e3), 1),
+           "us_per_launch": round(d_us, 2), "launches_per_step": L,
+           "GBps_algorithmic": round(dec_bytes / (d_us * 1e-6) / 1e9, 1),
+           "hbm_frac": round(dec_bytes / (d_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+           "kernels": "decode_split_kernel + decode_combine_kernel"}
+    dec_roof = {"bound": "hbm", "achieved": dec["GBps_algorithmic"], "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": dec["hbm_frac"], "traffic": None,
+                "kernel": dec["kernels"], "bytes_per_launch": dec_bytes}
+    if steady:
+        res["value"] = dec["tokens_per_s"]
+        res["unit"] = "tokens/s (decode attention, all layers)"
+        res["step_tokens_per_s"] = round(B / (ms_step / 1e3), 1)
+        res["roofline"] = dec_roof
+    else:
+        qbytes = QUANT_BYTES_PER_ELT_BF16 * elts_per_quant
+        q_gbps = qbytes / (q_us * 1e-6) / 1e9
+        res["value"] = round(bf16_bytes_step / (ms_step / 1e3) / 1e9, 2)
+        res["unit"] = "GB/s (bf16 K/V in, whole quantize+append+decode step)"
+        res["quantize"] = {"GBps_bf16_in": round(elts_per_quant * 2 / (q_us * 1e-6) / 1e9, 1),
+                           "us_per_launch": round(q_us, 2), "launches_per_step": q_launches,
+                           "GBps_algorithmic": round(q_gbps, 1),
+                           "hbm_frac": round(q_gbps / HBM_PEAK_GBPS, 4)}
+        res["roofline"] = {"bound": "hbm", "achieved": round(q_gbps, 1),
+                           "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                           "frac": round(q_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                           "kernel": "quantize_block_kernel<bf16>",
+                           "bytes_per_launch": qbytes}
+        res["roofline_decode"] = dec_roof
+    res["decode"] = dec
+    res["append"] = {"us_per_launch": round(a_us, 2), "launches_per_step": 2 * L}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(args, wl, xs, news, qs, steady, res["unit"],
+                                           bf16_bytes_step, cap)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(args, wl, xs, news, qs, steady, unit, bf16_bytes_step, cap):
+    """The oracle (fp64 C, unmodified) timed on this host's cores on a bounded
+    sample of the same step: whole (layer 0, sequence b, kv-head g) slices --
+    quantize all chunks of K and V, append the new token, decode the group's
+    query heads -- run one slice per thread, then scaled to the full step."""
+    import numpy as np
+
+    import oracle
+
+    oracle.lib()
+    threads = max(1, min(16, os.cpu_count() or 1))
+    n = args.cpu_slices or 2 * threads
+    B, Hkv, Hq, T = wl.batch, wl.kv_heads, wl.q_heads, wl.tokens
+    G = Hq // Hkv
+    rng = np.random.default_rng(0)
+    pairs = [(int(rng.integers(B)), int(rng.integers(Hkv))) for _ in range(n)]
+    inputs = []
+    for b, g in pairs:
+        xk = xs[0][0][b:b + 1, g:g + 1].double().cpu().numpy()
+        xv = xs[0][1][b:b + 1, g:g + 1].double().cpu().numpy()
+        nk = news[0][0][b:b + 1, g:g + 1].double().cpu().numpy()
+        nv = news[0][1][b:b + 1, g:g + 1].double().cpu().numpy()
+        q = qs[0][b:b + 1, g * G:(g + 1) * G].double().cpu().numpy()
+        inputs.append((xk, xv, nk, nv, q))
+
+    def one(item):
+        xk, xv, nk, nv, q = item
+        outs = []
+        for x, nt in ((xk, nk), (xv, nv)):
+            o = oracle.quantize_tensor(x, iters=args.iters, want_u=False)
+            codes = np.zeros((1, 1, cap, D), np.uint8)
+            rp = np.zeros((1, 1, cap))
+            c = np.zeros((1, 1, cap // CHUNK, D))
+            codes[:, :, :T], rp[:, :, :T], c[:, :, :T // CHUNK] = o["codes"], o["rp"], o["c"]
+            oracle.append(nt, [T], codes, rp, c)
+            outs.append((codes, rp, c))
+        oracle.decode_attn(q, *outs[0], *outs[1], [T + 1])
+
+    work = list(inputs)
+    lock = threading.Lock()
+
+    def worker():
+        while True:
+            with lock:
+                if not work:
+                    return
+                item = work.pop()
+            one(item)
+
+    log(f"[bench] cpu baseline: {n} slices on {threads} threads ...")
+    t0 = time.perf_counter()
+    ts = [threading.Thread(target=worker) for _ in range(threads)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    wall = time.perf_counter() - t0
+    slices_per_step = wl.layers * B * Hkv
+    step_s = wall * slices_per_step / n
+    if steady:
+        value = B / step_s
+    else:
+        value = bf16_bytes_step / step_s / 1e9
+    return {"value": round(value, 6), "unit": unit, "cores": threads, "kind": "oracle",
+            "wall_s": round(wall, 2),
+            "sample": f"{n} whole (layer 0, seq, kv-head) slices of the step "
+                      f"(quantize {2 * T // CHUNK} chunks of K+V incl. the oracle's "
+                      f"O(D^2) rotation, append 1 token each, decode {G} query heads over "
+                      f"{T + 1} tokens), {threads} threads, scaled by "
+                      f"{slices_per_step}/{n} to the full step"}
+
+
+if __name__ == "__main__":
+    main()

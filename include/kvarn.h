@@ -1,0 +1,186 @@
+/*
+ * kvarn.h -- C ABI of libkvarn.so, the MI355X (gfx950) KVarN KV-cache
+ * quantizer and the 2-bit decode attention that reads its cache.
+ *
+ * The method (arXiv 2606.03458, "KVarN: Variance-Normalized KV-Cache
+ * Quantization Mitigates Error Accumulation in Reasoning Tasks"; abstract as
+ * carried by the codewithpapers.app record; rndamp.com article on KVarN,
+ * sections "How It Works" and "Numbers"): each per-head K or V block is
+ * rotated by a Hadamard transform along the channel dimension, balanced on
+ * both axes by an iterative dual scaling, and stored at 2 bits; the
+ * dequantization applies both scales inside the attention kernel. The
+ * quantizer needs no calibration data, so no call below takes any.
+ *
+ * Conventions shared by every call
+ *  - Pointers marked (device) are HIP device pointers; (host) are host
+ *    pointers read synchronously before the call returns.
+ *  - The caller allocates and owns every buffer. The library allocates no
+ *    device memory, keeps no state between calls and is reentrant across
+ *    streams (two calls that write the same cache on different streams race).
+ *  - `stream` is a hipStream_t (NULL = default stream). Every call only
+ *    enqueues work and returns; the library never synchronizes. Device faults
+ *    surface at the caller's next synchronization.
+ *  - Arguments are validated on the host before any HIP call. On a validation
+ *    error the call returns a negative kvarn_status and enqueues nothing.
+ *    A failed launch returns KVARN_ERR_HIP.
+ *  - head_dim is fixed at 128 and the chunk (block) length at 128 tokens.
+ */
+#ifndef KVARN_H
+#define KVARN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    KVARN_HEAD_DIM = 128,   /* channels per head (power of two for the rotation) */
+    KVARN_CHUNK = 128,      /* tokens per quantization block */
+    KVARN_CHUNK_BYTES = 4096 /* packed 2-bit codes of one 128 x 128 block */
+};
+
+typedef enum {
+    KVARN_OK = 0,
+    KVARN_ERR_NULL = -1,      /* a required pointer is NULL */
+    KVARN_ERR_SHAPE = -2,     /* a size, stride or count is out of range */
+    KVARN_ERR_ALIGN = -3,     /* a pointer or stride breaks 16-byte alignment */
+    KVARN_ERR_DTYPE = -4,     /* unknown dtype or cache kind */
+    KVARN_ERR_CAPACITY = -5,  /* tokens + token_offset exceed the cache capacity */
+    KVARN_ERR_WORKSPACE = -6, /* workspace smaller than kvarn_decode_workspace_bytes */
+    KVARN_ERR_HIP = -7        /* a HIP launch or query failed */
+} kvarn_status;
+
+typedef enum { KVARN_DT_BF16 = 0, KVARN_DT_F32 = 1 } kvarn_dtype;
+
+/* K caches store codes token-major, V caches channel-major (see below). */
+typedef enum { KVARN_K = 0, KVARN_V = 1 } kvarn_kind;
+
+/*
+ * One K or V cache of one layer. All three arrays are (device) memory owned
+ * by the caller; capacity % 128 == 0; every pointer 16-byte aligned.
+ *
+ * codes      [batch][kv_heads][capacity/128][4096] bytes. Four 2-bit codes
+ *            per byte, lowest bits first. Within a 128-token chunk:
+ *              K: token t owns bytes [32 t, 32 t + 32); channel j sits in
+ *                 byte 32 t + j/4 at bits 2 (j % 4);
+ *              V: channel j owns bytes [32 j, 32 j + 32); token t sits in
+ *                 byte 32 j + t/4 at bits 2 (t % 4).
+ *            Code q in {0,1,2,3} stands for the level (q - 1.5).
+ * row_scale  [batch][kv_heads][capacity] fp32: per-token scale r'_t.
+ * col_scale  [batch][kv_heads][capacity/128][128] fp32: per-chunk, per-channel
+ *            scale c_j.
+ * The stored value is reconstructed in the rotated basis as
+ *   y_hat[t][j] = (code[t][j] - 1.5) * row_scale[t] * col_scale[t/128][j]
+ * and in the original basis as y_hat . H_128 / sqrt(128), H_128 the
+ * Sylvester-order Hadamard matrix (the "two scales" of the rndamp article's
+ * "Numbers" section).
+ */
+typedef struct {
+    uint8_t *codes;
+    float *row_scale;
+    float *col_scale;
+    int32_t batch;
+    int32_t kv_heads;
+    int32_t capacity;
+    int32_t kind; /* kvarn_kind */
+} kvarn_cache;
+
+/*
+ * kvarn_quantize -- quantize whole 128-token chunks of K or V into a cache
+ * (abstract: Hadamard rotation followed by dual-scaling variance
+ * normalization across both axes, 2-bit; "How It Works", items 1 and 2).
+ *
+ * For every (b, h) and every chunk of x's tokens [0, tokens):
+ *   y  = x_chunk . H_128 / sqrt(128)                 (rotation per token)
+ *   c  = 1; repeat `iters` times:                    (dual scaling)
+ *          r_i^2 = mean_j y_ij^2 / c_j^2 ;  c_j^2 = mean_i y_ij^2 / r_i^2
+ *   r'_i = max_j |y_ij| / c_j / 2                    (per-token range step)
+ *   code = min(3, floor(y_ij / (r'_i c_j) + 2))      (4-level mid-rise grid)
+ * and store codes, r' and c at cache slots [token_offset, token_offset+tokens).
+ * A zero token row stores r' = 0 and code 2; a zero column keeps c_j = 1.
+ * Non-finite input gives unspecified codes and scales for its chunk.
+ *
+ * x          (device) input, dtype `dtype`, logical shape
+ *            [dst->batch][dst->kv_heads][tokens][128], element (b,h,t,j) at
+ *            x + b*stride_b + h*stride_h + t*stride_t + j (strides in elements,
+ *            channels contiguous). x must be 16-byte aligned and every stride
+ *            a multiple of 16 bytes.
+ * tokens, token_offset  multiples of 128; token_offset + tokens <= capacity.
+ *            tokens == 0 is a no-op.
+ * iters      balancing iterations, 0..64 (the spec default is 4; 0 keeps c = 1,
+ *            i.e. rotation and per-token step only).
+ * dst        (host) cache descriptor; its arrays are written, nothing is read.
+ */
+int kvarn_quantize(const void *x, int32_t dtype, int64_t stride_b,
+                   int64_t stride_h, int64_t stride_t, int32_t tokens,
+                   int32_t token_offset, int32_t iters, const kvarn_cache *dst,
+                   void *stream);
+
+/*
+ * kvarn_append -- quantize one new token per sequence into an existing cache
+ * (rndamp article, "The Problem": during decoding the cache grows one token
+ * per step and errors carry from step to step).
+ *
+ * For each (b, h): pos = positions[b]; skipped when pos is outside
+ * [0, capacity). chunk k = pos / 128. When pos % 128 == 0 the chunk is opened:
+ * its column scales are copied from chunk k-1 of the same (b, h), or set to 1
+ * for k == 0. The token is rotated and coded against chunk k's column scales
+ * with its own range step r' = max_j |y_j| / c_j / 2, exactly as in
+ * kvarn_quantize; the chunk is not re-balanced. In a V cache, a token with
+ * pos % 4 == 0 rewrites its whole byte (the three later token slots of that
+ * byte become code 0); other tokens replace only their own 2 bits.
+ *
+ * x          (device) [batch][kv_heads][128], dtype `dtype`, contiguous,
+ *            16-byte aligned.
+ * positions  (device) int32 [batch].
+ */
+int kvarn_append(const void *x, int32_t dtype, const int32_t *positions,
+                 const kvarn_cache *dst, void *stream);
+
+/*
+ * kvarn_decode_workspace_bytes -- (host only) bytes of device workspace that
+ * kvarn_decode_attn needs for these sizes (split-KV partial results). Returns
+ * 0 for invalid sizes.
+ */
+size_t kvarn_decode_workspace_bytes(int32_t batch, int32_t q_heads,
+                                    int32_t capacity);
+
+/*
+ * kvarn_decode_attn -- one decoding step of grouped-query attention over the
+ * 2-bit cache, dequantizing on the fly with both scales fused ("Numbers":
+ * the second scale is folded into the dequantization kernel).
+ *
+ * For each sequence b and query head h (kv-head g = h / (q_heads/kv_heads)):
+ *   s_t = softmax_scale * < q[b][h], K_hat[b][g][t] >   for t in [0, L_b)
+ *   out[b][h] = sum_t softmax(s)_t * V_hat[b][g][t]
+ * with K_hat, V_hat the caches' reconstructions in the original basis
+ * (L_b = seq_lens[b]). A sequence with L_b outside [1, capacity] gets a zero
+ * output row.
+ *
+ * q          (device) [batch][q_heads][128], dtype q_dtype, contiguous,
+ *            unrotated (post positional encoding).
+ * k, v       (host) descriptors of the K and V caches of one layer: same
+ *            batch, kv_heads and capacity; kinds KVARN_K and KVARN_V.
+ * seq_lens   (device) int32 [batch].
+ * out        (device) fp32 [batch][q_heads][128], original basis.
+ * n_split    number of token splits per (b, kv-head); 0 lets the library
+ *            choose. Clamped to [1, capacity/128].
+ * workspace  (device) at least kvarn_decode_workspace_bytes(batch, q_heads,
+ *            capacity) bytes, 16-byte aligned; contents are scratch.
+ */
+int kvarn_decode_attn(const void *q, int32_t q_dtype, int32_t q_heads,
+                      const kvarn_cache *k, const kvarn_cache *v,
+                      const int32_t *seq_lens, float softmax_scale, float *out,
+                      int32_t n_split, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/* kvarn_status_string -- (host only) static text for a kvarn_status. */
+const char *kvarn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVARN_H */

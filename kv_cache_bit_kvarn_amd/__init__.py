@@ -1,0 +1,199 @@
+"""Python binding of libkvarn.so, the MI355X KVarN quantizer and 2-bit decode
+attention (C ABI declared in include/kvarn.h).
+
+Argument marshalling only: torch tensors are used for device memory and
+streams; every step of the method runs in the library's HIP kernels. There is
+no fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvarn.so")
+
+HEAD_DIM = 128
+CHUNK = 128
+CHUNK_BYTES = 4096
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_CAPACITY, ERR_WORKSPACE, ERR_HIP = (
+    0, -1, -2, -3, -4, -5, -6, -7)
+DT_BF16, DT_F32 = 0, 1
+K, V = 0, 1
+
+EXPORTED = ("kvarn_quantize", "kvarn_append", "kvarn_decode_workspace_bytes",
+            "kvarn_decode_attn", "kvarn_status_string")
+
+
+class KvarnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("row_scale", ctypes.c_void_p),
+                ("col_scale", ctypes.c_void_p), ("batch", ctypes.c_int32),
+                ("kv_heads", ctypes.c_int32), ("capacity", ctypes.c_int32),
+                ("kind", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load(path: str | None = None):
+    """Load libkvarn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with kv_cache_bit_kvarn_amd/build.py "
+                           "(or __graft_entry__.build()); there is no fallback path")
+    L = ctypes.CDLL(p)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    cd = ctypes.POINTER(CacheDesc)
+    L.kvarn_quantize.argtypes = [vp, i32, i64, i64, i64, i32, i32, i32, cd, vp]
+    L.kvarn_quantize.restype = ctypes.c_int
+    L.kvarn_append.argtypes = [vp, i32, vp, cd, vp]
+    L.kvarn_append.restype = ctypes.c_int
+    L.kvarn_decode_workspace_bytes.argtypes = [i32, i32, i32]
+    L.kvarn_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.kvarn_decode_attn.argtypes = [vp, i32, i32, cd, cd, vp, ctypes.c_float, vp, i32,
+                                    vp, ctypes.c_size_t, vp]
+    L.kvarn_decode_attn.restype = ctypes.c_int
+    L.kvarn_status_string.argtypes = [ctypes.c_int]
+    L.kvarn_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return load().kvarn_status_string(int(status)).decode()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DT_BF16
+    if t.dtype == torch.float32:
+        return DT_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _raise(st: int, what: str):
+    if st != OK:
+        raise KvarnError(st, what)
+
+
+@dataclass
+class Cache:
+    """One layer's K or V cache: device tensors in the layout of kvarn.h."""
+    codes: torch.Tensor      # uint8 [B, H, cap/128, 4096]
+    row_scale: torch.Tensor  # f32 [B, H, cap]
+    col_scale: torch.Tensor  # f32 [B, H, cap/128, 128]
+    kind: int
+
+    @staticmethod
+    def empty(batch: int, kv_heads: int, capacity: int, kind: int, device="cuda",
+              zero: bool = True) -> "Cache":
+        nch = capacity // CHUNK
+        f = torch.zeros if zero else torch.empty
+        return Cache(f((batch, kv_heads, nch, CHUNK_BYTES), dtype=torch.uint8, device=device),
+                     f((batch, kv_heads, capacity), dtype=torch.float32, device=device),
+                     f((batch, kv_heads, nch, HEAD_DIM), dtype=torch.float32, device=device),
+                     kind)
+
+    @property
+    def batch(self):
+        return self.codes.shape[0]
+
+    @property
+    def kv_heads(self):
+        return self.codes.shape[1]
+
+    @property
+    def capacity(self):
+        return self.row_scale.shape[2]
+
+    def desc(self) -> CacheDesc:
+        for t in (self.codes, self.row_scale, self.col_scale):
+            if not t.is_contiguous():
+                raise ValueError("cache tensors must be contiguous")
+        return CacheDesc(self.codes.data_ptr(), self.row_scale.data_ptr(),
+                         self.col_scale.data_ptr(), self.batch, self.kv_heads,
+                         self.capacity, self.kind)
+
+
+def quantize(x: torch.Tensor, cache: Cache, token_offset: int = 0, iters: int = 4,
+             stream=None) -> None:
+    """x [B, H, tokens, 128] (bf16/fp32, channels contiguous) -> cache slots
+    [token_offset, token_offset + tokens)."""
+    if x.dim() != 4 or x.shape[3] != HEAD_DIM or x.stride(3) != 1:
+        raise ValueError("x must be [B, H, T, 128] with contiguous channels")
+    if x.shape[0] != cache.batch or x.shape[1] != cache.kv_heads:
+        raise ValueError("x batch/heads differ from the cache")
+    d = cache.desc()
+    st = load().kvarn_quantize(x.data_ptr(), _dtype_code(x), x.stride(0), x.stride(1),
+                               x.stride(2), x.shape[2], token_offset, iters,
+                               ctypes.byref(d), _stream(stream))
+    _raise(st, "kvarn_quantize")
+
+
+def append(x: torch.Tensor, positions: torch.Tensor, cache: Cache, stream=None) -> None:
+    """x [B, H, 128] new tokens at positions [B] (int32, device)."""
+    if x.dim() != 3 or tuple(x.shape) != (cache.batch, cache.kv_heads, HEAD_DIM) or \
+            not x.is_contiguous():
+        raise ValueError("x must be contiguous [B, H, 128] matching the cache")
+    if positions.dtype != torch.int32 or positions.numel() != cache.batch:
+        raise ValueError("positions must be int32 [B]")
+    d = cache.desc()
+    st = load().kvarn_append(x.data_ptr(), _dtype_code(x), positions.data_ptr(),
+                             ctypes.byref(d), _stream(stream))
+    _raise(st, "kvarn_append")
+
+
+def decode_workspace_bytes(batch: int, q_heads: int, capacity: int) -> int:
+    return int(load().kvarn_decode_workspace_bytes(batch, q_heads, capacity))
+
+
+def decode_workspace(batch: int, q_heads: int, capacity: int, device="cuda") -> torch.Tensor:
+    n = decode_workspace_bytes(batch, q_heads, capacity)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def decode_attn(q: torch.Tensor, k: Cache, v: Cache, seq_lens: torch.Tensor,
+                out: torch.Tensor | None = None, softmax_scale: float | None = None,
+                n_split: int = 0, workspace: torch.Tensor | None = None,
+                stream=None) -> torch.Tensor:
+    """q [B, Hq, 128] -> out fp32 [B, Hq, 128] (original basis)."""
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM or not q.is_contiguous():
+        raise ValueError("q must be contiguous [B, Hq, 128]")
+    if seq_lens.dtype != torch.int32 or seq_lens.numel() != k.batch:
+        raise ValueError("seq_lens must be int32 [B]")
+    B, Hq = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, k.capacity, q.device)
+    if softmax_scale is None:
+        softmax_scale = HEAD_DIM ** -0.5
+    kd, vd = k.desc(), v.desc()
+    st = load().kvarn_decode_attn(q.data_ptr(), _dtype_code(q), Hq, ctypes.byref(kd),
+                                  ctypes.byref(vd), seq_lens.data_ptr(), softmax_scale,
+                                  out.data_ptr(), n_split, workspace.data_ptr(),
+                                  workspace.numel() * workspace.element_size(),
+                                  _stream(stream))
+    _raise(st, "kvarn_decode_attn")
+    return out

@@ -1,0 +1,165 @@
+// extern "C" entry points of libkvarn.so: host-side validation, grid sizing,
+// launch. Every check runs before any HIP call; a failed check enqueues
+// nothing. The library allocates nothing and never synchronizes.
+#include <limits.h>
+
+#include "kvarn_internal.h"
+
+using namespace kvarn;
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_cache(const kvarn_cache *c) {
+  if (!c) return KVARN_ERR_NULL;
+  if (!c->codes || !c->row_scale || !c->col_scale) return KVARN_ERR_NULL;
+  if (c->kind != KVARN_K && c->kind != KVARN_V) return KVARN_ERR_DTYPE;
+  if (c->batch < 0 || c->kv_heads < 0 || c->capacity < 0 || c->capacity % T != 0)
+    return KVARN_ERR_SHAPE;
+  if (!aligned16(c->codes) || !aligned16(c->row_scale) || !aligned16(c->col_scale))
+    return KVARN_ERR_ALIGN;
+  return KVARN_OK;
+}
+
+int dtype_size(int32_t dtype) {
+  if (dtype == KVARN_DT_BF16) return 2;
+  if (dtype == KVARN_DT_F32) return 4;
+  return 0;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? KVARN_OK : KVARN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int kvarn_quantize(const void *x, int32_t dtype, int64_t stride_b, int64_t stride_h,
+                   int64_t stride_t, int32_t tokens, int32_t token_offset, int32_t iters,
+                   const kvarn_cache *dst, void *stream) {
+  if (!x) return KVARN_ERR_NULL;
+  int st = check_cache(dst);
+  if (st != KVARN_OK) return st;
+  const int esz = dtype_size(dtype);
+  if (!esz) return KVARN_ERR_DTYPE;
+  if (tokens < 0 || token_offset < 0 || tokens % T || token_offset % T) return KVARN_ERR_SHAPE;
+  if (iters < 0 || iters > 64) return KVARN_ERR_SHAPE;
+  if (stride_b < 0 || stride_h < 0 || stride_t < D) return KVARN_ERR_SHAPE;
+  if ((int64_t)tokens + token_offset > dst->capacity) return KVARN_ERR_CAPACITY;
+  if (!aligned16(x) || (stride_b * esz) % 16 || (stride_h * esz) % 16 || (stride_t * esz) % 16)
+    return KVARN_ERR_ALIGN;
+  const int64_t blocks = (int64_t)dst->batch * dst->kv_heads * (tokens / T);
+  if (blocks > INT_MAX) return KVARN_ERR_SHAPE;
+  if (blocks == 0) return KVARN_OK;
+  QuantArgs a;
+  a.x = x;
+  a.dtype = dtype;
+  a.sb = stride_b;
+  a.sh = stride_h;
+  a.st = stride_t;
+  a.batch = dst->batch;
+  a.heads = dst->kv_heads;
+  a.chunks = tokens / T;
+  a.chunk0 = token_offset / T;
+  a.iters = iters;
+  a.capacity = dst->capacity;
+  a.kind = dst->kind;
+  a.codes = dst->codes;
+  a.row_scale = dst->row_scale;
+  a.col_scale = dst->col_scale;
+  return from_hip(launch_quantize(a, static_cast<hipStream_t>(stream)));
+}
+
+int kvarn_append(const void *x, int32_t dtype, const int32_t *positions,
+                 const kvarn_cache *dst, void *stream) {
+  if (!x || !positions) return KVARN_ERR_NULL;
+  int st = check_cache(dst);
+  if (st != KVARN_OK) return st;
+  if (!dtype_size(dtype)) return KVARN_ERR_DTYPE;
+  if (!aligned16(x)) return KVARN_ERR_ALIGN;
+  if ((int64_t)dst->batch * dst->kv_heads > INT_MAX) return KVARN_ERR_SHAPE;
+  if (dst->batch == 0 || dst->kv_heads == 0 || dst->capacity == 0) return KVARN_OK;
+  AppendArgs a;
+  a.x = x;
+  a.dtype = dtype;
+  a.pos = positions;
+  a.batch = dst->batch;
+  a.heads = dst->kv_heads;
+  a.capacity = dst->capacity;
+  a.kind = dst->kind;
+  a.codes = dst->codes;
+  a.row_scale = dst->row_scale;
+  a.col_scale = dst->col_scale;
+  return from_hip(launch_append(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t kvarn_decode_workspace_bytes(int32_t batch, int32_t q_heads, int32_t capacity) {
+  if (batch < 0 || q_heads < 0 || capacity < 0 || capacity % T) return 0;
+  return (size_t)batch * q_heads * (size_t)(capacity / T) * (2 + D) * sizeof(float);
+}
+
+int kvarn_decode_attn(const void *q, int32_t q_dtype, int32_t q_heads, const kvarn_cache *k,
+                      const kvarn_cache *v, const int32_t *seq_lens, float softmax_scale,
+                      float *out, int32_t n_split, void *workspace, size_t workspace_bytes,
+                      void *stream) {
+  if (!q || !seq_lens || !out) return KVARN_ERR_NULL;
+  int st = check_cache(k);
+  if (st != KVARN_OK) return st;
+  st = check_cache(v);
+  if (st != KVARN_OK) return st;
+  if (k->kind != KVARN_K || v->kind != KVARN_V) return KVARN_ERR_DTYPE;
+  if (!dtype_size(q_dtype)) return KVARN_ERR_DTYPE;
+  if (k->batch != v->batch || k->kv_heads != v->kv_heads || k->capacity != v->capacity)
+    return KVARN_ERR_SHAPE;
+  if (q_heads <= 0 || k->kv_heads <= 0 || q_heads % k->kv_heads) return KVARN_ERR_SHAPE;
+  if (q_heads / k->kv_heads > GQA_MAX) return KVARN_ERR_SHAPE;
+  if (k->capacity <= 0 || k->batch > 65535 || k->kv_heads > 65535 || q_heads > 65535)
+    return KVARN_ERR_SHAPE;
+  if (!(softmax_scale == softmax_scale)) return KVARN_ERR_SHAPE;  // NaN
+  if (!aligned16(q) || !aligned16(out)) return KVARN_ERR_ALIGN;
+  if (n_split < 0) return KVARN_ERR_SHAPE;
+  if (k->batch == 0) return KVARN_OK;
+  const int nch = k->capacity / T;
+  int ns = n_split == 0 ? decode_auto_splits(k->batch, k->kv_heads, k->capacity) : n_split;
+  if (ns > nch) ns = nch;
+  if (ns < 1) ns = 1;
+  const size_t need = kvarn_decode_workspace_bytes(k->batch, q_heads, k->capacity);
+  if (!workspace) return KVARN_ERR_NULL;
+  if (workspace_bytes < need) return KVARN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return KVARN_ERR_ALIGN;
+  DecodeArgs a;
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.batch = k->batch;
+  a.q_heads = q_heads;
+  a.kv_heads = k->kv_heads;
+  a.capacity = k->capacity;
+  a.n_split = ns;
+  a.k_codes = k->codes;
+  a.v_codes = v->codes;
+  a.k_row = k->row_scale;
+  a.k_col = k->col_scale;
+  a.v_row = v->row_scale;
+  a.v_col = v->col_scale;
+  a.lens = seq_lens;
+  a.scale = softmax_scale;
+  a.out = out;
+  a.partial = static_cast<float *>(workspace);
+  return from_hip(launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+const char *kvarn_status_string(int status) {
+  switch (status) {
+    case KVARN_OK: return "ok";
+    case KVARN_ERR_NULL: return "null pointer argument";
+    case KVARN_ERR_SHAPE: return "size, stride or count out of range";
+    case KVARN_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
+    case KVARN_ERR_DTYPE: return "unknown dtype or cache kind";
+    case KVARN_ERR_CAPACITY: return "tokens + token_offset exceed the cache capacity";
+    case KVARN_ERR_WORKSPACE: return "workspace smaller than kvarn_decode_workspace_bytes";
+    case KVARN_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

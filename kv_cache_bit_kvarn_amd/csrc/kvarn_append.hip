@@ -1,0 +1,117 @@
+// One-token append into a KVarN cache on gfx950 (rndamp article on KVarN,
+// "The Problem": the cache grows by one token per decoding step).
+//
+// One wave64 per (sequence, kv-head): lane l holds channels l and l + 64.
+// The token is rotated (Hadamard, unscaled: the 1/sqrt(128) is folded into
+// the row scale as in the block quantizer), coded against the column scales
+// of its chunk (copied forward from the previous chunk when the token opens
+// a chunk), with its own per-token range step. The block is never
+// re-balanced.
+#include "kvarn_internal.h"
+
+namespace kvarn {
+namespace {
+
+__device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+
+template <bool kF32>
+__global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
+  const int bh = blockIdx.x;
+  const int b = bh / a.heads;
+  const int lane = threadIdx.x;
+  const int pos = a.pos[b];
+  if (pos < 0 || pos >= a.capacity) return;  // uniform across the wave
+  const int k = pos / T, slot = pos - k * T;
+  const int64_t nch = a.capacity / T;
+
+  float y0, y1;  // channels lane, lane + 64
+  if constexpr (kF32) {
+    const float *x = static_cast<const float *>(a.x) + (int64_t)bh * D;
+    y0 = x[lane];
+    y1 = x[lane + 64];
+  } else {
+    const uint16_t *x = static_cast<const uint16_t *>(a.x) + (int64_t)bh * D;
+    y0 = __uint_as_float((uint32_t)x[lane] << 16);
+    y1 = __uint_as_float((uint32_t)x[lane + 64] << 16);
+  }
+  // rotation: channel bit 6 inside the lane, bits 0..5 across lanes
+  {
+    const float s = y0 + y1, d = y0 - y1;
+    y0 = s;
+    y1 = d;
+  }
+#pragma unroll
+  for (int bit = 1; bit < 64; bit <<= 1) {
+    const float p0 = shfl_xor(y0, bit), p1 = shfl_xor(y1, bit);
+    const bool hi = (lane & bit) != 0;
+    y0 = hi ? p0 - y0 : y0 + p0;
+    y1 = hi ? p1 - y1 : y1 + p1;
+  }
+
+  float *col = a.col_scale + ((int64_t)bh * nch + k) * D;
+  float c0, c1;
+  if (slot == 0) {
+    if (k > 0) {
+      c0 = col[lane - D];
+      c1 = col[lane + 64 - D];
+    } else {
+      c0 = 1.f;
+      c1 = 1.f;
+    }
+    col[lane] = c0;
+    col[lane + 64] = c1;
+  } else {
+    c0 = col[lane];
+    c1 = col[lane + 64];
+  }
+  const float z0 = y0 * (1.f / c0), z1 = y1 * (1.f / c1);
+  float m = fmaxf(fabsf(z0), fabsf(z1));
+#pragma unroll
+  for (int bit = 1; bit < 64; bit <<= 1) m = fmaxf(m, shfl_xor(m, bit));
+  if (lane == 0) a.row_scale[(int64_t)bh * a.capacity + pos] = m * kRangeFromUnscaled;
+  const float qs = m > 0.f ? 2.f / m : 0.f;
+  const uint32_t q0 = (uint32_t)fminf(fmaxf(fmaf(z0, qs, 2.f), 0.f), 3.f);
+  const uint32_t q1 = (uint32_t)fminf(fmaxf(fmaf(z1, qs, 2.f), 0.f), 3.f);
+
+  uint8_t *cb = a.codes + ((int64_t)bh * nch + k) * CHUNK_BYTES;
+  if (a.kind == KVARN_K) {
+    // token row: channel j -> byte j/4, bits 2 (j % 4). Lane l gathers the
+    // four codes of channels 4l..4l+3 (l < 16) or 64 + 4(l-16).. (l < 32).
+    const int src = 4 * (lane & 15);
+    uint32_t byte = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t v0 = (uint32_t)__shfl((int)q0, src + r, 64);
+      const uint32_t v1 = (uint32_t)__shfl((int)q1, src + r, 64);
+      byte |= ((lane < 16) ? v0 : v1) << (2 * r);
+    }
+    if (lane < 32) cb[slot * 32 + lane] = (uint8_t)byte;
+  } else {
+    // channel row j: token slot s -> byte s/4, bits 2 (s % 4)
+    const int sh = 2 * (slot & 3);
+    uint8_t *p0 = cb + lane * 32 + (slot >> 2);
+    uint8_t *p1 = cb + (lane + 64) * 32 + (slot >> 2);
+    if (sh == 0) {
+      *p0 = (uint8_t)q0;
+      *p1 = (uint8_t)q1;
+    } else {
+      const uint32_t keep = ~(3u << sh) & 0xFFu;
+      *p0 = (uint8_t)((*p0 & keep) | (q0 << sh));
+      *p1 = (uint8_t)((*p1 & keep) | (q1 << sh));
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendArgs &a, hipStream_t s) {
+  const int blocks = a.batch * a.heads;
+  if (blocks == 0) return hipSuccess;
+  if (a.dtype == KVARN_DT_F32)
+    hipLaunchKernelGGL(append_kernel<true>, dim3(blocks), dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL(append_kernel<false>, dim3(blocks), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace kvarn

@@ -1,0 +1,69 @@
+// Internal declarations shared by the HIP translation units of libkvarn.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvarn.h"
+
+namespace kvarn {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int D = KVARN_HEAD_DIM;      // channels per head
+constexpr int T = KVARN_CHUNK;         // tokens per block
+constexpr int CHUNK_BYTES = KVARN_CHUNK_BYTES;
+constexpr int GQA_MAX = 8;             // query heads per kv-head supported by decode
+
+// 1/sqrt(128)/2 = 2^-4.5: the rotation is applied unscaled on the device
+// (y' = sqrt(128) y); the range step r' = max|y/c|/2 then becomes
+// max|y'/c| * 2^-4.5, while c and every code are unchanged by that factor.
+constexpr float kRangeFromUnscaled = 0.044194173824159216f;
+constexpr float kInvSqrtD = 0.088388347648318447f;  // 1/sqrt(128)
+
+// ---- cross-lane helpers (DPP on gfx950, wave64) -------------------------
+__device__ __forceinline__ float dpp_xor1(float v) {
+  // quad_perm [1,0,3,2]: lane i reads lane i^1
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+// ---- launchers (validated arguments only) --------------------------------
+struct QuantArgs {
+  const void *x;
+  int dtype;
+  int64_t sb, sh, st;
+  int batch, heads, chunks, chunk0, iters, capacity, kind;
+  uint8_t *codes;
+  float *row_scale, *col_scale;
+};
+hipError_t launch_quantize(const QuantArgs &a, hipStream_t s);
+
+struct AppendArgs {
+  const void *x;
+  int dtype;
+  const int32_t *pos;
+  int batch, heads, capacity, kind;
+  uint8_t *codes;
+  float *row_scale, *col_scale;
+};
+hipError_t launch_append(const AppendArgs &a, hipStream_t s);
+
+struct DecodeArgs {
+  const void *q;
+  int q_dtype, batch, q_heads, kv_heads, capacity, n_split;
+  const uint8_t *k_codes, *v_codes;
+  const float *k_row, *k_col, *v_row, *v_col;
+  const int32_t *lens;
+  float scale;
+  float *out;
+  float *partial;  // [batch][q_heads][n_split][2 + D]
+};
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+int decode_auto_splits(int batch, int kv_heads, int capacity);
+
+}  // namespace kvarn
