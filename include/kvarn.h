@@ -108,7 +108,7 @@ typedef struct {
  *            channels contiguous). x must be 16-byte aligned and every stride
  *            a multiple of 16 bytes.
  * tokens, token_offset  multiples of 128; token_offset + tokens <= capacity.
- *            tokens == 0 is a no-op.
+ *            tokens == 0 is a no-op (x may then be NULL).
  * iters      balancing iterations, 0..64 (the spec default is 4; 0 keeps c = 1,
  *            i.e. rotation and per-token step only).
  * dst        (host) cache descriptor; its arrays are written, nothing is read.

@@ -37,9 +37,10 @@ extern "C" {
 int kvarn_quantize(const void *x, int32_t dtype, int64_t stride_b, int64_t stride_h,
                    int64_t stride_t, int32_t tokens, int32_t token_offset, int32_t iters,
                    const kvarn_cache *dst, void *stream) {
-  if (!x) return KVARN_ERR_NULL;
   int st = check_cache(dst);
   if (st != KVARN_OK) return st;
+  if (tokens == 0) return KVARN_OK;  // nothing to read or write; x may be NULL
+  if (!x) return KVARN_ERR_NULL;
   const int esz = dtype_size(dtype);
   if (!esz) return KVARN_ERR_DTYPE;
   if (tokens < 0 || token_offset < 0 || tokens % T || token_offset % T) return KVARN_ERR_SHAPE;
@@ -61,6 +62,9 @@ int kvarn_quantize(const void *x, int32_t dtype, int64_t stride_b, int64_t strid
   a.heads = dst->kv_heads;
   a.chunks = tokens / T;
   a.chunk0 = token_offset / T;
+  a.nblocks = (uint32_t)blocks;
+  a.div_chunks = make_fastdiv((uint32_t)a.chunks);
+  a.div_heads = make_fastdiv((uint32_t)a.heads);
   a.iters = iters;
   a.capacity = dst->capacity;
   a.kind = dst->kind;

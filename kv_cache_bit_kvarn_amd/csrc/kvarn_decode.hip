@@ -12,20 +12,107 @@
 // row scale of V into each probability, and the column scale of V into the
 // output; the output is rotated back after the split-KV merge.
 //
-// decode_split: grid (n_split, kv_heads, batch); each workgroup walks its
-// range of 128-token chunks with an online softmax and writes one partial
-// (m, l, acc[128]) per query head. decode_combine: grid (q_heads, batch);
-// log-sum-exp merge of the partials, then the inverse rotation.
+// decode_split: grid (n_split, kv_heads, batch), one wave64 per workgroup,
+// walking its range of 128-token chunks with an online softmax; the next
+// chunk's codes and scales are loaded while the current one is computed.
+// QK^T and PV run on v_mfma_f32_16x16x32_f16:
+//  * code operand: a 32-bit word holds 16 codes; AND-ing it with a mask that
+//    keeps one 2-bit field in each 16-bit half yields two fp16 subnormals
+//    c * 4^i * 2^-24 (i = the field's position), exactly. Eight masks (one
+//    shift) turn a word into the operand registers of two MFMA k-steps.
+//  * the other operand (query * c_K, or p * r'_V) carries 4^-i, a power-of-
+//    two range scale 2^sigma, and (query only) an fp16 hi/lo split, run as
+//    two k-passes over the same code registers, so scores keep ~22 bits;
+//  * the -1.5 offset of the levels is one more MFMA per chunk against a
+//    constant operand that encodes code 1 in every field.
+// decode_combine: grid (q_heads, batch): log-sum-exp merge of the partials
+// (m, l, acc[128]), then the inverse rotation.
 #include "kvarn_internal.h"
 
 namespace kvarn {
 namespace {
 
-constexpr int kThreads = 256;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
 constexpr float kLog2e = 1.4426950408889634f;
 
-// In-place Sylvester Hadamard transform (unscaled) of rows x[n][128] held in
-// LDS, all threads of the block cooperating.
+// ---- code word -> fp16 subnormal operands --------------------------------
+// A code word w holds codes c_0..c_15 at bits 2m. Output dwords (two fp16 each,
+// low half first):
+//   o[i]   = (c_i, c_{8+i}) * 4^i        i = 0..3   (k-step half 0)
+//   o[4]   = (c_4, c_12)    * 4^4                   (k-step half 1)
+//   o[5+i] = (c_{5+i}, c_{13+i}) * 4^i  i = 0..2   (k-step half 1)
+// all times 2^-24. The field scale of code index c is 4^f(c % 8) with
+// f = {0, 1, 2, 3, 4, 0, 1, 2}.
+__device__ __forceinline__ void unpack_codes(uint32_t w, u32x4 &h0, u32x4 &h1) {
+  const uint32_t x = w >> 10;
+  h0[0] = w & 0x00030003u;
+  h0[1] = w & 0x000C000Cu;
+  h0[2] = w & 0x00300030u;
+  h0[3] = w & 0x00C000C0u;
+  h1[0] = w & 0x03000300u;
+  h1[1] = x & 0x00030003u;
+  h1[2] = x & 0x000C000Cu;
+  h1[3] = x & 0x00300030u;
+}
+
+__host__ __device__ constexpr int field_exp(int c) {  // f(c % 8)
+  return (c & 7) < 5 ? (c & 7) : (c & 7) - 5;
+}
+
+// code index (0..15 within a word) held by k-slot e of k-step half hs
+__device__ __forceinline__ int slot_code(int hs, int e) {
+  if (hs == 0) return (e & 1) ? 8 + (e >> 1) : (e >> 1);
+  if (e < 2) return e ? 12 : 4;
+  return (e & 1) ? 13 + ((e - 3) >> 1) : 5 + ((e - 2) >> 1);
+}
+
+// lane-group g (0..3) covers code words 2g, 2g+1 of a row, i.e. elements
+// [32 g, 32 g + 32); k-step s (0..3) takes word 2g + (s >> 1), half s & 1.
+__device__ __forceinline__ int kslot_elem(int g, int s, int e) {
+  return 32 * g + 16 * (s >> 1) + slot_code(s & 1, e);
+}
+
+// position of element j in the [g][s][e] order of kslot_elem
+__device__ __forceinline__ int elem_slot_pos(int j) {
+  const int g = j >> 5, w = (j >> 4) & 1, c = j & 15;
+  int hs, e;
+  if (c < 4) { hs = 0; e = 2 * c; }
+  else if (c >= 8 && c < 12) { hs = 0; e = 2 * (c - 8) + 1; }
+  else if (c == 4) { hs = 1; e = 0; }
+  else if (c == 12) { hs = 1; e = 1; }
+  else if (c < 8) { hs = 1; e = 2 + 2 * (c - 5); }
+  else { hs = 1; e = 3 + 2 * (c - 13); }
+  return ((g * 4) + 2 * w + hs) * 8 + e;
+}
+
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
+
+__device__ __forceinline__ uint32_t pack_rtz(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
+__device__ __forceinline__ f32x4 mfma(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+// power-of-two scale 2^sigma with max * 2^sigma in [2^14, 2^15) (1 if max == 0)
+__device__ __forceinline__ float range_scale(float mx, int &sigma) {
+  sigma = 0;
+  if (mx > 0.f) {
+    sigma = 15 - __builtin_amdgcn_frexp_expf(mx);
+    sigma = sigma > 100 ? 100 : (sigma < -100 ? -100 : sigma);
+  }
+  return __builtin_ldexpf(1.f, sigma);
+}
+
+// In-place Sylvester Hadamard transform (unscaled) of rows x[n][128] in LDS.
 __device__ void lds_fwht_rows(float *x, int n) {
   for (int len = 1; len < D; len <<= 1) {
     for (int idx = threadIdx.x; idx < n * (D / 2); idx += blockDim.x) {
@@ -45,30 +132,49 @@ __device__ __forceinline__ float load_q(const void *q, int dtype, int64_t idx) {
   return __uint_as_float((uint32_t)static_cast<const uint16_t *>(q)[idx] << 16);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
-  return v;
-}
-
-struct SplitSmem {
-  float qh[GQA_MAX][D];  // rotated query * softmax scale * log2(e)
-  float a[GQA_MAX][D];   // qh * c_K of the current chunk
-  float s[GQA_MAX][T];   // scores (log2 units), then p * r'_V
-  float colk[D], colv[D], rowk[T], rowv[T];
-  float m[GQA_MAX], l[GQA_MAX], alpha[GQA_MAX];
+template <int GP>
+struct DecSmem {
+  float qt[GP][D];            // rotated, scaled query (setup only)
+  float ck[D];                // c_K in [g][s][e] order
+  float cv[16][8];            // cv[n][ct] = c_V[16 ct + n]
+  float rk[T];                // r'_K
+  float rv[T];                // r'_V * 4^-f(t % 8)
+  float sc[GP][T];            // raw QK results, then P' (fp32, natural order)
+  uint32_t ahi[GP][4][4][4];  // query operand, fp16 pairs, [m][g][s][dword]
+  uint32_t alo[GP][4][4][4];
+  float dc[GP];               // QK offset term per head
+  float alpha[GP];
 };
 
-template <int HPT>  // query heads per thread: ceil(G / 2)
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
-  __shared__ SplitSmem sm;
+struct ChunkRegs {
+  u32x2 k[8];  // K code words 2g, 2g+1 of token 16 tau + n
+  u32x2 v[8];  // V code words 2g, 2g+1 of channel 16 ct + n
+  u32x2 ck, cv, rk, rv;  // scales of elements 2l, 2l+1
+};
+
+__device__ __forceinline__ void load_chunk(const DecodeArgs &a, int64_t bg, int64_t nchunks, int k,
+                                           int lane, ChunkRegs &r) {
+  const int64_t chunk = bg * nchunks + k;
+  const int n = lane & 15, g = lane >> 4;
+  const uint8_t *kc = a.k_codes + chunk * CHUNK_BYTES + n * 32 + 8 * g;
+  const uint8_t *vc = a.v_codes + chunk * CHUNK_BYTES + n * 32 + 8 * g;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    r.k[t] = *reinterpret_cast<const u32x2 *>(kc + t * 16 * 32);
+    r.v[t] = *reinterpret_cast<const u32x2 *>(vc + t * 16 * 32);
+  }
+  r.ck = *reinterpret_cast<const u32x2 *>(a.k_col + chunk * D + 2 * lane);
+  r.cv = *reinterpret_cast<const u32x2 *>(a.v_col + chunk * D + 2 * lane);
+  const int64_t row = bg * (int64_t)a.capacity + (int64_t)k * T + 2 * lane;
+  r.rk = *reinterpret_cast<const u32x2 *>(a.k_row + row);
+  r.rv = *reinterpret_cast<const u32x2 *>(a.v_row + row);
+}
+
+template <int GP>
+__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
+  __shared__ DecSmem<GP> sm;
+  const int lane = threadIdx.x;
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x;
   const int G = a.q_heads / a.kv_heads;
   const int nch = a.capacity / T;
   const int len = a.lens[b];
@@ -77,127 +183,242 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   const int per = (nch + a.n_split - 1) / a.n_split;
   const int c0 = split * per;
   const int c1 = min(c0 + per, used);
-
-  // query: rotate, fold the softmax scale and log2(e)
-  for (int idx = tid; idx < G * D; idx += kThreads) {
-    const int hh = idx / D, j = idx - hh * D;
-    sm.qh[hh][j] = load_q(a.q, a.q_dtype, ((int64_t)b * a.q_heads + g * G + hh) * D + j);
-  }
-  if (tid < GQA_MAX) {
-    sm.m[tid] = -INFINITY;
-    sm.l[tid] = 0.f;
-    sm.alpha[tid] = 1.f;
-  }
-  __syncthreads();
-  lds_fwht_rows(&sm.qh[0][0], G);
-  const float qscale = a.scale * kLog2e * kInvSqrtD;
-  for (int idx = tid; idx < G * D; idx += kThreads) sm.qh[idx / D][idx % D] *= qscale;
-
-  const int j = tid & (D - 1);    // PV role: channel j
-  const int h0 = tid >> 7;        // heads h0, h0 + 2, ...
-  const int tt = tid & (T - 1);   // QK role: token tt
-  float acc[HPT];
-#pragma unroll
-  for (int r = 0; r < HPT; ++r) acc[r] = 0.f;
-
   const int64_t bg = (int64_t)b * a.kv_heads + g;
-  for (int k = c0; k < c1; ++k) {
-    const int64_t chunk = bg * nch + k;
-    __syncthreads();  // previous chunk done with the LDS
-    if (tid < D) {
-      sm.colk[tid] = a.k_col[chunk * D + tid];
-      sm.colv[tid] = a.v_col[chunk * D + tid];
-    } else {
-      const int t = tid - D;
-      sm.rowk[t] = a.k_row[bg * a.capacity + (int64_t)k * T + t];
-      sm.rowv[t] = a.v_row[bg * a.capacity + (int64_t)k * T + t];
-    }
-    __syncthreads();
-    for (int idx = tid; idx < 2 * HPT * D; idx += kThreads) {
-      const int hh = idx / D, jj = idx - hh * D;
-      sm.a[hh][jj] = hh < G ? sm.qh[hh][jj] * sm.colk[jj] : 0.f;
-      sm.s[hh][jj] = 0.f;
-    }
-    __syncthreads();
 
-    // ---- scores: s_t = r'_t * sum_j a_j (code_tj - 1.5) ----
-    {
-      const uint32_t *row = reinterpret_cast<const uint32_t *>(a.k_codes + chunk * CHUNK_BYTES + tt * 32);
-      const bool live = k * T + tt < len;
-      float s[HPT];
-#pragma unroll
-      for (int r = 0; r < HPT; ++r) s[r] = 0.f;
-#pragma unroll 1
-      for (int d = 0; d < 8; ++d) {
-        const uint32_t wdd = row[d];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float cv = (float)((wdd >> (2 * e)) & 3u) - 1.5f;
-#pragma unroll
-          for (int r = 0; r < HPT; ++r) s[r] = fmaf(sm.a[h0 + 2 * r][16 * d + e], cv, s[r]);
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < HPT; ++r)
-        if (h0 + 2 * r < G) sm.s[h0 + 2 * r][tt] = live ? s[r] * sm.rowk[tt] : -INFINITY;
-    }
-    __syncthreads();
-
-    // ---- online softmax, one wave per head ----
-    {
-      const int wv = tid >> 6, lane = tid & 63;
-      for (int hh = wv; hh < G; hh += kThreads / 64) {
-        const float s0 = sm.s[hh][lane], s1 = sm.s[hh][lane + 64];
-        const float mc = wave_max(fmaxf(s0, s1));
-        const float mo = sm.m[hh];
-        const float mn = fmaxf(mo, mc);
-        const float al = (mn == -INFINITY) ? 1.f : exp2f(mo - mn);
-        const float p0 = (mn == -INFINITY) ? 0.f : exp2f(s0 - mn);
-        const float p1 = (mn == -INFINITY) ? 0.f : exp2f(s1 - mn);
-        const float ps = wave_sum(p0 + p1);
-        sm.s[hh][lane] = p0 * sm.rowv[lane];
-        sm.s[hh][lane + 64] = p1 * sm.rowv[lane + 64];
-        if (lane == 0) {
-          sm.alpha[hh] = al;
-          sm.m[hh] = mn;
-          sm.l[hh] = sm.l[hh] * al + ps;
-        }
-      }
-    }
-    __syncthreads();
-
-    // ---- acc_j = acc_j * alpha + c_j * sum_t P_t (code_tj - 1.5) ----
-    {
-      const uint32_t *row = reinterpret_cast<const uint32_t *>(a.v_codes + chunk * CHUNK_BYTES + j * 32);
-      float s[HPT];
-#pragma unroll
-      for (int r = 0; r < HPT; ++r) s[r] = 0.f;
-#pragma unroll 1
-      for (int d = 0; d < 8; ++d) {
-        const uint32_t wdd = row[d];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float cv = (float)((wdd >> (2 * e)) & 3u) - 1.5f;
-#pragma unroll
-          for (int r = 0; r < HPT; ++r) s[r] = fmaf(sm.s[h0 + 2 * r][16 * d + e], cv, s[r]);
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < HPT; ++r) acc[r] = acc[r] * sm.alpha[h0 + 2 * r] + sm.colv[j] * s[r];
-    }
+  // ---- query: rotate; fold softmax scale, log2(e), 1/sqrt(128), 4^-f -----
+  for (int idx = lane; idx < GP * D; idx += 64) {
+    const int m = idx / D, j = idx - m * D;
+    sm.qt[m][j] = m < G ? load_q(a.q, a.q_dtype, ((int64_t)b * a.q_heads + g * G + m) * D + j) : 0.f;
   }
   __syncthreads();
-  // partial: [b][h][split][m, l, acc[128]]
+  lds_fwht_rows(&sm.qt[0][0], GP);
+  // this lane's a-operand units: head mu = (lane & 3) + 4u, group gu, k-step su
+  const int gu = (lane >> 2) & 3, su = lane >> 4;
+  constexpr int NU = GP / 4;
+  float qh[NU][8];
   {
+    const float qs = a.scale * kLog2e * kInvSqrtD;
 #pragma unroll
-    for (int r = 0; r < HPT; ++r) {
-      const int hh = h0 + 2 * r;
-      if (hh >= G) break;
-      float *pp = a.partial + (((int64_t)b * a.q_heads + g * G + hh) * a.n_split + split) * (2 + D);
-      pp[2 + j] = acc[r];
-      if (j == 0) {
-        pp[0] = sm.m[hh];
-        pp[1] = sm.l[hh];
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = kslot_elem(gu, su, e);
+        qh[u][e] = sm.qt[(lane & 3) + 4 * u][j] * qs * __builtin_ldexpf(1.f, -2 * field_exp(j));
+      }
+  }
+  // constant operand: code 1 in every field (the level offset term)
+  u32x4 one0, one1;
+  unpack_codes(0x55555555u, one0, one1);
+
+  // state: lanes 16 r' .. hold heads 4 (lane >> 4) + r of channel 16 ct + (lane & 15)
+  f32x4 acc[8];
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  constexpr int LPH = 64 / GP;  // softmax: lanes per head
+  constexpr int TPL = T / LPH;  // tokens per lane
+  const int sh = lane / LPH;    // softmax head of this lane
+  const int st0 = (lane % LPH) * TPL;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  ChunkRegs cur, nxt;
+  if (c0 < c1) load_chunk(a, bg, nch, c0, lane, cur);
+  const int n = lane & 15, lg = lane >> 4;
+  for (int k = c0; k < c1; ++k) {
+    if (k + 1 < c1) load_chunk(a, bg, nch, k + 1, lane, nxt);
+    const int nvalid = min(len - k * T, T);  // tokens [0, nvalid) of this chunk are live
+
+    // ---- scales to LDS ----
+    __syncthreads();  // previous chunk's readers are done
+    {
+      const float ck0 = __uint_as_float(cur.ck[0]), ck1 = __uint_as_float(cur.ck[1]);
+      sm.ck[elem_slot_pos(2 * lane)] = ck0;
+      sm.ck[elem_slot_pos(2 * lane + 1)] = ck1;
+      sm.cv[(2 * lane) & 15][(2 * lane) >> 4] = __uint_as_float(cur.cv[0]);
+      sm.cv[(2 * lane + 1) & 15][(2 * lane + 1) >> 4] = __uint_as_float(cur.cv[1]);
+      sm.rk[2 * lane] = __uint_as_float(cur.rk[0]);
+      sm.rk[2 * lane + 1] = __uint_as_float(cur.rk[1]);
+    }
+    // V row scales with their field scale; the chunk's range scale 2^sigma_v
+    float rv0 = 2 * lane < nvalid ? __uint_as_float(cur.rv[0]) : 0.f;
+    float rv1 = 2 * lane + 1 < nvalid ? __uint_as_float(cur.rv[1]) : 0.f;
+    int sig_v;
+    const float sv = range_scale(wave_max(fmaxf(rv0, rv1)), sig_v);
+    sm.rv[2 * lane] = rv0 * sv * __builtin_ldexpf(1.f, -2 * field_exp(2 * lane));
+    sm.rv[2 * lane + 1] = rv1 * sv * __builtin_ldexpf(1.f, -2 * field_exp(2 * lane + 1));
+    __syncthreads();
+
+    // ---- query operand: a = q * c_K * 2^sigma, fp16 hi/lo ----
+    int sig_q;
+    {
+      const f32x4 c0v = *reinterpret_cast<const f32x4 *>(&sm.ck[(gu * 4 + su) * 8]);
+      const f32x4 c1v = *reinterpret_cast<const f32x4 *>(&sm.ck[(gu * 4 + su) * 8 + 4]);
+      const float cc[8] = {c0v.x, c0v.y, c0v.z, c0v.w, c1v.x, c1v.y, c1v.z, c1v.w};
+      float av[NU][8];
+      float mx = 0.f;
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          av[u][e] = qh[u][e] * cc[e];
+          mx = fmaxf(mx, fabsf(av[u][e]));
+        }
+      const float sq = range_scale(wave_max(mx), sig_q);
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        u32x4 hi, lo;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          // hi = x truncated to fp16's 11 significant bits (exact in fp32 and,
+          // for |x| in the fp16 normal range, exact in fp16); lo = x - hi.
+          // Formed in fp32 so that no f16 -> f32 read-back of the packed hi
+          // pair exists (that pattern was mis-fused into v_fma_mix_f32 with
+          // the wrong source register by this compiler).
+          const float x0 = av[u][2 * d] * sq, x1 = av[u][2 * d + 1] * sq;
+          const float h0 = __uint_as_float(__float_as_uint(x0) & 0xFFFFE000u);
+          const float h1 = __uint_as_float(__float_as_uint(x1) & 0xFFFFE000u);
+          hi[d] = pack_rtz(h0, h1);
+          lo[d] = pack_rtz(x0 - h0, x1 - h1);
+        }
+        const int mu = (lane & 3) + 4 * u;
+        *reinterpret_cast<u32x4 *>(&sm.ahi[mu][gu][su][0]) = hi;
+        *reinterpret_cast<u32x4 *>(&sm.alo[mu][gu][su][0]) = lo;
+      }
+    }
+    __syncthreads();
+    u32x4 ahi[4], alo[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (n < GP) {
+        ahi[s] = *reinterpret_cast<const u32x4 *>(&sm.ahi[n][lg][s][0]);
+        alo[s] = *reinterpret_cast<const u32x4 *>(&sm.alo[n][lg][s][0]);
+      } else {
+        ahi[s] = u32x4{0u, 0u, 0u, 0u};
+        alo[s] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+
+    // ---- QK^T: 8 token tiles x (4 hi + 4 lo) k-steps, plus the offset term ----
+    {
+      f32x4 dcv = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        dcv = mfma(as_f16x8(ahi[s]), as_f16x8((s & 1) ? one1 : one0), dcv);
+        dcv = mfma(as_f16x8(alo[s]), as_f16x8((s & 1) ? one1 : one0), dcv);
+      }
+      if (n == 0 && lg < GP / 4) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm.dc[4 * lg + r] = dcv[r];
+      }
+    }
+#pragma unroll
+    for (int tau = 0; tau < 8; ++tau) {
+      u32x4 b0, b1, b2, b3;
+      unpack_codes(cur.k[tau][0], b0, b1);
+      unpack_codes(cur.k[tau][1], b2, b3);
+      f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
+      d = mfma(as_f16x8(ahi[0]), as_f16x8(b0), d);
+      d = mfma(as_f16x8(ahi[1]), as_f16x8(b1), d);
+      d = mfma(as_f16x8(ahi[2]), as_f16x8(b2), d);
+      d = mfma(as_f16x8(ahi[3]), as_f16x8(b3), d);
+      d = mfma(as_f16x8(alo[0]), as_f16x8(b0), d);
+      d = mfma(as_f16x8(alo[1]), as_f16x8(b1), d);
+      d = mfma(as_f16x8(alo[2]), as_f16x8(b2), d);
+      d = mfma(as_f16x8(alo[3]), as_f16x8(b3), d);
+      if (lg < GP / 4) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm.sc[4 * lg + r][16 * tau + n] = d[r];
+      }
+    }
+    __syncthreads();
+
+    // ---- online softmax: lane holds head sh, tokens [st0, st0 + TPL) ----
+    {
+      const float kscale = __builtin_ldexpf(1.f, 24 - sig_q);
+      const float off = 1.5f * sm.dc[sh];
+      float s[TPL];
+      float mc = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < TPL; ++i) {
+        const int t = st0 + i;
+        const float raw = sm.sc[sh][t];
+        s[i] = t < nvalid ? (raw - off) * (sm.rk[t] * kscale) : -INFINITY;
+        mc = fmaxf(mc, s[i]);
+      }
+#pragma unroll
+      for (int m = 1; m < LPH; m <<= 1) mc = fmaxf(mc, __shfl_xor(mc, m, 64));
+      // integer running max (log2 units): P' of a chunk then differs between
+      // split layouts only by powers of two, so its fp16 rounding does not
+      const float mn = fmaxf(m_run, ceilf(mc));
+      const float al = mn == -INFINITY ? 1.f : exp2f(m_run - mn);
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < TPL; ++i) {
+        const int t = st0 + i;
+        const float p = mn == -INFINITY ? 0.f : exp2f(s[i] - mn);
+        ps += p;
+        sm.sc[sh][t] = p * sm.rv[t];  // P' (fp32), natural order
+      }
+      l_run = l_run * al + ps;
+      m_run = mn;
+      if (lane % LPH == 0) sm.alpha[sh] = al;
+    }
+    __syncthreads();
+
+    // ---- PV: P' operand, 8 channel tiles x 4 k-steps, plus the offset term ----
+    {
+      u32x4 ap[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if (n < GP) {
+#pragma unroll
+          for (int d = 0; d < 4; ++d)
+            ap[s][d] = pack_rtz(sm.sc[n][kslot_elem(lg, s, 2 * d)],
+                                sm.sc[n][kslot_elem(lg, s, 2 * d + 1)]);
+        } else {
+          ap[s] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+      f32x4 dcp = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) dcp = mfma(as_f16x8(ap[s]), as_f16x8((s & 1) ? one1 : one0), dcp);
+      const float vscale = __builtin_ldexpf(1.f, 24 - sig_v);
+      f32x4 alr;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) alr[r] = (4 * lg + r < GP) ? sm.alpha[4 * lg + r] : 1.f;
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        u32x4 b0, b1, b2, b3;
+        unpack_codes(cur.v[ct][0], b0, b1);
+        unpack_codes(cur.v[ct][1], b2, b3);
+        f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
+        d = mfma(as_f16x8(ap[0]), as_f16x8(b0), d);
+        d = mfma(as_f16x8(ap[1]), as_f16x8(b1), d);
+        d = mfma(as_f16x8(ap[2]), as_f16x8(b2), d);
+        d = mfma(as_f16x8(ap[3]), as_f16x8(b3), d);
+        const float cvs = sm.cv[n][ct] * vscale;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[ct][r] = acc[ct][r] * alr[r] + cvs * (d[r] - 1.5f * dcp[r]);
+      }
+    }
+    cur = nxt;
+  }
+
+  // ---- partial results: (m, l, acc) per query head of this split ----
+#pragma unroll
+  for (int m = 1; m < LPH; m <<= 1) l_run += __shfl_xor(l_run, m, 64);
+  if (lane % LPH == 0 && sh < G) {
+    float *pp = a.partial + (((int64_t)b * a.q_heads + g * G + sh) * a.n_split + split) * (2 + D);
+    pp[0] = m_run;
+    pp[1] = l_run;
+  }
+  if (lg < GP / 4) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * lg + r;
+      if (h < G) {
+        float *pp = a.partial + (((int64_t)b * a.q_heads + g * G + h) * a.n_split + split) * (2 + D);
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) pp[2 + 16 * ct + n] = acc[ct][r];
       }
     }
   }
@@ -231,7 +452,8 @@ int decode_auto_splits(int batch, int kv_heads, int capacity) {
   const int nch = capacity / T;
   const int pairs = batch * kv_heads;
   if (pairs <= 0 || nch <= 0) return 1;
-  int s = (1024 + pairs - 1) / pairs;
+  // about 4096 single-wave workgroups: 16 per CU on 256 CUs
+  int s = (4096 + pairs - 1) / pairs;
   if (s > nch) s = nch;
   if (s < 1) s = 1;
   return s;
@@ -240,12 +462,10 @@ int decode_auto_splits(int batch, int kv_heads, int capacity) {
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
   if (a.batch == 0 || a.q_heads == 0) return hipSuccess;
   const dim3 grid(a.n_split, a.kv_heads, a.batch);
-  switch ((a.q_heads / a.kv_heads + 1) / 2) {
-    case 1: hipLaunchKernelGGL(decode_split_kernel<1>, grid, dim3(kThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(decode_split_kernel<2>, grid, dim3(kThreads), 0, s, a); break;
-    case 3: hipLaunchKernelGGL(decode_split_kernel<3>, grid, dim3(kThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL(decode_split_kernel<4>, grid, dim3(kThreads), 0, s, a); break;
-  }
+  if (a.q_heads / a.kv_heads <= 4)
+    hipLaunchKernelGGL(decode_split_kernel<4>, grid, dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL(decode_split_kernel<8>, grid, dim3(64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(a.q_heads, a.batch), dim3(D), 0, s, a);

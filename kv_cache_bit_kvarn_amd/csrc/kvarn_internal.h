@@ -33,11 +33,23 @@ __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u 
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 
 // ---- launchers (validated arguments only) --------------------------------
+// Division by a runtime divisor d (1 <= d < 2^31) of n < 2^31 as
+// (n * m) >> s with m = ceil(2^s / d), s = 31 + ceil(log2 d).
+struct FastDiv {
+  uint32_t d, m, s;
+};
+FastDiv make_fastdiv(uint32_t d);
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+  return (uint32_t)(((uint64_t)n * f.m) >> f.s);
+}
+
 struct QuantArgs {
   const void *x;
   int dtype;
   int64_t sb, sh, st;
   int batch, heads, chunks, chunk0, iters, capacity, kind;
+  uint32_t nblocks;     // batch * heads * chunks (< 2^31)
+  FastDiv div_chunks, div_heads;
   uint8_t *codes;
   float *row_scale, *col_scale;
 };

@@ -1,49 +1,81 @@
 // Block quantizer of the KVarN method on gfx950.
 //
 // One workgroup (256 threads, 4 wave64) quantizes one 128-token x 128-channel
-// block of K or V (one layer, sequence, kv-head, chunk):
-//   1. load bf16/fp32 -> fp32 registers (16-byte loads; one token row per
-//      lane pair, 64 channels per lane);
+// block of K or V (one layer, sequence, kv-head, chunk) at a time and walks
+// the blocks of the launch persistently (stride = grid), loading the next
+// block's bf16 input into registers while the current one is computed:
+//   1. bf16/fp32 -> fp32 registers (16-byte loads; one token row per lane
+//      pair, 64 channels per lane);
 //   2. Hadamard rotation along channels (rndamp article on KVarN, "How It
 //      Works", item 1): six butterfly stages inside each lane, the seventh
-//      between the two lanes of a token through DPP;
+//      between the two lanes of a token as one DPP-sourced v_fmac each;
 //   3. dual-scaling normalization ("How It Works", item 2; abstract: both
 //      axes of K and V): squared values P stay in registers for the row step
 //      and are staged once, transposed, in LDS for the column step;
-//   4. per-token range step, 2-bit codes, and packing (K token-major straight
-//      from registers, V channel-major through an LDS byte transpose);
-//   5. 16-byte stores of codes, fp32 row and column scales.
+//   4. per-token range step and 2-bit codes, packed four per byte
+//      (v_cvt_pk_u8_f32 + v_dot4_u32_u8); K token-major straight from
+//      registers, V channel-major through an LDS byte transpose;
+//   5. 16-byte stores of K codes, 4-byte stores of V code words, fp32 scales.
 // The rotation is applied without its 1/sqrt(128) factor; that factor leaves
 // the column scales and codes unchanged and is folded into the row scale.
+//
+// Code decision: the oracle takes code = floor(u + 2), u = y/(r' c) in [-2, 2].
+// Here t = u * (1 - 2^-20) + 1.5 is rounded to nearest by v_cvt_pk_u8_f32;
+// the shrink keeps the range-step element (|u| = 2) inside the grid, and the
+// result equals floor(u + 2) for every element farther than 2e-6 from a
+// rounding boundary u in {-1, 0, 1}.
 #include "kvarn_internal.h"
 
 namespace kvarn {
+
+FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  FastDiv f;
+  f.d = d;
+  f.s = 31 + l;
+  f.m = (uint32_t)(((1ull << f.s) + d - 1) / d);
+  return f;
+}
+
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int PT_STRIDE = T + 4;  // floats per row of the transposed P (bank spread)
-constexpr int CB_STRIDE = T + 16; // bytes per channel row of the V code transpose
+constexpr int PT_STRIDE = T + 4;   // floats per row of the transposed P (bank spread)
+constexpr int CB_PITCH = D + 16;   // bytes per token row of the V code staging
+constexpr float kGrid = 1.9999980926513672f;  // 2 (1 - 2^-20)
+constexpr uint32_t kPack4 = 0x40100401u;       // byte weights 1, 4, 16, 64
+
+constexpr int WPAD = 4;  // w[j] lives at w[j + WPAD * (j >= 64)]: halves on different banks
 
 struct QuantSmem {
-  float pt[D * PT_STRIDE];  // pt[j][i] = P_ij  (later reused for V code bytes)
-  float w[D];               // 1/c_j^2 while balancing, then 1/c_j
+  float w[D + WPAD];        // 1/c_j^2 while balancing, then 1/c_j
   float v[T];               // 1/r_i^2
-  float cpart[2][D];        // column sums over token halves
+  float pt[D * PT_STRIDE];  // pt[j][i] = P_ij (V blocks reuse it for code bytes)
 };
 
+__device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
 // Sum of 64 products in eight interleaved partial sums combined as a tree,
-// keeping fp32 rounding close to that of a pairwise sum.
+// keeping fp32 rounding close to that of a pairwise sum. LDS operands are
+// fetched eight vectors at a time ahead of their FMAs.
 __device__ __forceinline__ float dot64(const float (&p)[64], const float *w) {
   float acc[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r) acc[r] = 0.f;
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const f32x4 ww = reinterpret_cast<const f32x4 *>(w)[q];
-    acc[(4 * q + 0) & 7] = fmaf(p[4 * q + 0], ww.x, acc[(4 * q + 0) & 7]);
-    acc[(4 * q + 1) & 7] = fmaf(p[4 * q + 1], ww.y, acc[(4 * q + 1) & 7]);
-    acc[(4 * q + 2) & 7] = fmaf(p[4 * q + 2], ww.z, acc[(4 * q + 2) & 7]);
-    acc[(4 * q + 3) & 7] = fmaf(p[4 * q + 3], ww.w, acc[(4 * q + 3) & 7]);
+  for (int h = 0; h < 2; ++h) {
+    f32x4 ww[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) ww[q] = reinterpret_cast<const f32x4 *>(w)[8 * h + q];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int e = 32 * h + 4 * q;
+      acc[(e + 0) & 7] = fmaf(p[e + 0], ww[q].x, acc[(e + 0) & 7]);
+      acc[(e + 1) & 7] = fmaf(p[e + 1], ww[q].y, acc[(e + 1) & 7]);
+      acc[(e + 2) & 7] = fmaf(p[e + 2], ww[q].z, acc[(e + 2) & 7]);
+      acc[(e + 3) & 7] = fmaf(p[e + 3], ww[q].w, acc[(e + 3) & 7]);
+    }
   }
   return ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
 }
@@ -54,183 +86,280 @@ __device__ __forceinline__ float dot64_lds(const float *a, const float *b) {
 #pragma unroll
   for (int r = 0; r < 8; ++r) acc[r] = 0.f;
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const f32x4 x = reinterpret_cast<const f32x4 *>(a)[q];
-    const f32x4 y = reinterpret_cast<const f32x4 *>(b)[q];
-    acc[(4 * q + 0) & 7] = fmaf(x.x, y.x, acc[(4 * q + 0) & 7]);
-    acc[(4 * q + 1) & 7] = fmaf(x.y, y.y, acc[(4 * q + 1) & 7]);
-    acc[(4 * q + 2) & 7] = fmaf(x.z, y.z, acc[(4 * q + 2) & 7]);
-    acc[(4 * q + 3) & 7] = fmaf(x.w, y.w, acc[(4 * q + 3) & 7]);
+  for (int h = 0; h < 4; ++h) {
+    f32x4 x[4], y[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      x[q] = reinterpret_cast<const f32x4 *>(a)[4 * h + q];
+      y[q] = reinterpret_cast<const f32x4 *>(b)[4 * h + q];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = 16 * h + 4 * q;
+      acc[(e + 0) & 7] = fmaf(x[q].x, y[q].x, acc[(e + 0) & 7]);
+      acc[(e + 1) & 7] = fmaf(x[q].y, y[q].y, acc[(e + 1) & 7]);
+      acc[(e + 2) & 7] = fmaf(x[q].z, y[q].z, acc[(e + 2) & 7]);
+      acc[(e + 3) & 7] = fmaf(x[q].w, y[q].w, acc[(e + 3) & 7]);
+    }
   }
   return ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+}
+
+// Cross-lane butterfly of the top channel bit for 8 registers at once:
+// y = y(lane ^ 1) * s + y, one v_fmac_f32 with a DPP source each. With
+// s = +1 on the lane holding channel bit 6 = 0 this yields A + B there and
+// -(A - B) on the partner lane (s = -1); the sign of the partner lane is
+// tracked by the caller. The leading s_nop covers the DPP read-after-VALU-
+// write hazard (2 wait states) for registers written just before the block.
+__device__ __forceinline__ void butterfly_xor1_x8(float *y, float s) {
+  asm("s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %0, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %1, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %2, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %3, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %4, %4, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %5, %5, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %6, %6, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %7, %7, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+      : "+v"(y[0]), "+v"(y[1]), "+v"(y[2]), "+v"(y[3]), "+v"(y[4]), "+v"(y[5]), "+v"(y[6]),
+        "+v"(y[7])
+      : "v"(s));
+}
+
+struct BlockIdx {
+  uint32_t bh, kc, b, h;
+};
+__device__ __forceinline__ BlockIdx split_block(const QuantArgs &a, uint32_t blk) {
+  BlockIdx r;
+  r.bh = fdiv(blk, a.div_chunks);
+  r.kc = blk - r.bh * (uint32_t)a.chunks;
+  r.b = fdiv(r.bh, a.div_heads);
+  r.h = r.bh - r.b * (uint32_t)a.heads;
+  return r;
+}
+
+__device__ __forceinline__ int64_t x_offset(const QuantArgs &a, const BlockIdx &bi, int ti, int hf) {
+  return (int64_t)bi.b * a.sb + (int64_t)bi.h * a.sh + (int64_t)(bi.kc * T + ti) * a.st + 64 * hf;
+}
+
+__device__ __forceinline__ void load_bf16_block(const QuantArgs &a, uint32_t blk, int ti, int hf,
+                                                u32x4 (&xr)[8]) {
+  const BlockIdx bi = split_block(a, blk);
+  const u32x4 *src =
+      reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.x) + x_offset(a, bi, ti, hf));
+#pragma unroll
+  for (int q = 0; q < 8; ++q) xr[q] = __builtin_nontemporal_load(src + q);
 }
 
 template <bool kF32>
 __global__ __launch_bounds__(kThreads, 2) void quantize_block_kernel(QuantArgs a) {
   __shared__ QuantSmem sm;
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int ti = (tid >> 6) * 32 + (lane >> 1);  // token row of this lane pair
-  const int hf = lane & 1;                       // channels [64 hf, 64 hf + 64)
-
-  const int kc = blockIdx.x % a.chunks;
-  const int bh = blockIdx.x / a.chunks;
-  const int b = bh / a.heads, h = bh - b * a.heads;
-  const int chunk = a.chunk0 + kc;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int ti = wv * 32 + (lane >> 1);  // row role: token ti,
+  const int hf = lane & 1;               //   channels [64 hf, 64 hf + 64)
+  const int cj = 32 * wv + (lane & 31);  // column role: channel cj,
+  const int cg = lane >> 5;              //   tokens [64 cg, 64 cg + 64)
   const int64_t nch = a.capacity / T;
+  // the cross-lane butterfly leaves the hf = 1 lane's values negated
+  const float lane_sign = hf ? -1.f : 1.f;
 
-  // ---- 1. load -----------------------------------------------------------
-  float y[64];
-  const int64_t off = (int64_t)b * a.sb + (int64_t)h * a.sh +
-                      (int64_t)(kc * T + ti) * a.st + 64 * hf;
-  if constexpr (kF32) {
-    const f32x4 *src = reinterpret_cast<const f32x4 *>(static_cast<const float *>(a.x) + off);
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const f32x4 v = __builtin_nontemporal_load(src + q);
-      y[4 * q + 0] = v.x; y[4 * q + 1] = v.y; y[4 * q + 2] = v.z; y[4 * q + 3] = v.w;
-    }
-  } else {
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.x) + off);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const u32x4 u = __builtin_nontemporal_load(src + q);
-      y[8 * q + 0] = bf16_lo(u.x); y[8 * q + 1] = bf16_hi(u.x);
-      y[8 * q + 2] = bf16_lo(u.y); y[8 * q + 3] = bf16_hi(u.y);
-      y[8 * q + 4] = bf16_lo(u.z); y[8 * q + 5] = bf16_hi(u.z);
-      y[8 * q + 6] = bf16_lo(u.w); y[8 * q + 7] = bf16_hi(u.w);
-    }
+  u32x4 xr[8];
+  uint32_t blk = blockIdx.x;
+  if constexpr (!kF32) {
+    if (blk < a.nblocks) load_bf16_block(a, blk, ti, hf, xr);
   }
+  for (; blk < a.nblocks; blk += gridDim.x) {
+    const BlockIdx bi = split_block(a, blk);
+    const int64_t bh = bi.bh;
+    const int chunk = a.chunk0 + (int)bi.kc;
 
-  // ---- 2. rotation: y <- y . H_128 (Sylvester order, unscaled) -----------
+    // ---- 1. load -----------------------------------------------------------
+    float y[64];
+    if constexpr (kF32) {
+      const f32x4 *src =
+          reinterpret_cast<const f32x4 *>(static_cast<const float *>(a.x) + x_offset(a, bi, ti, hf));
 #pragma unroll
-  for (int len = 1; len < 64; len <<= 1) {
+      for (int q = 0; q < 16; ++q) {
+        const f32x4 v = __builtin_nontemporal_load(src + q);
+        y[4 * q + 0] = v.x; y[4 * q + 1] = v.y; y[4 * q + 2] = v.z; y[4 * q + 3] = v.w;
+      }
+    } else {
 #pragma unroll
-    for (int i = 0; i < 64; ++i) {
-      if ((i & len) == 0) {
-        const float p = y[i], q = y[i + len];
-        y[i] = p + q;
-        y[i + len] = p - q;
+      for (int q = 0; q < 8; ++q) {
+        const u32x4 u = xr[q];
+        y[8 * q + 0] = bf16_lo(u.x); y[8 * q + 1] = bf16_hi(u.x);
+        y[8 * q + 2] = bf16_lo(u.y); y[8 * q + 3] = bf16_hi(u.y);
+        y[8 * q + 4] = bf16_lo(u.z); y[8 * q + 5] = bf16_hi(u.z);
+        y[8 * q + 6] = bf16_lo(u.w); y[8 * q + 7] = bf16_hi(u.w);
+      }
+      // unconditional (clamped) prefetch keeps xr in place across iterations
+      const uint32_t nb = min(blk + gridDim.x, a.nblocks - 1);
+      load_bf16_block(a, nb, ti, hf, xr);
+    }
+
+    // ---- 2. rotation: y <- y . H_128 (Sylvester order, unscaled) -----------
+#pragma unroll
+    for (int len = 1; len < 64; len <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 64; ++i) {
+        if ((i & len) == 0) {
+          const float p = y[i], q = y[i + len];
+          y[i] = p + q;
+          y[i + len] = p - q;
+        }
       }
     }
-  }
-  {
-    // top channel bit lives across the lane pair: lane hf=0 holds A, hf=1
-    // holds B; the pair becomes (A + B, A - B) = fma(own, +-1, partner).
-    const float sgn = hf ? -1.f : 1.f;
 #pragma unroll
-    for (int i = 0; i < 64; ++i) y[i] = fmaf(y[i], sgn, dpp_xor1(y[i]));
-  }
+    for (int i = 0; i < 64; i += 8) butterfly_xor1_x8(y + i, lane_sign);
 
-  // ---- 3. dual scaling ---------------------------------------------------
-  float p[64];
+    // ---- 3. dual scaling ---------------------------------------------------
+    float p[64];
 #pragma unroll
-  for (int i = 0; i < 64; ++i) {
-    p[i] = y[i] * y[i];
-    sm.pt[(64 * hf + i) * PT_STRIDE + ti] = p[i];
-  }
-  if (tid < D) sm.w[tid] = 1.f;
-  __syncthreads();
-
-  const int cj = tid & (D - 1);  // column-owner role: channel cj,
-  const int cg = tid >> 7;       // tokens [64 cg, 64 cg + 64)
-  for (int it = 0; it < a.iters; ++it) {
-    // row step: r_i^2 = (1/D) sum_j P_ij / c_j^2  ->  v_i = 1/r_i^2
-    float s = dot64(p, sm.w + 64 * hf);
-    s += dpp_xor1(s);
-    if (hf == 0) sm.v[ti] = s > 0.f ? (float)D / s : 1.f;
-    __syncthreads();
-    // column step: c_j^2 = (1/T) sum_i P_ij / r_i^2  ->  w_j = 1/c_j^2
-    sm.cpart[cg][cj] = dot64_lds(sm.pt + cj * PT_STRIDE + 64 * cg, sm.v + 64 * cg);
-    __syncthreads();
-    if (tid < D) {
-      const float cm = (sm.cpart[0][tid] + sm.cpart[1][tid]) * (1.f / T);
-      sm.w[tid] = cm > 0.f ? 1.f / cm : 1.f;
+    for (int i = 0; i < 64; ++i) p[i] = y[i] * y[i];
+    if (a.kind == KVARN_V) __syncthreads();  // previous block's readers done with the staging
+    {
+      float *dst = sm.pt + 64 * hf * PT_STRIDE + ti;
+#pragma unroll
+      for (int i = 0; i < 64; ++i) dst[i * PT_STRIDE] = p[i];
     }
     __syncthreads();
-  }
-  float *rowp = a.row_scale + ((int64_t)bh * a.capacity + (int64_t)chunk * T);
-  float *colp = a.col_scale + ((int64_t)bh * nch + chunk) * D;
-  if (tid < D) {
-    float c = 1.f;
-    if (a.iters > 0) {
-      const float cm = (sm.cpart[0][tid] + sm.cpart[1][tid]) * (1.f / T);
-      c = cm > 0.f ? sqrtf(cm) : 1.f;
-    }
-    colp[tid] = c;
-    sm.w[tid] = 1.f / c;
-  }
-  __syncthreads();
 
-  // ---- 4. range step and codes --------------------------------------------
-  float m = 0.f;
-  {
-    const f32x4 *ic = reinterpret_cast<const f32x4 *>(sm.w + 64 * hf);
+    float *colp = a.col_scale + (bh * nch + chunk) * D;
+    for (int it = 0; it < a.iters; ++it) {
+      // row step: r_i^2 = (1/D) sum_j P_ij / c_j^2  ->  v_i = 1/r_i^2  (c = 1 first)
+      float s;
+      if (it == 0) {
+        float acc[8];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const f32x4 w4 = ic[q];
-      y[4 * q + 0] *= w4.x; y[4 * q + 1] *= w4.y; y[4 * q + 2] *= w4.z; y[4 * q + 3] *= w4.w;
-    }
+        for (int r = 0; r < 8; ++r) acc[r] = 0.f;
 #pragma unroll
-    for (int i = 0; i < 64; ++i) m = fmaxf(m, fabsf(y[i]));
-  }
-  m = fmaxf(m, dpp_xor1(m));
-  if (hf == 0) rowp[ti] = m * kRangeFromUnscaled;
-  const float qs = m > 0.f ? 2.f / m : 0.f;
-  uint32_t code[64];
-#pragma unroll
-  for (int i = 0; i < 64; ++i) {
-    const float t = fminf(fmaxf(fmaf(y[i], qs, 2.f), 0.f), 3.f);
-    code[i] = (uint32_t)t;
-  }
-
-  uint8_t *cbase = a.codes + ((int64_t)bh * nch + chunk) * CHUNK_BYTES;
-  if (a.kind == KVARN_K) {
-    u32x4 pk;
-    uint32_t *pw = reinterpret_cast<uint32_t *>(&pk);
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      uint32_t wv = 0;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) wv |= code[16 * d + k] << (2 * k);
-      pw[d] = wv;
-    }
-    *reinterpret_cast<u32x4 *>(cbase + ti * 32 + hf * 16) = pk;
-  } else {
-    // channel-major: stage one byte per code in LDS as cb[channel][token]
-    uint8_t *cb = reinterpret_cast<uint8_t *>(sm.pt);
-#pragma unroll
-    for (int i = 0; i < 64; ++i) cb[(64 * hf + i) * CB_STRIDE + ti] = (uint8_t)code[i];
-    __syncthreads();
-    const int j = tid >> 1, g = tid & 1;  // channel j, tokens [64 g, 64 g + 64)
-    const uint32_t *src = reinterpret_cast<const uint32_t *>(cb + j * CB_STRIDE + 64 * g);
-    u32x4 pk;
-    uint32_t *pw = reinterpret_cast<uint32_t *>(&pk);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t o = 0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t wd = src[4 * q + r];
-        const uint32_t byte = (wd & 0x3u) | ((wd >> 6) & 0xCu) | ((wd >> 12) & 0x30u) |
-                              ((wd >> 18) & 0xC0u);
-        o |= byte << (8 * r);
+        for (int i = 0; i < 64; ++i) acc[i & 7] += p[i];
+        s = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+      } else {
+        s = dot64(p, sm.w + (64 + WPAD) * hf);
       }
-      pw[q] = o;
+      s += dpp_xor1(s);
+      if (hf == 0) sm.v[ti] = s > 0.f ? (float)D * rcp(s) : 1.f;
+      __syncthreads();
+      // column step: c_j^2 = (1/T) sum_i P_ij / r_i^2  ->  w_j = 1/c_j^2
+      float cs = dot64_lds(sm.pt + cj * PT_STRIDE + 64 * cg, sm.v + 64 * cg);
+      cs += __shfl_xor(cs, 32, 64);
+      if (cg == 0) {
+        const float cm = cs * (1.f / T);
+        const int wj = cj + WPAD * (cj >> 6);
+        if (it + 1 < a.iters) {
+          sm.w[wj] = cm > 0.f ? rcp(cm) : 1.f;
+        } else {
+          colp[cj] = cm > 0.f ? sqrtf(cm) : 1.f;
+          sm.w[wj] = cm > 0.f ? __builtin_amdgcn_rsqf(cm) : 1.f;
+        }
+      }
+      __syncthreads();
     }
-    *reinterpret_cast<u32x4 *>(cbase + j * 32 + g * 16) = pk;
+    if (a.iters == 0) {
+      if (tid < D) {
+        colp[tid] = 1.f;
+        sm.w[tid + WPAD * (tid >> 6)] = 1.f;
+      }
+      __syncthreads();
+    }
+
+    // ---- 4. range step and codes --------------------------------------------
+    float m = 0.f;
+    {
+      const f32x4 *ic = reinterpret_cast<const f32x4 *>(sm.w + (64 + WPAD) * hf);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const f32x4 w4 = ic[q];
+        y[4 * q + 0] *= w4.x; y[4 * q + 1] *= w4.y; y[4 * q + 2] *= w4.z; y[4 * q + 3] *= w4.w;
+      }
+#pragma unroll
+      for (int i = 0; i < 64; ++i) m = fmaxf(m, fabsf(y[i]));
+    }
+    m = fmaxf(m, dpp_xor1(m));
+    if (hf == 0) a.row_scale[bh * a.capacity + (int64_t)chunk * T + ti] = m * kRangeFromUnscaled;
+    const float qs = m > 0.f ? lane_sign * kGrid * rcp(m) : 0.f;
+    // cw[d] byte k = code of channel 64 hf + 4 d + k
+    uint32_t cw[16];
+#pragma unroll
+    for (int d = 0; d < 16; ++d) {
+      uint32_t acc = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        acc = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(y[4 * d + k], qs, 1.5f), k, acc);
+      cw[d] = acc;
+    }
+
+    uint8_t *cbase = a.codes + (bh * nch + chunk) * CHUNK_BYTES;
+    if (a.kind == KVARN_K) {
+      u32x4 pk;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t o = __builtin_amdgcn_udot4(cw[4 * q + 0], kPack4, 0u, false);
+        o |= __builtin_amdgcn_udot4(cw[4 * q + 1], kPack4, 0u, false) << 8;
+        o |= __builtin_amdgcn_udot4(cw[4 * q + 2], kPack4, 0u, false) << 16;
+        o |= __builtin_amdgcn_udot4(cw[4 * q + 3], kPack4, 0u, false) << 24;
+        pk[q] = o;
+      }
+      *reinterpret_cast<u32x4 *>(cbase + ti * 32 + hf * 16) = pk;
+    } else {
+      // token-major byte staging, then each thread transposes 4 channels x
+      // 16 tokens: 4x4 byte transposes (v_perm) and 2-bit packing (v_dot4)
+      uint8_t *cb = reinterpret_cast<uint8_t *>(sm.pt);
+      u32x4 *dst = reinterpret_cast<u32x4 *>(cb + ti * CB_PITCH + 64 * hf);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        u32x4 v4;
+        v4[0] = cw[4 * q + 0]; v4[1] = cw[4 * q + 1]; v4[2] = cw[4 * q + 2]; v4[3] = cw[4 * q + 3];
+        dst[q] = v4;
+      }
+      __syncthreads();
+      const int j4 = tid & 31;   // channels [4 j4, 4 j4 + 4)
+      const int n4 = tid >> 5;   // tokens [16 n4, 16 n4 + 16)
+      uint32_t word[4] = {0u, 0u, 0u, 0u};  // per channel: 16 tokens, 2 bits each
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint8_t *src = cb + (16 * n4 + 4 * q) * CB_PITCH + 4 * j4;
+        const uint32_t w0 = *reinterpret_cast<const uint32_t *>(src);
+        const uint32_t w1 = *reinterpret_cast<const uint32_t *>(src + CB_PITCH);
+        const uint32_t w2 = *reinterpret_cast<const uint32_t *>(src + 2 * CB_PITCH);
+        const uint32_t w3 = *reinterpret_cast<const uint32_t *>(src + 3 * CB_PITCH);
+        const uint32_t t01l = __builtin_amdgcn_perm(w1, w0, 0x05010400u);
+        const uint32_t t01h = __builtin_amdgcn_perm(w1, w0, 0x07030602u);
+        const uint32_t t23l = __builtin_amdgcn_perm(w3, w2, 0x05010400u);
+        const uint32_t t23h = __builtin_amdgcn_perm(w3, w2, 0x07030602u);
+        const uint32_t o0 = __builtin_amdgcn_perm(t23l, t01l, 0x05040100u);
+        const uint32_t o1 = __builtin_amdgcn_perm(t23l, t01l, 0x07060302u);
+        const uint32_t o2 = __builtin_amdgcn_perm(t23h, t01h, 0x05040100u);
+        const uint32_t o3 = __builtin_amdgcn_perm(t23h, t01h, 0x07060302u);
+        word[0] |= __builtin_amdgcn_udot4(o0, kPack4, 0u, false) << (8 * q);
+        word[1] |= __builtin_amdgcn_udot4(o1, kPack4, 0u, false) << (8 * q);
+        word[2] |= __builtin_amdgcn_udot4(o2, kPack4, 0u, false) << (8 * q);
+        word[3] |= __builtin_amdgcn_udot4(o3, kPack4, 0u, false) << (8 * q);
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        *reinterpret_cast<uint32_t *>(cbase + (4 * j4 + s) * 32 + 4 * n4) = word[s];
+    }
   }
 }
 
 }  // namespace
 
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t s) {
-  const int64_t blocks = (int64_t)a.batch * a.heads * a.chunks;
-  if (blocks == 0) return hipSuccess;
+  if (a.nblocks == 0) return hipSuccess;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  // two resident workgroups per CU (LDS-limited); each walks blocks strided by the grid
+  const uint32_t resident = 2u * (uint32_t)(cus > 0 ? cus : 1);
+  const uint32_t blocks = a.nblocks < resident ? a.nblocks : resident;
   if (a.dtype == KVARN_DT_F32)
-    hipLaunchKernelGGL(quantize_block_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(quantize_block_kernel<true>, dim3(blocks), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(quantize_block_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(quantize_block_kernel<false>, dim3(blocks), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -52,6 +52,7 @@ def _q(lib, x=A, dtype=kv.DT_BF16, sb=4 * 512 * 128, sh=512 * 128, st=128, token
 
 def test_quantize_validation(lib):
     assert _q(lib, x=None) == kv.ERR_NULL
+    assert _q(lib, x=None, tokens=0) == kv.OK
     assert lib.kvarn_quantize(A, 0, 0, 0, 128, 128, 0, 4, None, None) == kv.ERR_NULL
     assert _q(lib, cache=_cache(codes=None)) == kv.ERR_NULL
     assert _q(lib, cache=_cache(row=None)) == kv.ERR_NULL
