@@ -132,6 +132,43 @@ __device__ __forceinline__ float load_q(const void *q, int dtype, int64_t idx) {
   return __uint_as_float((uint32_t)static_cast<const uint16_t *>(q)[idx] << 16);
 }
 
+// ---- cross-lane reductions on DPP (no LDS round trip) ----------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+constexpr int kQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+// max / sum over aligned groups of N lanes (N = 8 or 16); every lane gets it
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+  v = fmaxf(v, dpp<kQuadSwap1>(v));
+  v = fmaxf(v, dpp<kQuadSwap2>(v));
+  v = fmaxf(v, dpp<kRowHalfMirror>(v));
+  if constexpr (N == 16) v = fmaxf(v, dpp<kRowMirror>(v));
+  return v;
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp<kQuadSwap1>(v);
+  v += dpp<kQuadSwap2>(v);
+  v += dpp<kRowHalfMirror>(v);
+  if constexpr (N == 16) v += dpp<kRowMirror>(v);
+  return v;
+}
+// max over the wave, wave-uniform result
+__device__ __forceinline__ float wave_max_u(float v) {
+  v = group_max<16>(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 template <int GP>
 struct DecSmem {
   float qt[GP][D];            // rotated, scaled query (setup only)
@@ -139,10 +176,10 @@ struct DecSmem {
   float cv[16][8];            // cv[n][ct] = c_V[16 ct + n]
   float rk[T];                // r'_K
   float rv[T];                // r'_V * 4^-f(t % 8)
-  float sc[GP][T];            // raw QK results, then P' (fp32, natural order)
+  float sc[GP][T];            // QK results (offset already removed)
   uint32_t ahi[GP][4][4][4];  // query operand, fp16 pairs, [m][g][s][dword]
   uint32_t alo[GP][4][4][4];
-  float dc[GP];               // QK offset term per head
+  uint32_t ap[GP][4][4][4];   // P' operand, fp16 pairs, [m][g][s][dword]
   float alpha[GP];
 };
 
@@ -170,9 +207,214 @@ __device__ __forceinline__ void load_chunk(const DecodeArgs &a, int64_t bg, int6
   r.rv = *reinterpret_cast<const u32x2 *>(a.v_row + row);
 }
 
+// Per-lane state of one decode_split workgroup (one wave).
+template <int GP>
+struct SplitState {
+  static constexpr int NU = GP / 4;      // query-operand units per lane
+  static constexpr int LPH = 64 / GP;    // softmax lanes per head
+  static constexpr int NHW = 16 / LPH;   // half code words (8 tokens) per softmax lane
+  float qh[NU][8];                       // query * scales for this lane's units
+  f32x4 acc[8];                          // PV accumulators (rows = heads 4 lg + r)
+  float m_run, l_run;
+};
+
+template <int GP>
+__device__ __forceinline__ void process_chunk(const DecodeArgs &a, DecSmem<GP> &sm,
+                                              SplitState<GP> &st, const ChunkRegs &cur, int k,
+                                              int len, int lane, const u32x4 &one0,
+                                              const u32x4 &one1) {
+  constexpr int NU = SplitState<GP>::NU, LPH = SplitState<GP>::LPH, NHW = SplitState<GP>::NHW;
+  const int n = lane & 15, lg = lane >> 4;
+  const int gu = (lane >> 2) & 3, su = lane >> 4;
+  const int sh = lane / LPH;             // softmax head of this lane
+  const int nvalid = min(len - k * T, T);
+
+  // ---- scales to LDS ----
+  __syncthreads();  // previous chunk's LDS readers are done
+  sm.ck[elem_slot_pos(2 * lane)] = __uint_as_float(cur.ck[0]);
+  sm.ck[elem_slot_pos(2 * lane + 1)] = __uint_as_float(cur.ck[1]);
+  sm.cv[(2 * lane) & 15][(2 * lane) >> 4] = __uint_as_float(cur.cv[0]);
+  sm.cv[(2 * lane + 1) & 15][(2 * lane + 1) >> 4] = __uint_as_float(cur.cv[1]);
+  sm.rk[2 * lane] = __uint_as_float(cur.rk[0]);
+  sm.rk[2 * lane + 1] = __uint_as_float(cur.rk[1]);
+  const float rv0 = 2 * lane < nvalid ? __uint_as_float(cur.rv[0]) : 0.f;
+  const float rv1 = 2 * lane + 1 < nvalid ? __uint_as_float(cur.rv[1]) : 0.f;
+  int sig_v;
+  const float sv = range_scale(wave_max_u(fmaxf(rv0, rv1)), sig_v);
+  sm.rv[2 * lane] = rv0 * sv * __builtin_ldexpf(1.f, -2 * field_exp(2 * lane));
+  sm.rv[2 * lane + 1] = rv1 * sv * __builtin_ldexpf(1.f, -2 * field_exp(2 * lane + 1));
+  __syncthreads();
+
+  // ---- query operand: a = q * c_K * 2^sigma_q, fp16 hi/lo ----
+  int sig_q;
+  {
+    const f32x4 c0v = *reinterpret_cast<const f32x4 *>(&sm.ck[(gu * 4 + su) * 8]);
+    const f32x4 c1v = *reinterpret_cast<const f32x4 *>(&sm.ck[(gu * 4 + su) * 8 + 4]);
+    const float cc[8] = {c0v.x, c0v.y, c0v.z, c0v.w, c1v.x, c1v.y, c1v.z, c1v.w};
+    float av[NU][8];
+    float mx = 0.f;
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        av[u][e] = st.qh[u][e] * cc[e];
+        mx = fmaxf(mx, fabsf(av[u][e]));
+      }
+    const float sq = range_scale(wave_max_u(mx), sig_q);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      u32x4 hi, lo;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        // hi = x truncated to fp16's 11 significant bits (exact in fp32 and,
+        // for |x| in the fp16 normal range, exact in fp16); lo = x - hi.
+        // Formed in fp32 so that no f16 -> f32 read-back of the packed hi
+        // pair exists (that pattern was mis-fused into v_fma_mix_f32 with
+        // the wrong source register by this compiler).
+        const float x0 = av[u][2 * d] * sq, x1 = av[u][2 * d + 1] * sq;
+        const float h0 = __uint_as_float(__float_as_uint(x0) & 0xFFFFE000u);
+        const float h1 = __uint_as_float(__float_as_uint(x1) & 0xFFFFE000u);
+        hi[d] = pack_rtz(h0, h1);
+        lo[d] = pack_rtz(x0 - h0, x1 - h1);
+      }
+      const int mu = (lane & 3) + 4 * u;
+      *reinterpret_cast<u32x4 *>(&sm.ahi[mu][gu][su][0]) = hi;
+      *reinterpret_cast<u32x4 *>(&sm.alo[mu][gu][su][0]) = lo;
+    }
+  }
+  __syncthreads();
+  u32x4 ahi[4], alo[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    ahi[s] = n < GP ? *reinterpret_cast<const u32x4 *>(&sm.ahi[n][lg][s][0]) : u32x4{0u, 0u, 0u, 0u};
+    alo[s] = n < GP ? *reinterpret_cast<const u32x4 *>(&sm.alo[n][lg][s][0]) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // ---- QK^T: offset term first, then 8 token tiles x (4 hi + 4 lo) k-steps
+  // started from -1.5 * offset, so D = sum_j a_j (code_tj - 1.5) directly ----
+  {
+    f32x4 off = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      off = mfma(as_f16x8(ahi[s]), as_f16x8((s & 1) ? one1 : one0), off);
+      off = mfma(as_f16x8(alo[s]), as_f16x8((s & 1) ? one1 : one0), off);
+    }
+    off *= -1.5f;
+#pragma unroll
+    for (int tau = 0; tau < 8; ++tau) {
+      u32x4 b0, b1, b2, b3;
+      unpack_codes(cur.k[tau][0], b0, b1);
+      unpack_codes(cur.k[tau][1], b2, b3);
+      f32x4 d = mfma(as_f16x8(ahi[0]), as_f16x8(b0), off);
+      d = mfma(as_f16x8(ahi[1]), as_f16x8(b1), d);
+      d = mfma(as_f16x8(ahi[2]), as_f16x8(b2), d);
+      d = mfma(as_f16x8(ahi[3]), as_f16x8(b3), d);
+      d = mfma(as_f16x8(alo[0]), as_f16x8(b0), d);
+      d = mfma(as_f16x8(alo[1]), as_f16x8(b1), d);
+      d = mfma(as_f16x8(alo[2]), as_f16x8(b2), d);
+      d = mfma(as_f16x8(alo[3]), as_f16x8(b3), d);
+      if (lg < GP / 4) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm.sc[4 * lg + r][16 * tau + n] = d[r];
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- online softmax. A lane owns NHW half code words of head sh: the
+  // tokens 16 w + 4 hs + i and 16 w + 8 + 4 hs + i (i < 4), i.e. exactly
+  // the fp16 pairs of one P' operand dword quad ----
+  {
+    const float kscale = __builtin_ldexpf(1.f, 24 - sig_q);
+    float s[NHW][8];
+    float mc = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NHW; ++j) {
+      const int hw = (lane % LPH) * NHW + j;      // half-word index 0..15
+      const int t1 = 16 * (hw >> 1) + 4 * (hw & 1);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int t = t1 + 8 * q;
+        const f32x4 raw = *reinterpret_cast<const f32x4 *>(&sm.sc[sh][t]);
+        const f32x4 rk4 = *reinterpret_cast<const f32x4 *>(&sm.rk[t]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = raw[i] * (rk4[i] * kscale);
+          s[j][4 * q + i] = t + i < nvalid ? v : -INFINITY;
+          mc = fmaxf(mc, s[j][4 * q + i]);
+        }
+      }
+    }
+    mc = group_max<LPH>(mc);
+    // integer running max (log2 units): P' of a chunk then differs between
+    // split layouts only by powers of two, so its fp16 rounding does not
+    const float mn = fmaxf(st.m_run, ceilf(mc));
+    const float al = mn == -INFINITY ? 1.f : exp2f(st.m_run - mn);
+    float ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < NHW; ++j) {
+      const int hw = (lane % LPH) * NHW + j;
+      const int t1 = 16 * (hw >> 1) + 4 * (hw & 1);
+      const f32x4 rva = *reinterpret_cast<const f32x4 *>(&sm.rv[t1]);
+      const f32x4 rvb = *reinterpret_cast<const f32x4 *>(&sm.rv[t1 + 8]);
+      u32x4 pk;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pa = mn == -INFINITY ? 0.f : exp2f(s[j][i] - mn);
+        const float pb = mn == -INFINITY ? 0.f : exp2f(s[j][4 + i] - mn);
+        ps += pa + pb;
+        pk[i] = pack_rtz(pa * rva[i], pb * rvb[i]);
+      }
+      // dword quad (word hw >> 1, half hw & 1) of the P' operand of head sh:
+      // lane group g = word >> 1, k-step s = 2 (word & 1) + half
+      const int w = hw >> 1;
+      *reinterpret_cast<u32x4 *>(&sm.ap[sh][w >> 1][2 * (w & 1) + (hw & 1)][0]) = pk;
+    }
+    st.l_run = st.l_run * al + ps;
+    st.m_run = mn;
+    if (lane % LPH == 0) sm.alpha[sh] = al;
+  }
+  __syncthreads();
+
+  // ---- PV: 8 channel tiles x 4 k-steps, started from -1.5 * offset ----
+  {
+    u32x4 ap[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      ap[s] = n < GP ? *reinterpret_cast<const u32x4 *>(&sm.ap[n][lg][s][0]) : u32x4{0u, 0u, 0u, 0u};
+    f32x4 off = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) off = mfma(as_f16x8(ap[s]), as_f16x8((s & 1) ? one1 : one0), off);
+    off *= -1.5f;
+    f32x4 alr;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) alr[r] = (4 * lg + r < GP) ? sm.alpha[4 * lg + r] : 1.f;
+    // the running max moves by whole powers of two: rescale only when it moved
+    if (alr[0] != 1.f || alr[1] != 1.f || alr[2] != 1.f || alr[3] != 1.f) {
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) st.acc[ct] *= alr;
+    }
+    const float vscale = __builtin_ldexpf(1.f, 24 - sig_v);
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+      u32x4 b0, b1, b2, b3;
+      unpack_codes(cur.v[ct][0], b0, b1);
+      unpack_codes(cur.v[ct][1], b2, b3);
+      f32x4 d = mfma(as_f16x8(ap[0]), as_f16x8(b0), off);
+      d = mfma(as_f16x8(ap[1]), as_f16x8(b1), d);
+      d = mfma(as_f16x8(ap[2]), as_f16x8(b2), d);
+      d = mfma(as_f16x8(ap[3]), as_f16x8(b3), d);
+      const float cvs = sm.cv[n][ct] * vscale;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st.acc[ct][r] = fmaf(cvs, d[r], st.acc[ct][r]);
+    }
+  }
+}
+
 template <int GP>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   __shared__ DecSmem<GP> sm;
+  constexpr int NU = SplitState<GP>::NU, LPH = SplitState<GP>::LPH;
   const int lane = threadIdx.x;
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = a.q_heads / a.kv_heads;
@@ -192,224 +434,44 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   }
   __syncthreads();
   lds_fwht_rows(&sm.qt[0][0], GP);
-  // this lane's a-operand units: head mu = (lane & 3) + 4u, group gu, k-step su
-  const int gu = (lane >> 2) & 3, su = lane >> 4;
-  constexpr int NU = GP / 4;
-  float qh[NU][8];
+  SplitState<GP> st;
   {
+    const int gu = (lane >> 2) & 3, su = lane >> 4;
     const float qs = a.scale * kLog2e * kInvSqrtD;
 #pragma unroll
     for (int u = 0; u < NU; ++u)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int j = kslot_elem(gu, su, e);
-        qh[u][e] = sm.qt[(lane & 3) + 4 * u][j] * qs * __builtin_ldexpf(1.f, -2 * field_exp(j));
+        st.qh[u][e] = sm.qt[(lane & 3) + 4 * u][j] * qs * __builtin_ldexpf(1.f, -2 * field_exp(j));
       }
   }
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) st.acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m_run = -INFINITY;
+  st.l_run = 0.f;
   // constant operand: code 1 in every field (the level offset term)
   u32x4 one0, one1;
   unpack_codes(0x55555555u, one0, one1);
 
-  // state: lanes 16 r' .. hold heads 4 (lane >> 4) + r of channel 16 ct + (lane & 15)
-  f32x4 acc[8];
-#pragma unroll
-  for (int ct = 0; ct < 8; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  constexpr int LPH = 64 / GP;  // softmax: lanes per head
-  constexpr int TPL = T / LPH;  // tokens per lane
-  const int sh = lane / LPH;    // softmax head of this lane
-  const int st0 = (lane % LPH) * TPL;
-  float m_run = -INFINITY, l_run = 0.f;
-
+  // chunks [c0, c1); the next chunk's loads are in flight while the current
+  // one is computed
   ChunkRegs cur, nxt;
   if (c0 < c1) load_chunk(a, bg, nch, c0, lane, cur);
-  const int n = lane & 15, lg = lane >> 4;
   for (int k = c0; k < c1; ++k) {
     if (k + 1 < c1) load_chunk(a, bg, nch, k + 1, lane, nxt);
-    const int nvalid = min(len - k * T, T);  // tokens [0, nvalid) of this chunk are live
-
-    // ---- scales to LDS ----
-    __syncthreads();  // previous chunk's readers are done
-    {
-      const float ck0 = __uint_as_float(cur.ck[0]), ck1 = __uint_as_float(cur.ck[1]);
-      sm.ck[elem_slot_pos(2 * lane)] = ck0;
-      sm.ck[elem_slot_pos(2 * lane + 1)] = ck1;
-      sm.cv[(2 * lane) & 15][(2 * lane) >> 4] = __uint_as_float(cur.cv[0]);
-      sm.cv[(2 * lane + 1) & 15][(2 * lane + 1) >> 4] = __uint_as_float(cur.cv[1]);
-      sm.rk[2 * lane] = __uint_as_float(cur.rk[0]);
-      sm.rk[2 * lane + 1] = __uint_as_float(cur.rk[1]);
-    }
-    // V row scales with their field scale; the chunk's range scale 2^sigma_v
-    float rv0 = 2 * lane < nvalid ? __uint_as_float(cur.rv[0]) : 0.f;
-    float rv1 = 2 * lane + 1 < nvalid ? __uint_as_float(cur.rv[1]) : 0.f;
-    int sig_v;
-    const float sv = range_scale(wave_max(fmaxf(rv0, rv1)), sig_v);
-    sm.rv[2 * lane] = rv0 * sv * __builtin_ldexpf(1.f, -2 * field_exp(2 * lane));
-    sm.rv[2 * lane + 1] = rv1 * sv * __builtin_ldexpf(1.f, -2 * field_exp(2 * lane + 1));
-    __syncthreads();
-
-    // ---- query operand: a = q * c_K * 2^sigma, fp16 hi/lo ----
-    int sig_q;
-    {
-      const f32x4 c0v = *reinterpret_cast<const f32x4 *>(&sm.ck[(gu * 4 + su) * 8]);
-      const f32x4 c1v = *reinterpret_cast<const f32x4 *>(&sm.ck[(gu * 4 + su) * 8 + 4]);
-      const float cc[8] = {c0v.x, c0v.y, c0v.z, c0v.w, c1v.x, c1v.y, c1v.z, c1v.w};
-      float av[NU][8];
-      float mx = 0.f;
-#pragma unroll
-      for (int u = 0; u < NU; ++u)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          av[u][e] = qh[u][e] * cc[e];
-          mx = fmaxf(mx, fabsf(av[u][e]));
-        }
-      const float sq = range_scale(wave_max(mx), sig_q);
-#pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        u32x4 hi, lo;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          // hi = x truncated to fp16's 11 significant bits (exact in fp32 and,
-          // for |x| in the fp16 normal range, exact in fp16); lo = x - hi.
-          // Formed in fp32 so that no f16 -> f32 read-back of the packed hi
-          // pair exists (that pattern was mis-fused into v_fma_mix_f32 with
-          // the wrong source register by this compiler).
-          const float x0 = av[u][2 * d] * sq, x1 = av[u][2 * d + 1] * sq;
-          const float h0 = __uint_as_float(__float_as_uint(x0) & 0xFFFFE000u);
-          const float h1 = __uint_as_float(__float_as_uint(x1) & 0xFFFFE000u);
-          hi[d] = pack_rtz(h0, h1);
-          lo[d] = pack_rtz(x0 - h0, x1 - h1);
-        }
-        const int mu = (lane & 3) + 4 * u;
-        *reinterpret_cast<u32x4 *>(&sm.ahi[mu][gu][su][0]) = hi;
-        *reinterpret_cast<u32x4 *>(&sm.alo[mu][gu][su][0]) = lo;
-      }
-    }
-    __syncthreads();
-    u32x4 ahi[4], alo[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (n < GP) {
-        ahi[s] = *reinterpret_cast<const u32x4 *>(&sm.ahi[n][lg][s][0]);
-        alo[s] = *reinterpret_cast<const u32x4 *>(&sm.alo[n][lg][s][0]);
-      } else {
-        ahi[s] = u32x4{0u, 0u, 0u, 0u};
-        alo[s] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-
-    // ---- QK^T: 8 token tiles x (4 hi + 4 lo) k-steps, plus the offset term ----
-    {
-      f32x4 dcv = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        dcv = mfma(as_f16x8(ahi[s]), as_f16x8((s & 1) ? one1 : one0), dcv);
-        dcv = mfma(as_f16x8(alo[s]), as_f16x8((s & 1) ? one1 : one0), dcv);
-      }
-      if (n == 0 && lg < GP / 4) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sm.dc[4 * lg + r] = dcv[r];
-      }
-    }
-#pragma unroll
-    for (int tau = 0; tau < 8; ++tau) {
-      u32x4 b0, b1, b2, b3;
-      unpack_codes(cur.k[tau][0], b0, b1);
-      unpack_codes(cur.k[tau][1], b2, b3);
-      f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
-      d = mfma(as_f16x8(ahi[0]), as_f16x8(b0), d);
-      d = mfma(as_f16x8(ahi[1]), as_f16x8(b1), d);
-      d = mfma(as_f16x8(ahi[2]), as_f16x8(b2), d);
-      d = mfma(as_f16x8(ahi[3]), as_f16x8(b3), d);
-      d = mfma(as_f16x8(alo[0]), as_f16x8(b0), d);
-      d = mfma(as_f16x8(alo[1]), as_f16x8(b1), d);
-      d = mfma(as_f16x8(alo[2]), as_f16x8(b2), d);
-      d = mfma(as_f16x8(alo[3]), as_f16x8(b3), d);
-      if (lg < GP / 4) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sm.sc[4 * lg + r][16 * tau + n] = d[r];
-      }
-    }
-    __syncthreads();
-
-    // ---- online softmax: lane holds head sh, tokens [st0, st0 + TPL) ----
-    {
-      const float kscale = __builtin_ldexpf(1.f, 24 - sig_q);
-      const float off = 1.5f * sm.dc[sh];
-      float s[TPL];
-      float mc = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < TPL; ++i) {
-        const int t = st0 + i;
-        const float raw = sm.sc[sh][t];
-        s[i] = t < nvalid ? (raw - off) * (sm.rk[t] * kscale) : -INFINITY;
-        mc = fmaxf(mc, s[i]);
-      }
-#pragma unroll
-      for (int m = 1; m < LPH; m <<= 1) mc = fmaxf(mc, __shfl_xor(mc, m, 64));
-      // integer running max (log2 units): P' of a chunk then differs between
-      // split layouts only by powers of two, so its fp16 rounding does not
-      const float mn = fmaxf(m_run, ceilf(mc));
-      const float al = mn == -INFINITY ? 1.f : exp2f(m_run - mn);
-      float ps = 0.f;
-#pragma unroll
-      for (int i = 0; i < TPL; ++i) {
-        const int t = st0 + i;
-        const float p = mn == -INFINITY ? 0.f : exp2f(s[i] - mn);
-        ps += p;
-        sm.sc[sh][t] = p * sm.rv[t];  // P' (fp32), natural order
-      }
-      l_run = l_run * al + ps;
-      m_run = mn;
-      if (lane % LPH == 0) sm.alpha[sh] = al;
-    }
-    __syncthreads();
-
-    // ---- PV: P' operand, 8 channel tiles x 4 k-steps, plus the offset term ----
-    {
-      u32x4 ap[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        if (n < GP) {
-#pragma unroll
-          for (int d = 0; d < 4; ++d)
-            ap[s][d] = pack_rtz(sm.sc[n][kslot_elem(lg, s, 2 * d)],
-                                sm.sc[n][kslot_elem(lg, s, 2 * d + 1)]);
-        } else {
-          ap[s] = u32x4{0u, 0u, 0u, 0u};
-        }
-      }
-      f32x4 dcp = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) dcp = mfma(as_f16x8(ap[s]), as_f16x8((s & 1) ? one1 : one0), dcp);
-      const float vscale = __builtin_ldexpf(1.f, 24 - sig_v);
-      f32x4 alr;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) alr[r] = (4 * lg + r < GP) ? sm.alpha[4 * lg + r] : 1.f;
-#pragma unroll
-      for (int ct = 0; ct < 8; ++ct) {
-        u32x4 b0, b1, b2, b3;
-        unpack_codes(cur.v[ct][0], b0, b1);
-        unpack_codes(cur.v[ct][1], b2, b3);
-        f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
-        d = mfma(as_f16x8(ap[0]), as_f16x8(b0), d);
-        d = mfma(as_f16x8(ap[1]), as_f16x8(b1), d);
-        d = mfma(as_f16x8(ap[2]), as_f16x8(b2), d);
-        d = mfma(as_f16x8(ap[3]), as_f16x8(b3), d);
-        const float cvs = sm.cv[n][ct] * vscale;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[ct][r] = acc[ct][r] * alr[r] + cvs * (d[r] - 1.5f * dcp[r]);
-      }
-    }
+    process_chunk<GP>(a, sm, st, cur, k, len, lane, one0, one1);
     cur = nxt;
   }
 
   // ---- partial results: (m, l, acc) per query head of this split ----
-#pragma unroll
-  for (int m = 1; m < LPH; m <<= 1) l_run += __shfl_xor(l_run, m, 64);
+  const int sh = lane / LPH;
+  const float lsum = group_sum<LPH>(st.l_run);
+  const int n = lane & 15, lg = lane >> 4;
   if (lane % LPH == 0 && sh < G) {
     float *pp = a.partial + (((int64_t)b * a.q_heads + g * G + sh) * a.n_split + split) * (2 + D);
-    pp[0] = m_run;
-    pp[1] = l_run;
+    pp[0] = st.m_run;
+    pp[1] = lsum;
   }
   if (lg < GP / 4) {
 #pragma unroll
@@ -418,28 +480,58 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       if (h < G) {
         float *pp = a.partial + (((int64_t)b * a.q_heads + g * G + h) * a.n_split + split) * (2 + D);
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) pp[2 + 16 * ct + n] = acc[ct][r];
+        for (int ct = 0; ct < 8; ++ct) pp[2 + 16 * ct + n] = st.acc[ct][r];
       }
     }
   }
 }
 
+// Log-sum-exp merge of the split partials of one (sequence, query head), then
+// the inverse rotation. Thread s < n_split first reads split s's (m, l); the
+// block reduces the maximum and the weighted denominator; then every thread
+// (one output channel) walks the splits with independent, coalesced loads.
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
   __shared__ float o[D];
+  __shared__ float wgt[D];
+  __shared__ float red[4];
   const int h = blockIdx.x, b = blockIdx.y, j = threadIdx.x;
   const float *pp = a.partial + ((int64_t)b * a.q_heads + h) * a.n_split * (2 + D);
-  float M = -INFINITY;
-  for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, pp[s * (2 + D)]);
+  // pass 1: maximum of the split maxima
+  float mx = -INFINITY;
+  for (int s = j; s < a.n_split; s += D) mx = fmaxf(mx, pp[(int64_t)s * (2 + D)]);
+  mx = group_max<16>(mx);
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  if ((j & 63) == 0) red[j >> 6] = mx;
+  __syncthreads();
+  const float M = fmaxf(red[0], red[1]);
+  // pass 2: weights, denominator and numerator
   float num = 0.f, den = 0.f;
   if (M != -INFINITY) {
-    for (int s = 0; s < a.n_split; ++s) {
-      const float ms = pp[s * (2 + D)];
-      if (ms == -INFINITY) continue;
-      const float e = exp2f(ms - M);
-      den += e * pp[s * (2 + D) + 1];
-      num += e * pp[s * (2 + D) + 2 + j];
+    for (int base = 0; base < a.n_split; base += D) {
+      const int s = base + j;
+      float w = 0.f;
+      if (s < a.n_split) {
+        const float ms = pp[(int64_t)s * (2 + D)];
+        w = ms == -INFINITY ? 0.f : exp2f(ms - M);
+        den += w * pp[(int64_t)s * (2 + D) + 1];
+      }
+      __syncthreads();  // previous round's readers of wgt are done
+      wgt[j] = w;
+      __syncthreads();
+      const int cnt = min(D, a.n_split - base);
+      const float *col = pp + (int64_t)base * (2 + D) + 2 + j;
+#pragma unroll 8
+      for (int q = 0; q < cnt; ++q) num += wgt[q] * col[(int64_t)q * (2 + D)];
     }
   }
+  den = group_sum<16>(den);
+  den += __shfl_xor(den, 16, 64);
+  den += __shfl_xor(den, 32, 64);
+  __syncthreads();
+  if ((j & 63) == 0) red[2 + (j >> 6)] = den;
+  __syncthreads();
+  den = red[2] + red[3];
   o[j] = den > 0.f ? num / den : 0.f;
   __syncthreads();
   lds_fwht_rows(o, 1);
