@@ -169,17 +169,37 @@ __device__ __forceinline__ float wave_max_u(float v) {
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
+// Per-head rows are padded by 4 words so that rows of different heads start
+// on different LDS banks.
+constexpr int SC_PITCH = T + 4;       // floats per head row of sc
+constexpr int OP_PITCH = 4 * 4 * 4 + 4;  // words per head row of an operand array
+
+// LDS position of token t in the per-token arrays (sc, rk, rv): inside each
+// 16-token tile the four 4-token quads are permuted by an XOR that depends on
+// the tile pair, so that the softmax lanes' 16-byte reads (one tile per lane,
+// 8 lanes per LDS cycle) fall on distinct banks. Quads stay contiguous.
+__host__ __device__ constexpr int quad_swz(int tile) {  // {0, 2, 1, 3}[(tile >> 1) & 3]
+  return (((tile >> 1) & 1) << 1) | ((tile >> 2) & 1);
+}
+__host__ __device__ constexpr int tok_pos(int t) {
+  return (t & ~15) | ((((t >> 2) & 3) ^ quad_swz(t >> 4)) << 2) | (t & 3);
+}
+// Word offset of operand quad Q = 4 g + s (lane group g, k-step s) in a head
+// row of ahi/alo/ap: quads Q and Q + 8 are moved to different banks for the
+// softmax lanes' P' writes.
+__host__ __device__ constexpr int op_quad(int q) { return 4 * (q ^ ((q >> 3) & 1)); }
+
 template <int GP>
-struct DecSmem {
-  float qt[GP][D];            // rotated, scaled query (setup only)
-  float ck[D];                // c_K in [g][s][e] order
-  float cv[16][8];            // cv[n][ct] = c_V[16 ct + n]
-  float rk[T];                // r'_K
-  float rv[T];                // r'_V * 4^-f(t % 8)
-  float sc[GP][T];            // QK results (offset already removed)
-  uint32_t ahi[GP][4][4][4];  // query operand, fp16 pairs, [m][g][s][dword]
-  uint32_t alo[GP][4][4][4];
-  uint32_t ap[GP][4][4][4];   // P' operand, fp16 pairs, [m][g][s][dword]
+struct alignas(16) DecSmem {
+  alignas(16) float qt[GP][D];            // rotated, scaled query (setup only)
+  alignas(16) float ck[D];                // c_K in [g][s][e] order
+  alignas(16) float cv[16][9];            // cv[n][ct] = c_V[16 ct + n] (odd pitch)
+  alignas(16) float rk[T];                // r'_K, tok_pos order
+  alignas(16) float rv[T];                // r'_V * 4^-f(t % 8), tok_pos order
+  alignas(16) float sc[GP][SC_PITCH];     // QK results (offset already removed), tok_pos order
+  alignas(16) uint32_t ahi[GP][OP_PITCH]; // query operand, fp16 pairs, [m][(g * 4 + s) * 4 + dword]
+  alignas(16) uint32_t alo[GP][OP_PITCH];
+  alignas(16) uint32_t ap[GP][OP_PITCH];  // P' operand, same layout
   float alpha[GP];
 };
 
@@ -235,14 +255,15 @@ __device__ __forceinline__ void process_chunk(const DecodeArgs &a, DecSmem<GP> &
   sm.ck[elem_slot_pos(2 * lane + 1)] = __uint_as_float(cur.ck[1]);
   sm.cv[(2 * lane) & 15][(2 * lane) >> 4] = __uint_as_float(cur.cv[0]);
   sm.cv[(2 * lane + 1) & 15][(2 * lane + 1) >> 4] = __uint_as_float(cur.cv[1]);
-  sm.rk[2 * lane] = __uint_as_float(cur.rk[0]);
-  sm.rk[2 * lane + 1] = __uint_as_float(cur.rk[1]);
+  const int tp = tok_pos(2 * lane);  // 2 lane and 2 lane + 1 stay adjacent
+  sm.rk[tp] = __uint_as_float(cur.rk[0]);
+  sm.rk[tp + 1] = __uint_as_float(cur.rk[1]);
   const float rv0 = 2 * lane < nvalid ? __uint_as_float(cur.rv[0]) : 0.f;
   const float rv1 = 2 * lane + 1 < nvalid ? __uint_as_float(cur.rv[1]) : 0.f;
   int sig_v;
   const float sv = range_scale(wave_max_u(fmaxf(rv0, rv1)), sig_v);
-  sm.rv[2 * lane] = rv0 * sv * __builtin_ldexpf(1.f, -2 * field_exp(2 * lane));
-  sm.rv[2 * lane + 1] = rv1 * sv * __builtin_ldexpf(1.f, -2 * field_exp(2 * lane + 1));
+  sm.rv[tp] = rv0 * sv * __builtin_ldexpf(1.f, -2 * field_exp(2 * lane));
+  sm.rv[tp + 1] = rv1 * sv * __builtin_ldexpf(1.f, -2 * field_exp(2 * lane + 1));
   __syncthreads();
 
   // ---- query operand: a = q * c_K * 2^sigma_q, fp16 hi/lo ----
@@ -278,16 +299,16 @@ __device__ __forceinline__ void process_chunk(const DecodeArgs &a, DecSmem<GP> &
         lo[d] = pack_rtz(x0 - h0, x1 - h1);
       }
       const int mu = (lane & 3) + 4 * u;
-      *reinterpret_cast<u32x4 *>(&sm.ahi[mu][gu][su][0]) = hi;
-      *reinterpret_cast<u32x4 *>(&sm.alo[mu][gu][su][0]) = lo;
+      *reinterpret_cast<u32x4 *>(&sm.ahi[mu][op_quad(gu * 4 + su)]) = hi;
+      *reinterpret_cast<u32x4 *>(&sm.alo[mu][op_quad(gu * 4 + su)]) = lo;
     }
   }
   __syncthreads();
   u32x4 ahi[4], alo[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    ahi[s] = n < GP ? *reinterpret_cast<const u32x4 *>(&sm.ahi[n][lg][s][0]) : u32x4{0u, 0u, 0u, 0u};
-    alo[s] = n < GP ? *reinterpret_cast<const u32x4 *>(&sm.alo[n][lg][s][0]) : u32x4{0u, 0u, 0u, 0u};
+    ahi[s] = n < GP ? *reinterpret_cast<const u32x4 *>(&sm.ahi[n][op_quad(lg * 4 + s)]) : u32x4{0u, 0u, 0u, 0u};
+    alo[s] = n < GP ? *reinterpret_cast<const u32x4 *>(&sm.alo[n][op_quad(lg * 4 + s)]) : u32x4{0u, 0u, 0u, 0u};
   }
 
   // ---- QK^T: offset term first, then 8 token tiles x (4 hi + 4 lo) k-steps
@@ -315,7 +336,7 @@ __device__ __forceinline__ void process_chunk(const DecodeArgs &a, DecSmem<GP> &
       d = mfma(as_f16x8(alo[3]), as_f16x8(b3), d);
       if (lg < GP / 4) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sm.sc[4 * lg + r][16 * tau + n] = d[r];
+        for (int r = 0; r < 4; ++r) sm.sc[4 * lg + r][16 * tau + (n ^ (quad_swz(tau) << 2))] = d[r];
       }
     }
   }
@@ -335,8 +356,8 @@ __device__ __forceinline__ void process_chunk(const DecodeArgs &a, DecSmem<GP> &
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int t = t1 + 8 * q;
-        const f32x4 raw = *reinterpret_cast<const f32x4 *>(&sm.sc[sh][t]);
-        const f32x4 rk4 = *reinterpret_cast<const f32x4 *>(&sm.rk[t]);
+        const f32x4 raw = *reinterpret_cast<const f32x4 *>(&sm.sc[sh][tok_pos(t)]);
+        const f32x4 rk4 = *reinterpret_cast<const f32x4 *>(&sm.rk[tok_pos(t)]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float v = raw[i] * (rk4[i] * kscale);
@@ -355,8 +376,8 @@ __device__ __forceinline__ void process_chunk(const DecodeArgs &a, DecSmem<GP> &
     for (int j = 0; j < NHW; ++j) {
       const int hw = (lane % LPH) * NHW + j;
       const int t1 = 16 * (hw >> 1) + 4 * (hw & 1);
-      const f32x4 rva = *reinterpret_cast<const f32x4 *>(&sm.rv[t1]);
-      const f32x4 rvb = *reinterpret_cast<const f32x4 *>(&sm.rv[t1 + 8]);
+      const f32x4 rva = *reinterpret_cast<const f32x4 *>(&sm.rv[tok_pos(t1)]);
+      const f32x4 rvb = *reinterpret_cast<const f32x4 *>(&sm.rv[tok_pos(t1 + 8)]);
       u32x4 pk;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -368,7 +389,7 @@ __device__ __forceinline__ void process_chunk(const DecodeArgs &a, DecSmem<GP> &
       // dword quad (word hw >> 1, half hw & 1) of the P' operand of head sh:
       // lane group g = word >> 1, k-step s = 2 (word & 1) + half
       const int w = hw >> 1;
-      *reinterpret_cast<u32x4 *>(&sm.ap[sh][w >> 1][2 * (w & 1) + (hw & 1)][0]) = pk;
+      *reinterpret_cast<u32x4 *>(&sm.ap[sh][op_quad((w >> 1) * 4 + 2 * (w & 1) + (hw & 1))]) = pk;
     }
     st.l_run = st.l_run * al + ps;
     st.m_run = mn;
@@ -381,7 +402,7 @@ __device__ __forceinline__ void process_chunk(const DecodeArgs &a, DecSmem<GP> &
     u32x4 ap[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      ap[s] = n < GP ? *reinterpret_cast<const u32x4 *>(&sm.ap[n][lg][s][0]) : u32x4{0u, 0u, 0u, 0u};
+      ap[s] = n < GP ? *reinterpret_cast<const u32x4 *>(&sm.ap[n][op_quad(lg * 4 + s)]) : u32x4{0u, 0u, 0u, 0u};
     f32x4 off = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) off = mfma(as_f16x8(ap[s]), as_f16x8((s & 1) ? one1 : one0), off);
