@@ -14,6 +14,8 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
     # packed fp32 VALU ops stay off on the test machines
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results straight into VGPRs (no accumulator-register round trip)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
 ]
 

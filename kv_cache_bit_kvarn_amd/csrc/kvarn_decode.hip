@@ -12,19 +12,26 @@
 // row scale of V into each probability, and the column scale of V into the
 // output; the output is rotated back after the split-KV merge.
 //
-// decode_split: grid (n_split, kv_heads, batch), one wave64 per workgroup,
-// walking its range of 128-token chunks with an online softmax; the next
-// chunk's codes and scales are loaded while the current one is computed.
-// QK^T and PV run on v_mfma_f32_16x16x32_f16:
-//  * code operand: a 32-bit word holds 16 codes; AND-ing it with a mask that
-//    keeps one 2-bit field in each 16-bit half yields two fp16 subnormals
-//    c * 4^i * 2^-24 (i = the field's position), exactly. Eight masks (one
-//    shift) turn a word into the operand registers of two MFMA k-steps.
-//  * the other operand (query * c_K, or p * r'_V) carries 4^-i, a power-of-
-//    two range scale 2^sigma, and (query only) an fp16 hi/lo split, run as
-//    two k-passes over the same code registers, so scores keep ~22 bits;
-//  * the -1.5 offset of the levels is one more MFMA per chunk against a
-//    constant operand that encodes code 1 in every field.
+// decode_split: grid (n_split * head_groups, kv_heads, batch), one wave64 per
+// workgroup serving up to 4 query heads of one kv-head over its range of
+// 128-token chunks with an online softmax; the next chunk's codes and scales
+// are loaded while the current one is computed. Both products run on
+// v_mfma_scale_f32_16x16x128_f8f6f4, the cache codes being its fp4 operand:
+//  * a 2-bit code c in the low bits of a 4-bit field is the e2m1 number c/2,
+//    so w & 0x33333333 and (w >> 2) & 0x33333333 turn a code word into two
+//    operand registers (16 codes for 3 instructions), and c/2 - 3/4 is half
+//    the level c - 1.5;
+//  * the other operand (query * c_K, or p * r'_V) is fp8 e4m3, written as a
+//    sum of terms x = t0 + t1 + ... where each term is the fp8 rounding of
+//    what the earlier ones left (4 terms, ~16 significant bits, for the query;
+//    3 terms, ~12 bits, for the probabilities). Row 4 h + k of the 16-row
+//    operand holds term k of head h, so one MFMA covers 16 tokens (QK) or 16
+//    channels (PV) for all heads and terms, and the terms of a head land in
+//    the four accumulator registers of one lane;
+//  * a per-head power-of-two range scale (largest magnitude in [128, 256))
+//    is undone by the MFMA's per-row E8M0 scale;
+//  * the level offset is one MFMA per chunk against a constant-1.5 operand,
+//    fed in as the accumulator input.
 // decode_combine: grid (q_heads, batch): log-sum-exp merge of the partials
 // (m, l, acc[128]), then the inverse rotation.
 #include "kvarn_internal.h"
@@ -32,84 +39,123 @@
 namespace kvarn {
 namespace {
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int HG = 4;                       // query heads per workgroup
+constexpr uint32_t kFieldMask = 0x33333333u;  // low 2 bits of every 4-bit field
+constexpr uint32_t kFp4Half3 = 0x33333333u;   // e2m1 1.5 in every field
 
-// ---- code word -> fp16 subnormal operands --------------------------------
-// A code word w holds codes c_0..c_15 at bits 2m. Output dwords (two fp16 each,
-// low half first):
-//   o[i]   = (c_i, c_{8+i}) * 4^i        i = 0..3   (k-step half 0)
-//   o[4]   = (c_4, c_12)    * 4^4                   (k-step half 1)
-//   o[5+i] = (c_{5+i}, c_{13+i}) * 4^i  i = 0..2   (k-step half 1)
-// all times 2^-24. The field scale of code index c is 4^f(c % 8) with
-// f = {0, 1, 2, 3, 4, 0, 1, 2}.
-__device__ __forceinline__ void unpack_codes(uint32_t w, u32x4 &h0, u32x4 &h1) {
-  const uint32_t x = w >> 10;
-  h0[0] = w & 0x00030003u;
-  h0[1] = w & 0x000C000Cu;
-  h0[2] = w & 0x00300030u;
-  h0[3] = w & 0x00C000C0u;
-  h1[0] = w & 0x03000300u;
-  h1[1] = x & 0x00030003u;
-  h1[2] = x & 0x000C000Cu;
-  h1[3] = x & 0x00300030u;
+// ---- the k order shared by both MFMA operands -----------------------------
+// fp8 operand (8 dwords per lane, lane = row + 16 g): byte e holds
+//   k = 16 g + e (e < 16),  k = 48 + 16 g + e (e >= 16).
+// fp4 operand (4 dwords per lane, lane = column + 16 g): field e holds
+//   k = 32 g + e.
+// A code row (a token of K, a channel of V: 32 bytes) gives lane group g its
+// bytes [8 g, 8 g + 8) = words w0, w1, unpacked to the dwords
+//   w0 & M, (w0 >> 2) & M, w1 & M, (w1 >> 2) & M,
+// so field i of dword d carries code 32 g + 16 (d >> 1) + 2 i + (d & 1) of
+// the row. k_elem(k) is therefore the channel (QK) or token (PV) at index k.
+__host__ __device__ constexpr int k_elem(int k) {
+  return 32 * (k >> 5) + 16 * ((k >> 4) & 1) + 2 * (k & 7) + ((k >> 3) & 1);
 }
+__host__ __device__ constexpr int fp8_k(int g, int e) { return e < 16 ? 16 * g + e : 48 + 16 * g + e; }
 
-__host__ __device__ constexpr int field_exp(int c) {  // f(c % 8)
-  return (c & 7) < 5 ? (c & 7) : (c & 7) - 5;
+// The fp8 operand is built in 8-byte packets: slot s = 4 g + p is bytes
+// [8 p, 8 p + 8) of lane group g, and its byte j holds element
+// slot_elem(s, j) = 16 (s >> 2) + 64 ((s >> 1) & 1) + (s & 1) + 2 j.
+// Slot s is also the output column of the lane that computes it, so the
+// softmax lane of column s finds exactly the scores of its P' packet.
+__host__ __device__ constexpr int slot_elem(int s, int j) {
+  return k_elem(fp8_k(s >> 2, 8 * (s & 3) + j));
 }
+__host__ __device__ constexpr int elem_slot(int x) { return 4 * ((x >> 4) & 3) + 2 * (x >> 6) + (x & 1); }
+__host__ __device__ constexpr int elem_j(int x) { return (x >> 1) & 7; }
+// Per-element LDS arrays read slot-wise: 8 floats per slot and 4 floats of
+// padding after every 4 slots, so 16-byte reads by 8 lanes hit distinct banks.
+__host__ __device__ constexpr int slot_base(int s) { return 8 * s + 4 * (s >> 2); }
+__host__ __device__ constexpr int elem_pos(int x) { return slot_base(elem_slot(x)) + elem_j(x); }
+// c_V: channel c is read by the lanes of output column c % 16, tile c / 16
+__host__ __device__ constexpr int cv_pos(int c) { return slot_base(c & 15) + (c >> 4); }
+constexpr int SLOT_ARRAY = 8 * 16 + 4 * 4;
+constexpr int OP_ROW = 36;  // dwords per operand row: 4 lane groups x 8 + 4 padding
 
-// code index (0..15 within a word) held by k-slot e of k-step half hs
-__device__ __forceinline__ int slot_code(int hs, int e) {
-  if (hs == 0) return (e & 1) ? 8 + (e >> 1) : (e >> 1);
-  if (e < 2) return e ? 12 : 4;
-  return (e & 1) ? 13 + ((e - 3) >> 1) : 5 + ((e - 2) >> 1);
-}
-
-// lane-group g (0..3) covers code words 2g, 2g+1 of a row, i.e. elements
-// [32 g, 32 g + 32); k-step s (0..3) takes word 2g + (s >> 1), half s & 1.
-__device__ __forceinline__ int kslot_elem(int g, int s, int e) {
-  return 32 * g + 16 * (s >> 1) + slot_code(s & 1, e);
-}
-
-// position of element j in the [g][s][e] order of kslot_elem
-__device__ __forceinline__ int elem_slot_pos(int j) {
-  const int g = j >> 5, w = (j >> 4) & 1, c = j & 15;
-  int hs, e;
-  if (c < 4) { hs = 0; e = 2 * c; }
-  else if (c >= 8 && c < 12) { hs = 0; e = 2 * (c - 8) + 1; }
-  else if (c == 4) { hs = 1; e = 0; }
-  else if (c == 12) { hs = 1; e = 1; }
-  else if (c < 8) { hs = 1; e = 2 + 2 * (c - 5); }
-  else { hs = 1; e = 3 + 2 * (c - 13); }
-  return ((g * 4) + 2 * w + hs) * 8 + e;
-}
-
-__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
-
-__device__ __forceinline__ uint32_t pack_rtz(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
-}
-
-__device__ __forceinline__ f32x4 mfma(f16x8 a, f16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-  return v;
-}
-
-// power-of-two scale 2^sigma with max * 2^sigma in [2^14, 2^15) (1 if max == 0)
-__device__ __forceinline__ float range_scale(float mx, int &sigma) {
-  sigma = 0;
-  if (mx > 0.f) {
-    sigma = 15 - __builtin_amdgcn_frexp_expf(mx);
-    sigma = sigma > 100 ? 100 : (sigma < -100 ? -100 : sigma);
+__host__ __device__ constexpr bool check_maps() {
+  bool seen[D] = {};
+  for (int k = 0; k < D; ++k) {
+    const int e = k_elem(k);
+    if (e < 0 || e >= D || seen[e]) return false;
+    seen[e] = true;
   }
-  return __builtin_ldexpf(1.f, sigma);
+  for (int g = 0; g < 4; ++g)
+    for (int e = 0; e < 32; ++e) {
+      const int s = 4 * g + (e >> 3), j = e & 7, x = slot_elem(s, j);
+      if (x != 16 * (s >> 2) + 64 * ((s >> 1) & 1) + (s & 1) + 2 * j) return false;
+      if (elem_slot(x) != s || elem_j(x) != j) return false;
+    }
+  return true;
+}
+static_assert(check_maps(), "operand index maps are not consistent");
+
+__device__ __forceinline__ f32x4 mfma_f8f4(const u32x8 &a, const u32x4 &b, const f32x4 &c,
+                                           int scale_a) {
+  const i32x8 av = __builtin_bit_cast(i32x8, a);
+  const i32x8 bv = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
+  // A: fp8 e4m3 (format 0), B: fp4 e2m1 (format 4); B scale 2^0
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 4, 0, scale_a, 0, 127);
+}
+
+__device__ __forceinline__ u32x4 code_operand(const u32x2 &w) {
+  return u32x4{w[0] & kFieldMask, (w[0] >> 2) & kFieldMask, w[1] & kFieldMask,
+               (w[1] >> 2) & kFieldMask};
+}
+
+// x (|x| < 448) as NT fp8 terms; term k of the 8 values, in order, in out[k].
+template <int NT>
+__device__ __forceinline__ void fp8_terms(float (&x)[8], u32x2 (&out)[NT]) {
+#pragma unroll
+  for (int k = 0; k < NT; ++k) {
+    uint32_t w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0u, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], w0, true);
+    uint32_t w1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], 0u, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6], x[7], w1, true);
+    out[k] = u32x2{w0, w1};
+    if (k + 1 < NT) {
+      const f32x2 b0 = __builtin_amdgcn_cvt_pk_f32_fp8(w0, false);
+      const f32x2 b1 = __builtin_amdgcn_cvt_pk_f32_fp8(w0, true);
+      const f32x2 b2 = __builtin_amdgcn_cvt_pk_f32_fp8(w1, false);
+      const f32x2 b3 = __builtin_amdgcn_cvt_pk_f32_fp8(w1, true);
+      x[0] -= b0[0];
+      x[1] -= b0[1];
+      x[2] -= b1[0];
+      x[3] -= b1[1];
+      x[4] -= b2[0];
+      x[5] -= b2[1];
+      x[6] -= b3[0];
+      x[7] -= b3[1];
+    }
+  }
+}
+
+// exponent sigma with mx * 2^sigma in [128, 256) (0 when mx is 0)
+__device__ __forceinline__ int range_exp8(float mx) {
+  if (!(mx > 0.f)) return 0;
+  const int s = 8 - __builtin_amdgcn_frexp_expf(mx);
+  return s > 100 ? 100 : (s < -100 ? -100 : s);
+}
+
+// E8M0 scale byte 2^-sigma_h for the operand rows of this lane (head
+// (lane >> 2) & 3); sigma is uniform over each 16-lane row h.
+__device__ __forceinline__ int row_scale_byte(int sigma, int lane) {
+  const int s0 = __builtin_amdgcn_readlane(sigma, 0);
+  const int s1 = __builtin_amdgcn_readlane(sigma, 16);
+  const int s2 = __builtin_amdgcn_readlane(sigma, 32);
+  const int s3 = __builtin_amdgcn_readlane(sigma, 48);
+  const int h = (lane >> 2) & 3;
+  const int s = h == 0 ? s0 : (h == 1 ? s1 : (h == 2 ? s2 : s3));
+  return 127 - s;
 }
 
 // In-place Sylvester Hadamard transform (unscaled) of rows x[n][128] in LDS.
@@ -159,66 +205,34 @@ __device__ __forceinline__ float group_sum(float v) {
   if constexpr (N == 16) v += dpp<kRowMirror>(v);
   return v;
 }
-// max over the wave, wave-uniform result
-__device__ __forceinline__ float wave_max_u(float v) {
-  v = group_max<16>(v);
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
-}
 
-// Per-head rows are padded by 4 words so that rows of different heads start
-// on different LDS banks.
-constexpr int SC_PITCH = T + 4;       // floats per head row of sc
-constexpr int OP_PITCH = 4 * 4 * 4 + 4;  // words per head row of an operand array
-
-// LDS position of token t in the per-token arrays (sc, rk, rv): inside each
-// 16-token tile the four 4-token quads are permuted by an XOR that depends on
-// the tile pair, so that the softmax lanes' 16-byte reads (one tile per lane,
-// 8 lanes per LDS cycle) fall on distinct banks. Quads stay contiguous.
-__host__ __device__ constexpr int quad_swz(int tile) {  // {0, 2, 1, 3}[(tile >> 1) & 3]
-  return (((tile >> 1) & 1) << 1) | ((tile >> 2) & 1);
-}
-__host__ __device__ constexpr int tok_pos(int t) {
-  return (t & ~15) | ((((t >> 2) & 3) ^ quad_swz(t >> 4)) << 2) | (t & 3);
-}
-// Word offset of operand quad Q = 4 g + s (lane group g, k-step s) in a head
-// row of ahi/alo/ap: quads Q and Q + 8 are moved to different banks for the
-// softmax lanes' P' writes.
-__host__ __device__ constexpr int op_quad(int q) { return 4 * (q ^ ((q >> 3) & 1)); }
-
-template <int GP>
-struct alignas(16) DecSmem {
-  alignas(16) float qt[GP][D];            // rotated, scaled query (setup only)
-  alignas(16) float ck[D];                // c_K in [g][s][e] order
-  alignas(16) float cv[16][9];            // cv[n][ct] = c_V[16 ct + n] (odd pitch)
-  alignas(16) float rk[T];                // r'_K, tok_pos order
-  alignas(16) float rv[T];                // r'_V * 4^-f(t % 8), tok_pos order
-  alignas(16) float sc[GP][SC_PITCH];     // QK results (offset already removed), tok_pos order
-  alignas(16) uint32_t ahi[GP][OP_PITCH]; // query operand, fp16 pairs, [m][(g * 4 + s) * 4 + dword]
-  alignas(16) uint32_t alo[GP][OP_PITCH];
-  alignas(16) uint32_t ap[GP][OP_PITCH];  // P' operand, same layout
-  float alpha[GP];
+struct DecSmem {
+  alignas(16) float qt[HG][D];          // rotated query (setup only)
+  alignas(16) float ck[SLOT_ARRAY];     // c_K, elem_pos order
+  alignas(16) float cv[SLOT_ARRAY];     // c_V, cv_pos order
+  alignas(16) float rk[SLOT_ARRAY];     // r'_K, elem_pos order
+  alignas(16) float rv[SLOT_ARRAY];     // r'_V, elem_pos order
+  alignas(16) uint32_t aq[16][OP_ROW];  // QK fp8 operand, row 4 h + k = term k of head h
+  alignas(16) uint32_t ap[16][OP_ROW];  // PV fp8 operand, rows 4 h + 3 stay zero
 };
 
+// Codes and scales of one chunk, in the lane's operand order.
 struct ChunkRegs {
-  u32x2 k[8];  // K code words 2g, 2g+1 of token 16 tau + n
-  u32x2 v[8];  // V code words 2g, 2g+1 of channel 16 ct + n
-  u32x2 ck, cv, rk, rv;  // scales of elements 2l, 2l+1
+  u32x2 k[8];  // K bytes [8 g, 8 g + 8) of token slot_elem(n, tau)
+  u32x2 v[8];  // V bytes [8 g, 8 g + 8) of channel 16 ct + n
+  u32x2 ck, cv, rk, rv;  // scales of elements 2 lane, 2 lane + 1
 };
 
-__device__ __forceinline__ void load_chunk(const DecodeArgs &a, int64_t bg, int64_t nchunks, int k,
-                                           int lane, ChunkRegs &r) {
+__device__ __forceinline__ void load_chunk(const DecodeArgs &a, int64_t bg, int64_t nchunks,
+                                           int k, int lane, ChunkRegs &r) {
   const int64_t chunk = bg * nchunks + k;
   const int n = lane & 15, g = lane >> 4;
-  const uint8_t *kc = a.k_codes + chunk * CHUNK_BYTES + n * 32 + 8 * g;
-  const uint8_t *vc = a.v_codes + chunk * CHUNK_BYTES + n * 32 + 8 * g;
+  const uint8_t *kc = a.k_codes + chunk * CHUNK_BYTES + 32 * slot_elem(n, 0) + 8 * g;
+  const uint8_t *vc = a.v_codes + chunk * CHUNK_BYTES + 32 * n + 8 * g;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    r.k[t] = *reinterpret_cast<const u32x2 *>(kc + t * 16 * 32);
-    r.v[t] = *reinterpret_cast<const u32x2 *>(vc + t * 16 * 32);
+    r.k[t] = *reinterpret_cast<const u32x2 *>(kc + 64 * t);   // token + 2 t
+    r.v[t] = *reinterpret_cast<const u32x2 *>(vc + 512 * t);  // channel + 16 t
   }
   r.ck = *reinterpret_cast<const u32x2 *>(a.k_col + chunk * D + 2 * lane);
   r.cv = *reinterpret_cast<const u32x2 *>(a.v_col + chunk * D + 2 * lane);
@@ -227,218 +241,148 @@ __device__ __forceinline__ void load_chunk(const DecodeArgs &a, int64_t bg, int6
   r.rv = *reinterpret_cast<const u32x2 *>(a.v_row + row);
 }
 
-// Per-lane state of one decode_split workgroup (one wave).
-template <int GP>
 struct SplitState {
-  static constexpr int NU = GP / 4;      // query-operand units per lane
-  static constexpr int LPH = 64 / GP;    // softmax lanes per head
-  static constexpr int NHW = 16 / LPH;   // half code words (8 tokens) per softmax lane
-  float qh[NU][8];                       // query * scales for this lane's units
-  f32x4 acc[8];                          // PV accumulators (rows = heads 4 lg + r)
+  float qv[8];     // query (rotated, scaled) at the channels of this lane's slot
+  float acc[8];    // PV accumulators: head lane >> 4, channel 16 ct + (lane & 15)
   float m_run, l_run;
 };
 
-template <int GP>
-__device__ __forceinline__ void process_chunk(const DecodeArgs &a, DecSmem<GP> &sm,
-                                              SplitState<GP> &st, const ChunkRegs &cur, int k,
-                                              int len, int lane, const u32x4 &one0,
-                                              const u32x4 &one1) {
-  constexpr int NU = SplitState<GP>::NU, LPH = SplitState<GP>::LPH, NHW = SplitState<GP>::NHW;
-  const int n = lane & 15, lg = lane >> 4;
-  const int gu = (lane >> 2) & 3, su = lane >> 4;
-  const int sh = lane / LPH;             // softmax head of this lane
-  const int nvalid = min(len - k * T, T);
+__device__ __forceinline__ void process_chunk(DecSmem &sm, SplitState &st, const ChunkRegs &cur,
+                                              int nvalid, int lane) {
+  const int n = lane & 15, h = lane >> 4;
+  const int sb = slot_base(n);
 
   // ---- scales to LDS ----
-  __syncthreads();  // previous chunk's LDS readers are done
-  sm.ck[elem_slot_pos(2 * lane)] = __uint_as_float(cur.ck[0]);
-  sm.ck[elem_slot_pos(2 * lane + 1)] = __uint_as_float(cur.ck[1]);
-  sm.cv[(2 * lane) & 15][(2 * lane) >> 4] = __uint_as_float(cur.cv[0]);
-  sm.cv[(2 * lane + 1) & 15][(2 * lane + 1) >> 4] = __uint_as_float(cur.cv[1]);
-  const int tp = tok_pos(2 * lane);  // 2 lane and 2 lane + 1 stay adjacent
-  sm.rk[tp] = __uint_as_float(cur.rk[0]);
-  sm.rk[tp + 1] = __uint_as_float(cur.rk[1]);
-  const float rv0 = 2 * lane < nvalid ? __uint_as_float(cur.rv[0]) : 0.f;
-  const float rv1 = 2 * lane + 1 < nvalid ? __uint_as_float(cur.rv[1]) : 0.f;
-  int sig_v;
-  const float sv = range_scale(wave_max_u(fmaxf(rv0, rv1)), sig_v);
-  sm.rv[tp] = rv0 * sv * __builtin_ldexpf(1.f, -2 * field_exp(2 * lane));
-  sm.rv[tp + 1] = rv1 * sv * __builtin_ldexpf(1.f, -2 * field_exp(2 * lane + 1));
+  __syncthreads();  // the previous chunk's readers are done
+  {
+    const int e = 2 * lane;
+    const int pe = elem_pos(e), pc = cv_pos(e);  // element e + 1 sits 8 further on
+    sm.ck[pe] = __uint_as_float(cur.ck[0]);
+    sm.ck[pe + 8] = __uint_as_float(cur.ck[1]);
+    sm.cv[pc] = __uint_as_float(cur.cv[0]);
+    sm.cv[pc + 8] = __uint_as_float(cur.cv[1]);
+    sm.rk[pe] = __uint_as_float(cur.rk[0]);
+    sm.rk[pe + 8] = __uint_as_float(cur.rk[1]);
+    sm.rv[pe] = __uint_as_float(cur.rv[0]);
+    sm.rv[pe + 8] = __uint_as_float(cur.rv[1]);
+  }
   __syncthreads();
 
-  // ---- query operand: a = q * c_K * 2^sigma_q, fp16 hi/lo ----
-  int sig_q;
+  // ---- QK operand: head h, slot n: x = q * c_K * 2^sigma_h as 4 fp8 terms ----
+  int sa_q;
   {
-    const f32x4 c0v = *reinterpret_cast<const f32x4 *>(&sm.ck[(gu * 4 + su) * 8]);
-    const f32x4 c1v = *reinterpret_cast<const f32x4 *>(&sm.ck[(gu * 4 + su) * 8 + 4]);
-    const float cc[8] = {c0v.x, c0v.y, c0v.z, c0v.w, c1v.x, c1v.y, c1v.z, c1v.w};
-    float av[NU][8];
+    const f32x4 c0 = *reinterpret_cast<const f32x4 *>(&sm.ck[sb]);
+    const f32x4 c1 = *reinterpret_cast<const f32x4 *>(&sm.ck[sb + 4]);
+    float x[8];
     float mx = 0.f;
 #pragma unroll
-    for (int u = 0; u < NU; ++u)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        av[u][e] = st.qh[u][e] * cc[e];
-        mx = fmaxf(mx, fabsf(av[u][e]));
-      }
-    const float sq = range_scale(wave_max_u(mx), sig_q);
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      u32x4 hi, lo;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        // hi = x truncated to fp16's 11 significant bits (exact in fp32 and,
-        // for |x| in the fp16 normal range, exact in fp16); lo = x - hi.
-        // Formed in fp32 so that no f16 -> f32 read-back of the packed hi
-        // pair exists (that pattern was mis-fused into v_fma_mix_f32 with
-        // the wrong source register by this compiler).
-        const float x0 = av[u][2 * d] * sq, x1 = av[u][2 * d + 1] * sq;
-        const float h0 = __uint_as_float(__float_as_uint(x0) & 0xFFFFE000u);
-        const float h1 = __uint_as_float(__float_as_uint(x1) & 0xFFFFE000u);
-        hi[d] = pack_rtz(h0, h1);
-        lo[d] = pack_rtz(x0 - h0, x1 - h1);
-      }
-      const int mu = (lane & 3) + 4 * u;
-      *reinterpret_cast<u32x4 *>(&sm.ahi[mu][op_quad(gu * 4 + su)]) = hi;
-      *reinterpret_cast<u32x4 *>(&sm.alo[mu][op_quad(gu * 4 + su)]) = lo;
+    for (int j = 0; j < 8; ++j) {
+      x[j] = st.qv[j] * (j < 4 ? c0[j] : c1[j - 4]);
+      mx = fmaxf(mx, fabsf(x[j]));
     }
+    const int sig = range_exp8(group_max<16>(mx));
+    const float sc = __builtin_ldexpf(1.f, sig);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] *= sc;
+    u32x2 t[4];
+    fp8_terms<4>(x, t);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x2 *>(&sm.aq[4 * h + k][2 * n]) = t[k];
+    sa_q = row_scale_byte(sig, lane);
   }
   __syncthreads();
-  u32x4 ahi[4], alo[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    ahi[s] = n < GP ? *reinterpret_cast<const u32x4 *>(&sm.ahi[n][op_quad(lg * 4 + s)]) : u32x4{0u, 0u, 0u, 0u};
-    alo[s] = n < GP ? *reinterpret_cast<const u32x4 *>(&sm.alo[n][op_quad(lg * 4 + s)]) : u32x4{0u, 0u, 0u, 0u};
-  }
 
-  // ---- QK^T: offset term first, then 8 token tiles x (4 hi + 4 lo) k-steps
-  // started from -1.5 * offset, so D = sum_j a_j (code_tj - 1.5) directly ----
+  // ---- QK^T: 8 token tiles; the four terms of head h land in d[0..3] ----
+  float s[8];
   {
-    f32x4 off = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      off = mfma(as_f16x8(ahi[s]), as_f16x8((s & 1) ? one1 : one0), off);
-      off = mfma(as_f16x8(alo[s]), as_f16x8((s & 1) ? one1 : one0), off);
-    }
-    off *= -1.5f;
+    const u32x4 a0 = *reinterpret_cast<const u32x4 *>(&sm.aq[n][8 * h]);
+    const u32x4 a1 = *reinterpret_cast<const u32x4 *>(&sm.aq[n][8 * h + 4]);
+    const u32x8 aq = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    const u32x4 half3 = {kFp4Half3, kFp4Half3, kFp4Half3, kFp4Half3};
+    const f32x4 off = mfma_f8f4(aq, half3, f32x4{0.f, 0.f, 0.f, 0.f}, sa_q) * -0.5f;
 #pragma unroll
     for (int tau = 0; tau < 8; ++tau) {
-      u32x4 b0, b1, b2, b3;
-      unpack_codes(cur.k[tau][0], b0, b1);
-      unpack_codes(cur.k[tau][1], b2, b3);
-      f32x4 d = mfma(as_f16x8(ahi[0]), as_f16x8(b0), off);
-      d = mfma(as_f16x8(ahi[1]), as_f16x8(b1), d);
-      d = mfma(as_f16x8(ahi[2]), as_f16x8(b2), d);
-      d = mfma(as_f16x8(ahi[3]), as_f16x8(b3), d);
-      d = mfma(as_f16x8(alo[0]), as_f16x8(b0), d);
-      d = mfma(as_f16x8(alo[1]), as_f16x8(b1), d);
-      d = mfma(as_f16x8(alo[2]), as_f16x8(b2), d);
-      d = mfma(as_f16x8(alo[3]), as_f16x8(b3), d);
-      if (lg < GP / 4) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sm.sc[4 * lg + r][16 * tau + (n ^ (quad_swz(tau) << 2))] = d[r];
-      }
+      const f32x4 d = mfma_f8f4(aq, code_operand(cur.k[tau]), off, sa_q);
+      s[tau] = (d[0] + d[1]) + (d[2] + d[3]);
     }
   }
-  __syncthreads();
 
-  // ---- online softmax. A lane owns NHW half code words of head sh: the
-  // tokens 16 w + 4 hs + i and 16 w + 8 + 4 hs + i (i < 4), i.e. exactly
-  // the fp16 pairs of one P' operand dword quad ----
+  // ---- online softmax of head h over the tokens slot_elem(n, tau) ----
   {
-    const float kscale = __builtin_ldexpf(1.f, 24 - sig_q);
-    float s[NHW][8];
-    float mc = -INFINITY;
+    const f32x4 rk0 = *reinterpret_cast<const f32x4 *>(&sm.rk[sb]);
+    const f32x4 rk1 = *reinterpret_cast<const f32x4 *>(&sm.rk[sb + 4]);
 #pragma unroll
-    for (int j = 0; j < NHW; ++j) {
-      const int hw = (lane % LPH) * NHW + j;      // half-word index 0..15
-      const int t1 = 16 * (hw >> 1) + 4 * (hw & 1);
+    for (int j = 0; j < 8; ++j) s[j] *= (j < 4 ? rk0[j] : rk1[j - 4]);
+    if (nvalid < T) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int t = t1 + 8 * q;
-        const f32x4 raw = *reinterpret_cast<const f32x4 *>(&sm.sc[sh][tok_pos(t)]);
-        const f32x4 rk4 = *reinterpret_cast<const f32x4 *>(&sm.rk[tok_pos(t)]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v = raw[i] * (rk4[i] * kscale);
-          s[j][4 * q + i] = t + i < nvalid ? v : -INFINITY;
-          mc = fmaxf(mc, s[j][4 * q + i]);
-        }
-      }
+      for (int j = 0; j < 8; ++j)
+        if (slot_elem(n, j) >= nvalid) s[j] = -INFINITY;
     }
-    mc = group_max<LPH>(mc);
-    // integer running max (log2 units): P' of a chunk then differs between
-    // split layouts only by powers of two, so its fp16 rounding does not
+    float mc = s[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) mc = fmaxf(mc, s[j]);
+    mc = group_max<16>(mc);
+    // integer running max (log2 units): the probabilities of a chunk then
+    // differ between split layouts only by powers of two, which the range
+    // scale below absorbs exactly
     const float mn = fmaxf(st.m_run, ceilf(mc));
-    const float al = mn == -INFINITY ? 1.f : exp2f(st.m_run - mn);
-    float ps = 0.f;
+    const float al = exp2f(st.m_run - mn);  // 0 on the first chunk
+    const f32x4 rv0 = *reinterpret_cast<const f32x4 *>(&sm.rv[sb]);
+    const f32x4 rv1 = *reinterpret_cast<const f32x4 *>(&sm.rv[sb + 4]);
+    float w[8];
+    float ps = 0.f, mw = 0.f;
 #pragma unroll
-    for (int j = 0; j < NHW; ++j) {
-      const int hw = (lane % LPH) * NHW + j;
-      const int t1 = 16 * (hw >> 1) + 4 * (hw & 1);
-      const f32x4 rva = *reinterpret_cast<const f32x4 *>(&sm.rv[tok_pos(t1)]);
-      const f32x4 rvb = *reinterpret_cast<const f32x4 *>(&sm.rv[tok_pos(t1 + 8)]);
-      u32x4 pk;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pa = mn == -INFINITY ? 0.f : exp2f(s[j][i] - mn);
-        const float pb = mn == -INFINITY ? 0.f : exp2f(s[j][4 + i] - mn);
-        ps += pa + pb;
-        pk[i] = pack_rtz(pa * rva[i], pb * rvb[i]);
-      }
-      // dword quad (word hw >> 1, half hw & 1) of the P' operand of head sh:
-      // lane group g = word >> 1, k-step s = 2 (word & 1) + half
-      const int w = hw >> 1;
-      *reinterpret_cast<u32x4 *>(&sm.ap[sh][op_quad((w >> 1) * 4 + 2 * (w & 1) + (hw & 1))]) = pk;
+    for (int j = 0; j < 8; ++j) {
+      const float p = exp2f(s[j] - mn);
+      ps += p;
+      w[j] = p * (j < 4 ? rv0[j] : rv1[j - 4]);
     }
+    if (nvalid < T) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (slot_elem(n, j) >= nvalid) w[j] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mw = fmaxf(mw, w[j]);
+    const int sig = range_exp8(group_max<16>(mw));
+    const float sc = __builtin_ldexpf(1.f, sig);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j] *= sc;
+    u32x2 t[3];
+    fp8_terms<3>(w, t);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) *reinterpret_cast<u32x2 *>(&sm.ap[4 * h + k][2 * n]) = t[k];
     st.l_run = st.l_run * al + ps;
     st.m_run = mn;
-    if (lane % LPH == 0) sm.alpha[sh] = al;
-  }
-  __syncthreads();
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) st.acc[ct] *= al;
+    const int sa_p = row_scale_byte(sig, lane);
+    __syncthreads();
 
-  // ---- PV: 8 channel tiles x 4 k-steps, started from -1.5 * offset ----
-  {
-    u32x4 ap[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      ap[s] = n < GP ? *reinterpret_cast<const u32x4 *>(&sm.ap[n][op_quad(lg * 4 + s)]) : u32x4{0u, 0u, 0u, 0u};
-    f32x4 off = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) off = mfma(as_f16x8(ap[s]), as_f16x8((s & 1) ? one1 : one0), off);
-    off *= -1.5f;
-    f32x4 alr;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) alr[r] = (4 * lg + r < GP) ? sm.alpha[4 * lg + r] : 1.f;
-    // the running max moves by whole powers of two: rescale only when it moved
-    if (alr[0] != 1.f || alr[1] != 1.f || alr[2] != 1.f || alr[3] != 1.f) {
-#pragma unroll
-      for (int ct = 0; ct < 8; ++ct) st.acc[ct] *= alr;
-    }
-    const float vscale = __builtin_ldexpf(1.f, 24 - sig_v);
+    // ---- PV: 8 channel tiles ----
+    const u32x4 a0 = *reinterpret_cast<const u32x4 *>(&sm.ap[n][8 * h]);
+    const u32x4 a1 = *reinterpret_cast<const u32x4 *>(&sm.ap[n][8 * h + 4]);
+    const u32x8 ap = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    const u32x4 half3 = {kFp4Half3, kFp4Half3, kFp4Half3, kFp4Half3};
+    const f32x4 off = mfma_f8f4(ap, half3, f32x4{0.f, 0.f, 0.f, 0.f}, sa_p) * -0.5f;
+    const f32x4 cv0 = *reinterpret_cast<const f32x4 *>(&sm.cv[sb]);
+    const f32x4 cv1 = *reinterpret_cast<const f32x4 *>(&sm.cv[sb + 4]);
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
-      u32x4 b0, b1, b2, b3;
-      unpack_codes(cur.v[ct][0], b0, b1);
-      unpack_codes(cur.v[ct][1], b2, b3);
-      f32x4 d = mfma(as_f16x8(ap[0]), as_f16x8(b0), off);
-      d = mfma(as_f16x8(ap[1]), as_f16x8(b1), d);
-      d = mfma(as_f16x8(ap[2]), as_f16x8(b2), d);
-      d = mfma(as_f16x8(ap[3]), as_f16x8(b3), d);
-      const float cvs = sm.cv[n][ct] * vscale;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) st.acc[ct][r] = fmaf(cvs, d[r], st.acc[ct][r]);
+      const f32x4 d = mfma_f8f4(ap, code_operand(cur.v[ct]), off, sa_p);
+      st.acc[ct] = fmaf(ct < 4 ? cv0[ct] : cv1[ct - 4], (d[0] + d[1]) + d[2], st.acc[ct]);
     }
   }
 }
 
-template <int GP>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
-  __shared__ DecSmem<GP> sm;
-  constexpr int NU = SplitState<GP>::NU, LPH = SplitState<GP>::LPH;
+  __shared__ DecSmem sm;
   const int lane = threadIdx.x;
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = a.q_heads / a.kv_heads;
+  const int n_hg = (G + HG - 1) / HG;
+  const int split = blockIdx.x % a.n_split, hg = blockIdx.x / a.n_split;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int h0 = hg * HG, nh = min(HG, G - h0);  // query heads g * G + h0 + [0, nh)
   const int nch = a.capacity / T;
   const int len = a.lens[b];
   const bool valid = len >= 1 && len <= a.capacity;
@@ -447,63 +391,49 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const int c0 = split * per;
   const int c1 = min(c0 + per, used);
   const int64_t bg = (int64_t)b * a.kv_heads + g;
+  const int64_t qh0 = (int64_t)b * a.q_heads + (int64_t)g * G + h0;
+  (void)n_hg;
 
-  // ---- query: rotate; fold softmax scale, log2(e), 1/sqrt(128), 4^-f -----
-  for (int idx = lane; idx < GP * D; idx += 64) {
+  // ---- query: rotate; fold softmax scale, log2(e), 1/sqrt(128) and the 2
+  // of the half-level code values ----
+  for (int idx = lane; idx < HG * D; idx += 64) {
     const int m = idx / D, j = idx - m * D;
-    sm.qt[m][j] = m < G ? load_q(a.q, a.q_dtype, ((int64_t)b * a.q_heads + g * G + m) * D + j) : 0.f;
+    sm.qt[m][j] = m < nh ? load_q(a.q, a.q_dtype, (qh0 + m) * D + j) : 0.f;
   }
+  for (int idx = lane; idx < 16 * OP_ROW; idx += 64) (&sm.ap[0][0])[idx] = 0u;
   __syncthreads();
-  lds_fwht_rows(&sm.qt[0][0], GP);
-  SplitState<GP> st;
+  lds_fwht_rows(&sm.qt[0][0], HG);
+  SplitState st;
   {
-    const int gu = (lane >> 2) & 3, su = lane >> 4;
-    const float qs = a.scale * kLog2e * kInvSqrtD;
+    const float qs = 2.f * a.scale * kLog2e * kInvSqrtD;
 #pragma unroll
-    for (int u = 0; u < NU; ++u)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = kslot_elem(gu, su, e);
-        st.qh[u][e] = sm.qt[(lane & 3) + 4 * u][j] * qs * __builtin_ldexpf(1.f, -2 * field_exp(j));
-      }
+    for (int j = 0; j < 8; ++j) st.qv[j] = sm.qt[lane >> 4][slot_elem(lane & 15, j)] * qs;
   }
 #pragma unroll
-  for (int ct = 0; ct < 8; ++ct) st.acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int ct = 0; ct < 8; ++ct) st.acc[ct] = 0.f;
   st.m_run = -INFINITY;
   st.l_run = 0.f;
-  // constant operand: code 1 in every field (the level offset term)
-  u32x4 one0, one1;
-  unpack_codes(0x55555555u, one0, one1);
 
-  // chunks [c0, c1); the next chunk's loads are in flight while the current
-  // one is computed
   ChunkRegs cur, nxt;
   if (c0 < c1) load_chunk(a, bg, nch, c0, lane, cur);
   for (int k = c0; k < c1; ++k) {
     if (k + 1 < c1) load_chunk(a, bg, nch, k + 1, lane, nxt);
-    process_chunk<GP>(a, sm, st, cur, k, len, lane, one0, one1);
+    process_chunk(sm, st, cur, min(len - k * T, T), lane);
     cur = nxt;
   }
 
-  // ---- partial results: (m, l, acc) per query head of this split ----
-  const int sh = lane / LPH;
-  const float lsum = group_sum<LPH>(st.l_run);
-  const int n = lane & 15, lg = lane >> 4;
-  if (lane % LPH == 0 && sh < G) {
-    float *pp = a.partial + (((int64_t)b * a.q_heads + g * G + sh) * a.n_split + split) * (2 + D);
-    pp[0] = st.m_run;
-    pp[1] = lsum;
-  }
-  if (lg < GP / 4) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int h = 4 * lg + r;
-      if (h < G) {
-        float *pp = a.partial + (((int64_t)b * a.q_heads + g * G + h) * a.n_split + split) * (2 + D);
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct) pp[2 + 16 * ct + n] = st.acc[ct][r];
-      }
+  // ---- partial results (m, l, acc) of head h0 + (lane >> 4) for this split ----
+  const int h = lane >> 4, n = lane & 15;
+  const float lsum = group_sum<16>(st.l_run);
+  if (h < nh) {
+    float *pp = a.partial + ((qh0 + h) * a.n_split + split) * (2 + D);
+    if (n == 0) {
+      pp[0] = st.m_run;
+      pp[1] = lsum;
     }
+    // 2: the code operand carries c/2
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) pp[2 + 16 * ct + n] = 2.f * st.acc[ct];
   }
 }
 
@@ -574,11 +504,10 @@ int decode_auto_splits(int batch, int kv_heads, int capacity) {
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
   if (a.batch == 0 || a.q_heads == 0) return hipSuccess;
-  const dim3 grid(a.n_split, a.kv_heads, a.batch);
-  if (a.q_heads / a.kv_heads <= 4)
-    hipLaunchKernelGGL(decode_split_kernel<4>, grid, dim3(64), 0, s, a);
-  else
-    hipLaunchKernelGGL(decode_split_kernel<8>, grid, dim3(64), 0, s, a);
+  const int G = a.q_heads / a.kv_heads;
+  const int n_hg = (G + HG - 1) / HG;
+  const dim3 grid(a.n_split * n_hg, a.kv_heads, a.batch);
+  hipLaunchKernelGGL(decode_split_kernel, grid, dim3(64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(a.q_heads, a.batch), dim3(D), 0, s, a);
