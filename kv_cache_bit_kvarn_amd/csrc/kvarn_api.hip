@@ -123,14 +123,15 @@ int kvarn_decode_attn(const void *q, int32_t q_dtype, int32_t q_heads, const kva
   if (!aligned16(q) || !aligned16(out)) return KVARN_ERR_ALIGN;
   if (n_split < 0) return KVARN_ERR_SHAPE;
   if (k->batch == 0) return KVARN_OK;
-  const int nch = k->capacity / T;
-  int ns = n_split == 0 ? decode_auto_splits(k->batch, k->kv_heads, k->capacity) : n_split;
-  if (ns > nch) ns = nch;
-  if (ns < 1) ns = 1;
   const size_t need = kvarn_decode_workspace_bytes(k->batch, q_heads, k->capacity);
   if (!workspace) return KVARN_ERR_NULL;
   if (workspace_bytes < need) return KVARN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return KVARN_ERR_ALIGN;
+  // arguments are valid: from here on HIP may be queried
+  const int nch = k->capacity / T;
+  int ns = n_split == 0 ? decode_auto_splits(k->batch, k->kv_heads, q_heads, k->capacity) : n_split;
+  if (ns > nch) ns = nch;
+  if (ns < 1) ns = 1;
   DecodeArgs a;
   a.q = q;
   a.q_dtype = q_dtype;

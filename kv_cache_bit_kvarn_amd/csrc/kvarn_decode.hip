@@ -30,10 +30,14 @@
 //    the four accumulator registers of one lane;
 //  * a per-head power-of-two range scale (largest magnitude in [128, 256))
 //    is undone by the MFMA's per-row E8M0 scale;
-//  * the level offset is one MFMA per chunk against a constant-1.5 operand,
-//    fed in as the accumulator input.
+//  * the level offset is one MFMA per chunk against a constant -1.5 operand
+//    at scale 2^-1, fed in as the accumulator input.
 // decode_combine: grid (q_heads, batch): log-sum-exp merge of the partials
 // (m, l, acc[128]), then the inverse rotation.
+#include <algorithm>
+#include <atomic>
+#include <climits>
+
 #include "kvarn_internal.h"
 
 namespace kvarn {
@@ -46,7 +50,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int HG = 4;                       // query heads per workgroup
 constexpr uint32_t kFieldMask = 0x33333333u;  // low 2 bits of every 4-bit field
-constexpr uint32_t kFp4Half3 = 0x33333333u;   // e2m1 1.5 in every field
+constexpr uint32_t kFp4Neg3Half = 0xBBBBBBBBu;  // e2m1 -1.5 in every field
 
 // ---- the k order shared by both MFMA operands -----------------------------
 // fp8 operand (8 dwords per lane, lane = row + 16 g): byte e holds
@@ -99,12 +103,20 @@ __host__ __device__ constexpr bool check_maps() {
 }
 static_assert(check_maps(), "operand index maps are not consistent");
 
+// D = (A * 2^(scale_a - 127)) (B * 2^(SCALE_B - 127)) + C
+template <int SCALE_B = 127>
 __device__ __forceinline__ f32x4 mfma_f8f4(const u32x8 &a, const u32x4 &b, const f32x4 &c,
                                            int scale_a) {
   const i32x8 av = __builtin_bit_cast(i32x8, a);
   const i32x8 bv = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
-  // A: fp8 e4m3 (format 0), B: fp4 e2m1 (format 4); B scale 2^0
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 4, 0, scale_a, 0, 127);
+  // A: fp8 e4m3 (format 0), B: fp4 e2m1 (format 4)
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 4, 0, scale_a, 0, SCALE_B);
+}
+
+// -3/4 * (row sums of A): the level offset, as the accumulator input
+__device__ __forceinline__ f32x4 level_offset(const u32x8 &a, int scale_a) {
+  const u32x4 neg = {kFp4Neg3Half, kFp4Neg3Half, kFp4Neg3Half, kFp4Neg3Half};
+  return mfma_f8f4<126>(a, neg, f32x4{0.f, 0.f, 0.f, 0.f}, scale_a);  // -1.5 * 2^-1
 }
 
 __device__ __forceinline__ u32x4 code_operand(const u32x2 &w) {
@@ -298,8 +310,7 @@ __device__ __forceinline__ void process_chunk(DecSmem &sm, SplitState &st, const
     const u32x4 a0 = *reinterpret_cast<const u32x4 *>(&sm.aq[n][8 * h]);
     const u32x4 a1 = *reinterpret_cast<const u32x4 *>(&sm.aq[n][8 * h + 4]);
     const u32x8 aq = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-    const u32x4 half3 = {kFp4Half3, kFp4Half3, kFp4Half3, kFp4Half3};
-    const f32x4 off = mfma_f8f4(aq, half3, f32x4{0.f, 0.f, 0.f, 0.f}, sa_q) * -0.5f;
+    const f32x4 off = level_offset(aq, sa_q);
 #pragma unroll
     for (int tau = 0; tau < 8; ++tau) {
       const f32x4 d = mfma_f8f4(aq, code_operand(cur.k[tau]), off, sa_q);
@@ -354,8 +365,12 @@ __device__ __forceinline__ void process_chunk(DecSmem &sm, SplitState &st, const
     for (int k = 0; k < 3; ++k) *reinterpret_cast<u32x2 *>(&sm.ap[4 * h + k][2 * n]) = t[k];
     st.l_run = st.l_run * al + ps;
     st.m_run = mn;
+    // the running max moves by whole powers of two and seldom: rescale only
+    // when it moved for some head
+    if (__builtin_amdgcn_ballot_w64(al != 1.f)) {
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) st.acc[ct] *= al;
+      for (int ct = 0; ct < 8; ++ct) st.acc[ct] *= al;
+    }
     const int sa_p = row_scale_byte(sig, lane);
     __syncthreads();
 
@@ -363,8 +378,7 @@ __device__ __forceinline__ void process_chunk(DecSmem &sm, SplitState &st, const
     const u32x4 a0 = *reinterpret_cast<const u32x4 *>(&sm.ap[n][8 * h]);
     const u32x4 a1 = *reinterpret_cast<const u32x4 *>(&sm.ap[n][8 * h + 4]);
     const u32x8 ap = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-    const u32x4 half3 = {kFp4Half3, kFp4Half3, kFp4Half3, kFp4Half3};
-    const f32x4 off = mfma_f8f4(ap, half3, f32x4{0.f, 0.f, 0.f, 0.f}, sa_p) * -0.5f;
+    const f32x4 off = level_offset(ap, sa_p);
     const f32x4 cv0 = *reinterpret_cast<const f32x4 *>(&sm.cv[sb]);
     const f32x4 cv1 = *reinterpret_cast<const f32x4 *>(&sm.cv[sb + 4]);
 #pragma unroll
@@ -438,68 +452,112 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 }
 
 // Log-sum-exp merge of the split partials of one (sequence, query head), then
-// the inverse rotation. Thread s < n_split first reads split s's (m, l); the
-// block reduces the maximum and the weighted denominator; then every thread
-// (one output channel) walks the splits with independent, coalesced loads.
-__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
+// the inverse rotation. 256 threads: the block first reduces the maximum of
+// the split maxima, then takes the splits in rounds of 256; in a round each
+// thread weighs one split, and wave w accumulates splits w, w + 4, ... with
+// 8-byte loads of two channels per lane; the four waves' sums meet in LDS.
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
+  __shared__ float wgt[256];
+  __shared__ float red_m[4], red_l[4];
+  __shared__ f32x2 part[4][64];
   __shared__ float o[D];
-  __shared__ float wgt[D];
-  __shared__ float red[4];
-  const int h = blockIdx.x, b = blockIdx.y, j = threadIdx.x;
-  const float *pp = a.partial + ((int64_t)b * a.q_heads + h) * a.n_split * (2 + D);
-  // pass 1: maximum of the split maxima
+  const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  const int lane = t & 63, wv = t >> 6;
+  constexpr int ROW = 2 + D;
+  const float *pp = a.partial + ((int64_t)b * a.q_heads + h) * a.n_split * ROW;
   float mx = -INFINITY;
-  for (int s = j; s < a.n_split; s += D) mx = fmaxf(mx, pp[(int64_t)s * (2 + D)]);
+  for (int s = t; s < a.n_split; s += 256) mx = fmaxf(mx, pp[(int64_t)s * ROW]);
   mx = group_max<16>(mx);
   mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
   mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  if ((j & 63) == 0) red[j >> 6] = mx;
+  if (lane == 0) red_m[wv] = mx;
   __syncthreads();
-  const float M = fmaxf(red[0], red[1]);
-  // pass 2: weights, denominator and numerator
-  float num = 0.f, den = 0.f;
+  const float M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+  f32x2 num = {0.f, 0.f};
+  float den = 0.f;
   if (M != -INFINITY) {
-    for (int base = 0; base < a.n_split; base += D) {
-      const int s = base + j;
+    for (int base = 0; base < a.n_split; base += 256) {
+      const int s = base + t;
       float w = 0.f;
       if (s < a.n_split) {
-        const float ms = pp[(int64_t)s * (2 + D)];
+        const float ms = pp[(int64_t)s * ROW];
         w = ms == -INFINITY ? 0.f : exp2f(ms - M);
-        den += w * pp[(int64_t)s * (2 + D) + 1];
+        den += w * pp[(int64_t)s * ROW + 1];
       }
-      __syncthreads();  // previous round's readers of wgt are done
-      wgt[j] = w;
+      __syncthreads();  // the previous round's readers of wgt are done
+      wgt[t] = w;
       __syncthreads();
-      const int cnt = min(D, a.n_split - base);
-      const float *col = pp + (int64_t)base * (2 + D) + 2 + j;
-#pragma unroll 8
-      for (int q = 0; q < cnt; ++q) num += wgt[q] * col[(int64_t)q * (2 + D)];
+      const int cnt = min(256, a.n_split - base);
+      const float *col = pp + (int64_t)base * ROW + 2 + 2 * lane;
+#pragma unroll 4
+      for (int q = wv; q < cnt; q += 4) {
+        const f32x2 v = *reinterpret_cast<const f32x2 *>(col + (int64_t)q * ROW);
+        num += wgt[q] * v;
+      }
     }
   }
   den = group_sum<16>(den);
   den += __shfl_xor(den, 16, 64);
   den += __shfl_xor(den, 32, 64);
+  if (lane == 0) red_l[wv] = den;
+  part[wv][lane] = num;
   __syncthreads();
-  if ((j & 63) == 0) red[2 + (j >> 6)] = den;
-  __syncthreads();
-  den = red[2] + red[3];
-  o[j] = den > 0.f ? num / den : 0.f;
+  if (t < 64) {
+    const float L = (red_l[0] + red_l[1]) + (red_l[2] + red_l[3]);
+    const f32x2 sum = (part[0][t] + part[1][t]) + (part[2][t] + part[3][t]);
+    o[2 * t] = L > 0.f ? sum[0] / L : 0.f;
+    o[2 * t + 1] = L > 0.f ? sum[1] / L : 0.f;
+  }
   __syncthreads();
   lds_fwht_rows(o, 1);
-  a.out[((int64_t)b * a.q_heads + h) * D + j] = o[j] * kInvSqrtD;
+  if (t < D) a.out[((int64_t)b * a.q_heads + h) * D + t] = o[t] * kInvSqrtD;
 }
 
 }  // namespace
 
-int decode_auto_splits(int batch, int kv_heads, int capacity) {
+// Resident decode_split workgroups on the current device (CUs x blocks per
+// CU at this kernel's occupancy), queried once per device.
+static int resident_slots() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256 * 8;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0, per = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_split_kernel, 64, 0) !=
+          hipSuccess ||
+      per <= 0)
+    per = 8;
+  v = cus * per;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+int decode_auto_splits(int batch, int kv_heads, int q_heads, int capacity) {
   const int nch = capacity / T;
-  const int pairs = batch * kv_heads;
-  if (pairs <= 0 || nch <= 0) return 1;
-  // about 4096 single-wave workgroups: 16 per CU on 256 CUs
-  int s = (4096 + pairs - 1) / pairs;
-  if (s > nch) s = nch;
-  if (s < 1) s = 1;
-  return s;
+  if (batch <= 0 || kv_heads <= 0 || q_heads <= 0 || nch <= 0) return 1;
+  const int G = q_heads / kv_heads;
+  const int64_t pairs = (int64_t)batch * kv_heads * ((G + HG - 1) / HG);
+  const int64_t slots = resident_slots();
+  // cost of s splits in half-chunks: rounds of resident workgroups times the
+  // chunks of one workgroup plus half a chunk of set-up and merge work
+  const int64_t s_max = std::min<int64_t>(nch, 4 * slots / pairs + 1);
+  int best_s = 1;
+  int64_t best = INT64_MAX;
+  for (int64_t s = 1; s <= s_max; ++s) {
+    const int64_t per = (nch + s - 1) / s;
+    if ((nch + per - 1) / per != s) continue;  // same work split as a smaller s
+    const int64_t rounds = (pairs * s + slots - 1) / slots;
+    const int64_t cost = rounds * (2 * per + 1);
+    if (cost < best) {
+      best = cost;
+      best_s = (int)s;
+    }
+  }
+  return best_s;
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
@@ -510,7 +568,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(decode_split_kernel, grid, dim3(64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3(a.q_heads, a.batch), dim3(D), 0, s, a);
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(a.q_heads, a.batch), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

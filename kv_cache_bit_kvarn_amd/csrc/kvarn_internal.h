@@ -76,6 +76,6 @@ struct DecodeArgs {
   float *partial;  // [batch][q_heads][n_split][2 + D]
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
-int decode_auto_splits(int batch, int kv_heads, int capacity);
+int decode_auto_splits(int batch, int kv_heads, int q_heads, int capacity);
 
 }  // namespace kvarn
