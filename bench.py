@@ -48,7 +48,46 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-slices", type=int, default=0,
                    help="oracle slices for the CPU baseline (0 = 2 per thread)")
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="one device-to-device copy of this many MiB before the warmup: "
+                        "the reference kernel for calibrating HBM byte counters")
     return p.parse_args()
+
+
+# Measured HBM traffic of a kernel: rocprofv3 FETCH_SIZE and WRITE_SIZE per
+# dispatch, each scaled by the ratio that the same counter shows for a plain
+# copy of known size (profiles/traffic.json, written from those runs). It is
+# reported only while the kernel's sources are the ones that were profiled.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "quantize_block_kernel<bf16>": ["kv_cache_bit_kvarn_amd/csrc/kvarn_quantize.hip",
+                                    "kv_cache_bit_kvarn_amd/csrc/kvarn_internal.h"],
+    "decode_split_kernel + decode_combine_kernel": [
+        "kv_cache_bit_kvarn_amd/csrc/kvarn_decode.hip",
+        "kv_cache_bit_kvarn_amd/csrc/kvarn_internal.h"],
+}
+
+
+def sources_digest(kernel: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter runs, or None when the
+    kernel changed since (or was never profiled on this workload)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            entry = json.load(f)[kernel][workload]
+    except (OSError, KeyError, ValueError):
+        return None
+    if entry.get("sources_sha256") != sources_digest(kernel):
+        return None
+    return entry["hbm_bytes_per_launch"]
 
 
 def log(*a):
@@ -93,6 +132,15 @@ def main():
                        kv.Cache.empty(B, Hkv, cap, kv.V, device=dev)))
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
     ws = kv.decode_workspace(B, Hq, cap, device=dev)
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done")
     torch.cuda.synchronize()
     log(f"[bench] inputs ready in {time.time() - t0:.1f}s "
         f"({sum(x.numel() * 2 for p in xs for x in p) / 1e9:.2f} GB bf16 K/V)")
@@ -187,7 +235,8 @@ def main():
            "hbm_frac": round(dec_bytes / (d_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
            "kernels": "decode_split_kernel + decode_combine_kernel"}
     dec_roof = {"bound": "hbm", "achieved": dec["GBps_algorithmic"], "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": dec["hbm_frac"], "traffic": None,
+                "unit": "GB/s", "frac": dec["hbm_frac"],
+                "traffic": measured_traffic(dec["kernels"], wl.name),
                 "kernel": dec["kernels"], "bytes_per_launch": dec_bytes}
     if steady:
         res["value"] = dec["tokens_per_s"]
@@ -205,7 +254,8 @@ def main():
                            "hbm_frac": round(q_gbps / HBM_PEAK_GBPS, 4)}
         res["roofline"] = {"bound": "hbm", "achieved": round(q_gbps, 1),
                            "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                           "frac": round(q_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                           "frac": round(q_gbps / HBM_PEAK_GBPS, 4),
+                           "traffic": measured_traffic("quantize_block_kernel<bf16>", wl.name),
                            "kernel": "quantize_block_kernel<bf16>",
                            "bytes_per_launch": qbytes}
         res["roofline_decode"] = dec_roof
