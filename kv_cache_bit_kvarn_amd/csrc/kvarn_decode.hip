@@ -34,9 +34,7 @@
 //    at scale 2^-1, fed in as the accumulator input.
 // decode_combine: grid (q_heads, batch): log-sum-exp merge of the partials
 // (m, l, acc[128]), then the inverse rotation.
-#include <algorithm>
 #include <atomic>
-#include <climits>
 
 #include "kvarn_internal.h"
 
@@ -48,6 +46,8 @@ typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+// s_waitcnt operand on gfx9: vmcnt(0), expcnt and lgkmcnt left at their maxima
+constexpr int kVmcntZero = (0x7 << 4) | (0xF << 8);
 constexpr int HG = 4;                       // query heads per workgroup
 constexpr uint32_t kFieldMask = 0x33333333u;  // low 2 bits of every 4-bit field
 constexpr uint32_t kFp4Neg3Half = 0xBBBBBBBBu;  // e2m1 -1.5 in every field
@@ -170,7 +170,19 @@ __device__ __forceinline__ int row_scale_byte(int sigma, int lane) {
   return 127 - s;
 }
 
-// In-place Sylvester Hadamard transform (unscaled) of rows x[n][128] in LDS.
+// decode_split's workgroup is one wave, and the LDS accesses of one wave are
+// performed in program order: a cross-lane exchange through LDS then needs
+// only a wavefront-scope fence (which keeps the compiler from reordering the
+// accesses), not a barrier or a wait for the writes to complete.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// In-place Sylvester Hadamard transform (unscaled) of rows x[n][128] in LDS,
+// by a workgroup of one wave (kOneWave) or of several.
+template <bool kOneWave>
 __device__ void lds_fwht_rows(float *x, int n) {
   for (int len = 1; len < D; len <<= 1) {
     for (int idx = threadIdx.x; idx < n * (D / 2); idx += blockDim.x) {
@@ -181,13 +193,11 @@ __device__ void lds_fwht_rows(float *x, int n) {
       r[i] = u + v;
       r[i + len] = u - v;
     }
-    __syncthreads();
+    if constexpr (kOneWave)
+      wave_lds_sync();
+    else
+      lds_barrier();
   }
-}
-
-__device__ __forceinline__ float load_q(const void *q, int dtype, int64_t idx) {
-  if (dtype == KVARN_DT_F32) return static_cast<const float *>(q)[idx];
-  return __uint_as_float((uint32_t)static_cast<const uint16_t *>(q)[idx] << 16);
 }
 
 // ---- cross-lane reductions on DPP (no LDS round trip) ----------------------
@@ -265,7 +275,7 @@ __device__ __forceinline__ void process_chunk(DecSmem &sm, SplitState &st, const
   const int sb = slot_base(n);
 
   // ---- scales to LDS ----
-  __syncthreads();  // the previous chunk's readers are done
+  wave_lds_sync();  // after the previous chunk's readers
   {
     const int e = 2 * lane;
     const int pe = elem_pos(e), pc = cv_pos(e);  // element e + 1 sits 8 further on
@@ -278,7 +288,7 @@ __device__ __forceinline__ void process_chunk(DecSmem &sm, SplitState &st, const
     sm.rv[pe] = __uint_as_float(cur.rv[0]);
     sm.rv[pe + 8] = __uint_as_float(cur.rv[1]);
   }
-  __syncthreads();
+  wave_lds_sync();
 
   // ---- QK operand: head h, slot n: x = q * c_K * 2^sigma_h as 4 fp8 terms ----
   int sa_q;
@@ -302,7 +312,7 @@ __device__ __forceinline__ void process_chunk(DecSmem &sm, SplitState &st, const
     for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x2 *>(&sm.aq[4 * h + k][2 * n]) = t[k];
     sa_q = row_scale_byte(sig, lane);
   }
-  __syncthreads();
+  wave_lds_sync();
 
   // ---- QK^T: 8 token tiles; the four terms of head h land in d[0..3] ----
   float s[8];
@@ -311,11 +321,13 @@ __device__ __forceinline__ void process_chunk(DecSmem &sm, SplitState &st, const
     const u32x4 a1 = *reinterpret_cast<const u32x4 *>(&sm.aq[n][8 * h + 4]);
     const u32x8 aq = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
     const f32x4 off = level_offset(aq, sa_q);
+    // all eight products are independent: issue them back to back and sum
+    // the terms afterwards, so the MFMA latency is paid once
+    f32x4 d[8];
 #pragma unroll
-    for (int tau = 0; tau < 8; ++tau) {
-      const f32x4 d = mfma_f8f4(aq, code_operand(cur.k[tau]), off, sa_q);
-      s[tau] = (d[0] + d[1]) + (d[2] + d[3]);
-    }
+    for (int tau = 0; tau < 8; ++tau) d[tau] = mfma_f8f4(aq, code_operand(cur.k[tau]), off, sa_q);
+#pragma unroll
+    for (int tau = 0; tau < 8; ++tau) s[tau] = (d[tau][0] + d[tau][1]) + (d[tau][2] + d[tau][3]);
   }
 
   // ---- online softmax of head h over the tokens slot_elem(n, tau) ----
@@ -372,7 +384,7 @@ __device__ __forceinline__ void process_chunk(DecSmem &sm, SplitState &st, const
       for (int ct = 0; ct < 8; ++ct) st.acc[ct] *= al;
     }
     const int sa_p = row_scale_byte(sig, lane);
-    __syncthreads();
+    wave_lds_sync();
 
     // ---- PV: 8 channel tiles ----
     const u32x4 a0 = *reinterpret_cast<const u32x4 *>(&sm.ap[n][8 * h]);
@@ -381,11 +393,12 @@ __device__ __forceinline__ void process_chunk(DecSmem &sm, SplitState &st, const
     const f32x4 off = level_offset(ap, sa_p);
     const f32x4 cv0 = *reinterpret_cast<const f32x4 *>(&sm.cv[sb]);
     const f32x4 cv1 = *reinterpret_cast<const f32x4 *>(&sm.cv[sb + 4]);
+    f32x4 d[8];
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) {
-      const f32x4 d = mfma_f8f4(ap, code_operand(cur.v[ct]), off, sa_p);
-      st.acc[ct] = fmaf(ct < 4 ? cv0[ct] : cv1[ct - 4], (d[0] + d[1]) + d[2], st.acc[ct]);
-    }
+    for (int ct = 0; ct < 8; ++ct) d[ct] = mfma_f8f4(ap, code_operand(cur.v[ct]), off, sa_p);
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+      st.acc[ct] = fmaf(ct < 4 ? cv0[ct] : cv1[ct - 4], (d[ct][0] + d[ct][1]) + d[ct][2], st.acc[ct]);
   }
 }
 
@@ -409,14 +422,30 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   (void)n_hg;
 
   // ---- query: rotate; fold softmax scale, log2(e), 1/sqrt(128) and the 2
-  // of the half-level code values ----
-  for (int idx = lane; idx < HG * D; idx += 64) {
-    const int m = idx / D, j = idx - m * D;
-    sm.qt[m][j] = m < nh ? load_q(a.q, a.q_dtype, (qh0 + m) * D + j) : 0.f;
+  // of the half-level code values. The query loads go first and the first
+  // chunk's loads next, so that waiting for the query leaves the chunk in
+  // flight during the set-up ----
+  float qin[HG * D / 64];
+  if (a.q_dtype == KVARN_DT_F32) {
+    const float *qf = static_cast<const float *>(a.q);
+#pragma unroll
+    for (int r = 0; r < HG * D / 64; ++r)
+      qin[r] = qf[(qh0 + min(r / 2, nh - 1)) * D + lane + 64 * (r & 1)];
+  } else {
+    const uint16_t *qb = static_cast<const uint16_t *>(a.q);
+#pragma unroll
+    for (int r = 0; r < HG * D / 64; ++r)
+      qin[r] = __uint_as_float((uint32_t)qb[(qh0 + min(r / 2, nh - 1)) * D + lane + 64 * (r & 1)] << 16);
   }
+#pragma unroll
+  for (int r = 0; r < HG * D / 64; ++r) qin[r] = r / 2 < nh ? qin[r] : 0.f;
+  ChunkRegs cur, nxt;
+  if (c0 < c1) load_chunk(a, bg, nch, c0, lane, cur);
+#pragma unroll
+  for (int r = 0; r < HG * D / 64; ++r) sm.qt[r / 2][lane + 64 * (r & 1)] = qin[r];
   for (int idx = lane; idx < 16 * OP_ROW; idx += 64) (&sm.ap[0][0])[idx] = 0u;
-  __syncthreads();
-  lds_fwht_rows(&sm.qt[0][0], HG);
+  wave_lds_sync();
+  lds_fwht_rows<true>(&sm.qt[0][0], HG);
   SplitState st;
   {
     const float qs = 2.f * a.scale * kLog2e * kInvSqrtD;
@@ -428,8 +457,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   st.m_run = -INFINITY;
   st.l_run = 0.f;
 
-  ChunkRegs cur, nxt;
-  if (c0 < c1) load_chunk(a, bg, nch, c0, lane, cur);
+  // The first chunk has landed during the set-up. Waiting for it here, once,
+  // keeps the loop's own waits on the chunk loaded one iteration ahead (a
+  // load still pending on entry would make every iteration wait for the
+  // loads it has just issued: the counter completes in order).
+  __builtin_amdgcn_s_waitcnt(kVmcntZero);
   for (int k = c0; k < c1; ++k) {
     if (k + 1 < c1) load_chunk(a, bg, nch, k + 1, lane, nxt);
     process_chunk(sm, st, cur, min(len - k * T, T), lane);
@@ -509,55 +541,42 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     o[2 * t + 1] = L > 0.f ? sum[1] / L : 0.f;
   }
   __syncthreads();
-  lds_fwht_rows(o, 1);
+  lds_fwht_rows<false>(o, 1);
   if (t < D) a.out[((int64_t)b * a.q_heads + h) * D + t] = o[t] * kInvSqrtD;
 }
 
 }  // namespace
 
-// Resident decode_split workgroups on the current device (CUs x blocks per
-// CU at this kernel's occupancy), queried once per device.
-static int resident_slots() {
+// SIMDs of the current device (CUs x 4), queried once per device.
+static int device_simds() {
   static std::atomic<int> cache[64];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256 * 8;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1024;
   int v = cache[dev].load(std::memory_order_relaxed);
   if (v > 0) return v;
-  int cus = 0, per = 0;
+  int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus <= 0)
     cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_split_kernel, 64, 0) !=
-          hipSuccess ||
-      per <= 0)
-    per = 8;
-  v = cus * per;
+  v = 4 * cus;
   cache[dev].store(v, std::memory_order_relaxed);
   return v;
 }
 
+// Splits per (sequence, kv-head, head group): about two single-wave
+// workgroups per SIMD in one round. Fewer leave SIMDs without a second wave
+// to overlap with; more add per-workgroup set-up and merge work (and a second
+// round) for no gain (measured on the 8 x 8 x 32768 and 32 x 8 x 8192 caches).
 int decode_auto_splits(int batch, int kv_heads, int q_heads, int capacity) {
   const int nch = capacity / T;
   if (batch <= 0 || kv_heads <= 0 || q_heads <= 0 || nch <= 0) return 1;
   const int G = q_heads / kv_heads;
   const int64_t pairs = (int64_t)batch * kv_heads * ((G + HG - 1) / HG);
-  const int64_t slots = resident_slots();
-  // cost of s splits in half-chunks: rounds of resident workgroups times the
-  // chunks of one workgroup plus half a chunk of set-up and merge work
-  const int64_t s_max = std::min<int64_t>(nch, 4 * slots / pairs + 1);
-  int best_s = 1;
-  int64_t best = INT64_MAX;
-  for (int64_t s = 1; s <= s_max; ++s) {
-    const int64_t per = (nch + s - 1) / s;
-    if ((nch + per - 1) / per != s) continue;  // same work split as a smaller s
-    const int64_t rounds = (pairs * s + slots - 1) / slots;
-    const int64_t cost = rounds * (2 * per + 1);
-    if (cost < best) {
-      best = cost;
-      best_s = (int)s;
-    }
-  }
-  return best_s;
+  const int64_t target = 2 * (int64_t)device_simds();
+  int64_t s = (target + pairs / 2) / pairs;
+  if (s > nch) s = nch;
+  if (s < 1) s = 1;
+  return (int)s;
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {

@@ -29,6 +29,18 @@ __device__ __forceinline__ float dpp_xor1(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
 }
 
+// Workgroup barrier for LDS traffic only: the wave's LDS accesses complete
+// (lgkmcnt(0)), then s_barrier. Unlike __syncthreads() it does not wait for
+// outstanding global loads and stores, so a prefetch stays in flight across
+// it. The wavefront-scope fences keep the compiler from moving LDS accesses
+// across the barrier; LDS is coherent inside the workgroup.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | 0xF | (0x3 << 14));  // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 

@@ -85,13 +85,11 @@ __device__ __forceinline__ float quad_max(float s) {
   return fmaxf(s, dpp_f<kXor2>(s));
 }
 
-// Sum of 32 products in eight interleaved partial sums combined as a tree,
-// keeping fp32 rounding close to that of a pairwise sum. LDS operands are
-// fetched four vectors at a time ahead of their FMAs.
+// Sum of 32 products in four interleaved partial sums (eight terms each)
+// combined as a tree, keeping fp32 rounding close to that of a pairwise sum.
+// LDS operands are fetched four vectors at a time ahead of their FMAs.
 __device__ __forceinline__ float dot32(const float (&p)[CPT], const float *w) {
-  float acc[8];
-#pragma unroll
-  for (int r = 0; r < 8; ++r) acc[r] = 0.f;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     f32x4 ww[4];
@@ -100,20 +98,18 @@ __device__ __forceinline__ float dot32(const float (&p)[CPT], const float *w) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = 16 * h + 4 * q;
-      acc[(e + 0) & 7] = fmaf(p[e + 0], ww[q].x, acc[(e + 0) & 7]);
-      acc[(e + 1) & 7] = fmaf(p[e + 1], ww[q].y, acc[(e + 1) & 7]);
-      acc[(e + 2) & 7] = fmaf(p[e + 2], ww[q].z, acc[(e + 2) & 7]);
-      acc[(e + 3) & 7] = fmaf(p[e + 3], ww[q].w, acc[(e + 3) & 7]);
+      acc[0] = fmaf(p[e + 0], ww[q].x, acc[0]);
+      acc[1] = fmaf(p[e + 1], ww[q].y, acc[1]);
+      acc[2] = fmaf(p[e + 2], ww[q].z, acc[2]);
+      acc[3] = fmaf(p[e + 3], ww[q].w, acc[3]);
     }
   }
-  return ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
 // Same, both operands from LDS (column step: P_ij * v_i over 32 tokens).
 __device__ __forceinline__ float dot32_lds(const float *a, const float *b) {
-  float acc[8];
-#pragma unroll
-  for (int r = 0; r < 8; ++r) acc[r] = 0.f;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     f32x4 x[4], y[4];
@@ -125,13 +121,13 @@ __device__ __forceinline__ float dot32_lds(const float *a, const float *b) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = 16 * h + 4 * q;
-      acc[(e + 0) & 7] = fmaf(x[q].x, y[q].x, acc[(e + 0) & 7]);
-      acc[(e + 1) & 7] = fmaf(x[q].y, y[q].y, acc[(e + 1) & 7]);
-      acc[(e + 2) & 7] = fmaf(x[q].z, y[q].z, acc[(e + 2) & 7]);
-      acc[(e + 3) & 7] = fmaf(x[q].w, y[q].w, acc[(e + 3) & 7]);
+      acc[0] = fmaf(x[q].x, y[q].x, acc[0]);
+      acc[1] = fmaf(x[q].y, y[q].y, acc[1]);
+      acc[2] = fmaf(x[q].z, y[q].z, acc[2]);
+      acc[3] = fmaf(x[q].w, y[q].w, acc[3]);
     }
   }
-  return ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
 // Cross-lane butterfly of one channel bit for 8 registers at once:
@@ -253,31 +249,29 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
     float p[CPT];
 #pragma unroll
     for (int i = 0; i < CPT; ++i) p[i] = y[i] * y[i];
-    if (a.kind == KVARN_V) __syncthreads();  // previous block's readers done with the staging
+    if (a.kind == KVARN_V) lds_barrier();  // previous block's readers done with the staging
     {
       float *dst = sm.pt + pt_at(CPT * hq, ti);
 #pragma unroll
       for (int i = 0; i < CPT; ++i) dst[i * PT_STRIDE] = p[i];
     }
-    __syncthreads();
+    lds_barrier();
 
     float *colp = a.col_scale + (bh * nch + chunk) * D;
     for (int it = 0; it < a.iters; ++it) {
       // row step: r_i^2 = (1/D) sum_j P_ij / c_j^2  ->  v_i = 1/r_i^2  (c = 1 first)
       float s;
       if (it == 0) {
-        float acc[8];
+        float acc[4] = {p[0], p[1], p[2], p[3]};
 #pragma unroll
-        for (int r = 0; r < 8; ++r) acc[r] = 0.f;
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) acc[i & 7] += p[i];
-        s = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+        for (int i = 4; i < CPT; ++i) acc[i & 3] += p[i];
+        s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
       } else {
         s = dot32(p, sm.w + qpad(CPT * hq));
       }
       s = quad_sum(s);
       if (hq == 0) sm.v[qpad(ti)] = s > 0.f ? (float)D * rcp(s) : 1.f;
-      __syncthreads();
+      lds_barrier();
       // column step: c_j^2 = (1/T) sum_i P_ij / r_i^2  ->  w_j = 1/c_j^2
       float cs = dot32_lds(sm.pt + pt_at(cj, CPT * cq), sm.v + qpad(CPT * cq));
       cs = quad_sum(cs);
@@ -291,14 +285,14 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
           sm.w[wj] = cm > 0.f ? __builtin_amdgcn_rsqf(cm) : 1.f;
         }
       }
-      __syncthreads();
+      lds_barrier();
     }
     if (a.iters == 0) {
       if (tid < D) {
         colp[tid] = 1.f;
         sm.w[qpad(tid)] = 1.f;
       }
-      __syncthreads();
+      lds_barrier();
     }
 
     if constexpr (!kF32) {
@@ -358,7 +352,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
         v4[0] = cw[4 * q + 0]; v4[1] = cw[4 * q + 1]; v4[2] = cw[4 * q + 2]; v4[3] = cw[4 * q + 3];
         dst[q] = v4;
       }
-      __syncthreads();
+      lds_barrier();
       if (tid < 256) {
         const int j4 = tid & 31;   // channels [4 j4, 4 j4 + 4)
         const int n4 = tid >> 5;   // tokens [16 n4, 16 n4 + 16)
