@@ -120,7 +120,6 @@ __device__ __forceinline__ float dot32_lds(const float *a, const float *b) {
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int e = 16 * h + 4 * q;
       acc[0] = fmaf(x[q].x, y[q].x, acc[0]);
       acc[1] = fmaf(x[q].y, y[q].y, acc[1]);
       acc[2] = fmaf(x[q].z, y[q].z, acc[2]);
