@@ -32,6 +32,18 @@ D, CHUNK = 128, 128
 # algorithmic bytes per element of one quantize launch: 2 B bf16 in, 0.25 B
 # codes, 4 B row scale per 128 channels, 4 B column scale per 128 tokens
 QUANT_BYTES_PER_ELT_BF16 = 2.0 + 0.25 + 4.0 / 128 + 4.0 / 128
+# fp32 VALU peak without packed math (packed fp32 is not used on the test machines):
+# 256 CUs x 4 SIMDs x 16 lanes x 2 flop per FMA x 2.4 GHz
+VALU_F32_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+
+
+def quant_flop_per_elt(iters: int) -> int:
+    """Algorithmic fp32 operations per element of the quantizer: rotation 7
+    add/sub, square 1, per balancing sweep a row and a column FMA (4 flop),
+    scaling by 1/c 1, running |max| 1, code FMA 2, rounding 1."""
+    return 7 + 1 + 4 * iters + 1 + 1 + 2 + 1
+
+
 # algorithmic bytes per cached token per kv-head read by decode: 64 B codes
 # (K and V), 8 B row scales, 8 B column scales amortized over the chunk
 DECODE_BYTES_PER_TOKEN = 80.0
@@ -252,12 +264,19 @@ def main():
                            "us_per_launch": round(q_us, 2), "launches_per_step": q_launches,
                            "GBps_algorithmic": round(q_gbps, 1),
                            "hbm_frac": round(q_gbps / HBM_PEAK_GBPS, 4)}
-        res["roofline"] = {"bound": "hbm", "achieved": round(q_gbps, 1),
-                           "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                           "frac": round(q_gbps / HBM_PEAK_GBPS, 4),
+        # the quantizer is bound by VALU arithmetic, not by HBM: its roofline is
+        # the non-packed fp32 VALU peak; the HBM fraction stays beside it
+        q_tflops = quant_flop_per_elt(args.iters) * elts_per_quant / (q_us * 1e-6) / 1e12
+        res["roofline"] = {"bound": "alu", "achieved": round(q_tflops, 2),
+                           "peak": round(VALU_F32_PEAK_TFLOPS, 2), "unit": "TFLOP/s",
+                           "frac": round(q_tflops / VALU_F32_PEAK_TFLOPS, 4),
                            "traffic": measured_traffic("quantize_block_kernel<bf16>", wl.name),
                            "kernel": "quantize_block_kernel<bf16>",
-                           "bytes_per_launch": qbytes}
+                           "flop_per_element": quant_flop_per_elt(args.iters),
+                           "elements_per_launch": elts_per_quant,
+                           "bytes_per_launch": qbytes,
+                           "hbm_achieved_GBps": round(q_gbps, 1),
+                           "hbm_frac": round(q_gbps / HBM_PEAK_GBPS, 4)}
         res["roofline_decode"] = dec_roof
     res["decode"] = dec
     res["append"] = {"us_per_launch": round(a_us, 2), "launches_per_step": 2 * L}

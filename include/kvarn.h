@@ -49,10 +49,32 @@ typedef enum {
     KVARN_ERR_DTYPE = -4,     /* unknown dtype or cache kind */
     KVARN_ERR_CAPACITY = -5,  /* tokens + token_offset exceed the cache capacity */
     KVARN_ERR_WORKSPACE = -6, /* workspace smaller than kvarn_decode_workspace_bytes */
-    KVARN_ERR_HIP = -7        /* a HIP launch or query failed */
+    KVARN_ERR_HIP = -7,       /* a HIP launch or query failed */
+    KVARN_ERR_FLAGS = -8      /* a flag bit this call does not know */
 } kvarn_status;
 
 typedef enum { KVARN_DT_BF16 = 0, KVARN_DT_F32 = 1 } kvarn_dtype;
+
+/*
+ * Flags of the *_ex calls (0 = the method as specified).
+ *
+ * KVARN_FLAG_NO_ROTATE  the rotation is absorbed into the model's weights
+ *     (rndamp article on KVarN, "How It Works", item 1: the Hadamard transform
+ *     can be folded into existing weights): quantize and append take K/V that
+ *     are already rotated (x . H_128 / sqrt(128)) and skip the rotation;
+ *     decode takes the rotated query q . H_128 / sqrt(128) and returns the
+ *     output in the rotated basis (out . H_128 / sqrt(128) is the output in
+ *     the original basis).
+ * KVARN_FLAG_ONE_SCALE  (decode only) ablation of the second scale: the
+ *     column scales are treated as 1 and not read ("Numbers": two scales
+ *     instead of one; the cost of fusing the second one is what this
+ *     measures). Meaningful on caches quantized with iters = 0, whose column
+ *     scales are 1; on other caches it computes attention over y_hat / c.
+ */
+enum {
+    KVARN_FLAG_NO_ROTATE = 1u << 0,
+    KVARN_FLAG_ONE_SCALE = 1u << 1
+};
 
 /* K caches store codes token-major, V caches channel-major (see below). */
 typedef enum { KVARN_K = 0, KVARN_V = 1 } kvarn_kind;
@@ -118,6 +140,14 @@ int kvarn_quantize(const void *x, int32_t dtype, int64_t stride_b,
                    int32_t token_offset, int32_t iters, const kvarn_cache *dst,
                    void *stream);
 
+/* kvarn_quantize with flags: KVARN_FLAG_NO_ROTATE only (other bits give
+ * KVARN_ERR_FLAGS). With it, x is taken as already rotated and the row scale
+ * is r' = max_j |x_ij / c_j| / 2 of x itself. */
+int kvarn_quantize_ex(const void *x, int32_t dtype, int64_t stride_b,
+                      int64_t stride_h, int64_t stride_t, int32_t tokens,
+                      int32_t token_offset, int32_t iters, uint32_t flags,
+                      const kvarn_cache *dst, void *stream);
+
 /*
  * kvarn_append -- quantize one new token per sequence into an existing cache
  * (rndamp article, "The Problem": during decoding the cache grows one token
@@ -138,6 +168,10 @@ int kvarn_quantize(const void *x, int32_t dtype, int64_t stride_b,
  */
 int kvarn_append(const void *x, int32_t dtype, const int32_t *positions,
                  const kvarn_cache *dst, void *stream);
+
+/* kvarn_append with flags: KVARN_FLAG_NO_ROTATE only. */
+int kvarn_append_ex(const void *x, int32_t dtype, const int32_t *positions,
+                    uint32_t flags, const kvarn_cache *dst, void *stream);
 
 /*
  * kvarn_decode_workspace_bytes -- (host only) bytes of device workspace that
@@ -175,6 +209,13 @@ int kvarn_decode_attn(const void *q, int32_t q_dtype, int32_t q_heads,
                       const int32_t *seq_lens, float softmax_scale, float *out,
                       int32_t n_split, void *workspace, size_t workspace_bytes,
                       void *stream);
+
+/* kvarn_decode_attn with flags: KVARN_FLAG_NO_ROTATE, KVARN_FLAG_ONE_SCALE. */
+int kvarn_decode_attn_ex(const void *q, int32_t q_dtype, int32_t q_heads,
+                         const kvarn_cache *k, const kvarn_cache *v,
+                         const int32_t *seq_lens, float softmax_scale,
+                         uint32_t flags, float *out, int32_t n_split,
+                         void *workspace, size_t workspace_bytes, void *stream);
 
 /* kvarn_status_string -- (host only) static text for a kvarn_status. */
 const char *kvarn_status_string(int status);

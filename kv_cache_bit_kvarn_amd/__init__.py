@@ -22,11 +22,14 @@ CHUNK_BYTES = 4096
 
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_CAPACITY, ERR_WORKSPACE, ERR_HIP = (
     0, -1, -2, -3, -4, -5, -6, -7)
+ERR_FLAGS = -8
+FLAG_NO_ROTATE, FLAG_ONE_SCALE = 1, 2
 DT_BF16, DT_F32 = 0, 1
 K, V = 0, 1
 
-EXPORTED = ("kvarn_quantize", "kvarn_append", "kvarn_decode_workspace_bytes",
-            "kvarn_decode_attn", "kvarn_status_string")
+EXPORTED = ("kvarn_quantize", "kvarn_quantize_ex", "kvarn_append", "kvarn_append_ex",
+            "kvarn_decode_workspace_bytes", "kvarn_decode_attn", "kvarn_decode_attn_ex",
+            "kvarn_status_string")
 
 
 class KvarnError(RuntimeError):
@@ -66,6 +69,14 @@ def load(path: str | None = None):
     L.kvarn_decode_attn.argtypes = [vp, i32, i32, cd, cd, vp, ctypes.c_float, vp, i32,
                                     vp, ctypes.c_size_t, vp]
     L.kvarn_decode_attn.restype = ctypes.c_int
+    u32 = ctypes.c_uint32
+    L.kvarn_quantize_ex.argtypes = [vp, i32, i64, i64, i64, i32, i32, i32, u32, cd, vp]
+    L.kvarn_quantize_ex.restype = ctypes.c_int
+    L.kvarn_append_ex.argtypes = [vp, i32, vp, u32, cd, vp]
+    L.kvarn_append_ex.restype = ctypes.c_int
+    L.kvarn_decode_attn_ex.argtypes = [vp, i32, i32, cd, cd, vp, ctypes.c_float, u32, vp, i32,
+                                       vp, ctypes.c_size_t, vp]
+    L.kvarn_decode_attn_ex.restype = ctypes.c_int
     L.kvarn_status_string.argtypes = [ctypes.c_int]
     L.kvarn_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -137,30 +148,32 @@ class Cache:
 
 
 def quantize(x: torch.Tensor, cache: Cache, token_offset: int = 0, iters: int = 4,
-             stream=None) -> None:
+             stream=None, flags: int = 0) -> None:
     """x [B, H, tokens, 128] (bf16/fp32, channels contiguous) -> cache slots
-    [token_offset, token_offset + tokens)."""
+    [token_offset, token_offset + tokens). flags: FLAG_NO_ROTATE."""
     if x.dim() != 4 or x.shape[3] != HEAD_DIM or x.stride(3) != 1:
         raise ValueError("x must be [B, H, T, 128] with contiguous channels")
     if x.shape[0] != cache.batch or x.shape[1] != cache.kv_heads:
         raise ValueError("x batch/heads differ from the cache")
     d = cache.desc()
-    st = load().kvarn_quantize(x.data_ptr(), _dtype_code(x), x.stride(0), x.stride(1),
-                               x.stride(2), x.shape[2], token_offset, iters,
-                               ctypes.byref(d), _stream(stream))
+    st = load().kvarn_quantize_ex(x.data_ptr(), _dtype_code(x), x.stride(0), x.stride(1),
+                                  x.stride(2), x.shape[2], token_offset, iters, flags,
+                                  ctypes.byref(d), _stream(stream))
     _raise(st, "kvarn_quantize")
 
 
-def append(x: torch.Tensor, positions: torch.Tensor, cache: Cache, stream=None) -> None:
-    """x [B, H, 128] new tokens at positions [B] (int32, device)."""
+def append(x: torch.Tensor, positions: torch.Tensor, cache: Cache, stream=None,
+           flags: int = 0) -> None:
+    """x [B, H, 128] new tokens at positions [B] (int32, device). flags:
+    FLAG_NO_ROTATE."""
     if x.dim() != 3 or tuple(x.shape) != (cache.batch, cache.kv_heads, HEAD_DIM) or \
             not x.is_contiguous():
         raise ValueError("x must be contiguous [B, H, 128] matching the cache")
     if positions.dtype != torch.int32 or positions.numel() != cache.batch:
         raise ValueError("positions must be int32 [B]")
     d = cache.desc()
-    st = load().kvarn_append(x.data_ptr(), _dtype_code(x), positions.data_ptr(),
-                             ctypes.byref(d), _stream(stream))
+    st = load().kvarn_append_ex(x.data_ptr(), _dtype_code(x), positions.data_ptr(), flags,
+                                ctypes.byref(d), _stream(stream))
     _raise(st, "kvarn_append")
 
 
@@ -176,8 +189,10 @@ def decode_workspace(batch: int, q_heads: int, capacity: int, device="cuda") -> 
 def decode_attn(q: torch.Tensor, k: Cache, v: Cache, seq_lens: torch.Tensor,
                 out: torch.Tensor | None = None, softmax_scale: float | None = None,
                 n_split: int = 0, workspace: torch.Tensor | None = None,
-                stream=None) -> torch.Tensor:
-    """q [B, Hq, 128] -> out fp32 [B, Hq, 128] (original basis)."""
+                stream=None, flags: int = 0) -> torch.Tensor:
+    """q [B, Hq, 128] -> out fp32 [B, Hq, 128] (original basis; with
+    FLAG_NO_ROTATE q and out are in the rotated basis). flags: FLAG_NO_ROTATE,
+    FLAG_ONE_SCALE."""
     if q.dim() != 3 or q.shape[2] != HEAD_DIM or not q.is_contiguous():
         raise ValueError("q must be contiguous [B, Hq, 128]")
     if seq_lens.dtype != torch.int32 or seq_lens.numel() != k.batch:
@@ -190,10 +205,10 @@ def decode_attn(q: torch.Tensor, k: Cache, v: Cache, seq_lens: torch.Tensor,
     if softmax_scale is None:
         softmax_scale = HEAD_DIM ** -0.5
     kd, vd = k.desc(), v.desc()
-    st = load().kvarn_decode_attn(q.data_ptr(), _dtype_code(q), Hq, ctypes.byref(kd),
-                                  ctypes.byref(vd), seq_lens.data_ptr(), softmax_scale,
-                                  out.data_ptr(), n_split, workspace.data_ptr(),
-                                  workspace.numel() * workspace.element_size(),
-                                  _stream(stream))
+    st = load().kvarn_decode_attn_ex(q.data_ptr(), _dtype_code(q), Hq, ctypes.byref(kd),
+                                     ctypes.byref(vd), seq_lens.data_ptr(), softmax_scale,
+                                     flags, out.data_ptr(), n_split, workspace.data_ptr(),
+                                     workspace.numel() * workspace.element_size(),
+                                     _stream(stream))
     _raise(st, "kvarn_decode_attn")
     return out

@@ -34,9 +34,10 @@ int from_hip(hipError_t e) { return e == hipSuccess ? KVARN_OK : KVARN_ERR_HIP; 
 
 extern "C" {
 
-int kvarn_quantize(const void *x, int32_t dtype, int64_t stride_b, int64_t stride_h,
-                   int64_t stride_t, int32_t tokens, int32_t token_offset, int32_t iters,
-                   const kvarn_cache *dst, void *stream) {
+int kvarn_quantize_ex(const void *x, int32_t dtype, int64_t stride_b, int64_t stride_h,
+                      int64_t stride_t, int32_t tokens, int32_t token_offset, int32_t iters,
+                      uint32_t flags, const kvarn_cache *dst, void *stream) {
+  if (flags & ~(uint32_t)KVARN_FLAG_NO_ROTATE) return KVARN_ERR_FLAGS;
   int st = check_cache(dst);
   if (st != KVARN_OK) return st;
   if (tokens == 0) return KVARN_OK;  // nothing to read or write; x may be NULL
@@ -66,6 +67,7 @@ int kvarn_quantize(const void *x, int32_t dtype, int64_t stride_b, int64_t strid
   a.div_chunks = make_fastdiv((uint32_t)a.chunks);
   a.div_heads = make_fastdiv((uint32_t)a.heads);
   a.iters = iters;
+  a.flags = flags;
   a.capacity = dst->capacity;
   a.kind = dst->kind;
   a.codes = dst->codes;
@@ -74,8 +76,16 @@ int kvarn_quantize(const void *x, int32_t dtype, int64_t stride_b, int64_t strid
   return from_hip(launch_quantize(a, static_cast<hipStream_t>(stream)));
 }
 
-int kvarn_append(const void *x, int32_t dtype, const int32_t *positions,
-                 const kvarn_cache *dst, void *stream) {
+int kvarn_quantize(const void *x, int32_t dtype, int64_t stride_b, int64_t stride_h,
+                   int64_t stride_t, int32_t tokens, int32_t token_offset, int32_t iters,
+                   const kvarn_cache *dst, void *stream) {
+  return kvarn_quantize_ex(x, dtype, stride_b, stride_h, stride_t, tokens, token_offset, iters,
+                           0u, dst, stream);
+}
+
+int kvarn_append_ex(const void *x, int32_t dtype, const int32_t *positions, uint32_t flags,
+                    const kvarn_cache *dst, void *stream) {
+  if (flags & ~(uint32_t)KVARN_FLAG_NO_ROTATE) return KVARN_ERR_FLAGS;
   if (!x || !positions) return KVARN_ERR_NULL;
   int st = check_cache(dst);
   if (st != KVARN_OK) return st;
@@ -91,10 +101,16 @@ int kvarn_append(const void *x, int32_t dtype, const int32_t *positions,
   a.heads = dst->kv_heads;
   a.capacity = dst->capacity;
   a.kind = dst->kind;
+  a.flags = flags;
   a.codes = dst->codes;
   a.row_scale = dst->row_scale;
   a.col_scale = dst->col_scale;
   return from_hip(launch_append(a, static_cast<hipStream_t>(stream)));
+}
+
+int kvarn_append(const void *x, int32_t dtype, const int32_t *positions,
+                 const kvarn_cache *dst, void *stream) {
+  return kvarn_append_ex(x, dtype, positions, 0u, dst, stream);
 }
 
 size_t kvarn_decode_workspace_bytes(int32_t batch, int32_t q_heads, int32_t capacity) {
@@ -102,10 +118,11 @@ size_t kvarn_decode_workspace_bytes(int32_t batch, int32_t q_heads, int32_t capa
   return (size_t)batch * q_heads * (size_t)(capacity / T) * (2 + D) * sizeof(float);
 }
 
-int kvarn_decode_attn(const void *q, int32_t q_dtype, int32_t q_heads, const kvarn_cache *k,
-                      const kvarn_cache *v, const int32_t *seq_lens, float softmax_scale,
-                      float *out, int32_t n_split, void *workspace, size_t workspace_bytes,
-                      void *stream) {
+int kvarn_decode_attn_ex(const void *q, int32_t q_dtype, int32_t q_heads, const kvarn_cache *k,
+                         const kvarn_cache *v, const int32_t *seq_lens, float softmax_scale,
+                         uint32_t flags, float *out, int32_t n_split, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+  if (flags & ~(uint32_t)(KVARN_FLAG_NO_ROTATE | KVARN_FLAG_ONE_SCALE)) return KVARN_ERR_FLAGS;
   if (!q || !seq_lens || !out) return KVARN_ERR_NULL;
   int st = check_cache(k);
   if (st != KVARN_OK) return st;
@@ -148,9 +165,18 @@ int kvarn_decode_attn(const void *q, int32_t q_dtype, int32_t q_heads, const kva
   a.v_col = v->col_scale;
   a.lens = seq_lens;
   a.scale = softmax_scale;
+  a.flags = flags;
   a.out = out;
   a.partial = static_cast<float *>(workspace);
   return from_hip(launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+int kvarn_decode_attn(const void *q, int32_t q_dtype, int32_t q_heads, const kvarn_cache *k,
+                      const kvarn_cache *v, const int32_t *seq_lens, float softmax_scale,
+                      float *out, int32_t n_split, void *workspace, size_t workspace_bytes,
+                      void *stream) {
+  return kvarn_decode_attn_ex(q, q_dtype, q_heads, k, v, seq_lens, softmax_scale, 0u, out,
+                              n_split, workspace, workspace_bytes, stream);
 }
 
 const char *kvarn_status_string(int status) {
@@ -162,6 +188,7 @@ const char *kvarn_status_string(int status) {
     case KVARN_ERR_DTYPE: return "unknown dtype or cache kind";
     case KVARN_ERR_CAPACITY: return "tokens + token_offset exceed the cache capacity";
     case KVARN_ERR_WORKSPACE: return "workspace smaller than kvarn_decode_workspace_bytes";
+    case KVARN_ERR_FLAGS: return "flag bit not supported by this call";
     case KVARN_ERR_HIP: return "HIP launch failed";
     default: return "unknown status";
   }

@@ -14,7 +14,9 @@ namespace {
 
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
-template <bool kF32>
+// kRotate = false: the token is already rotated (rotation absorbed into the
+// model's weights).
+template <bool kF32, bool kRotate>
 __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
   const int bh = blockIdx.x;
   const int b = bh / a.heads;
@@ -35,17 +37,17 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
     y1 = __uint_as_float((uint32_t)x[lane + 64] << 16);
   }
   // rotation: channel bit 6 inside the lane, bits 0..5 across lanes
-  {
+  if constexpr (kRotate) {
     const float s = y0 + y1, d = y0 - y1;
     y0 = s;
     y1 = d;
-  }
 #pragma unroll
-  for (int bit = 1; bit < 64; bit <<= 1) {
-    const float p0 = shfl_xor(y0, bit), p1 = shfl_xor(y1, bit);
-    const bool hi = (lane & bit) != 0;
-    y0 = hi ? p0 - y0 : y0 + p0;
-    y1 = hi ? p1 - y1 : y1 + p1;
+    for (int bit = 1; bit < 64; bit <<= 1) {
+      const float p0 = shfl_xor(y0, bit), p1 = shfl_xor(y1, bit);
+      const bool hi = (lane & bit) != 0;
+      y0 = hi ? p0 - y0 : y0 + p0;
+      y1 = hi ? p1 - y1 : y1 + p1;
+    }
   }
 
   float *col = a.col_scale + ((int64_t)bh * nch + k) * D;
@@ -68,7 +70,8 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
   float m = fmaxf(fabsf(z0), fabsf(z1));
 #pragma unroll
   for (int bit = 1; bit < 64; bit <<= 1) m = fmaxf(m, shfl_xor(m, bit));
-  if (lane == 0) a.row_scale[(int64_t)bh * a.capacity + pos] = m * kRangeFromUnscaled;
+  if (lane == 0)
+    a.row_scale[(int64_t)bh * a.capacity + pos] = m * (kRotate ? kRangeFromUnscaled : kRangeFromRotated);
   const float qs = m > 0.f ? 2.f / m : 0.f;
   const uint32_t q0 = (uint32_t)fminf(fmaxf(fmaf(z0, qs, 2.f), 0.f), 3.f);
   const uint32_t q1 = (uint32_t)fminf(fmaxf(fmaf(z1, qs, 2.f), 0.f), 3.f);
@@ -107,10 +110,18 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
 hipError_t launch_append(const AppendArgs &a, hipStream_t s) {
   const int blocks = a.batch * a.heads;
   if (blocks == 0) return hipSuccess;
-  if (a.dtype == KVARN_DT_F32)
-    hipLaunchKernelGGL(append_kernel<true>, dim3(blocks), dim3(64), 0, s, a);
-  else
-    hipLaunchKernelGGL(append_kernel<false>, dim3(blocks), dim3(64), 0, s, a);
+  const bool rot = !(a.flags & KVARN_FLAG_NO_ROTATE);
+  if (a.dtype == KVARN_DT_F32) {
+    if (rot)
+      hipLaunchKernelGGL((append_kernel<true, true>), dim3(blocks), dim3(64), 0, s, a);
+    else
+      hipLaunchKernelGGL((append_kernel<true, false>), dim3(blocks), dim3(64), 0, s, a);
+  } else {
+    if (rot)
+      hipLaunchKernelGGL((append_kernel<false, true>), dim3(blocks), dim3(64), 0, s, a);
+    else
+      hipLaunchKernelGGL((append_kernel<false, false>), dim3(blocks), dim3(64), 0, s, a);
+  }
   return hipGetLastError();
 }
 

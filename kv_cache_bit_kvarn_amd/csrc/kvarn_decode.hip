@@ -245,6 +245,7 @@ struct ChunkRegs {
   u32x2 ck, cv, rk, rv;  // scales of elements 2 lane, 2 lane + 1
 };
 
+template <bool kTwoScales>
 __device__ __forceinline__ void load_chunk(const DecodeArgs &a, int64_t bg, int64_t nchunks,
                                            int k, int lane, ChunkRegs &r) {
   const int64_t chunk = bg * nchunks + k;
@@ -256,8 +257,10 @@ __device__ __forceinline__ void load_chunk(const DecodeArgs &a, int64_t bg, int6
     r.k[t] = *reinterpret_cast<const u32x2 *>(kc + 64 * t);   // token + 2 t
     r.v[t] = *reinterpret_cast<const u32x2 *>(vc + 512 * t);  // channel + 16 t
   }
-  r.ck = *reinterpret_cast<const u32x2 *>(a.k_col + chunk * D + 2 * lane);
-  r.cv = *reinterpret_cast<const u32x2 *>(a.v_col + chunk * D + 2 * lane);
+  if constexpr (kTwoScales) {
+    r.ck = *reinterpret_cast<const u32x2 *>(a.k_col + chunk * D + 2 * lane);
+    r.cv = *reinterpret_cast<const u32x2 *>(a.v_col + chunk * D + 2 * lane);
+  }
   const int64_t row = bg * (int64_t)a.capacity + (int64_t)k * T + 2 * lane;
   r.rk = *reinterpret_cast<const u32x2 *>(a.k_row + row);
   r.rv = *reinterpret_cast<const u32x2 *>(a.v_row + row);
@@ -269,8 +272,38 @@ struct SplitState {
   float m_run, l_run;
 };
 
+// The QK operand from this lane's 8 values x of head lane >> 4, slot
+// lane & 15: per-head range scale, 4 fp8 terms written to rows 4 h + k of
+// sm.aq. Returns this lane's E8M0 row-scale byte for the operand it reads.
+__device__ __forceinline__ int build_qk_operand(DecSmem &sm, float (&x)[8], int lane) {
+  const int n = lane & 15, h = lane >> 4;
+  float mx = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(x[j]));
+  const int sig = range_exp8(group_max<16>(mx));
+  const float sc = __builtin_ldexpf(1.f, sig);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] *= sc;
+  u32x2 t[4];
+  fp8_terms<4>(x, t);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x2 *>(&sm.aq[4 * h + k][2 * n]) = t[k];
+  return row_scale_byte(sig, lane);
+}
+
+__device__ __forceinline__ u32x8 read_operand(const uint32_t (&rows)[16][OP_ROW], int lane) {
+  const int n = lane & 15, h = lane >> 4;
+  const u32x4 a0 = *reinterpret_cast<const u32x4 *>(&rows[n][8 * h]);
+  const u32x4 a1 = *reinterpret_cast<const u32x4 *>(&rows[n][8 * h + 4]);
+  return u32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+}
+
+// kTwoScales = false: the column scales are taken as 1 (one-scale ablation);
+// the QK operand (aq_fixed, sa_fixed) is then the same for every chunk.
+template <bool kTwoScales>
 __device__ __forceinline__ void process_chunk(DecSmem &sm, SplitState &st, const ChunkRegs &cur,
-                                              int nvalid, int lane) {
+                                              int nvalid, int lane, const u32x8 &aq_fixed,
+                                              int sa_fixed) {
   const int n = lane & 15, h = lane >> 4;
   const int sb = slot_base(n);
 
@@ -279,10 +312,12 @@ __device__ __forceinline__ void process_chunk(DecSmem &sm, SplitState &st, const
   {
     const int e = 2 * lane;
     const int pe = elem_pos(e), pc = cv_pos(e);  // element e + 1 sits 8 further on
-    sm.ck[pe] = __uint_as_float(cur.ck[0]);
-    sm.ck[pe + 8] = __uint_as_float(cur.ck[1]);
-    sm.cv[pc] = __uint_as_float(cur.cv[0]);
-    sm.cv[pc + 8] = __uint_as_float(cur.cv[1]);
+    if constexpr (kTwoScales) {
+      sm.ck[pe] = __uint_as_float(cur.ck[0]);
+      sm.ck[pe + 8] = __uint_as_float(cur.ck[1]);
+      sm.cv[pc] = __uint_as_float(cur.cv[0]);
+      sm.cv[pc + 8] = __uint_as_float(cur.cv[1]);
+    }
     sm.rk[pe] = __uint_as_float(cur.rk[0]);
     sm.rk[pe + 8] = __uint_as_float(cur.rk[1]);
     sm.rv[pe] = __uint_as_float(cur.rv[0]);
@@ -291,35 +326,22 @@ __device__ __forceinline__ void process_chunk(DecSmem &sm, SplitState &st, const
   wave_lds_sync();
 
   // ---- QK operand: head h, slot n: x = q * c_K * 2^sigma_h as 4 fp8 terms ----
-  int sa_q;
-  {
+  int sa_q = sa_fixed;
+  u32x8 aq = aq_fixed;
+  if constexpr (kTwoScales) {
     const f32x4 c0 = *reinterpret_cast<const f32x4 *>(&sm.ck[sb]);
     const f32x4 c1 = *reinterpret_cast<const f32x4 *>(&sm.ck[sb + 4]);
     float x[8];
-    float mx = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      x[j] = st.qv[j] * (j < 4 ? c0[j] : c1[j - 4]);
-      mx = fmaxf(mx, fabsf(x[j]));
-    }
-    const int sig = range_exp8(group_max<16>(mx));
-    const float sc = __builtin_ldexpf(1.f, sig);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] *= sc;
-    u32x2 t[4];
-    fp8_terms<4>(x, t);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x2 *>(&sm.aq[4 * h + k][2 * n]) = t[k];
-    sa_q = row_scale_byte(sig, lane);
+    for (int j = 0; j < 8; ++j) x[j] = st.qv[j] * (j < 4 ? c0[j] : c1[j - 4]);
+    sa_q = build_qk_operand(sm, x, lane);
+    wave_lds_sync();
+    aq = read_operand(sm.aq, lane);
   }
-  wave_lds_sync();
 
   // ---- QK^T: 8 token tiles; the four terms of head h land in d[0..3] ----
   float s[8];
   {
-    const u32x4 a0 = *reinterpret_cast<const u32x4 *>(&sm.aq[n][8 * h]);
-    const u32x4 a1 = *reinterpret_cast<const u32x4 *>(&sm.aq[n][8 * h + 4]);
-    const u32x8 aq = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
     const f32x4 off = level_offset(aq, sa_q);
     // all eight products are independent: issue them back to back and sum
     // the terms afterwards, so the MFMA latency is paid once
@@ -387,21 +409,30 @@ __device__ __forceinline__ void process_chunk(DecSmem &sm, SplitState &st, const
     wave_lds_sync();
 
     // ---- PV: 8 channel tiles ----
-    const u32x4 a0 = *reinterpret_cast<const u32x4 *>(&sm.ap[n][8 * h]);
-    const u32x4 a1 = *reinterpret_cast<const u32x4 *>(&sm.ap[n][8 * h + 4]);
-    const u32x8 ap = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    const u32x8 ap = read_operand(sm.ap, lane);
     const f32x4 off = level_offset(ap, sa_p);
-    const f32x4 cv0 = *reinterpret_cast<const f32x4 *>(&sm.cv[sb]);
-    const f32x4 cv1 = *reinterpret_cast<const f32x4 *>(&sm.cv[sb + 4]);
+    f32x4 cv0 = {1.f, 1.f, 1.f, 1.f}, cv1 = cv0;
+    if constexpr (kTwoScales) {
+      cv0 = *reinterpret_cast<const f32x4 *>(&sm.cv[sb]);
+      cv1 = *reinterpret_cast<const f32x4 *>(&sm.cv[sb + 4]);
+    }
     f32x4 d[8];
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) d[ct] = mfma_f8f4(ap, code_operand(cur.v[ct]), off, sa_p);
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
-      st.acc[ct] = fmaf(ct < 4 ? cv0[ct] : cv1[ct - 4], (d[ct][0] + d[ct][1]) + d[ct][2], st.acc[ct]);
+    for (int ct = 0; ct < 8; ++ct) {
+      const float dv = (d[ct][0] + d[ct][1]) + d[ct][2];
+      if constexpr (kTwoScales)
+        st.acc[ct] = fmaf(ct < 4 ? cv0[ct] : cv1[ct - 4], dv, st.acc[ct]);
+      else
+        st.acc[ct] += dv;
+    }
   }
 }
 
+// kRotate = false: the query comes rotated (rotation absorbed into the model's
+// weights); kTwoScales = false: column scales taken as 1 (ablation).
+template <bool kRotate, bool kTwoScales>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   __shared__ DecSmem sm;
   const int lane = threadIdx.x;
@@ -440,17 +471,29 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
   for (int r = 0; r < HG * D / 64; ++r) qin[r] = r / 2 < nh ? qin[r] : 0.f;
   ChunkRegs cur, nxt;
-  if (c0 < c1) load_chunk(a, bg, nch, c0, lane, cur);
+  if (c0 < c1) load_chunk<kTwoScales>(a, bg, nch, c0, lane, cur);
 #pragma unroll
   for (int r = 0; r < HG * D / 64; ++r) sm.qt[r / 2][lane + 64 * (r & 1)] = qin[r];
   for (int idx = lane; idx < 16 * OP_ROW; idx += 64) (&sm.ap[0][0])[idx] = 0u;
   wave_lds_sync();
-  lds_fwht_rows<true>(&sm.qt[0][0], HG);
+  if constexpr (kRotate) lds_fwht_rows<true>(&sm.qt[0][0], HG);
   SplitState st;
   {
-    const float qs = 2.f * a.scale * kLog2e * kInvSqrtD;
+    // the unscaled rotation's 1/sqrt(128) applies only when it ran here
+    const float qs = 2.f * a.scale * kLog2e * (kRotate ? kInvSqrtD : 1.f);
 #pragma unroll
     for (int j = 0; j < 8; ++j) st.qv[j] = sm.qt[lane >> 4][slot_elem(lane & 15, j)] * qs;
+  }
+  // one scale: the QK operand does not change from chunk to chunk
+  u32x8 aq_fixed = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+  int sa_fixed = 127;
+  if constexpr (!kTwoScales) {
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = st.qv[j];
+    sa_fixed = build_qk_operand(sm, x, lane);
+    wave_lds_sync();
+    aq_fixed = read_operand(sm.aq, lane);
   }
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) st.acc[ct] = 0.f;
@@ -463,8 +506,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   // loads it has just issued: the counter completes in order).
   __builtin_amdgcn_s_waitcnt(kVmcntZero);
   for (int k = c0; k < c1; ++k) {
-    if (k + 1 < c1) load_chunk(a, bg, nch, k + 1, lane, nxt);
-    process_chunk(sm, st, cur, min(len - k * T, T), lane);
+    if (k + 1 < c1) load_chunk<kTwoScales>(a, bg, nch, k + 1, lane, nxt);
+    process_chunk<kTwoScales>(sm, st, cur, min(len - k * T, T), lane, aq_fixed, sa_fixed);
     cur = nxt;
   }
 
@@ -488,6 +531,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 // the split maxima, then takes the splits in rounds of 256; in a round each
 // thread weighs one split, and wave w accumulates splits w, w + 4, ... with
 // 8-byte loads of two channels per lane; the four waves' sums meet in LDS.
+template <bool kRotate>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   __shared__ float wgt[256];
   __shared__ float red_m[4], red_l[4];
@@ -541,8 +585,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     o[2 * t + 1] = L > 0.f ? sum[1] / L : 0.f;
   }
   __syncthreads();
-  lds_fwht_rows<false>(o, 1);
-  if (t < D) a.out[((int64_t)b * a.q_heads + h) * D + t] = o[t] * kInvSqrtD;
+  if constexpr (kRotate) lds_fwht_rows<false>(o, 1);
+  if (t < D) a.out[((int64_t)b * a.q_heads + h) * D + t] = kRotate ? o[t] * kInvSqrtD : o[t];
 }
 
 }  // namespace
@@ -584,10 +628,21 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
   const int G = a.q_heads / a.kv_heads;
   const int n_hg = (G + HG - 1) / HG;
   const dim3 grid(a.n_split * n_hg, a.kv_heads, a.batch);
-  hipLaunchKernelGGL(decode_split_kernel, grid, dim3(64), 0, s, a);
+  const bool rot = !(a.flags & KVARN_FLAG_NO_ROTATE), two = !(a.flags & KVARN_FLAG_ONE_SCALE);
+  if (rot && two)
+    hipLaunchKernelGGL((decode_split_kernel<true, true>), grid, dim3(64), 0, s, a);
+  else if (rot)
+    hipLaunchKernelGGL((decode_split_kernel<true, false>), grid, dim3(64), 0, s, a);
+  else if (two)
+    hipLaunchKernelGGL((decode_split_kernel<false, true>), grid, dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<false, false>), grid, dim3(64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3(a.q_heads, a.batch), dim3(256), 0, s, a);
+  if (rot)
+    hipLaunchKernelGGL((decode_combine_kernel<true>), dim3(a.q_heads, a.batch), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_combine_kernel<false>), dim3(a.q_heads, a.batch), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -22,6 +22,8 @@ constexpr int GQA_MAX = 8;             // query heads per kv-head supported by d
 // max|y'/c| * 2^-4.5, while c and every code are unchanged by that factor.
 constexpr float kRangeFromUnscaled = 0.044194173824159216f;
 constexpr float kInvSqrtD = 0.088388347648318447f;  // 1/sqrt(128)
+// r' = max|y/c|/2 for input that is already rotated (KVARN_FLAG_NO_ROTATE)
+constexpr float kRangeFromRotated = 0.5f;
 
 // ---- cross-lane helpers (DPP on gfx950, wave64) -------------------------
 __device__ __forceinline__ float dpp_xor1(float v) {
@@ -60,6 +62,7 @@ struct QuantArgs {
   int dtype;
   int64_t sb, sh, st;
   int batch, heads, chunks, chunk0, iters, capacity, kind;
+  uint32_t flags;       // KVARN_FLAG_NO_ROTATE
   uint32_t nblocks;     // batch * heads * chunks (< 2^31)
   FastDiv div_chunks, div_heads;
   uint8_t *codes;
@@ -72,6 +75,7 @@ struct AppendArgs {
   int dtype;
   const int32_t *pos;
   int batch, heads, capacity, kind;
+  uint32_t flags;  // KVARN_FLAG_NO_ROTATE
   uint8_t *codes;
   float *row_scale, *col_scale;
 };
@@ -80,6 +84,7 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t s);
 struct DecodeArgs {
   const void *q;
   int q_dtype, batch, q_heads, kv_heads, capacity, n_split;
+  uint32_t flags;  // KVARN_FLAG_NO_ROTATE, KVARN_FLAG_ONE_SCALE
   const uint8_t *k_codes, *v_codes;
   const float *k_row, *k_col, *v_row, *v_col;
   const int32_t *lens;

@@ -181,7 +181,9 @@ __device__ __forceinline__ void load_bf16_block(const QuantArgs &a, uint32_t blk
   for (int q = 0; q < 4; ++q) xr[q] = __builtin_nontemporal_load(src + q);
 }
 
-template <bool kF32>
+// kRotate = false: the input is already rotated (rotation absorbed into the
+// model's weights) and the rotation step is skipped.
+template <bool kF32, bool kRotate>
 __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a) {
   __shared__ QuantSmem sm;
   const int tid = threadIdx.x;
@@ -194,7 +196,10 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
   // the two cross-lane butterflies leave negated the values of the lanes
   // whose hq bit 0 (first) or bit 1 (second) is set
   const float s1 = (hq & 1) ? -1.f : 1.f, s2 = (hq & 2) ? -1.f : 1.f;
-  const float lane_sign = s1 * s2;
+  const float lane_sign = kRotate ? s1 * s2 : 1.f;
+  // r' from the running maximum: the unscaled rotation's 1/sqrt(128) and the
+  // 1/2 of the range step, or the 1/2 alone for pre-rotated input
+  const float range_factor = kRotate ? kRangeFromUnscaled : kRangeFromRotated;
 
   u32x4 xr[4];
   uint32_t blk = blockIdx.x;
@@ -228,21 +233,23 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
     }
 
     // ---- 2. rotation: y <- y . H_128 (Sylvester order, unscaled) -----------
+    if constexpr (kRotate) {
 #pragma unroll
-    for (int len = 1; len < CPT; len <<= 1) {
+      for (int len = 1; len < CPT; len <<= 1) {
 #pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        if ((i & len) == 0) {
-          const float p = y[i], q = y[i + len];
-          y[i] = p + q;
-          y[i + len] = p - q;
+        for (int i = 0; i < CPT; ++i) {
+          if ((i & len) == 0) {
+            const float p = y[i], q = y[i + len];
+            y[i] = p + q;
+            y[i + len] = p - q;
+          }
         }
       }
+#pragma unroll
+      for (int i = 0; i < CPT; i += 8) butterfly_xor1_x8(y + i, s1);
+#pragma unroll
+      for (int i = 0; i < CPT; i += 8) butterfly_xor2_x8(y + i, s2);
     }
-#pragma unroll
-    for (int i = 0; i < CPT; i += 8) butterfly_xor1_x8(y + i, s1);
-#pragma unroll
-    for (int i = 0; i < CPT; i += 8) butterfly_xor2_x8(y + i, s2);
 
     // ---- 3. dual scaling ---------------------------------------------------
     float p[CPT];
@@ -314,7 +321,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
       for (int i = 0; i < CPT; ++i) m = fmaxf(m, fabsf(y[i]));
     }
     m = quad_max(m);
-    if (hq == 0) a.row_scale[bh * a.capacity + (int64_t)chunk * T + ti] = m * kRangeFromUnscaled;
+    if (hq == 0) a.row_scale[bh * a.capacity + (int64_t)chunk * T + ti] = m * range_factor;
     const float qs = m > 0.f ? lane_sign * kGrid * rcp(m) : 0.f;
     // cw[d] byte k = code of channel 32 hq + 4 d + k
     uint32_t cw[8];
@@ -396,10 +403,18 @@ hipError_t launch_quantize(const QuantArgs &a, hipStream_t s) {
   // blocks strided by the grid
   const uint32_t resident = 2u * (uint32_t)(cus > 0 ? cus : 1);
   const uint32_t blocks = a.nblocks < resident ? a.nblocks : resident;
-  if (a.dtype == KVARN_DT_F32)
-    hipLaunchKernelGGL(quantize_block_kernel<true>, dim3(blocks), dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(quantize_block_kernel<false>, dim3(blocks), dim3(kThreads), 0, s, a);
+  const bool rot = !(a.flags & KVARN_FLAG_NO_ROTATE);
+  if (a.dtype == KVARN_DT_F32) {
+    if (rot)
+      hipLaunchKernelGGL((quantize_block_kernel<true, true>), dim3(blocks), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((quantize_block_kernel<true, false>), dim3(blocks), dim3(kThreads), 0, s, a);
+  } else {
+    if (rot)
+      hipLaunchKernelGGL((quantize_block_kernel<false, true>), dim3(blocks), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((quantize_block_kernel<false, false>), dim3(blocks), dim3(kThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -130,8 +130,28 @@ def test_decode_validation(lib):
     assert _d(lib, k=_cache(batch=0, kind=kv.K), v=_cache(batch=0, kind=kv.V)) == kv.OK
 
 
+def test_flags_validation(lib):
+    c = _cache()
+    assert lib.kvarn_quantize_ex(A, 0, 4 * 512 * 128, 512 * 128, 128, 256, 0, 4, 4,
+                                 ctypes.byref(c), None) == kv.ERR_FLAGS
+    assert lib.kvarn_quantize_ex(A, 0, 4 * 512 * 128, 512 * 128, 128, 256, 0, 4,
+                                 kv.FLAG_ONE_SCALE, ctypes.byref(c), None) == kv.ERR_FLAGS
+    assert lib.kvarn_quantize_ex(None, 0, 0, 0, 128, 256, 0, 4, kv.FLAG_NO_ROTATE,
+                                 ctypes.byref(c), None) == kv.ERR_NULL
+    assert lib.kvarn_append_ex(A, 0, B, kv.FLAG_ONE_SCALE, ctypes.byref(c), None) == kv.ERR_FLAGS
+    assert lib.kvarn_append_ex(None, 0, B, kv.FLAG_NO_ROTATE, ctypes.byref(c),
+                               None) == kv.ERR_NULL
+    k, v = _cache(kind=kv.K), _cache(kind=kv.V)
+    wsb = lib.kvarn_decode_workspace_bytes(k.batch, 16, k.capacity)
+    assert lib.kvarn_decode_attn_ex(A, 0, 16, ctypes.byref(k), ctypes.byref(v), B, 0.088, 8,
+                                    C, 0, 0x40000, wsb, None) == kv.ERR_FLAGS
+    assert lib.kvarn_decode_attn_ex(A, 0, 16, ctypes.byref(k), ctypes.byref(v), B, 0.088,
+                                    kv.FLAG_NO_ROTATE | kv.FLAG_ONE_SCALE, C, 0, 0x40000, 100,
+                                    None) == kv.ERR_WORKSPACE
+
+
 def test_status_strings(lib):
-    for st in (0, -1, -2, -3, -4, -5, -6, -7):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         s = kv.status_string(st)
         assert s and s != "unknown status"
     assert kv.status_string(-99) == "unknown status"
