@@ -60,6 +60,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-slices", type=int, default=0,
                    help="oracle slices for the CPU baseline (0 = 2 per thread)")
+    p.add_argument("--no-ablations", action="store_true",
+                   help="skip the ablation timings (balancing off, one scale, rotation off)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="one device-to-device copy of this many MiB before the warmup: "
                         "the reference kernel for calibrating HBM byte counters")
@@ -280,12 +282,61 @@ def main():
         res["roofline_decode"] = dec_roof
     res["decode"] = dec
     res["append"] = {"us_per_launch": round(a_us, 2), "launches_per_step": 2 * L}
+    if not args.no_ablations:
+        res["ablations"] = ablations(kv, torch, stream, xs[0], qs[0], caches[0], ws, out,
+                                     T + (args.warmup + args.steps if steady else 1), args.iters)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args, wl, xs, news, qs, steady, res["unit"],
                                            bf16_bytes_step, cap)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
+
+
+def ablations(kv, torch, stream, x_pair, q, cache_pair, ws, out, length, iters, reps=10):
+    """Layer-0 launches timed with HIP events outside the timed step:
+    the quantizer with and without balancing (iters vs 0: the cost of the
+    dual-scaling normalization), decode with both scales and with the column
+    scales taken as 1 (the cost of the second scale), and decode with the
+    rotation absorbed into the weights (no query rotation, no output
+    un-rotation). Scratch caches keep the benchmark's caches intact."""
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / reps
+
+    xk = x_pair[0]
+    kc, vc = cache_pair
+    scratch = kv.Cache.empty(kc.batch, kc.kv_heads, kc.capacity, kv.K, device=xk.device)
+    q_full = timed(lambda: kv.quantize(xk, scratch, iters=iters, stream=stream))
+    q_none = timed(lambda: kv.quantize(xk, scratch, iters=0, stream=stream))
+    q_norot = timed(lambda: kv.quantize(xk, scratch, iters=iters, stream=stream,
+                                        flags=kv.FLAG_NO_ROTATE))
+    del scratch
+    lens = torch.full((kc.batch,), length, dtype=torch.int32, device=xk.device)
+
+    def dec(flags):
+        return timed(lambda: kv.decode_attn(q, kc, vc, lens, out=out, workspace=ws,
+                                            stream=stream, flags=flags))
+    d_two, d_one, d_norot = dec(0), dec(kv.FLAG_ONE_SCALE), dec(kv.FLAG_NO_ROTATE)
+    return {
+        "quantize_us": {f"iters_{iters}": round(q_full, 2), "iters_0": round(q_none, 2),
+                        "no_rotate": round(q_norot, 2),
+                        "balancing_share": round((q_full - q_none) / q_full, 4)},
+        "decode_us": {"two_scales": round(d_two, 2), "one_scale": round(d_one, 2),
+                      "no_rotate": round(d_norot, 2),
+                      "second_scale_overhead": round((d_two - d_one) / d_one, 4)},
+        "note": "layer 0, K tensor for quantize; HIP events over "
+                f"{reps} launches after one warm launch",
+    }
 
 
 def cpu_baseline(args, wl, xs, news, qs, steady, unit, bf16_bytes_step, cap):

@@ -229,7 +229,6 @@ __device__ __forceinline__ float group_sum(float v) {
 }
 
 struct DecSmem {
-  alignas(16) float qt[HG][D];          // rotated query (setup only)
   alignas(16) float ck[SLOT_ARRAY];     // c_K, elem_pos order
   alignas(16) float cv[SLOT_ARRAY];     // c_V, cv_pos order
   alignas(16) float rk[SLOT_ARRAY];     // r'_K, elem_pos order
@@ -452,37 +451,68 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const int64_t qh0 = (int64_t)b * a.q_heads + (int64_t)g * G + h0;
   (void)n_hg;
 
-  // ---- query: rotate; fold softmax scale, log2(e), 1/sqrt(128) and the 2
-  // of the half-level code values. The query loads go first and the first
-  // chunk's loads next, so that waiting for the query leaves the chunk in
-  // flight during the set-up ----
-  float qin[HG * D / 64];
+  // ---- query: lane (slot n, head hl) keeps the channels of its slot,
+  // slot_elem(n, j) = c0 + (n & 1) + 2 j, and rotates them in registers: bits
+  // 1..3 of the channel index are in the lane (j), bits 0, 6, 4 and 5 are lane
+  // bits 0..3 of the 16-lane row that holds the head. Softmax scale, log2(e),
+  // 1/sqrt(128) and the 2 of the half-level code values are folded in. The
+  // query loads go first and the first chunk's loads next, so that waiting for
+  // the query leaves the chunk in flight during the set-up ----
+  const int n_l = lane & 15, hl = lane >> 4;
+  const int qc0 = slot_elem(n_l, 0) & ~1;  // 16-channel window holding the slot
+  const int64_t qrow = (qh0 + min(hl, nh - 1)) * D + qc0;
+  float qw[16];
   if (a.q_dtype == KVARN_DT_F32) {
-    const float *qf = static_cast<const float *>(a.q);
+    const f32x4 *qf = reinterpret_cast<const f32x4 *>(static_cast<const float *>(a.q) + qrow);
 #pragma unroll
-    for (int r = 0; r < HG * D / 64; ++r)
-      qin[r] = qf[(qh0 + min(r / 2, nh - 1)) * D + lane + 64 * (r & 1)];
+    for (int r = 0; r < 4; ++r) {
+      const f32x4 v4 = qf[r];
+      qw[4 * r] = v4[0]; qw[4 * r + 1] = v4[1]; qw[4 * r + 2] = v4[2]; qw[4 * r + 3] = v4[3];
+    }
   } else {
-    const uint16_t *qb = static_cast<const uint16_t *>(a.q);
+    const u32x4 *qb = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.q) + qrow);
 #pragma unroll
-    for (int r = 0; r < HG * D / 64; ++r)
-      qin[r] = __uint_as_float((uint32_t)qb[(qh0 + min(r / 2, nh - 1)) * D + lane + 64 * (r & 1)] << 16);
+    for (int r = 0; r < 2; ++r) {
+      const u32x4 u = qb[r];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qw[8 * r + 2 * e] = bf16_lo(u[e]);
+        qw[8 * r + 2 * e + 1] = bf16_hi(u[e]);
+      }
+    }
   }
-#pragma unroll
-  for (int r = 0; r < HG * D / 64; ++r) qin[r] = r / 2 < nh ? qin[r] : 0.f;
   ChunkRegs cur, nxt;
   if (c0 < c1) load_chunk<kTwoScales>(a, bg, nch, c0, lane, cur);
+  float qr[8];
 #pragma unroll
-  for (int r = 0; r < HG * D / 64; ++r) sm.qt[r / 2][lane + 64 * (r & 1)] = qin[r];
+  for (int jj = 0; jj < 8; ++jj) qr[jj] = hl < nh ? ((n_l & 1) ? qw[2 * jj + 1] : qw[2 * jj]) : 0.f;
+  if constexpr (kRotate) {
+#pragma unroll
+    for (int len = 1; len < 8; len <<= 1)
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj)
+        if ((jj & len) == 0) {
+          const float u = qr[jj], v = qr[jj + len];
+          qr[jj] = u + v;
+          qr[jj + len] = u - v;
+        }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+      const bool upper = (n_l & m) != 0;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const float p = __shfl_xor(qr[jj], m, 64);
+        qr[jj] = upper ? p - qr[jj] : qr[jj] + p;
+      }
+    }
+  }
   for (int idx = lane; idx < 16 * OP_ROW; idx += 64) (&sm.ap[0][0])[idx] = 0u;
-  wave_lds_sync();
-  if constexpr (kRotate) lds_fwht_rows<true>(&sm.qt[0][0], HG);
   SplitState st;
   {
     // the unscaled rotation's 1/sqrt(128) applies only when it ran here
     const float qs = 2.f * a.scale * kLog2e * (kRotate ? kInvSqrtD : 1.f);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) st.qv[j] = sm.qt[lane >> 4][slot_elem(lane & 15, j)] * qs;
+    for (int jj = 0; jj < 8; ++jj) st.qv[jj] = qr[jj] * qs;
   }
   // one scale: the QK operand does not change from chunk to chunk
   u32x8 aq_fixed = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
