@@ -31,7 +31,7 @@
 //  * a per-head power-of-two range scale (largest magnitude in [128, 256))
 //    is undone by the MFMA's per-row E8M0 scale;
 //  * the level offset is one MFMA per chunk against a constant -1.5 operand
-//    at scale 2^-1, fed in as the accumulator input.
+//    at scale 2^-1, added to each head's term sum.
 // decode_combine: grid (q_heads, batch): log-sum-exp merge of the partials
 // (m, l, acc[128]), then the inverse rotation.
 #include <atomic>
@@ -180,25 +180,6 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// In-place Sylvester Hadamard transform (unscaled) of rows x[n][128] in LDS,
-// by a workgroup of one wave (kOneWave) or of several.
-template <bool kOneWave>
-__device__ void lds_fwht_rows(float *x, int n) {
-  for (int len = 1; len < D; len <<= 1) {
-    for (int idx = threadIdx.x; idx < n * (D / 2); idx += blockDim.x) {
-      const int row = idx / (D / 2), p = idx - row * (D / 2);
-      const int i = (p / len) * 2 * len + (p % len);
-      float *r = x + row * D;
-      const float u = r[i], v = r[i + len];
-      r[i] = u + v;
-      r[i + len] = u - v;
-    }
-    if constexpr (kOneWave)
-      wave_lds_sync();
-    else
-      lds_barrier();
-  }
-}
 
 // ---- cross-lane reductions on DPP (no LDS round trip) ----------------------
 template <int CTRL>
@@ -341,14 +322,18 @@ __device__ __forceinline__ void process_chunk(DecSmem &sm, SplitState &st, const
   // ---- QK^T: 8 token tiles; the four terms of head h land in d[0..3] ----
   float s[8];
   {
-    const f32x4 off = level_offset(aq, sa_q);
-    // all eight products are independent: issue them back to back and sum
-    // the terms afterwards, so the MFMA latency is paid once
+    // all nine products are independent: issue them back to back and sum the
+    // terms afterwards, so the MFMA latency is paid once; the level offset of
+    // head h (the same for every token) is added after the term sum
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     f32x4 d[8];
 #pragma unroll
-    for (int tau = 0; tau < 8; ++tau) d[tau] = mfma_f8f4(aq, code_operand(cur.k[tau]), off, sa_q);
+    for (int tau = 0; tau < 8; ++tau) d[tau] = mfma_f8f4(aq, code_operand(cur.k[tau]), zero, sa_q);
+    const f32x4 off = level_offset(aq, sa_q);
+    const float off_h = (off[0] + off[1]) + (off[2] + off[3]);
 #pragma unroll
-    for (int tau = 0; tau < 8; ++tau) s[tau] = (d[tau][0] + d[tau][1]) + (d[tau][2] + d[tau][3]);
+    for (int tau = 0; tau < 8; ++tau)
+      s[tau] = ((d[tau][0] + d[tau][1]) + (d[tau][2] + d[tau][3])) + off_h;
   }
 
   // ---- online softmax of head h over the tokens slot_elem(n, tau) ----
@@ -409,18 +394,20 @@ __device__ __forceinline__ void process_chunk(DecSmem &sm, SplitState &st, const
 
     // ---- PV: 8 channel tiles ----
     const u32x8 ap = read_operand(sm.ap, lane);
-    const f32x4 off = level_offset(ap, sa_p);
     f32x4 cv0 = {1.f, 1.f, 1.f, 1.f}, cv1 = cv0;
     if constexpr (kTwoScales) {
       cv0 = *reinterpret_cast<const f32x4 *>(&sm.cv[sb]);
       cv1 = *reinterpret_cast<const f32x4 *>(&sm.cv[sb + 4]);
     }
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     f32x4 d[8];
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) d[ct] = mfma_f8f4(ap, code_operand(cur.v[ct]), off, sa_p);
+    for (int ct = 0; ct < 8; ++ct) d[ct] = mfma_f8f4(ap, code_operand(cur.v[ct]), zero, sa_p);
+    const f32x4 off = level_offset(ap, sa_p);
+    const float off_h = (off[0] + off[1]) + off[2];  // row 4 h + 3 is zero
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
-      const float dv = (d[ct][0] + d[ct][1]) + d[ct][2];
+      const float dv = ((d[ct][0] + d[ct][1]) + d[ct][2]) + off_h;
       if constexpr (kTwoScales)
         st.acc[ct] = fmaf(ct < 4 ? cv0[ct] : cv1[ct - 4], dv, st.acc[ct]);
       else
@@ -557,66 +544,95 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 }
 
 // Log-sum-exp merge of the split partials of one (sequence, query head), then
-// the inverse rotation. 256 threads: the block first reduces the maximum of
-// the split maxima, then takes the splits in rounds of 256; in a round each
-// thread weighs one split, and wave w accumulates splits w, w + 4, ... with
-// 8-byte loads of two channels per lane; the four waves' sums meet in LDS.
+// the inverse rotation. 256 threads; the splits are taken in rounds of 32:
+// all loads of a round are issued together (thread s < 32 reads split s's
+// (m, l); wave w reads two channels per lane of splits w, w + 4, ...), the
+// round is merged into a running maximum, and the four waves' sums meet in
+// LDS. Wave 0 then rotates the 128 channels back in registers (channel bit 6
+// in the lane, bits 0..5 across lanes).
 template <bool kRotate>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
-  __shared__ float wgt[256];
-  __shared__ float red_m[4], red_l[4];
+  constexpr int RS = 32;  // splits per round
+  __shared__ float wgt[RS];
+  __shared__ float red[4];
   __shared__ f32x2 part[4][64];
-  __shared__ float o[D];
   const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const int lane = t & 63, wv = t >> 6;
   constexpr int ROW = 2 + D;
   const float *pp = a.partial + ((int64_t)b * a.q_heads + h) * a.n_split * ROW;
-  float mx = -INFINITY;
-  for (int s = t; s < a.n_split; s += 256) mx = fmaxf(mx, pp[(int64_t)s * ROW]);
-  mx = group_max<16>(mx);
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  if (lane == 0) red_m[wv] = mx;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
   f32x2 num = {0.f, 0.f};
-  float den = 0.f;
-  if (M != -INFINITY) {
-    for (int base = 0; base < a.n_split; base += 256) {
-      const int s = base + t;
-      float w = 0.f;
-      if (s < a.n_split) {
-        const float ms = pp[(int64_t)s * ROW];
-        w = ms == -INFINITY ? 0.f : exp2f(ms - M);
-        den += w * pp[(int64_t)s * ROW + 1];
-      }
-      __syncthreads();  // the previous round's readers of wgt are done
-      wgt[t] = w;
+  float den = 0.f, m_run = -INFINITY;
+  for (int base = 0; base < a.n_split; base += RS) {
+    const int cnt = min(RS, a.n_split - base);
+    float ms = -INFINITY, ls = 0.f;
+    if (t < cnt) {
+      ms = pp[(int64_t)(base + t) * ROW];
+      ls = pp[(int64_t)(base + t) * ROW + 1];
+    }
+    f32x2 v[RS / 4];
+#pragma unroll
+    for (int i = 0; i < RS / 4; ++i) {
+      const int q = wv + 4 * i;
+      v[i] = q < cnt ? *reinterpret_cast<const f32x2 *>(pp + (int64_t)(base + q) * ROW + 2 + 2 * lane)
+                     : f32x2{0.f, 0.f};
+    }
+    // round maximum: threads 0..31 hold the round's split maxima (wave 0)
+    float mx = group_max<16>(ms);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    __syncthreads();  // the previous round's readers of wgt and red are done
+    if (t == 0) red[0] = mx;
+    __syncthreads();
+    const float m_new = fmaxf(m_run, red[0]);
+    if (m_new != -INFINITY) {
+      const float rescale = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+      const float w = ms == -INFINITY ? 0.f : exp2f(ms - m_new);
+      if (t < RS) wgt[t] = w;
       __syncthreads();
-      const int cnt = min(256, a.n_split - base);
-      const float *col = pp + (int64_t)base * ROW + 2 + 2 * lane;
-#pragma unroll 4
-      for (int q = wv; q < cnt; q += 4) {
-        const f32x2 v = *reinterpret_cast<const f32x2 *>(col + (int64_t)q * ROW);
-        num += wgt[q] * v;
-      }
+      num *= rescale;
+      den = den * rescale + w * ls;
+#pragma unroll
+      for (int i = 0; i < RS / 4; ++i) num += wgt[wv + 4 * i] * v[i];
+      m_run = m_new;
     }
   }
+  // denominators live in wave 0's first 32 lanes (one per split slot)
   den = group_sum<16>(den);
   den += __shfl_xor(den, 16, 64);
   den += __shfl_xor(den, 32, 64);
-  if (lane == 0) red_l[wv] = den;
+  __syncthreads();
+  if (t == 0) red[1] = den;
   part[wv][lane] = num;
   __syncthreads();
-  if (t < 64) {
-    const float L = (red_l[0] + red_l[1]) + (red_l[2] + red_l[3]);
-    const f32x2 sum = (part[0][t] + part[1][t]) + (part[2][t] + part[3][t]);
-    o[2 * t] = L > 0.f ? sum[0] / L : 0.f;
-    o[2 * t + 1] = L > 0.f ? sum[1] / L : 0.f;
+  if (wv == 0) {
+    const float L = red[1];
+    const f32x2 sum = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
+    // channels 2 lane and 2 lane + 1 -> lane holds channels lane and lane + 64
+    float x0 = L > 0.f ? sum[0] / L : 0.f, x1 = L > 0.f ? sum[1] / L : 0.f;
+    float *out = a.out + ((int64_t)b * a.q_heads + h) * D;
+    if constexpr (kRotate) {
+      // regroup: lane l needs channels l and l + 64; channel c sits in lane c / 2
+      const float e0 = __shfl(x0, lane >> 1, 64), o0 = __shfl(x1, lane >> 1, 64);
+      const float e1 = __shfl(x0, 32 + (lane >> 1), 64), o1 = __shfl(x1, 32 + (lane >> 1), 64);
+      float y0 = (lane & 1) ? o0 : e0;  // channel lane
+      float y1 = (lane & 1) ? o1 : e1;  // channel lane + 64
+      {
+        const float s0 = y0 + y1, d0 = y0 - y1;
+        y0 = s0;
+        y1 = d0;
+      }
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) {
+        const float p0 = __shfl_xor(y0, m, 64), p1 = __shfl_xor(y1, m, 64);
+        const bool upper = (lane & m) != 0;
+        y0 = upper ? p0 - y0 : y0 + p0;
+        y1 = upper ? p1 - y1 : y1 + p1;
+      }
+      out[lane] = y0 * kInvSqrtD;
+      out[lane + 64] = y1 * kInvSqrtD;
+    } else {
+      *reinterpret_cast<f32x2 *>(out + 2 * lane) = f32x2{x0, x1};
+    }
   }
-  __syncthreads();
-  if constexpr (kRotate) lds_fwht_rows<false>(o, 1);
-  if (t < D) a.out[((int64_t)b * a.q_heads + h) * D + t] = kRotate ? o[t] * kInvSqrtD : o[t];
 }
 
 }  // namespace
