@@ -46,8 +46,6 @@ typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-// s_waitcnt operand on gfx9: vmcnt(0), expcnt and lgkmcnt left at their maxima
-constexpr int kVmcntZero = (0x7 << 4) | (0xF << 8);
 constexpr int HG = 4;                       // query heads per workgroup
 constexpr uint32_t kFieldMask = 0x33333333u;  // low 2 bits of every 4-bit field
 constexpr uint32_t kFp4Neg3Half = 0xBBBBBBBBu;  // e2m1 -1.5 in every field

@@ -31,6 +31,9 @@ __device__ __forceinline__ float dpp_xor1(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
 }
 
+// s_waitcnt operand on gfx9: vmcnt(0), expcnt and lgkmcnt left at their maxima
+constexpr int kVmcntZero = (0x7 << 4) | (0xF << 8);
+
 // Workgroup barrier for LDS traffic only: the wave's LDS accesses complete
 // (lgkmcnt(0)), then s_barrier. Unlike __syncthreads() it does not wait for
 // outstanding global loads and stores, so a prefetch stays in flight across
