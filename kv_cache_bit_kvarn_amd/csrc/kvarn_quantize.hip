@@ -11,16 +11,18 @@
 //      bytes of each of 16 rows; the pieces are the B operands of the MFMAs;
 //   2. Hadamard rotation along channels (rndamp article on KVarN, "How It
 //      Works", item 1) as a dense product on the matrix cores:
-//      y^T = H_128 x^T with v_mfma_f32_16x16x32_bf16, 32 MFMAs per wave.
-//      Sylvester's H_128 has entry (-1)^popcount(i & j); split over the tile
-//      indices, each 16 x 32 tile of it is a sign (-1)^popcount((mt/2) & kk)
-//      times one of two lane-constant operands, so four operand registers
-//      (two tiles and their negations) cover the whole matrix. The result
-//      lands with lane (n, g) holding channels 16 mt + 4 g + r of its token.
+//      y^T = H_128 x^T with v_mfma_f32_16x16x32_bf16. Sylvester's H_128 has
+//      entry (-1)^popcount(i & j); split over the tile indices, each 16 x 32
+//      tile (mt, kk) of it is a sign (-1)^popcount((mt/2) & kk) times one of
+//      two lane-constant operands (mt % 2). So 8 MFMAs per wave (2 operands x
+//      4 input pieces) and a 4-point Hadamard transform over the pieces (64
+//      VALU adds per lane) give the product. The result lands with lane
+//      (n, g) holding channels 16 mt + 4 g + r of its token.
 //      bf16 inputs and +-1 are exact and the products accumulate in fp32;
 //      fp32 input is split exactly into three bf16 terms (three MFMAs per
-//      tile). With the rotation absorbed into the weights, the same MFMAs
-//      run on identity tiles (one per output tile), which copies x exactly;
+//      product). With the rotation absorbed into the weights, the same MFMAs
+//      run on identity tiles and the transform is skipped, which copies x
+//      exactly;
 //   3. dual-scaling normalization ("How It Works", item 2; abstract: both
 //      axes of K and V): the squares P = y^2 stay in registers (next to y)
 //      for the row step and are staged once, transposed, in LDS for the
@@ -108,6 +110,22 @@ static_assert(vs_at(7, 3, 7, 3) < PT_SIZE, "V staging fits in the P area");
 
 __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
+// Sum (max) over the four 16-lane rows of the wave, in every lane: the
+// permlane32 swap pairs rows 0-1 with rows 2-3, the permlane16 swap then row
+// 0 with 1 and 2 with 3 (VALU lane exchanges, no LDS round trip).
+__device__ __forceinline__ float rows_sum(float s) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  const float t = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float rows_max(float s) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  const float t = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // The value itself, hidden from the optimizer so that addresses built from it
 // are recomputed where they are used instead of being hoisted out of the block
 // loop and kept (or spilled) across the balancing.
@@ -169,21 +187,25 @@ __device__ __forceinline__ u32x4 identity_operand(int lane, int p) {
   return r;
 }
 
-// acc[mt] += (tile (mt, kk) of the rotation) x b, b = input channels
-// 32 kk + [0, 32) of the wave's 16 tokens. A tile with a negative sign
-// takes the negated b (sign bits flipped) against the same operand.
-template <bool kRotate, int KK>
+// acc[2 kk + p] += (operand p) x b, b = input channels 32 kk + [0, 32) of the
+// wave's 16 tokens. For the identity operands this is the output tile
+// mt = 2 kk + p itself. For the Hadamard operands the tile (mt, kk) of H_128
+// is sign((mt / 2) & kk) times operand mt % 2, so output tile mt = 2 s + p is
+// the 4-point Hadamard transform over kk of these products (finish_rotation).
+template <int KK>
 __device__ __forceinline__ void rotate_step(f32x4 (&acc)[8], const u32x4 &b, const u32x4 (&hp)[2]) {
-  if constexpr (kRotate) {
-    const u32x4 nb = b ^ 0x80008000u;
+  acc[2 * KK] = mfma_bf16(hp[0], b, acc[2 * KK]);
+  acc[2 * KK + 1] = mfma_bf16(hp[1], b, acc[2 * KK + 1]);
+}
+__device__ __forceinline__ void finish_rotation(f32x4 (&acc)[8]) {
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      const bool neg = __builtin_popcount((mt >> 1) & KK) & 1;
-      acc[mt] = mfma_bf16(hp[mt & 1], neg ? nb : b, acc[mt]);
-    }
-  } else {
-    acc[2 * KK] = mfma_bf16(hp[0], b, acc[2 * KK]);
-    acc[2 * KK + 1] = mfma_bf16(hp[1], b, acc[2 * KK + 1]);
+  for (int p = 0; p < 2; ++p) {
+    const f32x4 a0 = acc[p] + acc[2 + p], a1 = acc[p] - acc[2 + p];
+    const f32x4 a2 = acc[4 + p] + acc[6 + p], a3 = acc[4 + p] - acc[6 + p];
+    acc[p] = a0 + a2;
+    acc[2 + p] = a1 + a3;
+    acc[4 + p] = a0 - a2;
+    acc[6 + p] = a1 - a3;
   }
 }
 
@@ -345,19 +367,19 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
   {                                                           \
     u32x4 th, tm, tl;                                         \
     split_bf16x3(xv[2 * (KK)], xv[2 * (KK) + 1], th, tm, tl); \
-    rotate_step<kRotate, KK>(acc, tl, hp);                    \
-    rotate_step<kRotate, KK>(acc, tm, hp);                    \
-    rotate_step<kRotate, KK>(acc, th, hp);                    \
+    rotate_step<KK>(acc, tl, hp);                             \
+    rotate_step<KK>(acc, tm, hp);                             \
+    rotate_step<KK>(acc, th, hp);                             \
   }
     KVARN_ROTATE_F32(0) KVARN_ROTATE_F32(1) KVARN_ROTATE_F32(2) KVARN_ROTATE_F32(3)
 #undef KVARN_ROTATE_F32
   };
   auto rotate_bf16 = [&](const u32x4 (&x)[4], f32x4 (&acc)[8]) {
     const u32x4 hp[2] = {sm.hop[0][lane], sm.hop[1][lane]};
-    rotate_step<kRotate, 0>(acc, x[0], hp);
-    rotate_step<kRotate, 1>(acc, x[1], hp);
-    rotate_step<kRotate, 2>(acc, x[2], hp);
-    rotate_step<kRotate, 3>(acc, x[3], hp);
+    rotate_step<0>(acc, x[0], hp);
+    rotate_step<1>(acc, x[1], hp);
+    rotate_step<2>(acc, x[2], hp);
+    rotate_step<3>(acc, x[3], hp);
   };
 
   for (; blk < a.nblocks; blk += gridDim.x) {
@@ -380,6 +402,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
         const uint32_t nb = min(blk + gridDim.x, a.nblocks - 1);
         load_bf16_block(a, split_block(a, nb), ti, g, xn);
       }
+      if constexpr (kRotate) finish_rotation(acc);
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
         y[4 * mt + 0] = acc[mt].x; y[4 * mt + 1] = acc[mt].y;
@@ -414,15 +437,13 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
         const float2 wr = *reinterpret_cast<const float2 *>(sm.w + w_pair);
         s = row_dot(p, wr.x, wr.y);
       }
-      s += __shfl_xor(s, 16, 64);
-      s += __shfl_xor(s, 32, 64);
+      s = rows_sum(s);
       if (g == 0) sm.v[ti] = s > 0.f ? (float)D * rcp(s) : 1.f;
       lds_barrier();
       // column step: c_j^2 = (1/T) sum_i P_ij / r_i^2  ->  w_j = 1/c_j^2
       const float2 vr = *reinterpret_cast<const float2 *>(sm.v + CPT * g + 2 * n);
       float cs = col_dot(sm.pt + pt_at(cj, CPT * g), vr.x, vr.y);
-      cs += __shfl_xor(cs, 16, 64);
-      cs += __shfl_xor(cs, 32, 64);
+      cs = rows_sum(cs);
       if (g == 0) {
         cm = cs * (1.f / T);
         sm.w[wpad(cj)] = cm > 0.f ? rcp(cm) : 1.f;
@@ -453,8 +474,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
     float m = 0.f;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) m = fmaxf(m, fabsf(y[i]));
-    m = fmaxf(m, __shfl_xor(m, 16, 64));
-    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    m = rows_max(m);
     if (g == 0) a.row_scale[bh * a.capacity + (int64_t)chunk * T + ti] = m * range_factor;
     const float qs = m > 0.f ? kGrid * rcp(m) : 0.f;
     // cw[mt] byte r = code of channel 16 mt + 4 g + r
