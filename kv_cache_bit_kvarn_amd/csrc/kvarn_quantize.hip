@@ -11,18 +11,19 @@
 //      bytes of each of 16 rows; the pieces are the B operands of the MFMAs;
 //   2. Hadamard rotation along channels (rndamp article on KVarN, "How It
 //      Works", item 1) as a dense product on the matrix cores:
-//      y^T = H_128 x^T with v_mfma_f32_16x16x32_bf16. Sylvester's H_128 has
-//      entry (-1)^popcount(i & j); split over the tile indices, each 16 x 32
-//      tile (mt, kk) of it is a sign (-1)^popcount((mt/2) & kk) times one of
-//      two lane-constant operands (mt % 2). So 8 MFMAs per wave (2 operands x
-//      4 input pieces) and a 4-point Hadamard transform over the pieces (64
-//      VALU adds per lane) give the product. The result lands with lane
-//      (n, g) holding channels 16 mt + 4 g + r of its token.
+//      y^T = H_128 x^T with v_mfma_f32_16x16x32_bf16, 32 MFMAs per wave.
+//      Sylvester's H_128 has entry (-1)^popcount(i & j); split over the tile
+//      indices, each 16 x 32 tile (mt, kk) of it is a sign
+//      (-1)^popcount((mt/2) & kk) times one of two lane-constant operands
+//      (mt % 2), the sign going onto the input piece. The result lands with
+//      lane (n, g) holding channels 16 mt + 4 g + r of its token. (The
+//      product could also be 8 MFMAs and a 4-point transform over the pieces,
+//      but that moves 64 adds per lane onto the VALU, which bounds the
+//      kernel, while the matrix cores are mostly idle.)
 //      bf16 inputs and +-1 are exact and the products accumulate in fp32;
 //      fp32 input is split exactly into three bf16 terms (three MFMAs per
-//      product). With the rotation absorbed into the weights, the same MFMAs
-//      run on identity tiles and the transform is skipped, which copies x
-//      exactly;
+//      product). With the rotation absorbed into the weights, the MFMAs run
+//      on identity tiles (one per output tile), which copies x exactly;
 //   3. dual-scaling normalization ("How It Works", item 2; abstract: both
 //      axes of K and V): the squares P = y^2 stay in registers (next to y)
 //      for the row step and are staged once, transposed, in LDS for the
@@ -68,24 +69,25 @@ constexpr uint32_t kPack4 = 0x40100401u;       // byte weights 1, 4, 16, 64
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-// LDS layouts. gfx950's LDS has 64 four-byte banks; a ds_write_b32 or
-// ds_read_b64 is served one half-wave per pass, a ds_read_b128 in four passes
-// of 16 lanes (the quads of one half-wave whose quad index has the same
-// popcount parity), and a lane reading the same address as another still
-// takes its own bank slot. The layouts below are free of bank conflicts
-// under that model:
-//  * transposed P: entry (channel j, token i) at pt_at(j, i): rows 136
-//    floats apart, 4 more floats when channel bit 2 is set (a P write covers
+// LDS layouts. On gfx950 a ds_write_b32 is served one half-wave per pass with
+// the dword address taken modulo 32 as its bank; a ds_read_b64 one half-wave
+// per pass over 64 four-byte banks; a ds_read_b128 in four passes of 16 lanes
+// (the quads of one half-wave whose quad index has the same popcount parity)
+// over 64 banks; a lane reading the same address as another still takes its
+// own bank slot. The layouts below are free of bank conflicts under that
+// model:
+//  * transposed P: entry (channel j, token i) at pt_at(j, i): rows 132
+//    floats apart, 32 more floats per group of 8 channels (a P write covers
 //    16 tokens x channels 4 apart; a column-step read covers 16 channels);
 //  * per-channel w at wpad(j) (8 floats of padding after channel 63) and
 //    per-token v, each read once per lane as a pair and shared across a
 //    16-lane row by DPP broadcasts;
 //  * V code staging, in the P area once the column steps are done: word
 //    (mt, g, byte column 4 c + e) at vs_at(mt, g, c, e) = 32 (4 mt + g) +
-//    4 (c ^ mt) + e (16-byte chunks swizzled by mt).
-constexpr int PT_STRIDE = 136;
+//    4 (c ^ ((mt + 4 g) % 8)) + e (16-byte chunks swizzled).
+constexpr int PT_STRIDE = 132;
 __host__ __device__ constexpr int pt_at(int j, int i) {
-  return j * PT_STRIDE + 4 * ((j >> 2) & 1) + i;
+  return j * PT_STRIDE + 32 * (j >> 3) + i;
 }
 __host__ __device__ constexpr bool pt_rows_disjoint() {
   for (int j = 0; j + 1 < D; ++j)
@@ -96,7 +98,7 @@ static_assert(pt_rows_disjoint(), "rows of the transposed P overlap");
 constexpr int PT_SIZE = pt_at(D - 1, T - 1) + 1;
 __host__ __device__ constexpr int wpad(int j) { return j + 8 * (j >> 6); }
 __host__ __device__ constexpr int vs_at(int mt, int g, int c, int e) {
-  return 32 * (4 * mt + g) + 4 * (c ^ mt) + e;
+  return 32 * (4 * mt + g) + 4 * (c ^ ((mt + 4 * g) & 7)) + e;
 }
 
 struct QuantSmem {
@@ -187,25 +189,22 @@ __device__ __forceinline__ u32x4 identity_operand(int lane, int p) {
   return r;
 }
 
-// acc[2 kk + p] += (operand p) x b, b = input channels 32 kk + [0, 32) of the
-// wave's 16 tokens. For the identity operands this is the output tile
-// mt = 2 kk + p itself. For the Hadamard operands the tile (mt, kk) of H_128
-// is sign((mt / 2) & kk) times operand mt % 2, so output tile mt = 2 s + p is
-// the 4-point Hadamard transform over kk of these products (finish_rotation).
-template <int KK>
+// acc[mt] += (tile (mt, kk) of the rotation) x b, b = input channels
+// 32 kk + [0, 32) of the wave's 16 tokens. A Hadamard tile with a negative
+// sign takes the negated b (sign bits flipped) against the same operand; the
+// identity has one tile per output tile, at kk = mt / 2.
+template <bool kRotate, int KK>
 __device__ __forceinline__ void rotate_step(f32x4 (&acc)[8], const u32x4 &b, const u32x4 (&hp)[2]) {
-  acc[2 * KK] = mfma_bf16(hp[0], b, acc[2 * KK]);
-  acc[2 * KK + 1] = mfma_bf16(hp[1], b, acc[2 * KK + 1]);
-}
-__device__ __forceinline__ void finish_rotation(f32x4 (&acc)[8]) {
+  if constexpr (kRotate) {
+    const u32x4 nb = b ^ 0x80008000u;
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const f32x4 a0 = acc[p] + acc[2 + p], a1 = acc[p] - acc[2 + p];
-    const f32x4 a2 = acc[4 + p] + acc[6 + p], a3 = acc[4 + p] - acc[6 + p];
-    acc[p] = a0 + a2;
-    acc[2 + p] = a1 + a3;
-    acc[4 + p] = a0 - a2;
-    acc[6 + p] = a1 - a3;
+    for (int mt = 0; mt < 8; ++mt) {
+      const bool neg = __builtin_popcount((mt >> 1) & KK) & 1;
+      acc[mt] = mfma_bf16(hp[mt & 1], neg ? nb : b, acc[mt]);
+    }
+  } else {
+    acc[2 * KK] = mfma_bf16(hp[0], b, acc[2 * KK]);
+    acc[2 * KK + 1] = mfma_bf16(hp[1], b, acc[2 * KK + 1]);
   }
 }
 
@@ -247,6 +246,20 @@ __device__ __forceinline__ void split_bf16x3(const f32x4 &a, const f32x4 &b, u32
       : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])                                    \
       : "v"(w0), "v"(w1), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]),     \
         "v"(x[6]), "v"(x[7]))
+// Same, with acc[] set by the first four products instead of accumulated.
+#define KVARN_FMAC8_BCAST_FIRST(L0, L1, L2, L3, acc, w0, w1, x)                                  \
+  asm("s_nop 1\n\t"                                                                              \
+      "v_mul_f32_dpp %0, %4, %6 row_newbcast:" #L0 " row_mask:0xf bank_mask:0xf\n\t"             \
+      "v_mul_f32_dpp %1, %5, %7 row_newbcast:" #L0 " row_mask:0xf bank_mask:0xf\n\t"             \
+      "v_mul_f32_dpp %2, %4, %8 row_newbcast:" #L1 " row_mask:0xf bank_mask:0xf\n\t"             \
+      "v_mul_f32_dpp %3, %5, %9 row_newbcast:" #L1 " row_mask:0xf bank_mask:0xf\n\t"             \
+      "v_fmac_f32_dpp %0, %4, %10 row_newbcast:" #L2 " row_mask:0xf bank_mask:0xf\n\t"           \
+      "v_fmac_f32_dpp %1, %5, %11 row_newbcast:" #L2 " row_mask:0xf bank_mask:0xf\n\t"           \
+      "v_fmac_f32_dpp %2, %4, %12 row_newbcast:" #L3 " row_mask:0xf bank_mask:0xf\n\t"           \
+      "v_fmac_f32_dpp %3, %5, %13 row_newbcast:" #L3 " row_mask:0xf bank_mask:0xf"                 \
+      : "=&v"(acc[0]), "=&v"(acc[1]), "=&v"(acc[2]), "=&v"(acc[3])                                \
+      : "v"(w0), "v"(w1), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]),     \
+        "v"(x[6]), "v"(x[7]))
 // x[e] *= register w{e % 2} of row lane L{e / 2}.
 #define KVARN_MUL8_BCAST(L0, L1, L2, L3, w0, w1, x)                                               \
   asm("s_nop 1\n\t"                                                                              \
@@ -267,8 +280,8 @@ __device__ __forceinline__ void split_bf16x3(const f32x4 &a, const f32x4 &b, u32
 // 2 (n % 2) + {0, 1} (one 8-byte read), so element (mt, r) sits in register
 // r % 2 of lane 2 mt + r / 2. Four interleaved partial sums, tree-combined.
 __device__ __forceinline__ float row_dot(const float (&p)[CPT], float w0, float w1) {
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  KVARN_FMAC8_BCAST(0, 1, 2, 3, acc, w0, w1, (p + 0));
+  float acc[4];
+  KVARN_FMAC8_BCAST_FIRST(0, 1, 2, 3, acc, w0, w1, (p + 0));
   KVARN_FMAC8_BCAST(4, 5, 6, 7, acc, w0, w1, (p + 8));
   KVARN_FMAC8_BCAST(8, 9, 10, 11, acc, w0, w1, (p + 16));
   KVARN_FMAC8_BCAST(12, 13, 14, 15, acc, w0, w1, (p + 24));
@@ -278,18 +291,18 @@ __device__ __forceinline__ float row_dot(const float (&p)[CPT], float w0, float 
 // Column step: sum over 32 tokens of P_ij / r_i^2; row lane n holds 1/r^2 of
 // tokens 2 n + {0, 1} of the quarter. P is read two 16-byte vectors at a time.
 __device__ __forceinline__ float col_dot(const float *pc, float v0, float v1) {
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#define KVARN_COL_BLOCK(H, L0, L1, L2, L3)                                              \
+  float acc[4];
+#define KVARN_COL_BLOCK(H, L0, L1, L2, L3, FMAC)                                        \
   {                                                                                     \
     const f32x4 a0 = reinterpret_cast<const f32x4 *>(pc)[2 * (H)];                      \
     const f32x4 a1 = reinterpret_cast<const f32x4 *>(pc)[2 * (H) + 1];                  \
     const float x[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};                \
-    KVARN_FMAC8_BCAST(L0, L1, L2, L3, acc, v0, v1, x);                                  \
+    FMAC(L0, L1, L2, L3, acc, v0, v1, x);                                               \
   }
-  KVARN_COL_BLOCK(0, 0, 1, 2, 3)
-  KVARN_COL_BLOCK(1, 4, 5, 6, 7)
-  KVARN_COL_BLOCK(2, 8, 9, 10, 11)
-  KVARN_COL_BLOCK(3, 12, 13, 14, 15)
+  KVARN_COL_BLOCK(0, 0, 1, 2, 3, KVARN_FMAC8_BCAST_FIRST)
+  KVARN_COL_BLOCK(1, 4, 5, 6, 7, KVARN_FMAC8_BCAST)
+  KVARN_COL_BLOCK(2, 8, 9, 10, 11, KVARN_FMAC8_BCAST)
+  KVARN_COL_BLOCK(3, 12, 13, 14, 15, KVARN_FMAC8_BCAST)
 #undef KVARN_COL_BLOCK
   return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
@@ -367,19 +380,19 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
   {                                                           \
     u32x4 th, tm, tl;                                         \
     split_bf16x3(xv[2 * (KK)], xv[2 * (KK) + 1], th, tm, tl); \
-    rotate_step<KK>(acc, tl, hp);                             \
-    rotate_step<KK>(acc, tm, hp);                             \
-    rotate_step<KK>(acc, th, hp);                             \
+    rotate_step<kRotate, KK>(acc, tl, hp);                    \
+    rotate_step<kRotate, KK>(acc, tm, hp);                    \
+    rotate_step<kRotate, KK>(acc, th, hp);                    \
   }
     KVARN_ROTATE_F32(0) KVARN_ROTATE_F32(1) KVARN_ROTATE_F32(2) KVARN_ROTATE_F32(3)
 #undef KVARN_ROTATE_F32
   };
   auto rotate_bf16 = [&](const u32x4 (&x)[4], f32x4 (&acc)[8]) {
     const u32x4 hp[2] = {sm.hop[0][lane], sm.hop[1][lane]};
-    rotate_step<0>(acc, x[0], hp);
-    rotate_step<1>(acc, x[1], hp);
-    rotate_step<2>(acc, x[2], hp);
-    rotate_step<3>(acc, x[3], hp);
+    rotate_step<kRotate, 0>(acc, x[0], hp);
+    rotate_step<kRotate, 1>(acc, x[1], hp);
+    rotate_step<kRotate, 2>(acc, x[2], hp);
+    rotate_step<kRotate, 3>(acc, x[3], hp);
   };
 
   for (; blk < a.nblocks; blk += gridDim.x) {
@@ -389,6 +402,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
 
     // ---- 1-2. load and rotate ---------------------------------------------
     float y[CPT], p[CPT];
+    f32x4 gram = {0.f, 0.f, 0.f, 0.f};  // bf16: x x^T of the wave's 16 tokens
     {
       f32x4 acc[8];
 #pragma unroll
@@ -397,12 +411,16 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
         rotate_f32(bi, acc);
       } else {
         rotate_bf16(xn, acc);
+        // first row step by Parseval: sum_j y_j^2 = 128 sum_k x_k^2 (1 sum_k
+        // x_k^2 without the rotation); the diagonal of x x^T, from the same
+        // operand registers, lands in lane (n, g = n / 4), register n % 4
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) gram = mfma_bf16(xn[kk], xn[kk], gram);
         // next block's input, in flight during the whole block (the LDS-only
         // barriers below do not wait for it)
         const uint32_t nb = min(blk + gridDim.x, a.nblocks - 1);
         load_bf16_block(a, split_block(a, nb), ti, g, xn);
       }
-      if constexpr (kRotate) finish_rotation(acc);
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
         y[4 * mt + 0] = acc[mt].x; y[4 * mt + 1] = acc[mt].y;
@@ -422,24 +440,32 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
 #pragma unroll
         for (int r = 0; r < 4; ++r) dst[pt_at(16 * mt + r, 0)] = p[4 * mt + r];
     }
+    // first row step (c = 1): v_i = 1 / r_i^2 = D / sum_j P_ij, published with P
+    if (a.iters > 0) {
+      if constexpr (kF32) {
+        float t[4] = {p[0], p[1], p[2], p[3]};
+#pragma unroll
+        for (int i = 4; i < CPT; ++i) t[i & 3] += p[i];
+        const float s = rows_sum((t[0] + t[1]) + (t[2] + t[3]));
+        if (g == 0) sm.v[ti] = s > 0.f ? (float)D * rcp(s) : 1.f;
+      } else {
+        const int r = n & 3;
+        const float d = (r & 2) ? ((r & 1) ? gram.w : gram.z) : ((r & 1) ? gram.y : gram.x);
+        const float s = (kRotate ? (float)D : 1.f) * d;
+        if (g == (n >> 2)) sm.v[ti] = s > 0.f ? (float)D * rcp(s) : 1.f;
+      }
+    }
     lds_barrier();
 
     float cm = 1.f;  // c_j^2 of the last column step (lanes with g = 0)
     for (int it = 0; it < a.iters; ++it) {
-      // row step: r_i^2 = (1/D) sum_j P_ij / c_j^2  ->  v_i = 1/r_i^2  (c = 1 first)
-      float s;
-      if (it == 0) {
-        float t[4] = {p[0], p[1], p[2], p[3]};
-#pragma unroll
-        for (int i = 4; i < CPT; ++i) t[i & 3] += p[i];
-        s = (t[0] + t[1]) + (t[2] + t[3]);
-      } else {
+      if (it > 0) {
+        // row step: r_i^2 = (1/D) sum_j P_ij / c_j^2  ->  v_i = 1/r_i^2
         const float2 wr = *reinterpret_cast<const float2 *>(sm.w + w_pair);
-        s = row_dot(p, wr.x, wr.y);
+        const float s = rows_sum(row_dot(p, wr.x, wr.y));
+        if (g == 0) sm.v[ti] = s > 0.f ? (float)D * rcp(s) : 1.f;
+        lds_barrier();
       }
-      s = rows_sum(s);
-      if (g == 0) sm.v[ti] = s > 0.f ? (float)D * rcp(s) : 1.f;
-      lds_barrier();
       // column step: c_j^2 = (1/T) sum_i P_ij / r_i^2  ->  w_j = 1/c_j^2
       const float2 vr = *reinterpret_cast<const float2 *>(sm.v + CPT * g + 2 * n);
       float cs = col_dot(sm.pt + pt_at(cj, CPT * g), vr.x, vr.y);
