@@ -32,9 +32,11 @@ D, CHUNK = 128, 128
 # algorithmic bytes per element of one quantize launch: 2 B bf16 in, 0.25 B
 # codes, 4 B row scale per 128 channels, 4 B column scale per 128 tokens
 QUANT_BYTES_PER_ELT_BF16 = 2.0 + 0.25 + 4.0 / 128 + 4.0 / 128
-# fp32 VALU peak without packed math (packed fp32 is not used on the test machines):
-# 256 CUs x 4 SIMDs x 16 lanes x 2 flop per FMA x 2.4 GHz
-VALU_F32_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+# MI355X fp32 vector peak, published: 256 CUs x 4 SIMDs x 32 lanes per clock
+# x 2 flop per FMA x 2.4 GHz = 157.3 TFLOP/s. Plain (non-packed) v_fmac_f32
+# reaches it too: a throughput probe of independent FMAs measured 120 TFLOP/s
+# (DPP-sourced FMAs: 68-70).
+VALU_F32_PEAK_TFLOPS = 256 * 4 * 32 * 2 * 2.4e9 / 1e12
 
 
 def quant_flop_per_elt(iters: int) -> int:
@@ -266,19 +268,26 @@ def main():
                            "us_per_launch": round(q_us, 2), "launches_per_step": q_launches,
                            "GBps_algorithmic": round(q_gbps, 1),
                            "hbm_frac": round(q_gbps / HBM_PEAK_GBPS, 4)}
-        # the quantizer is bound by VALU arithmetic, not by HBM: its roofline is
-        # the non-packed fp32 VALU peak; the HBM fraction stays beside it
-        q_tflops = quant_flop_per_elt(args.iters) * elts_per_quant / (q_us * 1e-6) / 1e12
-        res["roofline"] = {"bound": "alu", "achieved": round(q_tflops, 2),
-                           "peak": round(VALU_F32_PEAK_TFLOPS, 2), "unit": "TFLOP/s",
-                           "frac": round(q_tflops / VALU_F32_PEAK_TFLOPS, 4),
+        # roofline of the quantizer: the larger of its ideal HBM time (bytes at
+        # the HBM peak) and its ideal ALU time (algorithmic fp32 operations at
+        # the VALU peak) names the bound; the other resource stays beside it
+        q_flop = quant_flop_per_elt(args.iters) * elts_per_quant
+        q_tflops = q_flop / (q_us * 1e-6) / 1e12
+        t_hbm = qbytes / (HBM_PEAK_GBPS * 1e9)
+        t_alu = q_flop / (VALU_F32_PEAK_TFLOPS * 1e12)
+        alu = {"achieved": round(q_tflops, 2), "peak": round(VALU_F32_PEAK_TFLOPS, 2),
+               "unit": "TFLOP/s", "frac": round(q_tflops / VALU_F32_PEAK_TFLOPS, 4),
+               "flop_per_element": quant_flop_per_elt(args.iters)}
+        hbm = {"achieved": round(q_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+               "frac": round(q_gbps / HBM_PEAK_GBPS, 4)}
+        bound, main, other = ("hbm", hbm, alu) if t_hbm >= t_alu else ("alu", alu, dict(hbm))
+        res["roofline"] = {"bound": bound, **main,
                            "traffic": measured_traffic("quantize_block_kernel<bf16>", wl.name),
                            "kernel": "quantize_block_kernel<bf16>",
-                           "flop_per_element": quant_flop_per_elt(args.iters),
                            "elements_per_launch": elts_per_quant,
                            "bytes_per_launch": qbytes,
-                           "hbm_achieved_GBps": round(q_gbps, 1),
-                           "hbm_frac": round(q_gbps / HBM_PEAK_GBPS, 4)}
+                           "ideal_us": {"hbm": round(t_hbm * 1e6, 2), "alu": round(t_alu * 1e6, 2)},
+                           ("alu" if bound == "hbm" else "hbm"): other}
         res["roofline_decode"] = dec_roof
     res["decode"] = dec
     res["append"] = {"us_per_launch": round(a_us, 2), "launches_per_step": 2 * L}
