@@ -73,9 +73,11 @@ def lib():
             L.kvo_decode_attn.argtypes = [_dp] + [ctypes.c_int] * 4 + [
                 _u8p, _dp, _dp, _u8p, _dp, _dp, ctypes.c_int, ctypes.c_int, _ip,
                 ctypes.c_double, _dp]
+            L.kvo_token_error.argtypes = [_dp, _dp, ctypes.c_int, ctypes.c_int, _dp, _dp]
             for name in ("kvo_rotate", "kvo_balance", "kvo_quantize_block",
                          "kvo_quantize_tensor", "kvo_append", "kvo_pack",
-                         "kvo_unpack", "kvo_dequant", "kvo_decode_attn"):
+                         "kvo_unpack", "kvo_dequant", "kvo_decode_attn",
+                         "kvo_token_error"):
                 getattr(L, name).restype = ctypes.c_int
             _lib = L
     return _lib
@@ -269,3 +271,27 @@ def boundary_mask(u, tol: float = 1e-5) -> np.ndarray:
     an fp64 and an fp32 evaluation."""
     u = np.asarray(u, dtype=np.float64)
     return np.min(np.abs(u[..., None] - np.array([-1.0, 0.0, 1.0])), axis=-1) < tol
+
+
+def token_error(x, xhat):
+    """Per-token (||xhat|| / ||x||, cos(xhat, x)) over the last axis of
+    x, xhat [..., D]; the magnitude and direction parts of the error
+    (kvo_token_error). Returns two arrays of shape x.shape[:-1]."""
+    x = _f64(x)
+    xhat = _f64(xhat)
+    if x.shape != xhat.shape:
+        raise ValueError("x and xhat differ in shape")
+    D = x.shape[-1]
+    n = x.size // D if D else 0
+    ratio = np.empty(x.shape[:-1])
+    cosine = np.empty(x.shape[:-1])
+    _check(lib().kvo_token_error(_ptr(x, _dp), _ptr(xhat, _dp), n, D, _ptr(ratio, _dp),
+                                 _ptr(cosine, _dp)), "token_error")
+    return ratio, cosine
+
+
+def cache_token_error(x, codes, rp, c, chunk: int = CHUNK):
+    """One (sequence, head): original tokens x[n][D] against the cache's
+    reconstruction of the same n tokens (codes unpacked [n][D], rp[n],
+    c[>=ceil(n/chunk)][D]) -> (ratio[n], cosine[n])."""
+    return token_error(x, dequant(codes, rp, c, chunk))

@@ -350,6 +350,43 @@ int kvo_dequant(const uint8_t *codes, const double *rp, const double *c, int n,
     return kvo_rotate(out, n, D, out);
 }
 
+/* Per-token magnitude and direction of a reconstruction. The rndamp article
+ * on KVarN, "The Problem", attributes the K error to wrong token magnitudes
+ * rather than to directional distortion, and its "How It Works" closing
+ * paragraph says the method minimizes the magnitude component. Reading taken
+ * (the pages give no formula): for each of the n tokens,
+ *   ratio_t  = ||xhat_t|| / ||x_t||                       (magnitude)
+ *   cosine_t = <xhat_t, x_t> / (||xhat_t|| ||x_t||)       (direction)
+ * Degenerate tokens: both zero -> (1, 1); x zero, xhat not -> (+inf, 0);
+ * xhat zero, x not -> (0, 0). x[n][D], xhat[n][D] -> ratio[n], cosine[n]. */
+int kvo_token_error(const double *x, const double *xhat, int n, int D,
+                    double *ratio, double *cosine) {
+    if (!x || !xhat || !ratio || !cosine || n < 0 || D <= 0) return KVO_ERR_ARG;
+    for (int t = 0; t < n; ++t) {
+        const double *a = x + (size_t)t * D, *b = xhat + (size_t)t * D;
+        double aa = 0.0, bb = 0.0, ab = 0.0;
+        for (int j = 0; j < D; ++j) {
+            aa += a[j] * a[j];
+            bb += b[j] * b[j];
+            ab += a[j] * b[j];
+        }
+        if (aa == 0.0 && bb == 0.0) {
+            ratio[t] = 1.0;
+            cosine[t] = 1.0;
+        } else if (aa == 0.0) {
+            ratio[t] = INFINITY;
+            cosine[t] = 0.0;
+        } else if (bb == 0.0) {
+            ratio[t] = 0.0;
+            cosine[t] = 0.0;
+        } else {
+            ratio[t] = sqrt(bb) / sqrt(aa);
+            cosine[t] = ab / (sqrt(aa) * sqrt(bb));
+        }
+    }
+    return KVO_OK;
+}
+
 /* Decode attention over the reconstructed cache (SC-12): for each sequence b
  * and query head h, kv-head g = h / (Hq / Hkv) (grouped-query attention);
  * K_hat, V_hat of (b, g) over tokens [0, len_b) in the original basis;
