@@ -63,7 +63,8 @@ def parse():
     p.add_argument("--cpu-slices", type=int, default=0,
                    help="oracle slices for the CPU baseline (0 = 2 per thread)")
     p.add_argument("--no-ablations", action="store_true",
-                   help="skip the ablation timings (balancing off, one scale, rotation off)")
+                   help="skip the ablation timings (balancing off, one scale, rotation off) "
+                        "and the error diagnostics")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="one device-to-device copy of this many MiB before the warmup: "
                         "the reference kernel for calibrating HBM byte counters")
@@ -294,12 +295,40 @@ def main():
     if not args.no_ablations:
         res["ablations"] = ablations(kv, torch, stream, xs[0], qs[0], caches[0], ws, out,
                                      T + (args.warmup + args.steps if steady else 1), args.iters)
+        res["error_diagnostics"] = error_diagnostics(kv, torch, stream, xs[0], caches[0],
+                                                     args.iters)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args, wl, xs, news, qs, steady, res["unit"],
                                            bf16_bytes_step, cap)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
+
+
+def error_diagnostics(kv, torch, stream, x_pair, cache_pair, iters):
+    """Magnitude vs direction of the quantization error on layer 0 (outside
+    the timed step): each token's squared error relative to ||x||^2 splits
+    exactly into (rho - 1)^2 (magnitude, rho = ||x_hat|| / ||x||) and
+    2 rho (1 - cos) (direction). Means over all tokens of K and V, quantized
+    with the balancing and without it, through kvarn_token_error."""
+    res = {}
+    for name, x, cache in (("K", x_pair[0], cache_pair[0]), ("V", x_pair[1], cache_pair[1])):
+        scratch = kv.Cache.empty(cache.batch, cache.kv_heads, cache.capacity, cache.kind,
+                                 device=x.device)
+        for it in (iters, 0):
+            kv.quantize(x, scratch, iters=it, stream=stream)
+            ratio, cosine = kv.token_error(x, scratch, stream=stream)
+            torch.cuda.synchronize()
+            r, c = ratio.double(), cosine.double()
+            res[f"{name}_iters_{it}"] = {
+                "magnitude": round(float(((r - 1) ** 2).mean()), 6),
+                "direction": round(float((2 * r * (1 - c)).mean()), 6),
+                "mean_ratio": round(float(r.mean()), 5),
+                "mean_cos": round(float(c.mean()), 5)}
+        del scratch
+    res["note"] = ("per-token squared error / ||x||^2 = magnitude + direction; means over "
+                   "layer 0's tokens")
+    return res
 
 
 def ablations(kv, torch, stream, x_pair, q, cache_pair, ws, out, length, iters, reps=10):

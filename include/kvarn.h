@@ -217,6 +217,38 @@ int kvarn_decode_attn_ex(const void *q, int32_t q_dtype, int32_t q_heads,
                          uint32_t flags, float *out, int32_t n_split,
                          void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * kvarn_token_error -- per-token magnitude and direction of the cache's
+ * reconstruction against the original K or V (rndamp article on KVarN,
+ * "The Problem": the error of K is one of token magnitude rather than of
+ * direction; "How It Works", closing paragraph: the method minimizes the
+ * magnitude component). A diagnostic; it reads the cache and writes nothing
+ * else.
+ *
+ * For every (b, h) and i in [0, tokens), cache slot t = token_offset + i:
+ *   ratio[b][h][i]  = ||x_hat_t|| / ||x_t||
+ *   cosine[b][h][i] = <x_hat_t, x_t> / (||x_hat_t|| ||x_t||)
+ * with x_t = x's token i and x_hat_t the cache's reconstruction of slot t
+ * (both in the original basis; the rotation preserves both numbers, so they
+ * are computed in the rotated one). Degenerate tokens: both zero -> (1, 1);
+ * x_t zero only -> (+inf, 0); x_hat_t zero only -> (0, 0). Sums in fp32.
+ *
+ * x          (device) as for kvarn_quantize: [batch][kv_heads][tokens][128],
+ *            dtype `dtype`, strides in elements, 16-byte aligned pointer and
+ *            strides. With KVARN_FLAG_NO_ROTATE x is taken as already rotated.
+ * tokens     any count >= 0 (0 is a no-op); token_offset >= 0;
+ *            token_offset + tokens <= capacity.
+ * cache      (host) descriptor, read only.
+ * ratio, cosine  (device) fp32 [batch][kv_heads][tokens], 4-byte aligned,
+ *            written.
+ * flags      KVARN_FLAG_NO_ROTATE only.
+ */
+int kvarn_token_error(const void *x, int32_t dtype, int64_t stride_b,
+                      int64_t stride_h, int64_t stride_t, int32_t tokens,
+                      int32_t token_offset, uint32_t flags,
+                      const kvarn_cache *cache, float *ratio, float *cosine,
+                      void *stream);
+
 /* kvarn_status_string -- (host only) static text for a kvarn_status. */
 const char *kvarn_status_string(int status);
 

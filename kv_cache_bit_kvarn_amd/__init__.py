@@ -29,7 +29,7 @@ K, V = 0, 1
 
 EXPORTED = ("kvarn_quantize", "kvarn_quantize_ex", "kvarn_append", "kvarn_append_ex",
             "kvarn_decode_workspace_bytes", "kvarn_decode_attn", "kvarn_decode_attn_ex",
-            "kvarn_status_string")
+            "kvarn_token_error", "kvarn_status_string")
 
 
 class KvarnError(RuntimeError):
@@ -77,6 +77,8 @@ def load(path: str | None = None):
     L.kvarn_decode_attn_ex.argtypes = [vp, i32, i32, cd, cd, vp, ctypes.c_float, u32, vp, i32,
                                        vp, ctypes.c_size_t, vp]
     L.kvarn_decode_attn_ex.restype = ctypes.c_int
+    L.kvarn_token_error.argtypes = [vp, i32, i64, i64, i64, i32, i32, u32, cd, vp, vp, vp]
+    L.kvarn_token_error.restype = ctypes.c_int
     L.kvarn_status_string.argtypes = [ctypes.c_int]
     L.kvarn_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -212,3 +214,27 @@ def decode_attn(q: torch.Tensor, k: Cache, v: Cache, seq_lens: torch.Tensor,
                                      _stream(stream))
     _raise(st, "kvarn_decode_attn")
     return out
+
+
+def token_error(x: torch.Tensor, cache: Cache, token_offset: int = 0, stream=None,
+                flags: int = 0, ratio: torch.Tensor | None = None,
+                cosine: torch.Tensor | None = None):
+    """Per-token ||x_hat|| / ||x|| and cos(x_hat, x) of the cache's
+    reconstruction of slots [token_offset, token_offset + T) against
+    x [B, H, T, 128] (bf16/fp32, channels contiguous). Returns (ratio,
+    cosine), fp32 [B, H, T]. flags: FLAG_NO_ROTATE (x already rotated)."""
+    if x.dim() != 4 or x.shape[3] != HEAD_DIM or x.stride(3) != 1:
+        raise ValueError("x must be [B, H, T, 128] with contiguous channels")
+    if x.shape[0] != cache.batch or x.shape[1] != cache.kv_heads:
+        raise ValueError("x batch/heads differ from the cache")
+    shape = (x.shape[0], x.shape[1], x.shape[2])
+    if ratio is None:
+        ratio = torch.empty(shape, dtype=torch.float32, device=x.device)
+    if cosine is None:
+        cosine = torch.empty(shape, dtype=torch.float32, device=x.device)
+    d = cache.desc()
+    st = load().kvarn_token_error(x.data_ptr(), _dtype_code(x), x.stride(0), x.stride(1),
+                                  x.stride(2), x.shape[2], token_offset, flags, ctypes.byref(d),
+                                  ratio.data_ptr(), cosine.data_ptr(), _stream(stream))
+    _raise(st, "kvarn_token_error")
+    return ratio, cosine

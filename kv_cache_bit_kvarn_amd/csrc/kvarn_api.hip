@@ -3,7 +3,7 @@
 // nothing. The library allocates nothing and never synchronizes.
 #include <limits.h>
 
-#include "kvarn_internal.h"
+#include "kvarn_diag.h"
 
 using namespace kvarn;
 
@@ -111,6 +111,45 @@ int kvarn_append_ex(const void *x, int32_t dtype, const int32_t *positions, uint
 int kvarn_append(const void *x, int32_t dtype, const int32_t *positions,
                  const kvarn_cache *dst, void *stream) {
   return kvarn_append_ex(x, dtype, positions, 0u, dst, stream);
+}
+
+int kvarn_token_error(const void *x, int32_t dtype, int64_t stride_b, int64_t stride_h,
+                      int64_t stride_t, int32_t tokens, int32_t token_offset, uint32_t flags,
+                      const kvarn_cache *cache, float *ratio, float *cosine, void *stream) {
+  if (flags & ~(uint32_t)KVARN_FLAG_NO_ROTATE) return KVARN_ERR_FLAGS;
+  int st = check_cache(cache);
+  if (st != KVARN_OK) return st;
+  if (tokens < 0 || token_offset < 0) return KVARN_ERR_SHAPE;
+  if (tokens == 0) return KVARN_OK;  // nothing to read or write
+  if (!x || !ratio || !cosine) return KVARN_ERR_NULL;
+  const int esz = dtype_size(dtype);
+  if (!esz) return KVARN_ERR_DTYPE;
+  if (stride_b < 0 || stride_h < 0 || stride_t < D) return KVARN_ERR_SHAPE;
+  if ((int64_t)tokens + token_offset > cache->capacity) return KVARN_ERR_CAPACITY;
+  if (!aligned16(x) || (stride_b * esz) % 16 || (stride_h * esz) % 16 || (stride_t * esz) % 16)
+    return KVARN_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(ratio) & 3u) || (reinterpret_cast<uintptr_t>(cosine) & 3u))
+    return KVARN_ERR_ALIGN;
+  if ((int64_t)cache->batch * cache->kv_heads * tokens == 0) return KVARN_OK;
+  DiagArgs a;
+  a.x = x;
+  a.dtype = dtype;
+  a.sb = stride_b;
+  a.sh = stride_h;
+  a.st = stride_t;
+  a.batch = cache->batch;
+  a.heads = cache->kv_heads;
+  a.tokens = tokens;
+  a.token_offset = token_offset;
+  a.capacity = cache->capacity;
+  a.kind = cache->kind;
+  a.flags = flags;
+  a.codes = cache->codes;
+  a.row_scale = cache->row_scale;
+  a.col_scale = cache->col_scale;
+  a.ratio = ratio;
+  a.cosine = cosine;
+  return from_hip(launch_token_error(a, static_cast<hipStream_t>(stream)));
 }
 
 size_t kvarn_decode_workspace_bytes(int32_t batch, int32_t q_heads, int32_t capacity) {

@@ -150,6 +150,31 @@ def test_flags_validation(lib):
                                     None) == kv.ERR_WORKSPACE
 
 
+def _te(lib, x=A, dtype=kv.DT_BF16, sb=4 * 512 * 128, sh=512 * 128, st=128, tokens=200, off=0,
+        flags=0, cache=None, ratio=0x50000, cosine=0x60000):
+    cache = cache or _cache()
+    return lib.kvarn_token_error(x, dtype, sb, sh, st, tokens, off, flags, ctypes.byref(cache),
+                                 ratio, cosine, None)
+
+
+def test_token_error_validation(lib):
+    assert _te(lib, flags=kv.FLAG_ONE_SCALE) == kv.ERR_FLAGS
+    assert _te(lib, x=None) == kv.ERR_NULL
+    assert _te(lib, ratio=None) == kv.ERR_NULL
+    assert _te(lib, cosine=None) == kv.ERR_NULL
+    assert _te(lib, x=None, tokens=0) == kv.OK
+    assert _te(lib, cache=_cache(codes=None)) == kv.ERR_NULL
+    assert _te(lib, dtype=3) == kv.ERR_DTYPE
+    assert _te(lib, tokens=-1) == kv.ERR_SHAPE
+    assert _te(lib, off=-128) == kv.ERR_SHAPE
+    assert _te(lib, st=64) == kv.ERR_SHAPE
+    assert _te(lib, tokens=200, off=400) == kv.ERR_CAPACITY
+    assert _te(lib, x=A + 2) == kv.ERR_ALIGN
+    assert _te(lib, st=132) == kv.ERR_ALIGN
+    assert _te(lib, ratio=0x50002) == kv.ERR_ALIGN
+    assert _te(lib, cache=_cache(batch=0)) == kv.OK
+
+
 def test_status_strings(lib):
     for st in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         s = kv.status_string(st)
