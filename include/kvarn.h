@@ -174,6 +174,33 @@ int kvarn_append_ex(const void *x, int32_t dtype, const int32_t *positions,
                     uint32_t flags, const kvarn_cache *dst, void *stream);
 
 /*
+ * kvarn_append_rebalance -- append with re-balancing at chunk close, the
+ * alternative to kvarn_append's frozen column scales (the pages do not fix
+ * how a new token enters the cache; the rndamp article's "The Problem" only
+ * says errors carry from one decoding step into the next).
+ *
+ * Each token is appended exactly as by kvarn_append_ex (coded at once against
+ * the open chunk's column scales) and is also stored, as given, in `window`
+ * at slot pos % 128 of its (b, h). When the token fills its chunk
+ * (pos % 128 == 127), that chunk is quantized again from the window with the
+ * full dual scaling, exactly as kvarn_quantize_ex would quantize those 128
+ * tokens with `iters` iterations, replacing the chunk's codes, row scales and
+ * column scales. Decode reads the cache as usual.
+ *
+ * window     (device) [batch][kv_heads][128][128] of `dtype`, 16-byte
+ *            aligned, caller-owned and kept between calls (no need to clear
+ *            it). A chunk is re-quantized correctly only if all its 128
+ *            tokens were appended through this call.
+ * iters      0..64, as for kvarn_quantize.
+ * flags      KVARN_FLAG_NO_ROTATE only.
+ * Other arguments as for kvarn_append. Two kernels are enqueued on `stream`.
+ */
+int kvarn_append_rebalance(const void *x, int32_t dtype,
+                           const int32_t *positions, void *window,
+                           int32_t iters, uint32_t flags,
+                           const kvarn_cache *dst, void *stream);
+
+/*
  * kvarn_decode_workspace_bytes -- (host only) bytes of device workspace that
  * kvarn_decode_attn needs for these sizes (split-KV partial results). Returns
  * 0 for invalid sizes.

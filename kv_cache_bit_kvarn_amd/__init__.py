@@ -29,7 +29,7 @@ K, V = 0, 1
 
 EXPORTED = ("kvarn_quantize", "kvarn_quantize_ex", "kvarn_append", "kvarn_append_ex",
             "kvarn_decode_workspace_bytes", "kvarn_decode_attn", "kvarn_decode_attn_ex",
-            "kvarn_token_error", "kvarn_status_string")
+            "kvarn_append_rebalance", "kvarn_token_error", "kvarn_status_string")
 
 
 class KvarnError(RuntimeError):
@@ -77,6 +77,8 @@ def load(path: str | None = None):
     L.kvarn_decode_attn_ex.argtypes = [vp, i32, i32, cd, cd, vp, ctypes.c_float, u32, vp, i32,
                                        vp, ctypes.c_size_t, vp]
     L.kvarn_decode_attn_ex.restype = ctypes.c_int
+    L.kvarn_append_rebalance.argtypes = [vp, i32, vp, vp, i32, u32, cd, vp]
+    L.kvarn_append_rebalance.restype = ctypes.c_int
     L.kvarn_token_error.argtypes = [vp, i32, i64, i64, i64, i32, i32, u32, cd, vp, vp, vp]
     L.kvarn_token_error.restype = ctypes.c_int
     L.kvarn_status_string.argtypes = [ctypes.c_int]
@@ -177,6 +179,31 @@ def append(x: torch.Tensor, positions: torch.Tensor, cache: Cache, stream=None,
     st = load().kvarn_append_ex(x.data_ptr(), _dtype_code(x), positions.data_ptr(), flags,
                                 ctypes.byref(d), _stream(stream))
     _raise(st, "kvarn_append")
+
+
+def append_window(batch: int, kv_heads: int, dtype=torch.bfloat16, device="cuda") -> torch.Tensor:
+    """A window for append_rebalance: [batch, kv_heads, 128, 128]."""
+    return torch.zeros((batch, kv_heads, CHUNK, HEAD_DIM), dtype=dtype, device=device)
+
+
+def append_rebalance(x: torch.Tensor, positions: torch.Tensor, cache: Cache,
+                     window: torch.Tensor, iters: int = 4, stream=None, flags: int = 0) -> None:
+    """append, plus the chunk re-quantized from `window` (same dtype as x,
+    [B, H, 128, 128], kept by the caller) when a token fills it. flags:
+    FLAG_NO_ROTATE."""
+    if x.dim() != 3 or tuple(x.shape) != (cache.batch, cache.kv_heads, HEAD_DIM) or \
+            not x.is_contiguous():
+        raise ValueError("x must be contiguous [B, H, 128] matching the cache")
+    if positions.dtype != torch.int32 or positions.numel() != cache.batch:
+        raise ValueError("positions must be int32 [B]")
+    if tuple(window.shape) != (cache.batch, cache.kv_heads, CHUNK, HEAD_DIM) or \
+            window.dtype != x.dtype or not window.is_contiguous():
+        raise ValueError("window must be contiguous [B, H, 128, 128] of x's dtype")
+    d = cache.desc()
+    st = load().kvarn_append_rebalance(x.data_ptr(), _dtype_code(x), positions.data_ptr(),
+                                       window.data_ptr(), iters, flags, ctypes.byref(d),
+                                       _stream(stream))
+    _raise(st, "kvarn_append_rebalance")
 
 
 def decode_workspace_bytes(batch: int, q_heads: int, capacity: int) -> int:

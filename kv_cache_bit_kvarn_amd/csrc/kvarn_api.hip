@@ -73,6 +73,7 @@ int kvarn_quantize_ex(const void *x, int32_t dtype, int64_t stride_b, int64_t st
   a.codes = dst->codes;
   a.row_scale = dst->row_scale;
   a.col_scale = dst->col_scale;
+  a.pos = nullptr;
   return from_hip(launch_quantize(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -105,12 +106,66 @@ int kvarn_append_ex(const void *x, int32_t dtype, const int32_t *positions, uint
   a.codes = dst->codes;
   a.row_scale = dst->row_scale;
   a.col_scale = dst->col_scale;
+  a.window = nullptr;
   return from_hip(launch_append(a, static_cast<hipStream_t>(stream)));
 }
 
 int kvarn_append(const void *x, int32_t dtype, const int32_t *positions,
                  const kvarn_cache *dst, void *stream) {
   return kvarn_append_ex(x, dtype, positions, 0u, dst, stream);
+}
+
+int kvarn_append_rebalance(const void *x, int32_t dtype, const int32_t *positions, void *window,
+                           int32_t iters, uint32_t flags, const kvarn_cache *dst, void *stream) {
+  if (flags & ~(uint32_t)KVARN_FLAG_NO_ROTATE) return KVARN_ERR_FLAGS;
+  if (!x || !positions || !window) return KVARN_ERR_NULL;
+  int st = check_cache(dst);
+  if (st != KVARN_OK) return st;
+  const int esz = dtype_size(dtype);
+  if (!esz) return KVARN_ERR_DTYPE;
+  if (!aligned16(x) || !aligned16(window)) return KVARN_ERR_ALIGN;
+  if (iters < 0 || iters > 64) return KVARN_ERR_SHAPE;
+  if ((int64_t)dst->batch * dst->kv_heads > INT_MAX) return KVARN_ERR_SHAPE;
+  if (dst->batch == 0 || dst->kv_heads == 0 || dst->capacity == 0) return KVARN_OK;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  AppendArgs p;
+  p.x = x;
+  p.dtype = dtype;
+  p.pos = positions;
+  p.batch = dst->batch;
+  p.heads = dst->kv_heads;
+  p.capacity = dst->capacity;
+  p.kind = dst->kind;
+  p.flags = flags;
+  p.codes = dst->codes;
+  p.row_scale = dst->row_scale;
+  p.col_scale = dst->col_scale;
+  p.window = window;
+  st = from_hip(launch_append(p, s));
+  if (st != KVARN_OK) return st;
+  // the chunks just filled, quantized again from the window
+  QuantArgs a;
+  a.x = window;
+  a.dtype = dtype;
+  a.sh = (int64_t)T * D;
+  a.sb = a.sh * dst->kv_heads;
+  a.st = D;
+  a.batch = dst->batch;
+  a.heads = dst->kv_heads;
+  a.chunks = 1;
+  a.chunk0 = 0;
+  a.nblocks = (uint32_t)(dst->batch * dst->kv_heads);
+  a.div_chunks = make_fastdiv(1u);
+  a.div_heads = make_fastdiv((uint32_t)a.heads);
+  a.iters = iters;
+  a.flags = flags;
+  a.capacity = dst->capacity;
+  a.kind = dst->kind;
+  a.codes = dst->codes;
+  a.row_scale = dst->row_scale;
+  a.col_scale = dst->col_scale;
+  a.pos = positions;
+  return from_hip(launch_quantize(a, s));
 }
 
 int kvarn_token_error(const void *x, int32_t dtype, int64_t stride_b, int64_t stride_h,

@@ -5,8 +5,9 @@
 // The token is rotated (Hadamard, unscaled: the 1/sqrt(128) is folded into
 // the row scale as in the block quantizer), coded against the column scales
 // of its chunk (copied forward from the previous chunk when the token opens
-// a chunk), with its own per-token range step. The block is never
-// re-balanced.
+// a chunk), with its own per-token range step. The block is not re-balanced
+// here; with a window the token is also kept, as given, for the re-balancing
+// of the chunk once it is full (kvarn_append_rebalance).
 #include "kvarn_internal.h"
 
 namespace kvarn {
@@ -31,10 +32,21 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
     const float *x = static_cast<const float *>(a.x) + (int64_t)bh * D;
     y0 = x[lane];
     y1 = x[lane + 64];
+    if (a.window) {
+      float *w = static_cast<float *>(a.window) + ((int64_t)bh * T + slot) * D;
+      w[lane] = y0;
+      w[lane + 64] = y1;
+    }
   } else {
     const uint16_t *x = static_cast<const uint16_t *>(a.x) + (int64_t)bh * D;
-    y0 = __uint_as_float((uint32_t)x[lane] << 16);
-    y1 = __uint_as_float((uint32_t)x[lane + 64] << 16);
+    const uint16_t u0 = x[lane], u1 = x[lane + 64];
+    y0 = __uint_as_float((uint32_t)u0 << 16);
+    y1 = __uint_as_float((uint32_t)u1 << 16);
+    if (a.window) {
+      uint16_t *w = static_cast<uint16_t *>(a.window) + ((int64_t)bh * T + slot) * D;
+      w[lane] = u0;
+      w[lane + 64] = u1;
+    }
   }
   // rotation: channel bit 6 inside the lane, bits 0..5 across lanes
   if constexpr (kRotate) {

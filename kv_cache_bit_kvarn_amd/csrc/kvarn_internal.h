@@ -67,6 +67,9 @@ struct QuantArgs {
   int batch, heads, chunks, chunk0, iters, capacity, kind;
   uint32_t flags;       // KVARN_FLAG_NO_ROTATE
   uint32_t nblocks;     // batch * heads * chunks (< 2^31)
+  // when set: x is a one-chunk window per (b, h) (chunks = 1) and block
+  // (b, h) goes to cache chunk pos[b] / 128, only when pos[b] % 128 == 127
+  const int32_t *pos;
   FastDiv div_chunks, div_heads;
   uint8_t *codes;
   float *row_scale, *col_scale;
@@ -81,6 +84,8 @@ struct AppendArgs {
   uint32_t flags;  // KVARN_FLAG_NO_ROTATE
   uint8_t *codes;
   float *row_scale, *col_scale;
+  void *window;    // when set: [batch][heads][128][128] of x's dtype; the token
+                   // is also stored, as given, at slot pos % 128
 };
 hipError_t launch_append(const AppendArgs &a, hipStream_t s);
 

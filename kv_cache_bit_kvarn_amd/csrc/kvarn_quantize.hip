@@ -334,7 +334,10 @@ __device__ __forceinline__ void load_bf16_block(const QuantArgs &a, const BlockI
 
 // kRotate = false: the input is already rotated (rotation absorbed into the
 // model's weights) and the MFMAs copy it through identity tiles.
-template <bool kF32, bool kRotate>
+// kPositions: x is a one-chunk window per (b, h); block (b, h) re-quantizes
+// cache chunk pos[b] / 128 only when pos[b] % 128 == 127, i.e. when the token
+// just appended at pos[b] filled its chunk (kvarn_append_rebalance).
+template <bool kF32, bool kRotate, bool kPositions>
 __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a) {
   __shared__ QuantSmem sm;
   const int tid = threadIdx.x;
@@ -398,7 +401,13 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
   for (; blk < a.nblocks; blk += gridDim.x) {
     const BlockIdx bi = split_block(a, blk);
     const int64_t bh = bi.bh;
-    const int chunk = a.chunk0 + (int)bi.kc;
+    int chunk = a.chunk0 + (int)bi.kc;
+    bool skip = false;
+    if constexpr (kPositions) {
+      const int pos = a.pos[bi.b];
+      skip = pos < 0 || pos >= a.capacity || pos % T != T - 1;
+      chunk = pos / T;
+    }
 
     // ---- 1-2. load and rotate ---------------------------------------------
     float y[CPT], p[CPT];
@@ -428,6 +437,13 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
       }
 #pragma unroll
       for (int i = 0; i < CPT; ++i) p[i] = y[i] * y[i];
+    }
+
+    if constexpr (kPositions) {
+      if (skip) {  // uniform over the workgroup; the prefetch above is kept
+        if constexpr (!kF32) __builtin_amdgcn_s_waitcnt(kVmcntZero);
+        continue;
+      }
     }
 
     // ---- 3. dual scaling ---------------------------------------------------
@@ -592,17 +608,22 @@ hipError_t launch_quantize(const QuantArgs &a, hipStream_t s) {
   const uint32_t resident = 2u * (uint32_t)(cus > 0 ? cus : 1);
   const uint32_t blocks = a.nblocks < resident ? a.nblocks : resident;
   const bool rot = !(a.flags & KVARN_FLAG_NO_ROTATE);
-  if (a.dtype == KVARN_DT_F32) {
-    if (rot)
-      hipLaunchKernelGGL((quantize_block_kernel<true, true>), dim3(blocks), dim3(kThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((quantize_block_kernel<true, false>), dim3(blocks), dim3(kThreads), 0, s, a);
+#define KVARN_LAUNCH_QUANT(F32, ROT, POS) \
+  hipLaunchKernelGGL((quantize_block_kernel<F32, ROT, POS>), dim3(blocks), dim3(kThreads), 0, s, a)
+  if (a.pos) {
+    if (a.dtype == KVARN_DT_F32) {
+      if (rot) KVARN_LAUNCH_QUANT(true, true, true); else KVARN_LAUNCH_QUANT(true, false, true);
+    } else {
+      if (rot) KVARN_LAUNCH_QUANT(false, true, true); else KVARN_LAUNCH_QUANT(false, false, true);
+    }
   } else {
-    if (rot)
-      hipLaunchKernelGGL((quantize_block_kernel<false, true>), dim3(blocks), dim3(kThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((quantize_block_kernel<false, false>), dim3(blocks), dim3(kThreads), 0, s, a);
+    if (a.dtype == KVARN_DT_F32) {
+      if (rot) KVARN_LAUNCH_QUANT(true, true, false); else KVARN_LAUNCH_QUANT(true, false, false);
+    } else {
+      if (rot) KVARN_LAUNCH_QUANT(false, true, false); else KVARN_LAUNCH_QUANT(false, false, false);
+    }
   }
+#undef KVARN_LAUNCH_QUANT
   return hipGetLastError();
 }
 

@@ -175,6 +175,24 @@ def test_token_error_validation(lib):
     assert _te(lib, cache=_cache(batch=0)) == kv.OK
 
 
+def test_append_rebalance_validation(lib):
+    c = _cache()
+    W = 0x70000
+    assert lib.kvarn_append_rebalance(A, 0, B, W, 4, kv.FLAG_ONE_SCALE, ctypes.byref(c),
+                                      None) == kv.ERR_FLAGS
+    assert lib.kvarn_append_rebalance(None, 0, B, W, 4, 0, ctypes.byref(c), None) == kv.ERR_NULL
+    assert lib.kvarn_append_rebalance(A, 0, None, W, 4, 0, ctypes.byref(c), None) == kv.ERR_NULL
+    assert lib.kvarn_append_rebalance(A, 0, B, None, 4, 0, ctypes.byref(c), None) == kv.ERR_NULL
+    assert lib.kvarn_append_rebalance(A, 0, B, W, 4, 0, None, None) == kv.ERR_NULL
+    assert lib.kvarn_append_rebalance(A, 9, B, W, 4, 0, ctypes.byref(c), None) == kv.ERR_DTYPE
+    assert lib.kvarn_append_rebalance(A, 0, B, W + 8, 4, 0, ctypes.byref(c), None) == kv.ERR_ALIGN
+    assert lib.kvarn_append_rebalance(A + 2, 0, B, W, 4, 0, ctypes.byref(c), None) == kv.ERR_ALIGN
+    assert lib.kvarn_append_rebalance(A, 0, B, W, 65, 0, ctypes.byref(c), None) == kv.ERR_SHAPE
+    assert lib.kvarn_append_rebalance(A, 0, B, W, -1, 0, ctypes.byref(c), None) == kv.ERR_SHAPE
+    z = _cache(batch=0)
+    assert lib.kvarn_append_rebalance(A, 0, B, W, 4, 0, ctypes.byref(z), None) == kv.OK
+
+
 def test_status_strings(lib):
     for st in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         s = kv.status_string(st)
