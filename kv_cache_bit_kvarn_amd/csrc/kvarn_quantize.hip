@@ -4,38 +4,42 @@
 // block of K or V (one layer, sequence, kv-head, chunk) at a time and walks
 // the blocks of the launch persistently (stride = grid), loading the next
 // block's bf16 input into registers while the current one is coded. Wave w
-// owns tokens [16 w, 16 w + 16); lane (n = lane % 16, g = lane / 16) holds
-// token 16 w + n.
-//   1. load: each lane reads four 16-byte pieces of its token row (channels
-//      32 kk + 8 g + [0, 8)), so one load instruction covers 64 contiguous
-//      bytes of each of 16 rows; the pieces are the B operands of the MFMAs;
+// owns tokens [16 w, 16 w + 16).
+//   1. load: lane (m = lane % 16, g = lane / 16) reads four 16-byte pieces of
+//      token 16 w + m (channels 32 kk + 8 g + [0, 8)), so one load instruction
+//      covers 64 contiguous bytes of each of 16 rows; the pieces are the A
+//      operands of the MFMAs;
 //   2. Hadamard rotation along channels (rndamp article on KVarN, "How It
 //      Works", item 1) as a dense product on the matrix cores:
-//      y^T = H_128 x^T with v_mfma_f32_16x16x32_bf16, 32 MFMAs per wave.
+//      y = x H_128 with v_mfma_f32_16x16x32_bf16, 32 MFMAs per wave.
 //      Sylvester's H_128 has entry (-1)^popcount(i & j); split over the tile
-//      indices, each 16 x 32 tile (mt, kk) of it is a sign
-//      (-1)^popcount((mt/2) & kk) times one of two lane-constant operands
-//      (mt % 2), the sign going onto the input piece. The result lands with
-//      lane (n, g) holding channels 16 mt + 4 g + r of its token. (The
-//      product could also be 8 MFMAs and a 4-point transform over the pieces,
-//      but that moves 64 adds per lane onto the VALU, which bounds the
-//      kernel, while the matrix cores are mostly idle.)
-//      bf16 inputs and +-1 are exact and the products accumulate in fp32;
-//      fp32 input is split exactly into three bf16 terms (three MFMAs per
-//      product). With the rotation absorbed into the weights, the MFMAs run
-//      on identity tiles (one per output tile), which copies x exactly;
+//      indices, each 32 x 16 tile (kk, nt) of it is a sign
+//      (-1)^popcount(kk & (nt/2)) times one of two lane-constant operands
+//      (nt % 2), the sign going onto the input piece. The result lands token
+//      by token: lane (n, g) holds tokens 16 w + 4 g + r (r < 4) of channels
+//      16 nt + n (nt < 8). bf16 inputs and +-1 are exact and the products
+//      accumulate in fp32; fp32 input is split exactly into three bf16 terms
+//      (three MFMAs per product). With the rotation absorbed into the
+//      weights, the MFMAs run on identity tiles (one per output tile), which
+//      copies x exactly;
 //   3. dual-scaling normalization ("How It Works", item 2; abstract: both
-//      axes of K and V): the squares P = y^2 stay in registers (next to y)
-//      for the row step and are staged once, transposed, in LDS for the
-//      column step; the per-channel and per-token factors are read once per
-//      lane and shared across 16-lane rows by DPP broadcasts; a token's four
-//      partial row sums meet through lane exchanges 16 and 32 apart;
-//   4. per-token range step and 2-bit codes (v_cvt_pk_u8_f32): K codes are
-//      packed four per byte (v_dot4_u32_u8) and transposed across the four
-//      lanes of a token (one permlane32 swap, one exchange 16 lanes apart) so
-//      that each lane stores 8 contiguous bytes of its token row; V codes are
-//      packed four tokens per byte with a shift and an OR across the four
-//      adjacent lanes, staged in LDS and stored as 4-byte words per channel.
+//      axes of K and V): the squares P = y^2 stay in registers next to y.
+//      Row step: each lane weighs its 8 channels of each of its 4 tokens by
+//      1/c^2 (8 registers) and the 16 lanes of a row combine their sums
+//      (two lane-pair exchanges that halve the values, then two rotations),
+//      with no LDS and no barrier. Column step: each lane weighs its 4 tokens
+//      of each of its 8 channels by 1/r^2; two permlane swaps sum over the
+//      wave's four rows and leave 2 channels per lane; the waves publish
+//      those partial sums (4 KB, double-buffered) and, after the sweep's one
+//      barrier, every wave adds up the 8 partials of its lanes' channels and
+//      spreads 1/c^2 back over its rows with the swaps in reverse;
+//   4. per-token range step and 2-bit codes (v_cvt_pk_u8_f32): K codes of
+//      four adjacent channels (four adjacent lanes) merge by a shift and an
+//      OR across the quad, pass through a small per-wave LDS area and leave
+//      as 8 contiguous bytes per lane (a wave writes its 16 token rows as
+//      one 512-byte span); V codes of a lane's 4 tokens form a byte in the
+//      lane, and a 4 x 4 byte transpose across the wave's rows (two permlane
+//      swaps) gives each lane two whole 4-byte words of channel rows.
 // The rotation is applied without its 1/sqrt(128) factor; that factor leaves
 // the column scales and codes unchanged and is folded into the row scale.
 //
@@ -63,70 +67,34 @@ FastDiv make_fastdiv(uint32_t d) {
 namespace {
 
 constexpr int kThreads = 512;
-constexpr int CPT = 32;                        // values per lane: channels (rows), tokens (columns)
+constexpr int kWaves = kThreads / 64;
+constexpr int CPT = 32;                        // values per lane: 4 tokens x 8 channels
 constexpr float kGrid = 1.9999980926513672f;  // 2 (1 - 2^-20)
 constexpr uint32_t kPack4 = 0x40100401u;       // byte weights 1, 4, 16, 64
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-// LDS layouts. On gfx950 a ds_write_b32 is served one half-wave per pass with
-// the dword address taken modulo 32 as its bank; a ds_read_b64 one half-wave
-// per pass over 64 four-byte banks; a ds_read_b128 in four passes of 16 lanes
-// (the quads of one half-wave whose quad index has the same popcount parity)
-// over 64 banks; a lane reading the same address as another still takes its
-// own bank slot. The layouts below are free of bank conflicts under that
-// model:
-//  * transposed P: entry (channel j, token i) at pt_at(j, i): rows 132
-//    floats apart, 32 more floats per group of 8 channels (a P write covers
-//    16 tokens x channels 4 apart; a column-step read covers 16 channels);
-//  * per-channel w at wpad(j) (8 floats of padding after channel 63) and
-//    per-token v, each read once per lane as a pair and shared across a
-//    16-lane row by DPP broadcasts;
-//  * V code staging, in the P area once the column steps are done: word
-//    (mt, g, byte column 4 c + e) at vs_at(mt, g, c, e) = 32 (4 mt + g) +
-//    4 (c ^ ((mt + 4 g) % 8)) + e (16-byte chunks swizzled).
-constexpr int PT_STRIDE = 132;
-__host__ __device__ constexpr int pt_at(int j, int i) {
-  return j * PT_STRIDE + 32 * (j >> 3) + i;
-}
-__host__ __device__ constexpr bool pt_rows_disjoint() {
-  for (int j = 0; j + 1 < D; ++j)
-    if (pt_at(j, T - 1) >= pt_at(j + 1, 0)) return false;
-  return true;
-}
-static_assert(pt_rows_disjoint(), "rows of the transposed P overlap");
-constexpr int PT_SIZE = pt_at(D - 1, T - 1) + 1;
-__host__ __device__ constexpr int wpad(int j) { return j + 8 * (j >> 6); }
-__host__ __device__ constexpr int vs_at(int mt, int g, int c, int e) {
-  return 32 * (4 * mt + g) + 4 * (c ^ ((mt + 4 * g) & 7)) + e;
-}
-
+// LDS. On gfx950 a ds_write_b32 is served one half-wave per pass with the
+// dword address taken modulo 32 as its bank; a ds_read_b32 pair
+// (ds_read2st64) of consecutive lanes reads consecutive dwords. Both areas
+// below are free of bank conflicts under that model:
+//  * part[buffer][wave][k][lane]: the column step's per-wave partial sums
+//    (lane (n, g) holds channels 16 A(g) + n and 16 (A(g) + 4) + n for
+//    k = 0, 1, the same in every wave); two buffers, alternated from one
+//    column step to the next, so a step's writes never meet the previous
+//    step's reads without a second barrier;
+//  * kst[wave]: K code staging, rows of KST_ROW words per group of 4 tokens
+//    (word (token r, half k, quad q) at KST_ROW g + 8 r + 4 k + q; the
+//    36-word rows put the two 16-lane rows of a half-wave on disjoint
+//    banks).
+constexpr int KST_ROW = 36;
 struct QuantSmem {
-  alignas(16) float w[wpad(D - 1) + 1];  // 1/c_j^2
-  alignas(16) float wc[wpad(D - 1) + 1]; // 1/c_j after the last column step
-  alignas(16) float v[T];                // 1/r_i^2
-  alignas(16) float pt[PT_SIZE];         // transposed P, then V code staging
-  alignas(16) u32x4 hop[2][64];          // rotation operands of each lane
+  alignas(16) float part[2][kWaves][2][64];
+  alignas(16) uint32_t kst[kWaves][4 * KST_ROW];
+  alignas(16) u32x4 hop[2][64];  // rotation operands of each lane
 };
-static_assert(vs_at(7, 3, 7, 3) < PT_SIZE, "V staging fits in the P area");
 
 __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
-
-// Sum (max) over the four 16-lane rows of the wave, in every lane: the
-// permlane32 swap pairs rows 0-1 with rows 2-3, the permlane16 swap then row
-// 0 with 1 and 2 with 3 (VALU lane exchanges, no LDS round trip).
-__device__ __forceinline__ float rows_sum(float s) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
-  const float t = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-__device__ __forceinline__ float rows_max(float s) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
-  const float t = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
 
 // The value itself, hidden from the optimizer so that addresses built from it
 // are recomputed where they are used instead of being hoisted out of the block
@@ -140,20 +108,95 @@ template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
 }
-constexpr int kXor1 = 0xB1;  // quad_perm [1,0,3,2]
-constexpr int kXor2 = 0x4E;  // quad_perm [2,3,0,1]
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+constexpr int kXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kRor4 = 0x124;  // row_ror:4, lane i of a row reads lane (i + 4) % 16
+constexpr int kRor8 = 0x128;  // row_ror:8
+
+template <bool kMax>
+__device__ __forceinline__ float combine(float a, float b) {
+  if constexpr (kMax) return fmaxf(a, b);
+  else return a + b;
+}
+
+// Totals (kMax: maxima) over the 16 lanes of a row of four per-token values
+// s[0..3]. Lane pairs 1 apart, then 2 apart, hand each other the values they
+// do not keep, so that lane n is left with token tsel(n) = 2 (n % 2) +
+// (n / 2) % 2 summed over its quad; rotations by 8 and by 4 lanes then add
+// the four quads (lanes n, n + 4, n + 8, n + 12 hold the same token).
+template <bool kMax>
+__device__ __forceinline__ float row_reduce4(const float (&s)[4], int n) {
+  const bool b0 = n & 1, b1 = n & 2;
+  float k0 = b0 ? s[2] : s[0], k1 = b0 ? s[3] : s[1];
+  const float e0 = b0 ? s[0] : s[2], e1 = b0 ? s[1] : s[3];
+  k0 = combine<kMax>(k0, dpp_f<kXor1>(e0));
+  k1 = combine<kMax>(k1, dpp_f<kXor1>(e1));
+  float k = b1 ? k1 : k0;
+  const float e = b1 ? k0 : k1;
+  k = combine<kMax>(k, dpp_f<kXor2>(e));
+  k = combine<kMax>(k, dpp_f<kRor8>(k));
+  return combine<kMax>(k, dpp_f<kRor4>(k));
+}
+__device__ __forceinline__ int tsel(int n) { return 2 * (n & 1) + ((n >> 1) & 1); }
+// Token R's value after row_reduce4, from the quad lane that holds it.
+template <int R>
+__device__ __forceinline__ float token_value(float x) {
+  constexpr int l = 2 * (R & 1) + (R >> 1);
+  return dpp_f<l * 0x55>(x);  // quad_perm [l, l, l, l]
+}
+
+// Column step, reduce: cp[nt] (channel 16 nt + n over the lane's 4 tokens)
+// summed over the wave's four 16-lane rows. The permlane32 swaps pair rows
+// g and g + 2 for tiles (2k, 2k + 1), the permlane16 swaps rows g and g + 1;
+// lane (n, g) ends with channels 16 A(g) + n (c0) and 16 (A(g) + 4) + n (c1),
+// A(g) = 2 (g % 2) + g / 2.
+__device__ __forceinline__ void col_reduce(const float (&cp)[8], float &c0, float &c1) {
+  float z[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(cp[2 * k]),
+                                                    __float_as_uint(cp[2 * k + 1]), false, false);
+    z[k] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+  }
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(z[0]), __float_as_uint(z[1]),
+                                                  false, false);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(z[2]), __float_as_uint(z[3]),
+                                                  false, false);
+  c0 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  c1 = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ int col_tile(int g) { return 2 * (g & 1) + (g >> 1); }
+// Column step, gather: the inverse movement; every lane receives the values
+// of channels 16 nt + n for nt = 0..7 in out[nt].
+__device__ __forceinline__ void col_gather(float c0, float c1, float (&out)[8]) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(c0), __float_as_uint(c0), false,
+                                                  false);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(c1), __float_as_uint(c1), false,
+                                                  false);
+  const uint32_t h[4] = {a[0], a[1], b[0], b[1]};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const auto s = __builtin_amdgcn_permlane32_swap(h[k], h[k], false, false);
+    out[2 * k] = __uint_as_float(s[0]);
+    out[2 * k + 1] = __uint_as_float(s[1]);
+  }
+}
 
 __device__ __forceinline__ f32x4 mfma_bf16(const u32x4 &a, const u32x4 &b, const f32x4 &c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// A operand of the rotation for output-channel tile parity p. Lane (m, g),
-// slot e multiplies input channel 32 kk + 8 g + e into output channel
-// 16 mt + m (the B operand's slot e of lane group g holds that channel):
-// popcount((16 mt + m) & (32 kk + 8 g + e)) splits into popcount(m & e),
-// m bit 3 with g bit 0, mt bit 0 (= p) with g bit 1, and (mt / 2) & kk; the
-// last part is the tile's sign, the others are fixed per lane and slot.
+// B operand of the rotation for output-channel tile parity p. Lane (n, g),
+// slot e multiplies input channel 32 kk + 8 g + e (slot e of the A operand's
+// lane group g) into output channel 16 nt + n: popcount((32 kk + 8 g + e) &
+// (16 nt + n)) splits into popcount(e & n), g bit 0 with n bit 3, g bit 1
+// with nt bit 0 (= p), and kk & (nt / 2); the last part is the tile's sign,
+// the others are fixed per lane and slot.
 __device__ __forceinline__ u32x4 hadamard_operand(int lane, int p) {
   const int m = lane & 15, g = lane >> 4;
   u32x4 r;
@@ -171,8 +214,8 @@ __device__ __forceinline__ u32x4 hadamard_operand(int lane, int p) {
   return r;
 }
 // Identity tile for input that is already rotated: output channel
-// 16 mt + m takes input channel 32 (mt / 2) + 8 g + e exactly when
-// g = 2 (mt % 2) + m / 8 and e = m % 8.
+// 16 nt + n takes input channel 32 (nt / 2) + 8 g + e exactly when
+// g = 2 (nt % 2) + n / 8 and e = n % 8.
 __device__ __forceinline__ u32x4 identity_operand(int lane, int p) {
   const int m = lane & 15, g = lane >> 4;
   u32x4 r;
@@ -189,22 +232,22 @@ __device__ __forceinline__ u32x4 identity_operand(int lane, int p) {
   return r;
 }
 
-// acc[mt] += (tile (mt, kk) of the rotation) x b, b = input channels
-// 32 kk + [0, 32) of the wave's 16 tokens. A Hadamard tile with a negative
-// sign takes the negated b (sign bits flipped) against the same operand; the
-// identity has one tile per output tile, at kk = mt / 2.
+// acc[nt] += x (input channels 32 kk + [0, 32) of the wave's 16 tokens) times
+// tile (kk, nt) of the rotation. A Hadamard tile with a negative sign takes
+// the negated x (sign bits flipped) against the same operand; the identity
+// has one tile per output tile, at kk = nt / 2.
 template <bool kRotate, int KK>
-__device__ __forceinline__ void rotate_step(f32x4 (&acc)[8], const u32x4 &b, const u32x4 (&hp)[2]) {
+__device__ __forceinline__ void rotate_step(f32x4 (&acc)[8], const u32x4 &x, const u32x4 (&hp)[2]) {
   if constexpr (kRotate) {
-    const u32x4 nb = b ^ 0x80008000u;
+    const u32x4 nx = x ^ 0x80008000u;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      const bool neg = __builtin_popcount((mt >> 1) & KK) & 1;
-      acc[mt] = mfma_bf16(hp[mt & 1], neg ? nb : b, acc[mt]);
+    for (int nt = 0; nt < 8; ++nt) {
+      const bool neg = __builtin_popcount((nt >> 1) & KK) & 1;
+      acc[nt] = mfma_bf16(neg ? nx : x, hp[nt & 1], acc[nt]);
     }
   } else {
-    acc[2 * KK] = mfma_bf16(hp[0], b, acc[2 * KK]);
-    acc[2 * KK + 1] = mfma_bf16(hp[1], b, acc[2 * KK + 1]);
+    acc[2 * KK] = mfma_bf16(x, hp[0], acc[2 * KK]);
+    acc[2 * KK + 1] = mfma_bf16(x, hp[1], acc[2 * KK + 1]);
   }
 }
 
@@ -229,82 +272,12 @@ __device__ __forceinline__ void split_bf16x3(const f32x4 &a, const f32x4 &b, u32
   }
 }
 
-// Eight products of a lane's values x[e] with values held across its 16-lane
-// row: x[e] meets register w{e % 2} of row lane L{e / 2} (v_fmac_f32_dpp with
-// row_newbcast, which reads that lane of the row), summed into acc[e % 4].
-// The leading s_nop covers the DPP read-after-VALU-write hazard.
-#define KVARN_FMAC8_BCAST(L0, L1, L2, L3, acc, w0, w1, x)                                        \
-  asm("s_nop 1\n\t"                                                                              \
-      "v_fmac_f32_dpp %0, %4, %6 row_newbcast:" #L0 " row_mask:0xf bank_mask:0xf\n\t"            \
-      "v_fmac_f32_dpp %1, %5, %7 row_newbcast:" #L0 " row_mask:0xf bank_mask:0xf\n\t"            \
-      "v_fmac_f32_dpp %2, %4, %8 row_newbcast:" #L1 " row_mask:0xf bank_mask:0xf\n\t"            \
-      "v_fmac_f32_dpp %3, %5, %9 row_newbcast:" #L1 " row_mask:0xf bank_mask:0xf\n\t"            \
-      "v_fmac_f32_dpp %0, %4, %10 row_newbcast:" #L2 " row_mask:0xf bank_mask:0xf\n\t"           \
-      "v_fmac_f32_dpp %1, %5, %11 row_newbcast:" #L2 " row_mask:0xf bank_mask:0xf\n\t"           \
-      "v_fmac_f32_dpp %2, %4, %12 row_newbcast:" #L3 " row_mask:0xf bank_mask:0xf\n\t"           \
-      "v_fmac_f32_dpp %3, %5, %13 row_newbcast:" #L3 " row_mask:0xf bank_mask:0xf"                 \
-      : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])                                    \
-      : "v"(w0), "v"(w1), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]),     \
-        "v"(x[6]), "v"(x[7]))
-// Same, with acc[] set by the first four products instead of accumulated.
-#define KVARN_FMAC8_BCAST_FIRST(L0, L1, L2, L3, acc, w0, w1, x)                                  \
-  asm("s_nop 1\n\t"                                                                              \
-      "v_mul_f32_dpp %0, %4, %6 row_newbcast:" #L0 " row_mask:0xf bank_mask:0xf\n\t"             \
-      "v_mul_f32_dpp %1, %5, %7 row_newbcast:" #L0 " row_mask:0xf bank_mask:0xf\n\t"             \
-      "v_mul_f32_dpp %2, %4, %8 row_newbcast:" #L1 " row_mask:0xf bank_mask:0xf\n\t"             \
-      "v_mul_f32_dpp %3, %5, %9 row_newbcast:" #L1 " row_mask:0xf bank_mask:0xf\n\t"             \
-      "v_fmac_f32_dpp %0, %4, %10 row_newbcast:" #L2 " row_mask:0xf bank_mask:0xf\n\t"           \
-      "v_fmac_f32_dpp %1, %5, %11 row_newbcast:" #L2 " row_mask:0xf bank_mask:0xf\n\t"           \
-      "v_fmac_f32_dpp %2, %4, %12 row_newbcast:" #L3 " row_mask:0xf bank_mask:0xf\n\t"           \
-      "v_fmac_f32_dpp %3, %5, %13 row_newbcast:" #L3 " row_mask:0xf bank_mask:0xf"                 \
-      : "=&v"(acc[0]), "=&v"(acc[1]), "=&v"(acc[2]), "=&v"(acc[3])                                \
-      : "v"(w0), "v"(w1), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]),     \
-        "v"(x[6]), "v"(x[7]))
-// x[e] *= register w{e % 2} of row lane L{e / 2}.
-#define KVARN_MUL8_BCAST(L0, L1, L2, L3, w0, w1, x)                                               \
-  asm("s_nop 1\n\t"                                                                              \
-      "v_mul_f32_dpp %0, %8, %0 row_newbcast:" #L0 " row_mask:0xf bank_mask:0xf\n\t"             \
-      "v_mul_f32_dpp %1, %9, %1 row_newbcast:" #L0 " row_mask:0xf bank_mask:0xf\n\t"             \
-      "v_mul_f32_dpp %2, %8, %2 row_newbcast:" #L1 " row_mask:0xf bank_mask:0xf\n\t"             \
-      "v_mul_f32_dpp %3, %9, %3 row_newbcast:" #L1 " row_mask:0xf bank_mask:0xf\n\t"             \
-      "v_mul_f32_dpp %4, %8, %4 row_newbcast:" #L2 " row_mask:0xf bank_mask:0xf\n\t"             \
-      "v_mul_f32_dpp %5, %9, %5 row_newbcast:" #L2 " row_mask:0xf bank_mask:0xf\n\t"             \
-      "v_mul_f32_dpp %6, %8, %6 row_newbcast:" #L3 " row_mask:0xf bank_mask:0xf\n\t"             \
-      "v_mul_f32_dpp %7, %9, %7 row_newbcast:" #L3 " row_mask:0xf bank_mask:0xf"                   \
-      : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),      \
-        "+v"(x[7])                                                                                \
-      : "v"(w0), "v"(w1))
-
-// Row step: sum over the lane's 32 channels of p[4 mt + r] / c^2 of channel
-// 16 mt + 4 g + r. Row lane n holds 1/c^2 of channels 16 (n / 2) + 4 g +
-// 2 (n % 2) + {0, 1} (one 8-byte read), so element (mt, r) sits in register
-// r % 2 of lane 2 mt + r / 2. Four interleaved partial sums, tree-combined.
-__device__ __forceinline__ float row_dot(const float (&p)[CPT], float w0, float w1) {
-  float acc[4];
-  KVARN_FMAC8_BCAST_FIRST(0, 1, 2, 3, acc, w0, w1, (p + 0));
-  KVARN_FMAC8_BCAST(4, 5, 6, 7, acc, w0, w1, (p + 8));
-  KVARN_FMAC8_BCAST(8, 9, 10, 11, acc, w0, w1, (p + 16));
-  KVARN_FMAC8_BCAST(12, 13, 14, 15, acc, w0, w1, (p + 24));
-  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
-}
-
-// Column step: sum over 32 tokens of P_ij / r_i^2; row lane n holds 1/r^2 of
-// tokens 2 n + {0, 1} of the quarter. P is read two 16-byte vectors at a time.
-__device__ __forceinline__ float col_dot(const float *pc, float v0, float v1) {
-  float acc[4];
-#define KVARN_COL_BLOCK(H, L0, L1, L2, L3, FMAC)                                        \
-  {                                                                                     \
-    const f32x4 a0 = reinterpret_cast<const f32x4 *>(pc)[2 * (H)];                      \
-    const f32x4 a1 = reinterpret_cast<const f32x4 *>(pc)[2 * (H) + 1];                  \
-    const float x[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};                \
-    FMAC(L0, L1, L2, L3, acc, v0, v1, x);                                               \
-  }
-  KVARN_COL_BLOCK(0, 0, 1, 2, 3, KVARN_FMAC8_BCAST_FIRST)
-  KVARN_COL_BLOCK(1, 4, 5, 6, 7, KVARN_FMAC8_BCAST)
-  KVARN_COL_BLOCK(2, 8, 9, 10, 11, KVARN_FMAC8_BCAST)
-  KVARN_COL_BLOCK(3, 12, 13, 14, 15, KVARN_FMAC8_BCAST)
-#undef KVARN_COL_BLOCK
-  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+// LDS accesses of the wave complete and are visible to its other lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | 0xF | (0x3 << 14));  // lgkmcnt(0) only
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 struct BlockIdx {
@@ -332,6 +305,11 @@ __device__ __forceinline__ void load_bf16_block(const QuantArgs &a, const BlockI
   for (int kk = 0; kk < 4; ++kk) xr[kk] = __builtin_nontemporal_load(src + 4 * kk);
 }
 
+// One of four values chosen by a lane index i < 4.
+__device__ __forceinline__ uint32_t pick4(int i, uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3) {
+  return (i & 2) ? ((i & 1) ? v3 : v2) : ((i & 1) ? v1 : v0);
+}
+
 // kRotate = false: the input is already rotated (rotation absorbed into the
 // model's weights) and the MFMAs copy it through identity tiles.
 // kPositions: x is a one-chunk window per (b, h); block (b, h) re-quantizes
@@ -343,11 +321,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
-  const int ti = 16 * wv + n;             // token of the lane (rows, codes)
-  // column step: channel cj = 16 w + n, token quarter g (its 16-lane row)
-  const int cj = 16 * wv + n;
-  // the 1/c^2 pair this lane shares with its row (row step, range step)
-  const int w_pair = wpad(16 * (n >> 1) + 4 * g + 2 * (n & 1));
+  const int ti = 16 * wv + n;  // token whose input row the lane loads
   const int64_t nch = a.capacity / T;
   // r' from the running maximum: the unscaled rotation's 1/sqrt(128) and the
   // 1/2 of the range step, or the 1/2 alone for pre-rotated input
@@ -362,7 +336,6 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
   }
   lds_barrier();
 
-  // y = x . H (or x) for the lane's token: acc[mt][r] = channel 16 mt + 4 g + r.
   u32x4 xn[4];  // next block's bf16 input
   uint32_t blk = blockIdx.x;
   if constexpr (!kF32) {
@@ -398,6 +371,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
     rotate_step<kRotate, 3>(acc, x[3], hp);
   };
 
+  int buf = 0;  // partial-sum buffer of the next column step
   for (; blk < a.nblocks; blk += gridDim.x) {
     const BlockIdx bi = split_block(a, blk);
     const int64_t bh = bi.bh;
@@ -410,12 +384,13 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
     }
 
     // ---- 1-2. load and rotate ---------------------------------------------
+    // y[4 nt + r]: token 16 wv + 4 g + r, channel 16 nt + n
     float y[CPT], p[CPT];
     f32x4 gram = {0.f, 0.f, 0.f, 0.f};  // bf16: x x^T of the wave's 16 tokens
     {
       f32x4 acc[8];
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < 8; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
       if constexpr (kF32) {
         rotate_f32(bi, acc);
       } else {
@@ -431,9 +406,9 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
         load_bf16_block(a, split_block(a, nb), ti, g, xn);
       }
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        y[4 * mt + 0] = acc[mt].x; y[4 * mt + 1] = acc[mt].y;
-        y[4 * mt + 2] = acc[mt].z; y[4 * mt + 3] = acc[mt].w;
+      for (int nt = 0; nt < 8; ++nt) {
+        y[4 * nt + 0] = acc[nt].x; y[4 * nt + 1] = acc[nt].y;
+        y[4 * nt + 2] = acc[nt].z; y[4 * nt + 3] = acc[nt].w;
       }
 #pragma unroll
       for (int i = 0; i < CPT; ++i) p[i] = y[i] * y[i];
@@ -447,55 +422,81 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
     }
 
     // ---- 3. dual scaling ---------------------------------------------------
-    if (a.kind == KVARN_V) lds_barrier();  // previous block's readers done with the staging
-    {
-      // pt_at(16 mt + 4 g + r, ti) = pt_at(4 g, ti) + pt_at(16 mt + r, 0) for r < 4
-      float *dst = sm.pt + pt_at(4 * g, ti);
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dst[pt_at(16 * mt + r, 0)] = p[4 * mt + r];
-    }
-    // first row step (c = 1): v_i = 1 / r_i^2 = D / sum_j P_ij, published with P
+    float w[8];                  // 1/c^2 of channels 16 nt + n; 1/c after the last column step
+    float cm0 = 1.f, cm1 = 1.f;  // c^2 of the lane's two column-step channels
     if (a.iters > 0) {
-      if constexpr (kF32) {
-        float t[4] = {p[0], p[1], p[2], p[3]};
+      float v[4];  // 1/r^2 of the lane's tokens
+      {
+        // first row step (c = 1): v_i = 1 / r_i^2 = D / sum_j P_ij
+        float tot;
+        if constexpr (kF32) {
+          float s[4];
 #pragma unroll
-        for (int i = 4; i < CPT; ++i) t[i & 3] += p[i];
-        const float s = rows_sum((t[0] + t[1]) + (t[2] + t[3]));
-        if (g == 0) sm.v[ti] = s > 0.f ? (float)D * rcp(s) : 1.f;
-      } else {
-        const int r = n & 3;
-        const float d = (r & 2) ? ((r & 1) ? gram.w : gram.z) : ((r & 1) ? gram.y : gram.x);
-        const float s = (kRotate ? (float)D : 1.f) * d;
-        if (g == (n >> 2)) sm.v[ti] = s > 0.f ? (float)D * rcp(s) : 1.f;
+          for (int r = 0; r < 4; ++r)
+            s[r] = ((p[r] + p[4 + r]) + (p[8 + r] + p[12 + r])) +
+                   ((p[16 + r] + p[20 + r]) + (p[24 + r] + p[28 + r]));
+          tot = row_reduce4<false>(s, n);
+        } else {
+          // token 4 g + tsel(n) sits in lane 16 g + 4 g + tsel(n), register tsel(n)
+          const int r = n & 3;
+          const float d = (r & 2) ? ((r & 1) ? gram.w : gram.z) : ((r & 1) ? gram.y : gram.x);
+          const int t = fresh(tid);
+          const int src = 20 * ((t >> 4) & 3) + tsel(t);
+          tot = (kRotate ? (float)D : 1.f) * __shfl(d, src, 64);
+        }
+        const float vt = tot > 0.f ? (float)D * rcp(tot) : 1.f;
+        v[0] = token_value<0>(vt); v[1] = token_value<1>(vt);
+        v[2] = token_value<2>(vt); v[3] = token_value<3>(vt);
       }
-    }
-    lds_barrier();
-
-    float cm = 1.f;  // c_j^2 of the last column step (lanes with g = 0)
-    for (int it = 0; it < a.iters; ++it) {
-      if (it > 0) {
-        // row step: r_i^2 = (1/D) sum_j P_ij / c_j^2  ->  v_i = 1/r_i^2
-        const float2 wr = *reinterpret_cast<const float2 *>(sm.w + w_pair);
-        const float s = rows_sum(row_dot(p, wr.x, wr.y));
-        if (g == 0) sm.v[ti] = s > 0.f ? (float)D * rcp(s) : 1.f;
+      for (int it = 0;;) {
+        // column step: c_j^2 = (1/T) sum_i P_ij / r_i^2
+        float cp[8];
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt)
+          cp[nt] = fmaf(p[4 * nt + 3], v[3],
+                        fmaf(p[4 * nt + 2], v[2], fmaf(p[4 * nt + 1], v[1], p[4 * nt] * v[0])));
+        float c0, c1;
+        col_reduce(cp, c0, c1);
+        float *pb = &sm.part[buf][0][0][0] + (fresh(tid) & 63);
+        {
+          float *own = pb + 128 * (fresh(tid) >> 6);
+          own[0] = c0;
+          own[64] = c1;
+        }
         lds_barrier();
+        float q0[kWaves], q1[kWaves];
+#pragma unroll
+        for (int u = 0; u < kWaves; ++u) {
+          q0[u] = pb[(2 * u) * 64];
+          q1[u] = pb[(2 * u + 1) * 64];
+        }
+        buf ^= 1;
+        cm0 = (((q0[0] + q0[1]) + (q0[2] + q0[3])) + ((q0[4] + q0[5]) + (q0[6] + q0[7]))) *
+              (1.f / T);
+        cm1 = (((q1[0] + q1[1]) + (q1[2] + q1[3])) + ((q1[4] + q1[5]) + (q1[6] + q1[7]))) *
+              (1.f / T);
+        if (++it == a.iters) break;
+        col_gather(cm0 > 0.f ? rcp(cm0) : 1.f, cm1 > 0.f ? rcp(cm1) : 1.f, w);
+        // row step: r_i^2 = (1/D) sum_j P_ij / c_j^2  ->  v_i = 1/r_i^2
+        float s[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e =
+              fmaf(p[12 + r], w[3], fmaf(p[8 + r], w[2], fmaf(p[4 + r], w[1], p[r] * w[0])));
+          const float f =
+              fmaf(p[28 + r], w[7], fmaf(p[24 + r], w[6], fmaf(p[20 + r], w[5], p[16 + r] * w[4])));
+          s[r] = e + f;
+        }
+        const float tot = row_reduce4<false>(s, n);
+        const float vt = tot > 0.f ? (float)D * rcp(tot) : 1.f;
+        v[0] = token_value<0>(vt); v[1] = token_value<1>(vt);
+        v[2] = token_value<2>(vt); v[3] = token_value<3>(vt);
       }
-      // column step: c_j^2 = (1/T) sum_i P_ij / r_i^2  ->  w_j = 1/c_j^2
-      const float2 vr = *reinterpret_cast<const float2 *>(sm.v + CPT * g + 2 * n);
-      float cs = col_dot(sm.pt + pt_at(cj, CPT * g), vr.x, vr.y);
-      cs = rows_sum(cs);
-      if (g == 0) {
-        cm = cs * (1.f / T);
-        sm.w[wpad(cj)] = cm > 0.f ? rcp(cm) : 1.f;
-        if (it + 1 == a.iters) sm.wc[wpad(cj)] = cm > 0.f ? __builtin_amdgcn_rsqf(cm) : 1.f;
-      }
-      lds_barrier();
-    }
-    if (a.iters == 0) {
-      if (tid < D) sm.wc[wpad(fresh(tid))] = 1.f;
-      lds_barrier();
+      col_gather(cm0 > 0.f ? __builtin_amdgcn_rsqf(cm0) : 1.f,
+                 cm1 > 0.f ? __builtin_amdgcn_rsqf(cm1) : 1.f, w);
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) w[nt] = 1.f;
     }
 
     // ---- 4. range step and codes --------------------------------------------
@@ -504,93 +505,104 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
     // the next block start without waiting for this block's stores (vector
     // memory counts retire in order).
     if constexpr (!kF32) __builtin_amdgcn_s_waitcnt(kVmcntZero);
-    if (g == 0) a.col_scale[(bh * nch + chunk) * D + fresh(cj)] = cm > 0.f ? sqrtf(cm) : 1.f;
-    {
-      // y / c, with 1/c shared across the row as 1/c^2 is in the row step
-      const float2 wr = *reinterpret_cast<const float2 *>(sm.wc + w_pair);
-      KVARN_MUL8_BCAST(0, 1, 2, 3, wr.x, wr.y, (y + 0));
-      KVARN_MUL8_BCAST(4, 5, 6, 7, wr.x, wr.y, (y + 8));
-      KVARN_MUL8_BCAST(8, 9, 10, 11, wr.x, wr.y, (y + 16));
-      KVARN_MUL8_BCAST(12, 13, 14, 15, wr.x, wr.y, (y + 24));
+    if (wv == 0) {  // every wave holds the same column scales
+      const int t = fresh(tid);
+      float *cs = a.col_scale + (bh * nch + chunk) * D + 16 * col_tile(t >> 4) + (t & 15);
+      cs[0] = cm0 > 0.f ? sqrtf(cm0) : 1.f;
+      cs[64] = cm1 > 0.f ? sqrtf(cm1) : 1.f;
     }
-    float m = 0.f;
+    float mx[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) m = fmaxf(m, fabsf(y[i]));
-    m = rows_max(m);
-    if (g == 0) a.row_scale[bh * a.capacity + (int64_t)chunk * T + ti] = m * range_factor;
-    const float qs = m > 0.f ? kGrid * rcp(m) : 0.f;
-    // cw[mt] byte r = code of channel 16 mt + 4 g + r
-    uint32_t cw[8];
+    for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      uint32_t c = 0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        c = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(y[4 * mt + r], qs, 1.5f), r, c);
-      cw[mt] = c;
+      for (int r = 0; r < 4; ++r) {
+        y[4 * nt + r] *= w[nt];
+        mx[r] = fmaxf(mx[r], fabsf(y[4 * nt + r]));
+      }
+    const float m = row_reduce4<true>(mx, n);  // token 4 g + tsel(n)
+    if (n < 4) {  // lane t % 16 < 4 of row (t / 16) % 4: token 4 (t / 16) + tsel(t) of the block
+      const int t = fresh(tid);
+      a.row_scale[bh * a.capacity + (int64_t)chunk * T + 4 * (t >> 4) + tsel(t)] = m * range_factor;
     }
+    const float qt = m > 0.f ? kGrid * rcp(m) : 0.f;
+    const float qs[4] = {token_value<0>(qt), token_value<1>(qt), token_value<2>(qt),
+                         token_value<3>(qt)};
 
     uint8_t *cbase = a.codes + (bh * nch + chunk) * CHUNK_BYTES;
     if (a.kind == KVARN_K) {
-      // token-row byte 4 mt + g (channels 16 mt + 4 g + [0, 4)) of every mt;
-      // d0 = bytes of mt 0-3, d1 = mt 4-7. Viewed as 16-bit pieces
-      // P[g][k] = (byte 8 k + g, byte 8 k + 4 + g), lane g must end with
-      // P[0..3][g]: a 4 x 4 transpose across the lanes 16 apart.
+      // kw[r][k] byte i = code of token 4 g + r, channel 16 (4 k + i) + n;
+      // shifted to bit 2 (n % 4) and ORed over the quad it becomes token-row
+      // byte 16 k + 4 i + n / 4 (channels 4 (4 k + i) + n / 4 .. + 4)
+      uint32_t kw[4][2];
+      const int sh = 2 * (fresh(tid) & 3);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          uint32_t c = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            c = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(y[4 * (4 * k + i) + r], qs[r], 1.5f), i, c);
+          c <<= sh;
+          c |= dpp_u<kXor1>(c);
+          kw[r][k] = c | dpp_u<kXor2>(c);
+        }
+      // lane (q = n / 4, s = n % 4) stages token s's two words of quad q
+      const int t = fresh(tid);
+      const int s = t & 3, q = (t >> 2) & 3;
+      uint32_t *ks = &sm.kst[0][0] + 4 * KST_ROW * (t >> 6) + KST_ROW * ((t >> 4) & 3);
+      ks[8 * s + q] = pick4(s, kw[0][0], kw[1][0], kw[2][0], kw[3][0]);
+      ks[8 * s + 4 + q] = pick4(s, kw[0][1], kw[1][1], kw[2][1], kw[3][1]);
+      wave_lds_sync();
+      // lane n takes bytes [8 n, 8 n + 8) of the row of tokens 4 g .. 4 g + 3:
+      // token n / 4 (= q), half k = s / 2, bytes 2 (s % 2) and 2 (s % 2) + 1
+      // of the four quads' words
+      const u32x4 wq = *reinterpret_cast<const u32x4 *>(ks + 8 * q + 4 * (s >> 1));
+      const uint32_t sel = 0x05010400u + 0x02020202u * (uint32_t)(s & 1);
+      const uint32_t t01 = __builtin_amdgcn_perm(wq.y, wq.x, sel);
+      const uint32_t t23 = __builtin_amdgcn_perm(wq.w, wq.z, sel);
+      const u32x2 pk = {__builtin_amdgcn_perm(t23, t01, 0x05040100u),
+                        __builtin_amdgcn_perm(t23, t01, 0x07060302u)};
+      // tokens 16 wv + 4 g + [0, 4) are 128 contiguous bytes from (16 wv + 4 g) * 32
+      *reinterpret_cast<u32x2 *>(cbase + 8 * (t & 511)) = pk;
+    } else {
+      // bt[nt]: the V byte of channel 16 nt + n, tokens 16 wv + 4 g + [0, 4)
+      // (byte column 4 wv + g of the channel row)
       uint32_t bt[8];
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) bt[mt] = __builtin_amdgcn_udot4(cw[mt], kPack4, 0u, false);
-      uint32_t d0 = bt[0] | (bt[1] << 8) | (bt[2] << 16) | (bt[3] << 24);
-      uint32_t d1 = bt[4] | (bt[5] << 8) | (bt[6] << 16) | (bt[7] << 24);
-      // lanes 0-31 trade d0 of lanes 32-63 for their own d1
-      const auto sw = __builtin_amdgcn_permlane32_swap(d0, d1, false, false);
-      d0 = sw[0];
-      d1 = sw[1];
-      // now lane (a = g / 2, b = g % 2) holds P[b][2a, 2a+1] in d0 and
-      // P[2 + b][2a, 2a+1] in d1; the pair (b = 0, 1) trades halves
-      const bool odd = g & 1;
-      const uint32_t lo_h = __builtin_amdgcn_perm(d1, d0, 0x05040100u);  // pieces 2a
-      const uint32_t hi_h = __builtin_amdgcn_perm(d1, d0, 0x07060302u);  // pieces 2a + 1
-      const uint32_t own = odd ? hi_h : lo_h;
-      const uint32_t got = (uint32_t)__shfl_xor((int)(odd ? lo_h : hi_h), 16, 64);
-      const u32x2 pk = {
-          __builtin_amdgcn_perm(got, own, odd ? 0x02060004u : 0x06020400u),
-          __builtin_amdgcn_perm(got, own, odd ? 0x03070105u : 0x07030501u)};
-      *reinterpret_cast<u32x2 *>(cbase + fresh(ti * 32 + 8 * g)) = pk;
-    } else {
-      // four adjacent lanes (tokens 4 q' + [0, 4)) merge their codes into
-      // V bytes: byte r of x[mt] = channel 16 mt + 4 g + r, tokens 4 q'..+3
-      const int sh = 2 * (n & 3);
-      uint32_t x[8];
+      for (int nt = 0; nt < 8; ++nt) {
+        uint32_t c = 0;
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        uint32_t t = cw[mt] << sh;
-        t |= dpp_u<kXor1>(t);
-        x[mt] = t | dpp_u<kXor2>(t);
+        for (int r = 0; r < 4; ++r)
+          c = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(y[4 * nt + r], qs[r], 1.5f), r, c);
+        bt[nt] = __builtin_amdgcn_udot4(c, kPack4, 0u, false);
       }
-      // lane k = n % 4 of each four stages x[k] and x[k + 4]
-      const int k = n & 3;
-      const uint32_t xa = (k & 2) ? ((k & 1) ? x[3] : x[2]) : ((k & 1) ? x[1] : x[0]);
-      const uint32_t xb = (k & 2) ? ((k & 1) ? x[7] : x[6]) : ((k & 1) ? x[5] : x[4]);
-      uint32_t *vs = reinterpret_cast<uint32_t *>(sm.pt);
-      vs[vs_at(k, g, wv, n >> 2)] = xa;
-      vs[vs_at(k + 4, g, wv, n >> 2)] = xb;
-      lds_barrier();
-      if (tid < 256) {
-        // 4 x 4 byte transpose: words = byte columns 4 b0 + [0, 4) of
-        // channels 16 mt + 4 gg + [0, 4) -> one word per channel
-        const int t = fresh(tid);
-        const int b0 = t & 7, gg = (t >> 3) & 3, mt = t >> 5;
-        const u32x4 w = *reinterpret_cast<const u32x4 *>(vs + vs_at(mt, gg, b0, 0));
-        const uint32_t t01l = __builtin_amdgcn_perm(w.y, w.x, 0x05010400u);
-        const uint32_t t01h = __builtin_amdgcn_perm(w.y, w.x, 0x07030602u);
-        const uint32_t t23l = __builtin_amdgcn_perm(w.w, w.z, 0x05010400u);
-        const uint32_t t23h = __builtin_amdgcn_perm(w.w, w.z, 0x07030602u);
-        uint8_t *dst = cbase + (16 * mt + 4 * gg) * 32 + 4 * b0;
-        *reinterpret_cast<uint32_t *>(dst) = __builtin_amdgcn_perm(t23l, t01l, 0x05040100u);
-        *reinterpret_cast<uint32_t *>(dst + 32) = __builtin_amdgcn_perm(t23l, t01l, 0x07060302u);
-        *reinterpret_cast<uint32_t *>(dst + 64) = __builtin_amdgcn_perm(t23h, t01h, 0x05040100u);
-        *reinterpret_cast<uint32_t *>(dst + 96) = __builtin_amdgcn_perm(t23h, t01h, 0x07060302u);
-      }
+      // 4 x 4 byte transposes across the rows g (lanes 16 apart) of
+      // p0 = bytes of tiles 0-3 and p1 = tiles 4-7: lane g ends with the
+      // words of tiles g and 4 + g. Rows g and g ^ 2 (permlane32) trade the
+      // column pair the other keeps, then rows g and g ^ 1 (permlane16) the
+      // column the other keeps.
+      const uint32_t p0 = bt[0] | (bt[1] << 8) | (bt[2] << 16) | (bt[3] << 24);
+      const uint32_t p1 = bt[4] | (bt[5] << 8) | (bt[6] << 16) | (bt[7] << 24);
+      const int t = fresh(tid);
+      const uint32_t hi = (t >> 5) & 1, odd = (t >> 4) & 1;  // g / 2, g % 2
+      const uint32_t k1 = __builtin_amdgcn_perm(p1, p0, 0x05040100u + 0x02020202u * hi);
+      const uint32_t s1 = __builtin_amdgcn_perm(p1, p0, 0x07060302u - 0x02020202u * hi);
+      const auto x1 = __builtin_amdgcn_permlane32_swap(s1, s1, false, false);
+      const uint32_t r1 = hi ? x1[0] : x1[1];
+      const uint32_t k2 = __builtin_amdgcn_perm(r1, k1, 0x06040200u + 0x01010101u * odd);
+      const uint32_t s2 = __builtin_amdgcn_perm(r1, k1, 0x07050301u - 0x01010101u * odd);
+      const auto x2 = __builtin_amdgcn_permlane16_swap(s2, s2, false, false);
+      const uint32_t r2 = odd ? x2[0] : x2[1];
+      // byte rho of the word is row rho's byte: kept (rho = g: byte 0,
+      // rho = g ^ 2: byte 2) or received (rho = g ^ 1: byte 4, g ^ 3: byte 6),
+      // i.e. byte f(rho ^ g) with f = (0, 4, 2, 6)
+      const uint32_t sel = __builtin_amdgcn_perm(
+          0u, 0x06020400u, 0x03020100u ^ (0x01010101u * (uint32_t)((t >> 4) & 3)));
+      uint8_t *dst = cbase + (t & 63) * 32 + 4 * (t >> 6);  // channel 16 g + n, byte column 4 wv
+      *reinterpret_cast<uint32_t *>(dst) = __builtin_amdgcn_perm(r2, k2, sel);
+      *reinterpret_cast<uint32_t *>(dst + 64 * 32) =
+          __builtin_amdgcn_perm(r2, k2, sel + 0x01010101u);
     }
   }
 }
@@ -603,8 +615,8 @@ hipError_t launch_quantize(const QuantArgs &a, hipStream_t s) {
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  // two resident workgroups per CU (LDS- and register-limited); each walks
-  // blocks strided by the grid
+  // two resident workgroups per CU (register-limited); each walks blocks
+  // strided by the grid
   const uint32_t resident = 2u * (uint32_t)(cus > 0 ? cus : 1);
   const uint32_t blocks = a.nblocks < resident ? a.nblocks : resident;
   const bool rot = !(a.flags & KVARN_FLAG_NO_ROTATE);
