@@ -86,11 +86,23 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 //  * kst[wave]: K code staging, rows of KST_ROW words per group of 4 tokens
 //    (word (token r, half k, quad q) at KST_ROW g + 8 r + 4 k + q; the
 //    36-word rows put the two 16-lane rows of a half-wave on disjoint
-//    banks).
+//    banks);
+//  * vst[buffer]: V code staging, word (channel j, wave w) at VST_ROW j + w
+//    (9-word rows: the 32 channels of a half-wave's write fall on distinct
+//    banks); two buffers alternated by V block, so that one barrier per
+//    block orders the writes before the reads and the reads before the
+//    buffer's next writes.
+//  * wgat[wave]: the wave's own copy of a per-channel value (1/c^2, then
+//    1/c), written by lane (n, g) for its two channels and read back by
+//    every lane for channels 16 nt + n: a wave-local LDS round trip in place
+//    of lane exchanges.
 constexpr int KST_ROW = 36;
+constexpr int VST_ROW = 9;
 struct QuantSmem {
   alignas(16) float part[2][kWaves][2][64];
+  alignas(16) float wgat[kWaves][D];
   alignas(16) uint32_t kst[kWaves][4 * KST_ROW];
+  alignas(16) uint32_t vst[2][D * VST_ROW];
   alignas(16) u32x4 hop[2][64];  // rotation operands of each lane
 };
 
@@ -117,9 +129,12 @@ constexpr int kXor2 = 0x4E;   // quad_perm [2,3,0,1]
 constexpr int kRor4 = 0x124;  // row_ror:4, lane i of a row reads lane (i + 4) % 16
 constexpr int kRor8 = 0x128;  // row_ror:8
 
+// kMax: maxima of non-negative values, taken on their bit patterns (the
+// order of non-negative floats is that of their patterns as unsigned
+// integers), which needs no NaN canonicalization and folds the DPP operand.
 template <bool kMax>
 __device__ __forceinline__ float combine(float a, float b) {
-  if constexpr (kMax) return fmaxf(a, b);
+  if constexpr (kMax) return __uint_as_float(max(__float_as_uint(a), __float_as_uint(b)));
   else return a + b;
 }
 
@@ -149,6 +164,8 @@ __device__ __forceinline__ float token_value(float x) {
   return dpp_f<l * 0x55>(x);  // quad_perm [l, l, l, l]
 }
 
+__device__ __forceinline__ int col_tile(int g) { return 2 * (g & 1) + (g >> 1); }
+
 // Column step, reduce: cp[nt] (channel 16 nt + n over the lane's 4 tokens)
 // summed over the wave's four 16-lane rows. The permlane32 swaps pair rows
 // g and g + 2 for tiles (2k, 2k + 1), the permlane16 swaps rows g and g + 1;
@@ -169,21 +186,24 @@ __device__ __forceinline__ void col_reduce(const float (&cp)[8], float &c0, floa
   c0 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
   c1 = __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
-__device__ __forceinline__ int col_tile(int g) { return 2 * (g & 1) + (g >> 1); }
-// Column step, gather: the inverse movement; every lane receives the values
-// of channels 16 nt + n for nt = 0..7 in out[nt].
-__device__ __forceinline__ void col_gather(float c0, float c1, float (&out)[8]) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(c0), __float_as_uint(c0), false,
-                                                  false);
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(c1), __float_as_uint(c1), false,
-                                                  false);
-  const uint32_t h[4] = {a[0], a[1], b[0], b[1]};
+// LDS accesses of the wave complete and are visible to its other lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | 0xF | (0x3 << 14));  // lgkmcnt(0) only
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Column step, gather: every lane receives the values of channels 16 nt + n
+// (nt = 0..7) in out[nt], through the wave's own LDS copy wg (channel j at
+// wg[j]); c0, c1 are the lane's channels 16 A(g) + n and 16 (A(g) + 4) + n.
+__device__ __forceinline__ void col_gather(float *wg, int t, float c0, float c1, float (&out)[8]) {
+  const int n = t & 15, g = (t >> 4) & 3;
+  wg[16 * col_tile(g) + n] = c0;
+  wg[16 * (col_tile(g) + 4) + n] = c1;
+  wave_lds_sync();
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const auto s = __builtin_amdgcn_permlane32_swap(h[k], h[k], false, false);
-    out[2 * k] = __uint_as_float(s[0]);
-    out[2 * k + 1] = __uint_as_float(s[1]);
-  }
+  for (int nt = 0; nt < 8; ++nt) out[nt] = wg[16 * nt + n];
 }
 
 __device__ __forceinline__ f32x4 mfma_bf16(const u32x4 &a, const u32x4 &b, const f32x4 &c) {
@@ -270,14 +290,6 @@ __device__ __forceinline__ void split_bf16x3(const f32x4 &a, const f32x4 &b, u32
     mid[q] = __builtin_amdgcn_perm(um[2 * q + 1], um[2 * q], 0x07060302u);
     lo[q] = __builtin_amdgcn_perm(ul[2 * q + 1], ul[2 * q], 0x07060302u);
   }
-}
-
-// LDS accesses of the wave complete and are visible to its other lanes.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_s_waitcnt((0x7 << 4) | 0xF | (0x3 << 14));  // lgkmcnt(0) only
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 struct BlockIdx {
@@ -371,7 +383,8 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
     rotate_step<kRotate, 3>(acc, x[3], hp);
   };
 
-  int buf = 0;  // partial-sum buffer of the next column step
+  int buf = 0;   // partial-sum buffer of the next column step
+  int vbuf = 0;  // V staging buffer of the next V block
   for (; blk < a.nblocks; blk += gridDim.x) {
     const BlockIdx bi = split_block(a, blk);
     const int64_t bh = bi.bh;
@@ -423,7 +436,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
 
     // ---- 3. dual scaling ---------------------------------------------------
     float w[8];                  // 1/c^2 of channels 16 nt + n; 1/c after the last column step
-    float cm0 = 1.f, cm1 = 1.f;  // c^2 of the lane's two column-step channels
+    float cm0 = 1.f, cm1 = 1.f;  // c^2 of the lane's two column-step channels, then c
     if (a.iters > 0) {
       float v[4];  // 1/r^2 of the lane's tokens
       {
@@ -476,7 +489,11 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
         cm1 = (((q1[0] + q1[1]) + (q1[2] + q1[3])) + ((q1[4] + q1[5]) + (q1[6] + q1[7]))) *
               (1.f / T);
         if (++it == a.iters) break;
-        col_gather(cm0 > 0.f ? rcp(cm0) : 1.f, cm1 > 0.f ? rcp(cm1) : 1.f, w);
+        {
+          const int t = fresh(tid);
+          col_gather(&sm.wgat[t >> 6][0], t, cm0 > 0.f ? rcp(cm0) : 1.f, cm1 > 0.f ? rcp(cm1) : 1.f,
+                     w);
+        }
         // row step: r_i^2 = (1/D) sum_j P_ij / c_j^2  ->  v_i = 1/r_i^2
         float s[4];
 #pragma unroll
@@ -492,8 +509,12 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
         v[0] = token_value<0>(vt); v[1] = token_value<1>(vt);
         v[2] = token_value<2>(vt); v[3] = token_value<3>(vt);
       }
-      col_gather(cm0 > 0.f ? __builtin_amdgcn_rsqf(cm0) : 1.f,
-                 cm1 > 0.f ? __builtin_amdgcn_rsqf(cm1) : 1.f, w);
+      const int t = fresh(tid);
+      const float i0 = cm0 > 0.f ? __builtin_amdgcn_rsqf(cm0) : 1.f;
+      const float i1 = cm1 > 0.f ? __builtin_amdgcn_rsqf(cm1) : 1.f;
+      col_gather(&sm.wgat[t >> 6][0], t, i0, i1, w);
+      cm0 = cm0 > 0.f ? cm0 * i0 : 1.f;  // c = c^2 / sqrt(c^2)
+      cm1 = cm1 > 0.f ? cm1 * i1 : 1.f;
     } else {
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) w[nt] = 1.f;
@@ -508,8 +529,8 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
     if (wv == 0) {  // every wave holds the same column scales
       const int t = fresh(tid);
       float *cs = a.col_scale + (bh * nch + chunk) * D + 16 * col_tile(t >> 4) + (t & 15);
-      cs[0] = cm0 > 0.f ? sqrtf(cm0) : 1.f;
-      cs[64] = cm1 > 0.f ? sqrtf(cm1) : 1.f;
+      cs[0] = cm0;
+      cs[64] = cm1;
     }
     float mx[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -547,12 +568,16 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
           c |= dpp_u<kXor1>(c);
           kw[r][k] = c | dpp_u<kXor2>(c);
         }
-      // lane (q = n / 4, s = n % 4) stages token s's two words of quad q
+      // the four lanes of quad q hold the same words: each writes all eight
+      // (token r, half k) words of the quad (equal values to equal addresses)
       const int t = fresh(tid);
       const int s = t & 3, q = (t >> 2) & 3;
       uint32_t *ks = &sm.kst[0][0] + 4 * KST_ROW * (t >> 6) + KST_ROW * ((t >> 4) & 3);
-      ks[8 * s + q] = pick4(s, kw[0][0], kw[1][0], kw[2][0], kw[3][0]);
-      ks[8 * s + 4 + q] = pick4(s, kw[0][1], kw[1][1], kw[2][1], kw[3][1]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        ks[8 * r + q] = kw[r][0];
+        ks[8 * r + 4 + q] = kw[r][1];
+      }
       wave_lds_sync();
       // lane n takes bytes [8 n, 8 n + 8) of the row of tokens 4 g .. 4 g + 3:
       // token n / 4 (= q), half k = s / 2, bytes 2 (s % 2) and 2 (s % 2) + 1
@@ -599,10 +624,20 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
       // i.e. byte f(rho ^ g) with f = (0, 4, 2, 6)
       const uint32_t sel = __builtin_amdgcn_perm(
           0u, 0x06020400u, 0x03020100u ^ (0x01010101u * (uint32_t)((t >> 4) & 3)));
-      uint8_t *dst = cbase + (t & 63) * 32 + 4 * (t >> 6);  // channel 16 g + n, byte column 4 wv
-      *reinterpret_cast<uint32_t *>(dst) = __builtin_amdgcn_perm(r2, k2, sel);
-      *reinterpret_cast<uint32_t *>(dst + 64 * 32) =
-          __builtin_amdgcn_perm(r2, k2, sel + 0x01010101u);
+      // the words of channels 16 g + n (= t % 64) and 64 + 16 g + n, byte
+      // column 4 wv, go through LDS so that the block leaves as 4 KB of
+      // contiguous 8-byte stores
+      uint32_t *vs = &sm.vst[vbuf][0];
+      vs[VST_ROW * (t & 63) + (t >> 6)] = __builtin_amdgcn_perm(r2, k2, sel);
+      vs[VST_ROW * ((t & 63) + 64) + (t >> 6)] = __builtin_amdgcn_perm(r2, k2, sel + 0x01010101u);
+      vbuf ^= 1;
+      lds_barrier();
+      // thread u: channel u / 4, byte columns 8 (u % 4) + [0, 8) = the words
+      // of waves 2 (u % 4) and 2 (u % 4) + 1; channel row j starts at 32 j
+      const int u = fresh(tid);
+      const uint32_t *src = vs + VST_ROW * (u >> 2) + 2 * (u & 3);
+      const u32x2 word = {src[0], src[1]};
+      *reinterpret_cast<u32x2 *>(cbase + 8 * u) = word;
     }
   }
 }
