@@ -470,12 +470,10 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
                         fmaf(p[4 * nt + 2], v[2], fmaf(p[4 * nt + 1], v[1], p[4 * nt] * v[0])));
         float c0, c1;
         col_reduce(cp, c0, c1);
-        float *pb = &sm.part[buf][0][0][0] + (fresh(tid) & 63);
-        {
-          float *own = pb + 128 * (fresh(tid) >> 6);
-          own[0] = c0;
-          own[64] = c1;
-        }
+        // (lane-dependent offsets kept in registers across the block loop)
+        float *pb = &sm.part[buf][0][0][0] + lane;
+        pb[128 * wv] = c0;
+        pb[128 * wv + 64] = c1;
         lds_barrier();
         float q0[kWaves], q1[kWaves];
 #pragma unroll
@@ -489,11 +487,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
         cm1 = (((q1[0] + q1[1]) + (q1[2] + q1[3])) + ((q1[4] + q1[5]) + (q1[6] + q1[7]))) *
               (1.f / T);
         if (++it == a.iters) break;
-        {
-          const int t = fresh(tid);
-          col_gather(&sm.wgat[t >> 6][0], t, cm0 > 0.f ? rcp(cm0) : 1.f, cm1 > 0.f ? rcp(cm1) : 1.f,
-                     w);
-        }
+        col_gather(&sm.wgat[wv][0], tid, cm0 > 0.f ? rcp(cm0) : 1.f, cm1 > 0.f ? rcp(cm1) : 1.f, w);
         // row step: r_i^2 = (1/D) sum_j P_ij / c_j^2  ->  v_i = 1/r_i^2
         float s[4];
 #pragma unroll
@@ -509,10 +503,9 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
         v[0] = token_value<0>(vt); v[1] = token_value<1>(vt);
         v[2] = token_value<2>(vt); v[3] = token_value<3>(vt);
       }
-      const int t = fresh(tid);
       const float i0 = cm0 > 0.f ? __builtin_amdgcn_rsqf(cm0) : 1.f;
       const float i1 = cm1 > 0.f ? __builtin_amdgcn_rsqf(cm1) : 1.f;
-      col_gather(&sm.wgat[t >> 6][0], t, i0, i1, w);
+      col_gather(&sm.wgat[wv][0], tid, i0, i1, w);
       cm0 = cm0 > 0.f ? cm0 * i0 : 1.f;  // c = c^2 / sqrt(c^2)
       cm1 = cm1 > 0.f ? cm1 * i1 : 1.f;
     } else {
