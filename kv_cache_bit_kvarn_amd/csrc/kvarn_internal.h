@@ -33,6 +33,8 @@ __device__ __forceinline__ float dpp_xor1(float v) {
 
 // s_waitcnt operand on gfx9: vmcnt(0), expcnt and lgkmcnt left at their maxima
 constexpr int kVmcntZero = (0x7 << 4) | (0xF << 8);
+// vmcnt(2), expcnt and lgkmcnt left at their maxima
+constexpr int kVmcntTwo = 2 | (0x7 << 4) | (0xF << 8);
 
 // Workgroup barrier for LDS traffic only: the wave's LDS accesses complete
 // (lgkmcnt(0)), then s_barrier. Unlike __syncthreads() it does not wait for

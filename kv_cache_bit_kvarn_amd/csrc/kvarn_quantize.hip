@@ -104,6 +104,10 @@ struct QuantSmem {
   alignas(16) uint32_t kst[kWaves][4 * KST_ROW];
   alignas(16) uint32_t vst[2][D * VST_ROW];
   alignas(16) u32x4 hop[2][64];  // rotation operands of each lane
+  // bf16 input two blocks ahead, streamed by the wave straight into its own
+  // slice (piece kk of lane l at xin[wave][kk][l], the order the direct
+  // global-to-LDS load writes in)
+  alignas(16) u32x4 xin[kWaves][4][64];
 };
 
 __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
@@ -317,6 +321,19 @@ __device__ __forceinline__ void load_bf16_block(const QuantArgs &a, const BlockI
   for (int kk = 0; kk < 4; ++kk) xr[kk] = __builtin_nontemporal_load(src + 4 * kk);
 }
 
+// The same pieces as load_bf16_block, copied by the memory system straight
+// into the wave's LDS slice (global_load_lds_dwordx4: lane l's 16 bytes land
+// at slice[kk][l]); counted by vmcnt like any load.
+__device__ __forceinline__ void prefetch_bf16_block_lds(const QuantArgs &a, const BlockIdx &bi,
+                                                        int ti, int g, u32x4 (*slice)[64]) {
+  const u32x4 *src =
+      reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.x) + x_offset(a, bi, ti)) + g;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    __builtin_amdgcn_global_load_lds(src + 4 * kk,
+                                     (__attribute__((address_space(3))) void *)&slice[kk][0], 16, 0, 0);
+}
+
 // One of four values chosen by a lane index i < 4.
 __device__ __forceinline__ uint32_t pick4(int i, uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3) {
   return (i & 2) ? ((i & 1) ? v3 : v2) : ((i & 1) ? v1 : v0);
@@ -348,12 +365,18 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
   }
   lds_barrier();
 
-  u32x4 xn[4];  // next block's bf16 input
+  // bf16 input: the block being started is in xn (registers); the next one
+  // is in the wave's LDS slice xin[wv] or on its way there
+  u32x4 xn[4];
   uint32_t blk = blockIdx.x;
   if constexpr (!kF32) {
-    if (blk < a.nblocks) load_bf16_block(a, split_block(a, blk), ti, g, xn);
-    // Waited for here once, so that the loop head does not merge a pending
-    // first load into every block's wait.
+    if (blk < a.nblocks) {
+      load_bf16_block(a, split_block(a, blk), ti, g, xn);
+      prefetch_bf16_block_lds(a, split_block(a, min(blk + gridDim.x, a.nblocks - 1)), ti, g,
+                              sm.xin[wv]);
+    }
+    // waited for here once, so that the loop head does not merge the first
+    // loads into every block's wait
     __builtin_amdgcn_s_waitcnt(kVmcntZero);
   }
   auto rotate_f32 = [&](const BlockIdx &bi, f32x4 (&acc)[8]) {  // three bf16 terms per piece
@@ -413,10 +436,21 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
         // operand registers, lands in lane (n, g = n / 4), register n % 4
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) gram = mfma_bf16(xn[kk], xn[kk], gram);
-        // next block's input, in flight during the whole block (the LDS-only
-        // barriers below do not wait for it)
-        const uint32_t nb = min(blk + gridDim.x, a.nblocks - 1);
-        load_bf16_block(a, split_block(a, nb), ti, g, xn);
+        // next block's input from the LDS slice into xn, then the block after
+        // it into the slice: in flight during this whole block and the next
+        // one's rotation (the LDS-only barriers below do not wait for it).
+        // The slice's load was issued one block ago; every block issues at
+        // least two stores after it (its codes and its row scales, or it
+        // waits for everything when it skips), and vector memory counts
+        // retire in order, so vmcnt(2) means the load has landed while the
+        // last block's stores may still be in flight. The slice is the wave's
+        // own: LDS ordering within the wave is all that is needed after that.
+        __builtin_amdgcn_s_waitcnt(kVmcntTwo);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) xn[kk] = sm.xin[wv][kk][lane];
+        __builtin_amdgcn_s_waitcnt((0x7 << 4) | 0xF | (0x3 << 14));  // lgkmcnt(0): reads done
+        const uint32_t nb = min(blk + 2 * gridDim.x, a.nblocks - 1);
+        prefetch_bf16_block_lds(a, split_block(a, nb), ti, g, sm.xin[wv]);
       }
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
@@ -514,11 +548,6 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
     }
 
     // ---- 4. range step and codes --------------------------------------------
-    // Only the next block's input is in flight here, and it has had the whole
-    // balancing to arrive: waiting now, before this block's first store, lets
-    // the next block start without waiting for this block's stores (vector
-    // memory counts retire in order).
-    if constexpr (!kF32) __builtin_amdgcn_s_waitcnt(kVmcntZero);
     if (wv == 0) {  // every wave holds the same column scales
       const int t = fresh(tid);
       float *cs = a.col_scale + (bh * nch + chunk) * D + 16 * col_tile(t >> 4) + (t & 15);
@@ -633,6 +662,9 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
       *reinterpret_cast<u32x2 *>(cbase + 8 * u) = word;
     }
   }
+  // the last prefetch into the LDS slice lands before the workgroup (and its
+  // LDS) goes away
+  if constexpr (!kF32) __builtin_amdgcn_s_waitcnt(kVmcntZero);
 }
 
 }  // namespace
