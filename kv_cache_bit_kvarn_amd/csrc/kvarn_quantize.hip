@@ -103,7 +103,7 @@ struct QuantSmem {
   alignas(16) float wgat[kWaves][D];
   alignas(16) uint32_t kst[kWaves][4 * KST_ROW];
   alignas(16) uint32_t vst[2][D * VST_ROW];
-  alignas(16) u32x4 hop[2][64];  // rotation operands of each lane
+  alignas(16) u32x4 hop[4][64];  // rotation operands of each lane (2, 3: negated)
   // bf16 input two blocks ahead, streamed by the wave straight into its own
   // slice (piece kk of lane l at xin[wave][kk][l], the order the direct
   // global-to-LDS load writes in)
@@ -258,16 +258,16 @@ __device__ __forceinline__ u32x4 identity_operand(int lane, int p) {
 
 // acc[nt] += x (input channels 32 kk + [0, 32) of the wave's 16 tokens) times
 // tile (kk, nt) of the rotation. A Hadamard tile with a negative sign takes
-// the negated x (sign bits flipped) against the same operand; the identity
-// has one tile per output tile, at kk = nt / 2.
+// the negated operand hp[2 + nt % 2] (kept in LDS next to the positive ones,
+// so that no sign flips cost vector instructions); the identity has one tile
+// per output tile, at kk = nt / 2.
 template <bool kRotate, int KK>
-__device__ __forceinline__ void rotate_step(f32x4 (&acc)[8], const u32x4 &x, const u32x4 (&hp)[2]) {
+__device__ __forceinline__ void rotate_step(f32x4 (&acc)[8], const u32x4 &x, const u32x4 (&hp)[4]) {
   if constexpr (kRotate) {
-    const u32x4 nx = x ^ 0x80008000u;
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
       const bool neg = __builtin_popcount((nt >> 1) & KK) & 1;
-      acc[nt] = mfma_bf16(neg ? nx : x, hp[nt & 1], acc[nt]);
+      acc[nt] = mfma_bf16(x, hp[(neg ? 2 : 0) + (nt & 1)], acc[nt]);
     }
   } else {
     acc[2 * KK] = mfma_bf16(x, hp[0], acc[2 * KK]);
@@ -360,8 +360,11 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
   // P and the next block's input through the balancing)
   if (tid < 64) {
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
-      sm.hop[p][lane] = kRotate ? hadamard_operand(lane, p) : identity_operand(lane, p);
+    for (int p = 0; p < 2; ++p) {
+      const u32x4 h = kRotate ? hadamard_operand(lane, p) : identity_operand(lane, p);
+      sm.hop[p][lane] = h;
+      sm.hop[2 + p][lane] = h ^ 0x80008000u;  // bf16 sign bits flipped
+    }
   }
   lds_barrier();
 
@@ -380,7 +383,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
     __builtin_amdgcn_s_waitcnt(kVmcntZero);
   }
   auto rotate_f32 = [&](const BlockIdx &bi, f32x4 (&acc)[8]) {  // three bf16 terms per piece
-    const u32x4 hp[2] = {sm.hop[0][lane], sm.hop[1][lane]};
+    const u32x4 hp[4] = {sm.hop[0][lane], sm.hop[1][lane], sm.hop[2][lane], sm.hop[3][lane]};
     const f32x4 *src =
         reinterpret_cast<const f32x4 *>(static_cast<const float *>(a.x) + x_offset(a, bi, ti)) +
         2 * g;
@@ -399,7 +402,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
 #undef KVARN_ROTATE_F32
   };
   auto rotate_bf16 = [&](const u32x4 (&x)[4], f32x4 (&acc)[8]) {
-    const u32x4 hp[2] = {sm.hop[0][lane], sm.hop[1][lane]};
+    const u32x4 hp[4] = {sm.hop[0][lane], sm.hop[1][lane], sm.hop[2][lane], sm.hop[3][lane]};
     rotate_step<kRotate, 0>(acc, x[0], hp);
     rotate_step<kRotate, 1>(acc, x[1], hp);
     rotate_step<kRotate, 2>(acc, x[2], hp);
