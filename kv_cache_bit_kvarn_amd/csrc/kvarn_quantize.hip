@@ -71,6 +71,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int CPT = 32;                        // values per lane: 4 tokens x 8 channels
 constexpr float kGrid = 1.9999980926513672f;  // 2 (1 - 2^-20)
 constexpr uint32_t kPack4 = 0x40100401u;       // byte weights 1, 4, 16, 64
+constexpr float kTiny = 1.17549435e-38f;       // smallest normal fp32
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -475,9 +476,16 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
     float w[8];                  // 1/c^2 of channels 16 nt + n; 1/c after the last column step
     float cm0 = 1.f, cm1 = 1.f;  // c^2 of the lane's two column-step channels, then c
     if (a.iters > 0) {
-      float v[4];  // 1/r^2 of the lane's tokens
+      // v_i = 1 / (T r_i^2) of the lane's tokens. With D = T the row step's
+      // 1/D and the column step's 1/T cancel: v_i = 1 / sum_j P_ij / c_j^2,
+      // and the column step's weighted sum is c_j^2 itself. A zero row or
+      // column (all its P are 0) takes the reciprocal of the smallest normal
+      // number instead of 1: its products are 0 either way, and its stored
+      // scales are set below.
+      static_assert(D == T, "the row and column normalizations cancel only for square blocks");
+      float v[4];
       {
-        // first row step (c = 1): v_i = 1 / r_i^2 = D / sum_j P_ij
+        // first row step (c = 1): v_i = 1 / sum_j P_ij
         float tot;
         if constexpr (kF32) {
           float s[4];
@@ -494,12 +502,12 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
           const int src = 20 * ((t >> 4) & 3) + tsel(t);
           tot = (kRotate ? (float)D : 1.f) * __shfl(d, src, 64);
         }
-        const float vt = tot > 0.f ? (float)D * rcp(tot) : 1.f;
+        const float vt = rcp(fmaxf(tot, kTiny));
         v[0] = token_value<0>(vt); v[1] = token_value<1>(vt);
         v[2] = token_value<2>(vt); v[3] = token_value<3>(vt);
       }
       for (int it = 0;;) {
-        // column step: c_j^2 = (1/T) sum_i P_ij / r_i^2
+        // column step: c_j^2 = (1/T) sum_i P_ij / r_i^2 = sum_i P_ij v_i
         float cp[8];
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt)
@@ -519,24 +527,21 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
           q1[u] = pb[(2 * u + 1) * 64];
         }
         buf ^= 1;
-        cm0 = (((q0[0] + q0[1]) + (q0[2] + q0[3])) + ((q0[4] + q0[5]) + (q0[6] + q0[7]))) *
-              (1.f / T);
-        cm1 = (((q1[0] + q1[1]) + (q1[2] + q1[3])) + ((q1[4] + q1[5]) + (q1[6] + q1[7]))) *
-              (1.f / T);
+        cm0 = ((q0[0] + q0[1]) + (q0[2] + q0[3])) + ((q0[4] + q0[5]) + (q0[6] + q0[7]));
+        cm1 = ((q1[0] + q1[1]) + (q1[2] + q1[3])) + ((q1[4] + q1[5]) + (q1[6] + q1[7]));
         if (++it == a.iters) break;
-        col_gather(&sm.wgat[wv][0], tid, cm0 > 0.f ? rcp(cm0) : 1.f, cm1 > 0.f ? rcp(cm1) : 1.f, w);
-        // row step: r_i^2 = (1/D) sum_j P_ij / c_j^2  ->  v_i = 1/r_i^2
+        col_gather(&sm.wgat[wv][0], tid, rcp(fmaxf(cm0, kTiny)), rcp(fmaxf(cm1, kTiny)), w);
+        // row step: r_i^2 = (1/D) sum_j P_ij / c_j^2  ->  v_i = 1 / sum_j P_ij / c_j^2
         float s[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float e =
-              fmaf(p[12 + r], w[3], fmaf(p[8 + r], w[2], fmaf(p[4 + r], w[1], p[r] * w[0])));
-          const float f =
-              fmaf(p[28 + r], w[7], fmaf(p[24 + r], w[6], fmaf(p[20 + r], w[5], p[16 + r] * w[4])));
-          s[r] = e + f;
+          float e = p[r] * w[0];
+#pragma unroll
+          for (int nt = 1; nt < 8; ++nt) e = fmaf(p[4 * nt + r], w[nt], e);
+          s[r] = e;
         }
         const float tot = row_reduce4<false>(s, n);
-        const float vt = tot > 0.f ? (float)D * rcp(tot) : 1.f;
+        const float vt = rcp(fmaxf(tot, kTiny));
         v[0] = token_value<0>(vt); v[1] = token_value<1>(vt);
         v[2] = token_value<2>(vt); v[3] = token_value<3>(vt);
       }
