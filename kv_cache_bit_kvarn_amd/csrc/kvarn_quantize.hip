@@ -79,11 +79,15 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // dword address taken modulo 32 as its bank; a ds_read_b32 pair
 // (ds_read2st64) of consecutive lanes reads consecutive dwords. Both areas
 // below are free of bank conflicts under that model:
-//  * part[buffer][wave][k][lane]: the column step's per-wave partial sums
-//    (lane (n, g) holds channels 16 A(g) + n and 16 (A(g) + 4) + n for
-//    k = 0, 1, the same in every wave); two buffers, alternated from one
-//    column step to the next, so a step's writes never meet the previous
-//    step's reads without a second barrier;
+//  * cpart: the column step's partial sums, cp[nt] of lane l of wave u at
+//    cpart[CP_PLANE nt + CP_WAVE u + l]. A wave's write of one nt covers 64
+//    consecutive words; a reading lane (n, g) of wave w takes plane w, waves
+//    2 g and 2 g + 1, rows r, at CP_PLANE w + CP_WAVE (2 g + s) + 16 r + n,
+//    and the 72-word wave stride puts the four lane rows 144 words (16 banks)
+//    apart, so neither side has bank conflicts;
+//  * ctot: the per-channel result of a column step (1/c^2, and 1/c after the
+//    last one), written by the wave that reduced the channel and read by
+//    every lane for channels 16 nt + n;
 //  * kst[wave]: K code staging, rows of KST_ROW words per group of 4 tokens
 //    (word (token r, half k, quad q) at KST_ROW g + 8 r + 4 k + q; the
 //    36-word rows put the two 16-lane rows of a half-wave on disjoint
@@ -93,15 +97,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 //    banks); two buffers alternated by V block, so that one barrier per
 //    block orders the writes before the reads and the reads before the
 //    buffer's next writes.
-//  * wgat[wave]: the wave's own copy of a per-channel value (1/c^2, then
-//    1/c), written by lane (n, g) for its two channels and read back by
-//    every lane for channels 16 nt + n: a wave-local LDS round trip in place
-//    of lane exchanges.
 constexpr int KST_ROW = 36;
 constexpr int VST_ROW = 9;
+constexpr int CP_WAVE = 72;
+constexpr int CP_PLANE = kWaves * CP_WAVE;
 struct QuantSmem {
-  alignas(16) float part[2][kWaves][2][64];
-  alignas(16) float wgat[kWaves][D];
+  alignas(16) float cpart[8 * CP_PLANE];
+  alignas(16) float ctot[D];
   alignas(16) uint32_t kst[kWaves][4 * KST_ROW];
   alignas(16) uint32_t vst[2][D * VST_ROW];
   alignas(16) u32x4 hop[4][64];  // rotation operands of each lane (2, 3: negated)
@@ -169,27 +171,16 @@ __device__ __forceinline__ float token_value(float x) {
   return dpp_f<l * 0x55>(x);  // quad_perm [l, l, l, l]
 }
 
-__device__ __forceinline__ int col_tile(int g) { return 2 * (g & 1) + (g >> 1); }
-
-// Column step, reduce: cp[nt] (channel 16 nt + n over the lane's 4 tokens)
-// summed over the wave's four 16-lane rows. The permlane32 swaps pair rows
-// g and g + 2 for tiles (2k, 2k + 1), the permlane16 swaps rows g and g + 1;
-// lane (n, g) ends with channels 16 A(g) + n (c0) and 16 (A(g) + 4) + n (c1),
-// A(g) = 2 (g % 2) + g / 2.
-__device__ __forceinline__ void col_reduce(const float (&cp)[8], float &c0, float &c1) {
-  float z[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(cp[2 * k]),
-                                                    __float_as_uint(cp[2 * k + 1]), false, false);
-    z[k] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
-  }
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(z[0]), __float_as_uint(z[1]),
-                                                  false, false);
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(z[2]), __float_as_uint(z[3]),
-                                                  false, false);
-  c0 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  c1 = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+// Sum over the four 16-lane rows of a wave, in every lane: permlane32 swaps
+// of the value with itself add rows g and g + 2, permlane16 swaps then add
+// rows g and g + 1.
+__device__ __forceinline__ float sum_rows(float h) {
+  const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(h), __float_as_uint(h), false,
+                                                  false);
+  h = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+  const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(h), __float_as_uint(h), false,
+                                                  false);
+  return __uint_as_float(y[0]) + __uint_as_float(y[1]);
 }
 // LDS accesses of the wave complete and are visible to its other lanes.
 __device__ __forceinline__ void wave_lds_sync() {
@@ -197,18 +188,6 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_s_waitcnt((0x7 << 4) | 0xF | (0x3 << 14));  // lgkmcnt(0) only
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Column step, gather: every lane receives the values of channels 16 nt + n
-// (nt = 0..7) in out[nt], through the wave's own LDS copy wg (channel j at
-// wg[j]); c0, c1 are the lane's channels 16 A(g) + n and 16 (A(g) + 4) + n.
-__device__ __forceinline__ void col_gather(float *wg, int t, float c0, float c1, float (&out)[8]) {
-  const int n = t & 15, g = (t >> 4) & 3;
-  wg[16 * col_tile(g) + n] = c0;
-  wg[16 * (col_tile(g) + 4) + n] = c1;
-  wave_lds_sync();
-#pragma unroll
-  for (int nt = 0; nt < 8; ++nt) out[nt] = wg[16 * nt + n];
 }
 
 __device__ __forceinline__ f32x4 mfma_bf16(const u32x4 &a, const u32x4 &b, const f32x4 &c) {
@@ -410,7 +389,6 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
     rotate_step<kRotate, 3>(acc, x[3], hp);
   };
 
-  int buf = 0;   // partial-sum buffer of the next column step
   int vbuf = 0;  // V staging buffer of the next V block
   for (; blk < a.nblocks; blk += gridDim.x) {
     const BlockIdx bi = split_block(a, blk);
@@ -474,7 +452,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
 
     // ---- 3. dual scaling ---------------------------------------------------
     float w[8];                  // 1/c^2 of channels 16 nt + n; 1/c after the last column step
-    float cm0 = 1.f, cm1 = 1.f;  // c^2 of the lane's two column-step channels, then c
+    float cm = 1.f;  // c^2 of channel 16 wv + n after a column step, then c
     if (a.iters > 0) {
       // v_i = 1 / (T r_i^2) of the lane's tokens. With D = T the row step's
       // 1/D and the column step's 1/T cancel: v_i = 1 / sum_j P_ij / c_j^2,
@@ -507,30 +485,40 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
         v[2] = token_value<2>(vt); v[3] = token_value<3>(vt);
       }
       for (int it = 0;;) {
-        // column step: c_j^2 = (1/T) sum_i P_ij / r_i^2 = sum_i P_ij v_i
+        // column step: c_j^2 = (1/T) sum_i P_ij / r_i^2 = sum_i P_ij v_i. The
+        // lane's 8 partial sums (its 4 tokens of channels 16 nt + n) go to
+        // LDS; wave w then adds up channel 16 w + n: lane (n, g) takes waves
+        // 2 g and 2 g + 1, all four rows, and the lane rows meet by swaps.
         float cp[8];
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt)
           cp[nt] = fmaf(p[4 * nt + 3], v[3],
                         fmaf(p[4 * nt + 2], v[2], fmaf(p[4 * nt + 1], v[1], p[4 * nt] * v[0])));
-        float c0, c1;
-        col_reduce(cp, c0, c1);
-        // (lane-dependent offsets kept in registers across the block loop)
-        float *pb = &sm.part[buf][0][0][0] + lane;
-        pb[128 * wv] = c0;
-        pb[128 * wv + 64] = c1;
-        lds_barrier();
-        float q0[kWaves], q1[kWaves];
+        {
+          float *pw = sm.cpart + CP_WAVE * wv + lane;
 #pragma unroll
-        for (int u = 0; u < kWaves; ++u) {
-          q0[u] = pb[(2 * u) * 64];
-          q1[u] = pb[(2 * u + 1) * 64];
+          for (int nt = 0; nt < 8; ++nt) pw[CP_PLANE * nt] = cp[nt];
         }
-        buf ^= 1;
-        cm0 = ((q0[0] + q0[1]) + (q0[2] + q0[3])) + ((q0[4] + q0[5]) + (q0[6] + q0[7]));
-        cm1 = ((q1[0] + q1[1]) + (q1[2] + q1[3])) + ((q1[4] + q1[5]) + (q1[6] + q1[7]));
+        lds_barrier();
+        {
+          const float *pr = sm.cpart + CP_PLANE * wv + 2 * CP_WAVE * g + n;
+          float q[8];
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) q[4 * u + r] = pr[CP_WAVE * u + 16 * r];
+          cm = sum_rows(((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7])));
+        }
         if (++it == a.iters) break;
-        col_gather(&sm.wgat[wv][0], tid, rcp(fmaxf(cm0, kTiny)), rcp(fmaxf(cm1, kTiny)), w);
+        // 1/c^2 of channel 16 wv + n (the four lanes of each channel write the
+        // same value), then every lane takes channels 16 nt + n
+        sm.ctot[16 * wv + n] = rcp(fmaxf(cm, kTiny));
+        lds_barrier();
+        {
+          const float *pg = sm.ctot + n;
+#pragma unroll
+          for (int nt = 0; nt < 8; ++nt) w[nt] = pg[16 * nt];
+        }
         // row step: r_i^2 = (1/D) sum_j P_ij / c_j^2  ->  v_i = 1 / sum_j P_ij / c_j^2
         float s[4];
 #pragma unroll
@@ -545,23 +533,24 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
         v[0] = token_value<0>(vt); v[1] = token_value<1>(vt);
         v[2] = token_value<2>(vt); v[3] = token_value<3>(vt);
       }
-      const float i0 = cm0 > 0.f ? __builtin_amdgcn_rsqf(cm0) : 1.f;
-      const float i1 = cm1 > 0.f ? __builtin_amdgcn_rsqf(cm1) : 1.f;
-      col_gather(&sm.wgat[wv][0], tid, i0, i1, w);
-      cm0 = cm0 > 0.f ? cm0 * i0 : 1.f;  // c = c^2 / sqrt(c^2)
-      cm1 = cm1 > 0.f ? cm1 * i1 : 1.f;
+      // c and 1/c of channel 16 wv + n (a zero column keeps c = 1)
+      const float ic = cm > 0.f ? __builtin_amdgcn_rsqf(cm) : 1.f;
+      cm = cm > 0.f ? cm * ic : 1.f;  // c = c^2 / sqrt(c^2)
+      {
+        float *pg = sm.ctot + (fresh(tid) & 15);
+        pg[16 * wv] = ic;
+        lds_barrier();
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) w[nt] = pg[16 * nt];
+      }
     } else {
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) w[nt] = 1.f;
     }
 
     // ---- 4. range step and codes --------------------------------------------
-    if (wv == 0) {  // every wave holds the same column scales
-      const int t = fresh(tid);
-      float *cs = a.col_scale + (bh * nch + chunk) * D + 16 * col_tile(t >> 4) + (t & 15);
-      cs[0] = cm0;
-      cs[64] = cm1;
-    }
+    if (g == 0)  // wave wv holds the column scales of channels 16 wv + [0, 16)
+      a.col_scale[(bh * nch + chunk) * D + 16 * wv + (fresh(tid) & 15)] = cm;
     float mx[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt)
