@@ -81,10 +81,11 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // below are free of bank conflicts under that model:
 //  * cpart: the column step's partial sums, cp[nt] of lane l of wave u at
 //    cpart[CP_PLANE nt + CP_WAVE u + l]. A wave's write of one nt covers 64
-//    consecutive words; a reading lane (n, g) of wave w takes plane w, waves
-//    2 g and 2 g + 1, rows r, at CP_PLANE w + CP_WAVE (2 g + s) + 16 r + n,
-//    and the 72-word wave stride puts the four lane rows 144 words (16 banks)
-//    apart, so neither side has bank conflicts;
+//    consecutive words; reading lane l of wave w takes plane w, channel
+//    16 w + l / 4 of waves 2 (l % 4) + s (s < 2) and rows r, at
+//    CP_PLANE w + CP_WAVE (2 (l % 4) + s) + 16 r + l / 4, and the 72-word
+//    wave stride puts the four lanes of a quad 144 words (16 banks) apart, so
+//    neither side has bank conflicts;
 //  * ctot: the per-channel result of a column step (1/c^2, and 1/c after the
 //    last one), written by the wave that reduced the channel and read by
 //    every lane for channels 16 nt + n;
@@ -171,17 +172,6 @@ __device__ __forceinline__ float token_value(float x) {
   return dpp_f<l * 0x55>(x);  // quad_perm [l, l, l, l]
 }
 
-// Sum over the four 16-lane rows of a wave, in every lane: permlane32 swaps
-// of the value with itself add rows g and g + 2, permlane16 swaps then add
-// rows g and g + 1.
-__device__ __forceinline__ float sum_rows(float h) {
-  const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(h), __float_as_uint(h), false,
-                                                  false);
-  h = __uint_as_float(x[0]) + __uint_as_float(x[1]);
-  const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(h), __float_as_uint(h), false,
-                                                  false);
-  return __uint_as_float(y[0]) + __uint_as_float(y[1]);
-}
 // LDS accesses of the wave complete and are visible to its other lanes.
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -319,6 +309,11 @@ __device__ __forceinline__ uint32_t pick4(int i, uint32_t v0, uint32_t v1, uint3
   return (i & 2) ? ((i & 1) ? v3 : v2) : ((i & 1) ? v1 : v0);
 }
 
+// b * 0x01010101 for b < 256: byte 0 of b in all four bytes, by a byte
+// permute (a full-rate instruction; a 32-bit integer multiply issues at a
+// quarter of the rate)
+__device__ __forceinline__ uint32_t bytes4(uint32_t b) { return __builtin_amdgcn_perm(0u, b, 0u); }
+
 // kRotate = false: the input is already rotated (rotation absorbed into the
 // model's weights) and the MFMAs copy it through identity tiles.
 // kPositions: x is a one-chunk window per (b, h); block (b, h) re-quantizes
@@ -452,7 +447,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
 
     // ---- 3. dual scaling ---------------------------------------------------
     float w[8];                  // 1/c^2 of channels 16 nt + n; 1/c after the last column step
-    float cm = 1.f;  // c^2 of channel 16 wv + n after a column step, then c
+    float cm = 1.f;  // c^2 of channel 16 wv + lane / 4 after a column step, then c
     if (a.iters > 0) {
       // v_i = 1 / (T r_i^2) of the lane's tokens. With D = T the row step's
       // 1/D and the column step's 1/T cancel: v_i = 1 / sum_j P_ij / c_j^2,
@@ -487,8 +482,9 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
       for (int it = 0;;) {
         // column step: c_j^2 = (1/T) sum_i P_ij / r_i^2 = sum_i P_ij v_i. The
         // lane's 8 partial sums (its 4 tokens of channels 16 nt + n) go to
-        // LDS; wave w then adds up channel 16 w + n: lane (n, g) takes waves
-        // 2 g and 2 g + 1, all four rows, and the lane rows meet by swaps.
+        // LDS; wave w then adds up channel 16 w + l / 4: lane l takes waves
+        // 2 (l % 4) and 2 (l % 4) + 1, all four rows, and the quad's four
+        // lanes meet by two DPP adds.
         float cp[8];
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt)
@@ -501,18 +497,20 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
         }
         lds_barrier();
         {
-          const float *pr = sm.cpart + CP_PLANE * wv + 2 * CP_WAVE * g + n;
+          const float *pr = sm.cpart + CP_PLANE * wv + 2 * CP_WAVE * (lane & 3) + (lane >> 2);
           float q[8];
 #pragma unroll
           for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int r = 0; r < 4; ++r) q[4 * u + r] = pr[CP_WAVE * u + 16 * r];
-          cm = sum_rows(((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7])));
+          cm = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+          cm += dpp_f<kXor1>(cm);
+          cm += dpp_f<kXor2>(cm);
         }
         if (++it == a.iters) break;
-        // 1/c^2 of channel 16 wv + n (the four lanes of each channel write the
-        // same value), then every lane takes channels 16 nt + n
-        sm.ctot[16 * wv + n] = rcp(fmaxf(cm, kTiny));
+        // 1/c^2 of channel 16 wv + l / 4 (the four lanes of each channel write
+        // the same value), then every lane takes channels 16 nt + n
+        sm.ctot[16 * wv + (lane >> 2)] = rcp(fmaxf(cm, kTiny));
         lds_barrier();
         {
           const float *pg = sm.ctot + n;
@@ -533,13 +531,13 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
         v[0] = token_value<0>(vt); v[1] = token_value<1>(vt);
         v[2] = token_value<2>(vt); v[3] = token_value<3>(vt);
       }
-      // c and 1/c of channel 16 wv + n (a zero column keeps c = 1)
+      // c and 1/c of channel 16 wv + l / 4 (a zero column keeps c = 1)
       const float ic = cm > 0.f ? __builtin_amdgcn_rsqf(cm) : 1.f;
       cm = cm > 0.f ? cm * ic : 1.f;  // c = c^2 / sqrt(c^2)
+      sm.ctot[16 * wv + (lane >> 2)] = ic;
+      lds_barrier();
       {
-        float *pg = sm.ctot + (fresh(tid) & 15);
-        pg[16 * wv] = ic;
-        lds_barrier();
+        const float *pg = sm.ctot + (fresh(tid) & 15);
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) w[nt] = pg[16 * nt];
       }
@@ -549,8 +547,8 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
     }
 
     // ---- 4. range step and codes --------------------------------------------
-    if (g == 0)  // wave wv holds the column scales of channels 16 wv + [0, 16)
-      a.col_scale[(bh * nch + chunk) * D + 16 * wv + (fresh(tid) & 15)] = cm;
+    if ((lane & 3) == 0)  // wave wv holds the column scales of channels 16 wv + [0, 16)
+      a.col_scale[(bh * nch + chunk) * D + 16 * wv + ((fresh(tid) & 63) >> 2)] = cm;
     float mx[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt)
@@ -591,7 +589,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
       // (token r, half k) words of the quad (equal values to equal addresses)
       const int t = fresh(tid);
       const int s = t & 3, q = (t >> 2) & 3;
-      uint32_t *ks = &sm.kst[0][0] + 4 * KST_ROW * (t >> 6) + KST_ROW * ((t >> 4) & 3);
+      uint32_t *ks = &sm.kst[wv][0] + KST_ROW * ((t >> 4) & 3);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         ks[8 * r + q] = kw[r][0];
@@ -602,7 +600,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
       // token n / 4 (= q), half k = s / 2, bytes 2 (s % 2) and 2 (s % 2) + 1
       // of the four quads' words
       const u32x4 wq = *reinterpret_cast<const u32x4 *>(ks + 8 * q + 4 * (s >> 1));
-      const uint32_t sel = 0x05010400u + 0x02020202u * (uint32_t)(s & 1);
+      const uint32_t sel = 0x05010400u + bytes4(2u * (uint32_t)(s & 1));
       const uint32_t t01 = __builtin_amdgcn_perm(wq.y, wq.x, sel);
       const uint32_t t23 = __builtin_amdgcn_perm(wq.w, wq.z, sel);
       const u32x2 pk = {__builtin_amdgcn_perm(t23, t01, 0x05040100u),
@@ -630,19 +628,19 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
       const uint32_t p1 = bt[4] | (bt[5] << 8) | (bt[6] << 16) | (bt[7] << 24);
       const int t = fresh(tid);
       const uint32_t hi = (t >> 5) & 1, odd = (t >> 4) & 1;  // g / 2, g % 2
-      const uint32_t k1 = __builtin_amdgcn_perm(p1, p0, 0x05040100u + 0x02020202u * hi);
-      const uint32_t s1 = __builtin_amdgcn_perm(p1, p0, 0x07060302u - 0x02020202u * hi);
+      const uint32_t k1 = __builtin_amdgcn_perm(p1, p0, 0x05040100u + bytes4(2u * hi));
+      const uint32_t s1 = __builtin_amdgcn_perm(p1, p0, 0x07060302u - bytes4(2u * hi));
       const auto x1 = __builtin_amdgcn_permlane32_swap(s1, s1, false, false);
       const uint32_t r1 = hi ? x1[0] : x1[1];
-      const uint32_t k2 = __builtin_amdgcn_perm(r1, k1, 0x06040200u + 0x01010101u * odd);
-      const uint32_t s2 = __builtin_amdgcn_perm(r1, k1, 0x07050301u - 0x01010101u * odd);
+      const uint32_t k2 = __builtin_amdgcn_perm(r1, k1, 0x06040200u + bytes4(odd));
+      const uint32_t s2 = __builtin_amdgcn_perm(r1, k1, 0x07050301u - bytes4(odd));
       const auto x2 = __builtin_amdgcn_permlane16_swap(s2, s2, false, false);
       const uint32_t r2 = odd ? x2[0] : x2[1];
       // byte rho of the word is row rho's byte: kept (rho = g: byte 0,
       // rho = g ^ 2: byte 2) or received (rho = g ^ 1: byte 4, g ^ 3: byte 6),
       // i.e. byte f(rho ^ g) with f = (0, 4, 2, 6)
       const uint32_t sel = __builtin_amdgcn_perm(
-          0u, 0x06020400u, 0x03020100u ^ (0x01010101u * (uint32_t)((t >> 4) & 3)));
+          0u, 0x06020400u, 0x03020100u ^ bytes4((uint32_t)((t >> 4) & 3)));
       // the words of channels 16 g + n (= t % 64) and 64 + 16 g + n, byte
       // column 4 wv, go through LDS so that the block leaves as 4 KB of
       // contiguous 8-byte stores
