@@ -223,6 +223,13 @@ struct ChunkRegs {
   u32x2 ck, cv, rk, rv;  // scales of elements 2 lane, 2 lane + 1
 };
 
+// The cache is streamed once per decode step: non-temporal loads, which keep
+// it from displacing reused lines in the caches.
+template <typename V>
+__device__ __forceinline__ V stream_load(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const V *>(p));
+}
+
 template <bool kTwoScales>
 __device__ __forceinline__ void load_chunk(const DecodeArgs &a, int64_t bg, int64_t nchunks,
                                            int k, int lane, ChunkRegs &r) {
@@ -232,16 +239,16 @@ __device__ __forceinline__ void load_chunk(const DecodeArgs &a, int64_t bg, int6
   const uint8_t *vc = a.v_codes + chunk * CHUNK_BYTES + 32 * n + 8 * g;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    r.k[t] = *reinterpret_cast<const u32x2 *>(kc + 64 * t);   // token + 2 t
-    r.v[t] = *reinterpret_cast<const u32x2 *>(vc + 512 * t);  // channel + 16 t
+    r.k[t] = stream_load<u32x2>(kc + 64 * t);   // token + 2 t
+    r.v[t] = stream_load<u32x2>(vc + 512 * t);  // channel + 16 t
   }
   if constexpr (kTwoScales) {
-    r.ck = *reinterpret_cast<const u32x2 *>(a.k_col + chunk * D + 2 * lane);
-    r.cv = *reinterpret_cast<const u32x2 *>(a.v_col + chunk * D + 2 * lane);
+    r.ck = stream_load<u32x2>(a.k_col + chunk * D + 2 * lane);
+    r.cv = stream_load<u32x2>(a.v_col + chunk * D + 2 * lane);
   }
   const int64_t row = bg * (int64_t)a.capacity + (int64_t)k * T + 2 * lane;
-  r.rk = *reinterpret_cast<const u32x2 *>(a.k_row + row);
-  r.rv = *reinterpret_cast<const u32x2 *>(a.v_row + row);
+  r.rk = stream_load<u32x2>(a.k_row + row);
+  r.rv = stream_load<u32x2>(a.v_row + row);
 }
 
 struct SplitState {
