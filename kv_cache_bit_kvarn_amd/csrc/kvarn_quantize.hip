@@ -304,11 +304,6 @@ __device__ __forceinline__ void prefetch_bf16_block_lds(const QuantArgs &a, cons
                                      (__attribute__((address_space(3))) void *)&slice[kk][0], 16, 0, 0);
 }
 
-// One of four values chosen by a lane index i < 4.
-__device__ __forceinline__ uint32_t pick4(int i, uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3) {
-  return (i & 2) ? ((i & 1) ? v3 : v2) : ((i & 1) ? v1 : v0);
-}
-
 // b * 0x01010101 for b < 256: byte 0 of b in all four bytes, by a byte
 // permute (a full-rate instruction; a 32-bit integer multiply issues at a
 // quarter of the rate)
