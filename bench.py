@@ -74,7 +74,8 @@ def parse():
 # Measured HBM traffic of a kernel: rocprofv3 FETCH_SIZE and WRITE_SIZE per
 # dispatch, each scaled by the ratio that the same counter shows for a plain
 # copy of known size (profiles/traffic.json, written from those runs). It is
-# reported only while the kernel's sources are the ones that were profiled.
+# reported only while the kernel's sources are the ones that were profiled
+# (their code: comments and layout are left out of the digest).
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "quantize_block_kernel<bf16>": ["kv_cache_bit_kvarn_amd/csrc/kvarn_quantize.hip",
@@ -87,10 +88,14 @@ KERNEL_SOURCES = {
 
 def sources_digest(kernel: str) -> str:
     import hashlib
+    import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)  # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

@@ -28,11 +28,13 @@
 //      1/c^2 (8 registers) and the 16 lanes of a row combine their sums
 //      (two lane-pair exchanges that halve the values, then two rotations),
 //      with no LDS and no barrier. Column step: each lane weighs its 4 tokens
-//      of each of its 8 channels by 1/r^2; two permlane swaps sum over the
-//      wave's four rows and leave 2 channels per lane; the waves publish
-//      those partial sums (4 KB, double-buffered) and, after the sweep's one
-//      barrier, every wave adds up the 8 partials of its lanes' channels and
-//      spreads 1/c^2 back over its rows with the swaps in reverse;
+//      of each of its 8 channels by 1/r^2 and writes the 8 partial sums to
+//      LDS unreduced; after a barrier wave w adds up channels 16 w + [0, 16)
+//      only (lane l: channel 16 w + l / 4, 8 of its 32 partials, the quad's
+//      four lanes meeting by DPP adds), writes 1/c^2 to a shared 128-entry
+//      array and, after a second barrier, every lane reads the 8 values of
+//      its channels. (Each wave adding up all 128 channels itself would need
+//      one barrier less but three times the VALU instructions.)
 //   4. per-token range step and 2-bit codes (v_cvt_pk_u8_f32): K codes of
 //      four adjacent channels (four adjacent lanes) merge by a shift and an
 //      OR across the quad, pass through a small per-wave LDS area and leave
