@@ -284,11 +284,18 @@ __device__ __forceinline__ int64_t x_offset(const QuantArgs &a, const BlockIdx &
   return (int64_t)bi.b * a.sb + (int64_t)bi.h * a.sh + (int64_t)(bi.kc * T + ti) * a.st;
 }
 
+// bf16 input of block bi: a wave-uniform base (its first token row) plus the
+// lane's fixed byte offset xlane = 2 ti st + 16 g (token ti, channels 8 g ..).
+__device__ __forceinline__ const char *x_block_bf16(const QuantArgs &a, const BlockIdx &bi,
+                                                    int64_t xlane) {
+  return static_cast<const char *>(a.x) +
+         2 * ((int64_t)bi.b * a.sb + (int64_t)bi.h * a.sh + (int64_t)(bi.kc * T) * a.st) + xlane;
+}
+
 // Piece kk of the lane's token row: channels 32 kk + 8 g + [0, 8).
-__device__ __forceinline__ void load_bf16_block(const QuantArgs &a, const BlockIdx &bi, int ti,
-                                                int g, u32x4 (&xr)[4]) {
-  const u32x4 *src =
-      reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.x) + x_offset(a, bi, ti)) + g;
+__device__ __forceinline__ void load_bf16_block(const QuantArgs &a, const BlockIdx &bi,
+                                                int64_t xlane, u32x4 (&xr)[4]) {
+  const u32x4 *src = reinterpret_cast<const u32x4 *>(x_block_bf16(a, bi, xlane));
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) xr[kk] = __builtin_nontemporal_load(src + 4 * kk);
 }
@@ -297,9 +304,8 @@ __device__ __forceinline__ void load_bf16_block(const QuantArgs &a, const BlockI
 // into the wave's LDS slice (global_load_lds_dwordx4: lane l's 16 bytes land
 // at slice[kk][l]); counted by vmcnt like any load.
 __device__ __forceinline__ void prefetch_bf16_block_lds(const QuantArgs &a, const BlockIdx &bi,
-                                                        int ti, int g, u32x4 (*slice)[64]) {
-  const u32x4 *src =
-      reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.x) + x_offset(a, bi, ti)) + g;
+                                                        int64_t xlane, u32x4 (*slice)[64]) {
+  const u32x4 *src = reinterpret_cast<const u32x4 *>(x_block_bf16(a, bi, xlane));
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
     __builtin_amdgcn_global_load_lds(src + 4 * kk,
@@ -320,9 +326,11 @@ template <bool kF32, bool kRotate, bool kPositions>
 __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a) {
   __shared__ QuantSmem sm;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wv = tid >> 6;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar LDS addresses
   const int n = lane & 15, g = lane >> 4;
   const int ti = 16 * wv + n;  // token whose input row the lane loads
+  const int64_t xlane = 2 * (int64_t)ti * a.st + 16 * g;  // its bytes within a bf16 block
   const int64_t nch = a.capacity / T;
   // r' from the running maximum: the unscaled rotation's 1/sqrt(128) and the
   // 1/2 of the range step, or the 1/2 alone for pre-rotated input
@@ -346,8 +354,8 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
   uint32_t blk = blockIdx.x;
   if constexpr (!kF32) {
     if (blk < a.nblocks) {
-      load_bf16_block(a, split_block(a, blk), ti, g, xn);
-      prefetch_bf16_block_lds(a, split_block(a, min(blk + gridDim.x, a.nblocks - 1)), ti, g,
+      load_bf16_block(a, split_block(a, blk), xlane, xn);
+      prefetch_bf16_block_lds(a, split_block(a, min(blk + gridDim.x, a.nblocks - 1)), xlane,
                               sm.xin[wv]);
     }
     // waited for here once, so that the loop head does not merge the first
@@ -424,7 +432,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
         for (int kk = 0; kk < 4; ++kk) xn[kk] = sm.xin[wv][kk][lane];
         __builtin_amdgcn_s_waitcnt((0x7 << 4) | 0xF | (0x3 << 14));  // lgkmcnt(0): reads done
         const uint32_t nb = min(blk + 2 * gridDim.x, a.nblocks - 1);
-        prefetch_bf16_block_lds(a, split_block(a, nb), ti, g, sm.xin[wv]);
+        prefetch_bf16_block_lds(a, split_block(a, nb), xlane, sm.xin[wv]);
       }
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
