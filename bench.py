@@ -5,7 +5,10 @@ One step = the whole path over one batch of synthetic input:
   for every layer: quantize K and V (all 128-token chunks), append one new
   token to each, and run one decode-attention step over the 2-bit cache.
 (The Llama-3-8B-shaped workload quantizes its cache once, before timing, and
-its step is append + decode per layer: steady-state decoding.)
+its step is append + decode per layer: steady-state decoding. Its step is
+captured once in a HIP graph and the replays are timed: the GPU work per
+layer (two appends, one decode) is shorter than the host's per-call launch
+overhead, so eager launches would leave the GPU waiting on the host.)
 
 Default workload: Qwen3-4B-shaped full cache (36 layers, batch 8, 8 kv-heads
 x 128, 32768 tokens, 32 query heads), the largest of the workloads and the
@@ -137,8 +140,8 @@ def main():
     dev = torch.device("cuda:0")
     L, B, Hkv, Hq, T = wl.layers, wl.batch, wl.kv_heads, wl.q_heads, wl.tokens
     cap = T + CHUNK
-    if steady and args.steps + args.warmup > CHUNK:
-        sys.exit("steady-state workload: steps + warmup must be <= 128")
+    if steady and args.steps + args.warmup >= CHUNK:
+        sys.exit("steady-state workload: steps + warmup must be < 128")
 
     log(f"[bench] workload {wl.name}: generating inputs on {dev} ...")
     t0 = time.time()
@@ -215,26 +218,32 @@ def main():
     torch.cuda.synchronize()
 
     rec = {"quantize": [], "append": [], "decode": []}
-    log(f"[bench] timing {args.steps} steps")
-    start, end = ev(), ev()
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i, rec)
-    end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_step = total_ms / args.steps
+    if steady:
+        ms_step, a_us, d_us = steady_graph_timing(kv, torch, args, caches, news, qs, out, ws, L, B, T)
+        q_us = None
+    else:
+        log(f"[bench] timing {args.steps} steps")
+        start, end = ev(), ev()
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(args.steps):
+            step(args.warmup + i, rec)
+        end.record(stream)
+        torch.cuda.synchronize()
+        total_ms = start.elapsed_time(end)
+        ms_step = total_ms / args.steps
 
-    def avg_us(name):
-        v = [a.elapsed_time(b_) * 1e3 for a, b_ in rec[name]]
-        return (sum(v) / len(v)) if v else None
+        def avg_us(name):
+            v = [a.elapsed_time(b_) * 1e3 for a, b_ in rec[name]]
+            return (sum(v) / len(v)) if v else None
 
-    q_us, a_us, d_us = avg_us("quantize"), avg_us("append"), avg_us("decode")
+        q_us, a_us, d_us = avg_us("quantize"), avg_us("append"), avg_us("decode")
     elts_per_quant = B * Hkv * T * D
     q_launches = 0 if steady else 2 * L
     bf16_bytes_step = q_launches * elts_per_quant * 2
-    dec_tokens = (T + args.warmup + args.steps // 2 + 1) if steady else (T + 1)
+    # tokens attended per decode: the graph-timed decodes of the steady-state
+    # workload run after the timed steps, over T + warmup + steps + 1 tokens
+    dec_tokens = (T + args.warmup + args.steps + 1) if steady else (T + 1)
     dec_bytes = DECODE_BYTES_PER_TOKEN * dec_tokens * B * Hkv + B * Hq * D * (2 + 4)
     decode_ms_step = L * d_us / 1e3
 
@@ -380,6 +389,64 @@ def ablations(kv, torch, stream, x_pair, q, cache_pair, ws, out, length, iters, 
         "note": "layer 0, K tensor for quantize; HIP events over "
                 f"{reps} launches after one warm launch",
     }
+
+
+def steady_graph_timing(kv, torch, args, caches, news, qs, out, ws, L, B, T):
+    """Steady-state decoding timed on HIP-graph replays (torch.cuda.CUDAGraph).
+
+    G_step holds one step: for every layer, append K and V at pos, decode over
+    lens; then pos and lens advance by one, so each replay is the next step.
+    G_dec holds the L decodes alone and G_app the 2 L appends alone (at a fixed
+    position, so replaying them rewrites the same slots); their replays give
+    the per-launch times. The positions continue from the eager warmup steps.
+    Returns (ms per step, us per append, us per decode)."""
+    dev = out.device
+    pos = torch.full((B,), T + args.warmup, dtype=torch.int32, device=dev)
+    lens = pos + 1
+    torch.cuda.synchronize()
+
+    def layer_appends(layer):
+        kc, vc = caches[layer]
+        kv.append(news[layer][0], pos, kc)
+        kv.append(news[layer][1], pos, vc)
+
+    def layer_decode(layer):
+        kc, vc = caches[layer]
+        kv.decode_attn(qs[layer], kc, vc, lens, out=out, workspace=ws)
+
+    g_step, g_dec, g_app = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_step):
+        for layer in range(L):
+            layer_appends(layer)
+            layer_decode(layer)
+        pos.add_(1)
+        lens.add_(1)
+    with torch.cuda.graph(g_dec):
+        for layer in range(L):
+            layer_decode(layer)
+    with torch.cuda.graph(g_app):
+        for layer in range(L):
+            layer_appends(layer)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def timed(g, n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(n):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n  # ms per replay
+
+    log(f"[bench] timing {args.steps} steps (HIP graph replays)")
+    ms_step = timed(g_step, args.steps)
+    reps = max(args.steps, 10)
+    d_us = timed(g_dec, reps) * 1e3 / L
+    a_us = timed(g_app, reps) * 1e3 / (2 * L)
+    return ms_step, a_us, d_us
 
 
 def cpu_baseline(args, wl, xs, news, qs, steady, unit, bf16_bytes_step, cap):
