@@ -72,7 +72,6 @@ constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int CPT = 32;                        // values per lane: 4 tokens x 8 channels
 constexpr float kGrid = 1.9999980926513672f;  // 2 (1 - 2^-20)
-constexpr uint32_t kPack4 = 0x40100401u;       // byte weights 1, 4, 16, 64
 constexpr float kTiny = 1.17549435e-38f;       // smallest normal fp32
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -613,24 +612,28 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
       // tokens 16 wv + 4 g + [0, 4) are 128 contiguous bytes from (16 wv + 4 g) * 32
       *reinterpret_cast<u32x2 *>(cbase + 8 * (t & 511)) = pk;
     } else {
-      // bt[nt]: the V byte of channel 16 nt + n, tokens 16 wv + 4 g + [0, 4)
-      // (byte column 4 wv + g of the channel row)
-      uint32_t bt[8];
+      // Byte j of p0 (p1) is the V byte of channel 16 j + n (16 (4 + j) + n),
+      // tokens 16 wv + 4 g + [0, 4) (byte column 4 wv + g of the channel
+      // row). The codes of token r of the four tiles are converted into the
+      // bytes of one word, and the four tokens' words meet by shifts of 2 r
+      // within the bytes (no field reaches the next byte).
+      uint32_t xa[4], xb[4];
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        uint32_t c = 0;
+      for (int r = 0; r < 4; ++r) {
+        xa[r] = 0;
+        xb[r] = 0;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          c = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(y[4 * nt + r], qs[r], 1.5f), r, c);
-        bt[nt] = __builtin_amdgcn_udot4(c, kPack4, 0u, false);
+        for (int j = 0; j < 4; ++j) {
+          xa[r] = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(y[4 * j + r], qs[r], 1.5f), j, xa[r]);
+          xb[r] = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(y[4 * (4 + j) + r], qs[r], 1.5f), j, xb[r]);
+        }
       }
-      // 4 x 4 byte transposes across the rows g (lanes 16 apart) of
-      // p0 = bytes of tiles 0-3 and p1 = tiles 4-7: lane g ends with the
-      // words of tiles g and 4 + g. Rows g and g ^ 2 (permlane32) trade the
-      // column pair the other keeps, then rows g and g ^ 1 (permlane16) the
-      // column the other keeps.
-      const uint32_t p0 = bt[0] | (bt[1] << 8) | (bt[2] << 16) | (bt[3] << 24);
-      const uint32_t p1 = bt[4] | (bt[5] << 8) | (bt[6] << 16) | (bt[7] << 24);
+      const uint32_t p0 = (xa[0] | (xa[1] << 2)) | ((xa[2] << 4) | (xa[3] << 6));
+      const uint32_t p1 = (xb[0] | (xb[1] << 2)) | ((xb[2] << 4) | (xb[3] << 6));
+      // 4 x 4 byte transposes across the rows g (lanes 16 apart) of p0 and
+      // p1: lane g ends with the words of tiles g and 4 + g. Rows g and g ^ 2
+      // (permlane32) trade the column pair the other keeps, then rows g and
+      // g ^ 1 (permlane16) the column the other keeps.
       const int t = fresh(tid);
       const uint32_t hi = (t >> 5) & 1, odd = (t >> 4) & 1;  // g / 2, g % 2
       const uint32_t k1 = __builtin_amdgcn_perm(p1, p0, 0x05040100u + bytes4(2u * hi));
