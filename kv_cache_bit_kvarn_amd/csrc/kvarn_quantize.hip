@@ -40,8 +40,10 @@
 //      OR across the quad, pass through a small per-wave LDS area and leave
 //      as 8 contiguous bytes per lane (a wave writes its 16 token rows as
 //      one 512-byte span); V codes of a lane's 4 tokens form a byte in the
-//      lane, and a 4 x 4 byte transpose across the wave's rows (two permlane
-//      swaps) gives each lane two whole 4-byte words of channel rows.
+//      lane (shifts inside the bytes of words that each hold one token of
+//      four channel tiles), and a 4 x 4 byte transpose across the wave's rows
+//      (two permlane swaps) gives each lane two whole 4-byte words of channel
+//      rows.
 // The rotation is applied without its 1/sqrt(128) factor; that factor leaves
 // the column scales and codes unchanged and is folded into the row scale.
 //
