@@ -119,14 +119,6 @@ struct QuantSmem {
 
 __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// The value itself, hidden from the optimizer so that addresses built from it
-// are recomputed where they are used instead of being hoisted out of the block
-// loop and kept (or spilled) across the balancing.
-__device__ __forceinline__ int fresh(int x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
@@ -477,7 +469,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
           // token 4 g + tsel(n) sits in lane 16 g + 4 g + tsel(n), register tsel(n)
           const int r = n & 3;
           const float d = (r & 2) ? ((r & 1) ? gram.w : gram.z) : ((r & 1) ? gram.y : gram.x);
-          const int t = fresh(tid);
+          const int t = tid;
           const int src = 20 * ((t >> 4) & 3) + tsel(t);
           tot = (kRotate ? (float)D : 1.f) * __shfl(d, src, 64);
         }
@@ -543,7 +535,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
       sm.ctot[16 * wv + (lane >> 2)] = ic;
       lds_barrier();
       {
-        const float *pg = sm.ctot + (fresh(tid) & 15);
+        const float *pg = sm.ctot + (tid & 15);
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) w[nt] = pg[16 * nt];
       }
@@ -554,7 +546,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
 
     // ---- 4. range step and codes --------------------------------------------
     if ((lane & 3) == 0)  // wave wv holds the column scales of channels 16 wv + [0, 16)
-      a.col_scale[(bh * nch + chunk) * D + 16 * wv + ((fresh(tid) & 63) >> 2)] = cm;
+      a.col_scale[(bh * nch + chunk) * D + 16 * wv + ((tid & 63) >> 2)] = cm;
     float mx[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt)
@@ -565,7 +557,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
       }
     const float m = row_reduce4<true>(mx, n);  // token 4 g + tsel(n)
     if (n < 4) {  // lane t % 16 < 4 of row (t / 16) % 4: token 4 (t / 16) + tsel(t) of the block
-      const int t = fresh(tid);
+      const int t = tid;
       a.row_scale[bh * a.capacity + (int64_t)chunk * T + 4 * (t >> 4) + tsel(t)] = m * range_factor;
     }
     const float qt = m > 0.f ? kGrid * rcp(m) : 0.f;
@@ -578,7 +570,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
       // shifted to bit 2 (n % 4) and ORed over the quad it becomes token-row
       // byte 16 k + 4 i + n / 4 (channels 4 (4 k + i) + n / 4 .. + 4)
       uint32_t kw[4][2];
-      const int sh = 2 * (fresh(tid) & 3);
+      const int sh = 2 * (tid & 3);
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -593,7 +585,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
         }
       // the four lanes of quad q hold the same words: each writes all eight
       // (token r, half k) words of the quad (equal values to equal addresses)
-      const int t = fresh(tid);
+      const int t = tid;
       const int s = t & 3, q = (t >> 2) & 3;
       uint32_t *ks = &sm.kst[wv][0] + KST_ROW * ((t >> 4) & 3);
 #pragma unroll
@@ -636,7 +628,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
       // p1: lane g ends with the words of tiles g and 4 + g. Rows g and g ^ 2
       // (permlane32) trade the column pair the other keeps, then rows g and
       // g ^ 1 (permlane16) the column the other keeps.
-      const int t = fresh(tid);
+      const int t = tid;
       const uint32_t hi = (t >> 5) & 1, odd = (t >> 4) & 1;  // g / 2, g % 2
       const uint32_t k1 = __builtin_amdgcn_perm(p1, p0, 0x05040100u + bytes4(2u * hi));
       const uint32_t s1 = __builtin_amdgcn_perm(p1, p0, 0x07060302u - bytes4(2u * hi));
@@ -661,7 +653,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
       lds_barrier();
       // thread u: channel u / 4, byte columns 8 (u % 4) + [0, 8) = the words
       // of waves 2 (u % 4) and 2 (u % 4) + 1; channel row j starts at 32 j
-      const int u = fresh(tid);
+      const int u = tid;
       const uint32_t *src = vs + VST_ROW * (u >> 2) + 2 * (u & 3);
       const u32x2 word = {src[0], src[1]};
       *reinterpret_cast<u32x2 *>(cbase + 8 * u) = word;
