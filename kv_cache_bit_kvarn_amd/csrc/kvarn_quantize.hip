@@ -80,8 +80,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // LDS. On gfx950 a ds_write_b32 is served one half-wave per pass with the
 // dword address taken modulo 32 as its bank; a ds_read_b32 pair
-// (ds_read2st64) of consecutive lanes reads consecutive dwords. Both areas
-// below are free of bank conflicts under that model:
+// (ds_read2st64) of consecutive lanes reads consecutive dwords. The areas
+// below are laid out for that model:
 //  * cpart: the column step's partial sums, cp[nt] of lane l of wave u at
 //    cpart[CP_PLANE nt + CP_WAVE u + l]. A wave's write of one nt covers 64
 //    consecutive words; reading lane l of wave w takes plane w, channel
@@ -91,7 +91,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 //    neither side has bank conflicts;
 //  * ctot: the per-channel result of a column step (1/c^2, and 1/c after the
 //    last one), written by the wave that reduced the channel and read by
-//    every lane for channels 16 nt + n;
+//    every lane for channels 16 nt + n (the four lane rows of a wave read the
+//    same words);
 //  * kst[wave]: K code staging, rows of KST_ROW words per group of 4 tokens
 //    (word (token r, half k, quad q) at KST_ROW g + 8 r + 4 k + q; the
 //    36-word rows put the two 16-lane rows of a half-wave on disjoint
