@@ -58,6 +58,24 @@ def test_decode_splits_agree(kvarn):
         assert rel_l2(o.cpu().numpy(), outs[0].cpu().numpy()) < 1e-5
 
 
+def test_decode_many_splits_merge_in_rounds(kvarn, oracle):
+    """More than 32 splits: the merge takes the partials in rounds of 32 with
+    a running maximum. Every split count agrees with one split, and with the
+    oracle, over a cache of 80 chunks with a ragged last chunk."""
+    cap = 80 * 128
+    kc, vc, hk, hv = _random_caches(kvarn, 2, 1, cap, seed=5)
+    q = kvgen.queries(14, 0, 2, 4, dtype=torch.bfloat16)
+    lens = [cap, cap - 77]
+    L = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    outs = [kvarn.decode_attn(q.cuda(), kc, vc, L, n_split=n) for n in (1, 33, 64, 80)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert rel_l2(o.cpu().numpy(), outs[0].cpu().numpy()) < 1e-5
+    err = rel_l2(outs[2].cpu().numpy(), _oracle_on(oracle, q, hk, hv, lens))
+    log(f"[test] decode 64 splits over 80 chunks: rel L2 {err:.3e}")
+    assert err <= ATTN_RL2
+
+
 def test_decode_invalid_lengths_give_zero(kvarn):
     kc, vc, _, _ = _random_caches(kvarn, 3, 1, 256, seed=4)
     q = kvgen.queries(13, 0, 3, 4, device="cuda")
