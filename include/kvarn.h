@@ -123,6 +123,12 @@ typedef struct {
  * and store codes, r' and c at cache slots [token_offset, token_offset+tokens).
  * A zero token row stores r' = 0 and code 2; a zero column keeps c_j = 1.
  * Non-finite input gives unspecified codes and scales for its chunk.
+ * The arithmetic is fp32 on the unscaled rotation (y sqrt(128)): a token's
+ * energy 128 sum_j x_j^2 must stay below 2^127 (|x| below about 2^53). Over
+ * that range, scaling x by 2^k scales r' by exactly 2^k and leaves codes and c
+ * bit-identical, as long as the squared rotated values stay normal fp32
+ * numbers. A nonzero token whose energy is below 2^-126 is weighted as if it
+ * were 2^-126.
  *
  * x          (device) input, dtype `dtype`, logical shape
  *            [dst->batch][dst->kv_heads][tokens][128], element (b,h,t,j) at

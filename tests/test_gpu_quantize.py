@@ -121,6 +121,25 @@ def test_power_of_two_token_scaling_is_bit_exact(kvarn):
     assert torch.equal(c1.row_scale * s[..., 0], c2.row_scale)
 
 
+@pytest.mark.parametrize("kind", [kvgen.K, kvgen.V])
+@pytest.mark.parametrize("k", [-40, -20, 20, 40])
+def test_power_of_two_tensor_scaling_is_bit_exact(kvarn, kind, k):
+    """Scaling the whole input by 2^k, far from unit magnitudes, scales every
+    row scale by exactly 2^k and leaves codes and column scales bit-identical:
+    the fp32 sums stay normal and finite over this range (|x| up to about
+    2^48, squared rotated values down to about 2^-110 here)."""
+    log(f"[test] tensor scaling 2^{k} kind={kind}")
+    x = kvgen.kv_tensor(21, 0, kind, 1, 2, 512, 0.5, dtype=torch.bfloat16, device="cuda")
+    c1 = kvarn.Cache.empty(1, 2, 512, kind, device="cuda")
+    c2 = kvarn.Cache.empty(1, 2, 512, kind, device="cuda")
+    kvarn.quantize(x, c1)
+    kvarn.quantize((x * 2.0 ** k).contiguous(), c2)
+    torch.cuda.synchronize()
+    assert torch.equal(c1.codes, c2.codes)
+    assert torch.equal(c1.col_scale, c2.col_scale)
+    assert torch.equal(c1.row_scale * 2.0 ** k, c2.row_scale)
+
+
 def test_block_independence(kvarn):
     """Quantizing a subset of chunks gives the same bytes as the same chunks of
     a full run."""
