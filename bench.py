@@ -345,13 +345,18 @@ def error_diagnostics(kv, torch, stream, x_pair, cache_pair, iters):
     return res
 
 
-def ablations(kv, torch, stream, x_pair, q, cache_pair, ws, out, length, iters, reps=10):
+def ablations(kv, torch, stream, x_pair, q, cache_pair, ws, out, length, iters, reps=20,
+              rounds=3):
     """Layer-0 launches timed with HIP events outside the timed step:
     the quantizer with and without balancing (iters vs 0: the cost of the
     dual-scaling normalization), decode with both scales and with the column
     scales taken as 1 (the cost of the second scale), and decode with the
     rotation absorbed into the weights (no query rotation, no output
-    un-rotation). Scratch caches keep the benchmark's caches intact."""
+    un-rotation). The variants are timed in turn, `rounds` times over, and
+    each reports the median of its rounds: the shader clock moves by several
+    percent within a second of a change of load, which one short run per
+    variant, always in the same order, would take for a difference between
+    the variants. Scratch caches keep the benchmark's caches intact."""
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     def timed(fn):
@@ -368,26 +373,35 @@ def ablations(kv, torch, stream, x_pair, q, cache_pair, ws, out, length, iters, 
     xk = x_pair[0]
     kc, vc = cache_pair
     scratch = kv.Cache.empty(kc.batch, kc.kv_heads, kc.capacity, kv.K, device=xk.device)
-    q_full = timed(lambda: kv.quantize(xk, scratch, iters=iters, stream=stream))
-    q_none = timed(lambda: kv.quantize(xk, scratch, iters=0, stream=stream))
-    q_norot = timed(lambda: kv.quantize(xk, scratch, iters=iters, stream=stream,
-                                        flags=kv.FLAG_NO_ROTATE))
-    del scratch
     lens = torch.full((kc.batch,), length, dtype=torch.int32, device=xk.device)
 
     def dec(flags):
-        return timed(lambda: kv.decode_attn(q, kc, vc, lens, out=out, workspace=ws,
-                                            stream=stream, flags=flags))
-    d_two, d_one, d_norot = dec(0), dec(kv.FLAG_ONE_SCALE), dec(kv.FLAG_NO_ROTATE)
+        return lambda: kv.decode_attn(q, kc, vc, lens, out=out, workspace=ws, stream=stream,
+                                      flags=flags)
+    variants = {
+        "q_full": lambda: kv.quantize(xk, scratch, iters=iters, stream=stream),
+        "q_none": lambda: kv.quantize(xk, scratch, iters=0, stream=stream),
+        "q_norot": lambda: kv.quantize(xk, scratch, iters=iters, stream=stream,
+                                       flags=kv.FLAG_NO_ROTATE),
+        "d_two": dec(0),
+        "d_one": dec(kv.FLAG_ONE_SCALE),
+        "d_norot": dec(kv.FLAG_NO_ROTATE),
+    }
+    times = {k: [] for k in variants}
+    for _ in range(rounds):
+        for k, fn in variants.items():
+            times[k].append(timed(fn))
+    del scratch
+    t = {k: sorted(v)[len(v) // 2] for k, v in times.items()}
     return {
-        "quantize_us": {f"iters_{iters}": round(q_full, 2), "iters_0": round(q_none, 2),
-                        "no_rotate": round(q_norot, 2),
-                        "balancing_share": round((q_full - q_none) / q_full, 4)},
-        "decode_us": {"two_scales": round(d_two, 2), "one_scale": round(d_one, 2),
-                      "no_rotate": round(d_norot, 2),
-                      "second_scale_overhead": round((d_two - d_one) / d_one, 4)},
-        "note": "layer 0, K tensor for quantize; HIP events over "
-                f"{reps} launches after one warm launch",
+        "quantize_us": {f"iters_{iters}": round(t["q_full"], 2), "iters_0": round(t["q_none"], 2),
+                        "no_rotate": round(t["q_norot"], 2),
+                        "balancing_share": round((t["q_full"] - t["q_none"]) / t["q_full"], 4)},
+        "decode_us": {"two_scales": round(t["d_two"], 2), "one_scale": round(t["d_one"], 2),
+                      "no_rotate": round(t["d_norot"], 2),
+                      "second_scale_overhead": round((t["d_two"] - t["d_one"]) / t["d_one"], 4)},
+        "note": f"layer 0, K tensor for quantize; HIP events over {reps} launches after one "
+                f"warm launch; variants timed in turn, median of {rounds} rounds",
     }
 
 
