@@ -2,8 +2,12 @@
 """Benchmark of the KVarN hot path on one MI355X.
 
 One step = the whole path over one batch of synthetic input:
-  for every layer: quantize K and V (all 128-token chunks), append one new
-  token to each, and run one decode-attention step over the 2-bit cache.
+  quantize K and V of every layer (all 128-token chunks), then, layer by
+  layer, append one new token to K and V and run one decode-attention step
+  over the 2-bit cache.
+Quantizing every layer before the first decode keeps each decode reading a
+cache that was written more than 256 MB earlier: the 256 MB memory-side cache
+(MALL) holds none of it, so every reported decode time is an HBM time.
 (The Llama-3-8B-shaped workload quantizes its cache once, before timing, and
 its step is append + decode per layer: steady-state decoding. Its step is
 captured once in a HIP graph and the replays are timed: the GPU work per
@@ -11,8 +15,9 @@ layer (two appends, one decode) is shorter than the host's per-call launch
 overhead, so eager launches would leave the GPU waiting on the host.)
 
 Default workload: Qwen3-4B-shaped full cache (36 layers, batch 8, 8 kv-heads
-x 128, 32768 tokens, 32 query heads), the largest of the workloads and the
-one that does not fit in the 256 MB last-level cache.
+x 128, 32768 tokens, 32 query heads). The same JSON line also carries the
+Llama-3-8B-shaped steady-state decode and the long-horizon stress shape as
+sub-results (`workloads`), measured after the timed step.
 
 Prints ONE JSON line. Per-kernel durations come from HIP events recorded on
 the launch stream around every launch in the timed region.
@@ -31,15 +36,31 @@ sys.path.insert(0, ROOT)
 
 METRIC = "quantize GB/s (bf16 in) + 2-bit decode-attn tokens/s; % of HBM peak"
 HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E, published
+MALL_BYTES = 256 << 20           # MI355X memory-side last-level cache
 D, CHUNK = 128, 128
 # algorithmic bytes per element of one quantize launch: 2 B bf16 in, 0.25 B
 # codes, 4 B row scale per 128 channels, 4 B column scale per 128 tokens
 QUANT_BYTES_PER_ELT_BF16 = 2.0 + 0.25 + 4.0 / 128 + 4.0 / 128
 # MI355X fp32 vector peak, published: 256 CUs x 4 SIMDs x 32 lanes per clock
 # x 2 flop per FMA x 2.4 GHz = 157.3 TFLOP/s. Plain (non-packed) v_fmac_f32
-# reaches it too: a throughput probe of independent FMAs measured 120 TFLOP/s
-# (DPP-sourced FMAs: 68-70).
+# reaches most of it: a throughput probe of independent FMAs measured
+# 120 TFLOP/s (DPP-sourced FMAs: 68-70).
 VALU_F32_PEAK_TFLOPS = 256 * 4 * 32 * 2 * 2.4e9 / 1e12
+# the machine's CPU share for one GPU: worker pools stay within it
+HOST_THREAD_CAP = 16
+
+QUANT_ARITH = ("rotation: bf16 x (+-1) products on the matrix cores with fp32 accumulation "
+               "(exact for bf16 input); balancing, range step and code decision: fp32 VALU")
+DECODE_ARITH = ("scaled MFMA f8f6f4: 2-bit cache codes as fp4 e2m1 operands; query*c_K as "
+                "4 fp8 e4m3 terms (~16 significant bits), p*r'_V as 3 fp8 e4m3 terms (~12 bits), "
+                "per-head power-of-two range scales; fp32 accumulation; online softmax, "
+                "split merge and inverse rotation in fp32")
+
+# the pages' own figure (rndamp.com article on KVarN, section "Numbers"):
+# 1.9 ms of variance normalization against 1050 ms of token generation for
+# Qwen3-4B on an unnamed GPU; batch, length and call count are not stated
+PAGES_NORMALIZATION_MS = 1.9
+PAGES_GENERATION_MS = 1050.0
 
 
 def quant_flop_per_elt(iters: int) -> int:
@@ -68,6 +89,8 @@ def parse():
     p.add_argument("--no-ablations", action="store_true",
                    help="skip the ablation timings (balancing off, one scale, rotation off) "
                         "and the error diagnostics")
+    p.add_argument("--no-subworkloads", action="store_true",
+                   help="skip the Llama-3-8B steady-state and stress sub-results")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="one device-to-device copy of this many MiB before the warmup: "
                         "the reference kernel for calibrating HBM byte counters")
@@ -87,6 +110,7 @@ KERNEL_SOURCES = {
         "kv_cache_bit_kvarn_amd/csrc/kvarn_decode.hip",
         "kv_cache_bit_kvarn_amd/csrc/kvarn_internal.h"],
 }
+DECODE_KERNELS = "decode_split_kernel + decode_combine_kernel"
 
 
 def sources_digest(kernel: str) -> str:
@@ -119,6 +143,29 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def decode_bytes(tokens: int, B: int, Hkv: int, Hq: int) -> float:
+    """Algorithmic bytes of one decode call: the cache stream plus q and out."""
+    return DECODE_BYTES_PER_TOKEN * tokens * B * Hkv + B * Hq * D * (2 + 4)
+
+
+def hbm_entry(nbytes: float, us: float) -> dict:
+    gbps = nbytes / (us * 1e-6) / 1e9
+    return {"GBps_algorithmic": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
+def timed_events(torch, stream, fns):
+    """HIP events on `stream` around each call of fns; returns microseconds."""
+    evs = []
+    for fn in fns:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1e3 for a, b in evs]
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -147,14 +194,18 @@ def main():
     t0 = time.time()
     xs, news, qs, caches = [], [], [], []
     for layer in range(L):
-        xk = kvgen.kv_tensor(wl.seed, layer, kvgen.K, B, Hkv, T, wl.sigma, device=dev)
-        xv = kvgen.kv_tensor(wl.seed, layer, kvgen.V, B, Hkv, T, wl.sigma, device=dev)
-        xs.append((xk, xv))
+        if steady:
+            xs.append(None)
+        else:
+            xs.append((kvgen.kv_tensor(wl.seed, layer, kvgen.K, B, Hkv, T, wl.sigma, device=dev),
+                       kvgen.kv_tensor(wl.seed, layer, kvgen.V, B, Hkv, T, wl.sigma, device=dev)))
         news.append((kvgen.new_tokens(wl.seed, layer, kvgen.K, B, Hkv, wl.sigma, device=dev),
                      kvgen.new_tokens(wl.seed, layer, kvgen.V, B, Hkv, wl.sigma, device=dev)))
         qs.append(kvgen.queries(wl.seed, layer, B, Hq, device=dev))
         caches.append((kv.Cache.empty(B, Hkv, cap, kv.K, device=dev),
                        kv.Cache.empty(B, Hkv, cap, kv.V, device=dev)))
+    if steady:
+        build_steady_caches(kv, kvgen, torch, wl, caches, args.iters, dev)
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
     ws = kv.decode_workspace(B, Hq, cap, device=dev)
     if args.calib_copy_mib > 0:
@@ -167,50 +218,37 @@ def main():
         del src, dst
         log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done")
     torch.cuda.synchronize()
-    log(f"[bench] inputs ready in {time.time() - t0:.1f}s "
-        f"({sum(x.numel() * 2 for p in xs for x in p) / 1e9:.2f} GB bf16 K/V)")
+    log(f"[bench] inputs ready in {time.time() - t0:.1f}s")
 
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-
-    if steady:
-        for layer in range(L):
-            kv.quantize(xs[layer][0], caches[layer][0], iters=args.iters)
-            kv.quantize(xs[layer][1], caches[layer][1], iters=args.iters)
-        torch.cuda.synchronize()
 
     def step(i: int, rec: dict | None):
         p = (T + i) if steady else T
         pos = torch.full((B,), p, dtype=torch.int32, device=dev)
         lens = torch.full((B,), p + 1, dtype=torch.int32, device=dev)
+
+        def launch(name, fn):
+            if rec is None:
+                fn()
+                return
+            a, b_ = ev(), ev()
+            a.record(stream)
+            fn()
+            b_.record(stream)
+            rec[name].append((a, b_))
+
+        if not steady:
+            for layer in range(L):
+                for x, c in ((xs[layer][0], caches[layer][0]), (xs[layer][1], caches[layer][1])):
+                    launch("quantize", lambda x=x, c=c: kv.quantize(x, c, iters=args.iters,
+                                                                    stream=stream))
         for layer in range(L):
             kc, vc = caches[layer]
-            if not steady:
-                for x, c in ((xs[layer][0], kc), (xs[layer][1], vc)):
-                    if rec is not None:
-                        a, b_ = ev(), ev()
-                        a.record(stream)
-                        kv.quantize(x, c, iters=args.iters, stream=stream)
-                        b_.record(stream)
-                        rec["quantize"].append((a, b_))
-                    else:
-                        kv.quantize(x, c, iters=args.iters, stream=stream)
             for n, c in ((news[layer][0], kc), (news[layer][1], vc)):
-                if rec is not None:
-                    a, b_ = ev(), ev()
-                    a.record(stream)
-                    kv.append(n, pos, c, stream=stream)
-                    b_.record(stream)
-                    rec["append"].append((a, b_))
-                else:
-                    kv.append(n, pos, c, stream=stream)
-            if rec is not None:
-                a, b_ = ev(), ev()
-                a.record(stream)
-            kv.decode_attn(qs[layer], kc, vc, lens, out=out, workspace=ws, stream=stream)
-            if rec is not None:
-                b_.record(stream)
-                rec["decode"].append((a, b_))
+                launch("append", lambda n=n, c=c: kv.append(n, pos, c, stream=stream))
+            launch("decode", lambda kc=kc, vc=vc, layer=layer: kv.decode_attn(
+                qs[layer], kc, vc, lens, out=out, workspace=ws, stream=stream))
 
     log(f"[bench] warmup {args.warmup} steps")
     for i in range(args.warmup):
@@ -219,7 +257,8 @@ def main():
 
     rec = {"quantize": [], "append": [], "decode": []}
     if steady:
-        ms_step, a_us, d_us = steady_graph_timing(kv, torch, args, caches, news, qs, out, ws, L, B, T)
+        ms_step, a_us, d_us = steady_graph_timing(kv, torch, args.warmup, args.steps, caches,
+                                                  news, qs, out, ws, L, B, T)
         q_us = None
     else:
         log(f"[bench] timing {args.steps} steps")
@@ -230,8 +269,7 @@ def main():
             step(args.warmup + i, rec)
         end.record(stream)
         torch.cuda.synchronize()
-        total_ms = start.elapsed_time(end)
-        ms_step = total_ms / args.steps
+        ms_step = start.elapsed_time(end) / args.steps
 
         def avg_us(name):
             v = [a.elapsed_time(b_) * 1e3 for a, b_ in rec[name]]
@@ -244,7 +282,7 @@ def main():
     # tokens attended per decode: the graph-timed decodes of the steady-state
     # workload run after the timed steps, over T + warmup + steps + 1 tokens
     dec_tokens = (T + args.warmup + args.steps + 1) if steady else (T + 1)
-    dec_bytes = DECODE_BYTES_PER_TOKEN * dec_tokens * B * Hkv + B * Hq * D * (2 + 4)
+    dec_bytes = decode_bytes(dec_tokens, B, Hkv, Hq)
     decode_ms_step = L * d_us / 1e3
 
     res = {
@@ -258,17 +296,18 @@ def main():
                    "balancing_iters": args.iters, "input_dtype": "bf16",
                    "token_scale_sigma": wl.sigma,
                    "step": "append+decode per layer" if steady else
-                           "quantize K,V + append + decode per layer"},
+                           "quantize K,V of every layer, then append + decode per layer"},
     }
     dec = {"tokens_per_s": round(B / (decode_ms_step / 1e3), 1),
            "us_per_launch": round(d_us, 2), "launches_per_step": L,
-           "GBps_algorithmic": round(dec_bytes / (d_us * 1e-6) / 1e9, 1),
-           "hbm_frac": round(dec_bytes / (d_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-           "kernels": "decode_split_kernel + decode_combine_kernel"}
+           **hbm_entry(dec_bytes, d_us), "kernels": DECODE_KERNELS,
+           "decode_arith": DECODE_ARITH,
+           "cache_regime": "HBM: each decode reads a layer whose cache was written more "
+                           "than 256 MB of traffic earlier"}
     dec_roof = {"bound": "hbm", "achieved": dec["GBps_algorithmic"], "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": dec["hbm_frac"],
-                "traffic": measured_traffic(dec["kernels"], wl.name),
-                "kernel": dec["kernels"], "bytes_per_launch": dec_bytes}
+                "traffic": measured_traffic(DECODE_KERNELS, wl.name),
+                "kernel": DECODE_KERNELS, "bytes_per_launch": dec_bytes}
     if steady:
         res["value"] = dec["tokens_per_s"]
         res["unit"] = "tokens/s (decode attention, all layers)"
@@ -276,117 +315,158 @@ def main():
         res["roofline"] = dec_roof
     else:
         qbytes = QUANT_BYTES_PER_ELT_BF16 * elts_per_quant
-        q_gbps = qbytes / (q_us * 1e-6) / 1e9
         res["value"] = round(bf16_bytes_step / (ms_step / 1e3) / 1e9, 2)
         res["unit"] = "GB/s (bf16 K/V in, whole quantize+append+decode step)"
         res["quantize"] = {"GBps_bf16_in": round(elts_per_quant * 2 / (q_us * 1e-6) / 1e9, 1),
                            "us_per_launch": round(q_us, 2), "launches_per_step": q_launches,
-                           "GBps_algorithmic": round(q_gbps, 1),
-                           "hbm_frac": round(q_gbps / HBM_PEAK_GBPS, 4)}
-        # roofline of the quantizer: the larger of its ideal HBM time (bytes at
-        # the HBM peak) and its ideal ALU time (algorithmic fp32 operations at
-        # the VALU peak) names the bound; the other resource stays beside it
-        q_flop = quant_flop_per_elt(args.iters) * elts_per_quant
-        q_tflops = q_flop / (q_us * 1e-6) / 1e12
-        t_hbm = qbytes / (HBM_PEAK_GBPS * 1e9)
-        t_alu = q_flop / (VALU_F32_PEAK_TFLOPS * 1e12)
-        alu = {"achieved": round(q_tflops, 2), "peak": round(VALU_F32_PEAK_TFLOPS, 2),
-               "unit": "TFLOP/s", "frac": round(q_tflops / VALU_F32_PEAK_TFLOPS, 4),
-               "flop_per_element": quant_flop_per_elt(args.iters)}
-        hbm = {"achieved": round(q_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-               "frac": round(q_gbps / HBM_PEAK_GBPS, 4)}
-        bound, main, other = ("hbm", hbm, alu) if t_hbm >= t_alu else ("alu", alu, dict(hbm))
-        res["roofline"] = {"bound": bound, **main,
-                           "traffic": measured_traffic("quantize_block_kernel<bf16>", wl.name),
-                           "kernel": "quantize_block_kernel<bf16>",
-                           "elements_per_launch": elts_per_quant,
-                           "bytes_per_launch": qbytes,
-                           "ideal_us": {"hbm": round(t_hbm * 1e6, 2), "alu": round(t_alu * 1e6, 2)},
-                           ("alu" if bound == "hbm" else "hbm"): other}
+                           **hbm_entry(qbytes, q_us), "quantize_arith": QUANT_ARITH}
+        res["roofline"] = quant_roofline(qbytes, elts_per_quant, q_us, args.iters, wl.name)
         res["roofline_decode"] = dec_roof
+        res["pages_context"] = {
+            "pages_normalization_ms": PAGES_NORMALIZATION_MS,
+            "pages_generation_ms": PAGES_GENERATION_MS,
+            "pages_share": round(PAGES_NORMALIZATION_MS / PAGES_GENERATION_MS, 5),
+            "source": "rndamp.com article on KVarN, section Numbers (Qwen3-4B, unnamed GPU, "
+                      "batch and length not stated)",
+            "this_quantize_ms_per_step": round(q_launches * q_us / 1e3, 3),
+            "this_step_ms": round(ms_step, 3),
+            "this_quantize_share_of_step": round(q_launches * q_us / 1e3 / ms_step, 4),
+            "note": "context only, not a like-for-like comparison: here the whole 36-layer "
+                    "cache of batch 8 x 32768 tokens is quantized in every step"}
     res["decode"] = dec
     res["append"] = {"us_per_launch": round(a_us, 2), "launches_per_step": 2 * L}
-    if not args.no_ablations:
-        res["ablations"] = ablations(kv, torch, stream, xs[0], qs[0], caches[0], ws, out,
-                                     T + (args.warmup + args.steps if steady else 1), args.iters)
+
+    cpu_inputs = None
+    if not args.no_cpu_baseline and not steady:
+        cpu_inputs = cpu_sample(args, wl, xs, news, qs)
+    if not args.no_ablations and not steady:
+        res["ablations"] = ablations(kv, torch, stream, xs, qs, caches, ws, out, T + 1,
+                                     args.iters)
         res["error_diagnostics"] = error_diagnostics(kv, torch, stream, xs[0], caches[0],
-                                                     args.iters)
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(args, wl, xs, news, qs, steady, res["unit"],
-                                           bf16_bytes_step, cap)
+                                                     args.iters, res["ablations"])
+    if not args.no_subworkloads and args.workload == 2:
+        del xs, caches, news, qs, out, ws
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        res["workloads"] = {}
+        sub = kvgen.WORKLOADS[3]
+        res["workloads"][sub.name] = steady_workload(kv, kvgen, torch, sub, args, dev)
+        torch.cuda.empty_cache()
+        sub = kvgen.WORKLOADS[4]
+        res["workloads"][sub.name] = stress_workload(kv, kvgen, torch, sub, args, dev, stream)
+        torch.cuda.empty_cache()
+    if cpu_inputs is not None:
+        res["cpu_baseline"] = cpu_baseline(args, wl, cpu_inputs, res["unit"], bf16_bytes_step,
+                                           cap)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
 
 
-def error_diagnostics(kv, torch, stream, x_pair, cache_pair, iters):
+def quant_roofline(qbytes, elts, q_us, iters, wl_name):
+    """Roofline of the quantizer: the larger of its ideal HBM time (bytes at
+    the HBM peak) and its ideal ALU time (algorithmic fp32 operations at the
+    VALU peak) names the bound; the other resource stays beside it."""
+    q_gbps = qbytes / (q_us * 1e-6) / 1e9
+    q_flop = quant_flop_per_elt(iters) * elts
+    q_tflops = q_flop / (q_us * 1e-6) / 1e12
+    t_hbm = qbytes / (HBM_PEAK_GBPS * 1e9)
+    t_alu = q_flop / (VALU_F32_PEAK_TFLOPS * 1e12)
+    alu = {"achieved": round(q_tflops, 2), "peak": round(VALU_F32_PEAK_TFLOPS, 2),
+           "unit": "TFLOP/s", "frac": round(q_tflops / VALU_F32_PEAK_TFLOPS, 4),
+           "flop_per_element": quant_flop_per_elt(iters)}
+    hbm = {"achieved": round(q_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+           "frac": round(q_gbps / HBM_PEAK_GBPS, 4)}
+    bound, main, other = ("hbm", hbm, alu) if t_hbm >= t_alu else ("alu", alu, dict(hbm))
+    return {"bound": bound, **main,
+            "traffic": measured_traffic("quantize_block_kernel<bf16>", wl_name),
+            "kernel": "quantize_block_kernel<bf16>",
+            "elements_per_launch": elts, "bytes_per_launch": qbytes,
+            "ideal_us": {"hbm": round(t_hbm * 1e6, 2), "alu": round(t_alu * 1e6, 2)},
+            ("alu" if bound == "hbm" else "hbm"): other}
+
+
+def error_diagnostics(kv, torch, stream, x_pair, cache_pair, iters, abl):
     """Magnitude vs direction of the quantization error on layer 0 (outside
-    the timed step): each token's squared error relative to ||x||^2 splits
+    the timed step), for the 2 x 2 of rotation {on, off} x balancing
+    {iters, 0} sweeps. Each token's squared error relative to ||x||^2 splits
     exactly into (rho - 1)^2 (magnitude, rho = ||x_hat|| / ||x||) and
-    2 rho (1 - cos) (direction). Means over all tokens of K and V, quantized
-    with the balancing and without it, through kvarn_token_error."""
+    2 rho (1 - cos) (direction). Rotation off quantizes x itself in its own
+    basis (KVARN_FLAG_NO_ROTATE on the raw input) and measures the error in
+    that basis. Means over all tokens of K and V, through kvarn_token_error;
+    each cell carries the quantize time of that variant (ablations)."""
     res = {}
+    qt = abl["quantize_us"] if abl else {}
+    cell_time = {(True, iters): qt.get(f"iters_{iters}"), (True, 0): qt.get("iters_0"),
+                 (False, iters): qt.get("no_rotate"), (False, 0): qt.get("no_rotate_iters_0")}
     for name, x, cache in (("K", x_pair[0], cache_pair[0]), ("V", x_pair[1], cache_pair[1])):
         scratch = kv.Cache.empty(cache.batch, cache.kv_heads, cache.capacity, cache.kind,
                                  device=x.device)
-        for it in (iters, 0):
-            kv.quantize(x, scratch, iters=it, stream=stream)
-            ratio, cosine = kv.token_error(x, scratch, stream=stream)
-            torch.cuda.synchronize()
-            r, c = ratio.double(), cosine.double()
-            res[f"{name}_iters_{it}"] = {
-                "magnitude": round(float(((r - 1) ** 2).mean()), 6),
-                "direction": round(float((2 * r * (1 - c)).mean()), 6),
-                "mean_ratio": round(float(r.mean()), 5),
-                "mean_cos": round(float(c.mean()), 5)}
+        for rot in (True, False):
+            flags = 0 if rot else kv.FLAG_NO_ROTATE
+            for it in (iters, 0):
+                kv.quantize(x, scratch, iters=it, stream=stream, flags=flags)
+                ratio, cosine = kv.token_error(x, scratch, stream=stream, flags=flags)
+                torch.cuda.synchronize()
+                r, c = ratio.double(), cosine.double()
+                res[f"{name}_rotate_{'on' if rot else 'off'}_iters_{it}"] = {
+                    "magnitude": round(float(((r - 1) ** 2).mean()), 6),
+                    "direction": round(float((2 * r * (1 - c)).mean()), 6),
+                    "mean_ratio": round(float(r.mean()), 5),
+                    "mean_cos": round(float(c.mean()), 5),
+                    "quantize_us": cell_time.get((rot, it))}
         del scratch
     res["note"] = ("per-token squared error / ||x||^2 = magnitude + direction; means over "
-                   "layer 0's tokens")
+                   "layer 0's tokens; rotation off = quantized in the original basis")
     return res
 
 
-def ablations(kv, torch, stream, x_pair, q, cache_pair, ws, out, length, iters, reps=20,
-              rounds=3):
-    """Layer-0 launches timed with HIP events outside the timed step:
+def ablations(kv, torch, stream, xs, qs, caches, ws, out, length, iters, rounds=3):
+    """Launch times of the variants outside the timed step, with HIP events:
     the quantizer with and without balancing (iters vs 0: the cost of the
-    dual-scaling normalization), decode with both scales and with the column
-    scales taken as 1 (the cost of the second scale), and decode with the
-    rotation absorbed into the weights (no query rotation, no output
-    un-rotation). The variants are timed in turn, `rounds` times over, and
-    each reports the median of its rounds: the shader clock moves by several
-    percent within a second of a change of load, which one short run per
-    variant, always in the same order, would take for a difference between
-    the variants. Scratch caches keep the benchmark's caches intact."""
-    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    dual-scaling normalization) and with the rotation absorbed (with and
+    without balancing), decode with both scales and with the column scales
+    taken as 1 (the cost of the second scale), and decode with the rotation
+    absorbed (no query rotation, no output un-rotation).
+    Each repetition reads another layer's input (quantize: 537 MB of K per
+    layer) or cache (decode: 168 MB per layer), in turn over all layers, so
+    no repetition finds its data in the 256 MB memory-side cache: these are
+    HBM times, as in the timed step. The variants are timed in turn, `rounds`
+    times over, and each reports the median of its rounds: the shader clock
+    moves by several percent within a second of a change of load. Scratch
+    caches keep the benchmark's caches intact."""
+    L = len(xs)
+    kc0 = caches[0][0]
+    scratch = kv.Cache.empty(kc0.batch, kc0.kv_heads, kc0.capacity, kv.K, device=kc0.codes.device)
+    lens = torch.full((kc0.batch,), length, dtype=torch.int32, device=kc0.codes.device)
 
-    def timed(fn):
-        fn()
-        torch.cuda.synchronize()
-        a, b = ev(), ev()
-        a.record(stream)
-        for _ in range(reps):
-            fn()
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) * 1e3 / reps
-
-    xk = x_pair[0]
-    kc, vc = cache_pair
-    scratch = kv.Cache.empty(kc.batch, kc.kv_heads, kc.capacity, kv.K, device=xk.device)
-    lens = torch.full((kc.batch,), length, dtype=torch.int32, device=xk.device)
+    def quant(it, flags):
+        return lambda i: kv.quantize(xs[i % L][0], scratch, iters=it, stream=stream, flags=flags)
 
     def dec(flags):
-        return lambda: kv.decode_attn(q, kc, vc, lens, out=out, workspace=ws, stream=stream,
-                                      flags=flags)
+        return lambda i: kv.decode_attn(qs[i % L], caches[i % L][0], caches[i % L][1], lens,
+                                        out=out, workspace=ws, stream=stream, flags=flags)
     variants = {
-        "q_full": lambda: kv.quantize(xk, scratch, iters=iters, stream=stream),
-        "q_none": lambda: kv.quantize(xk, scratch, iters=0, stream=stream),
-        "q_norot": lambda: kv.quantize(xk, scratch, iters=iters, stream=stream,
-                                       flags=kv.FLAG_NO_ROTATE),
+        "q_full": quant(iters, 0),
+        "q_none": quant(0, 0),
+        "q_norot": quant(iters, kv.FLAG_NO_ROTATE),
+        "q_norot_none": quant(0, kv.FLAG_NO_ROTATE),
         "d_two": dec(0),
         "d_one": dec(kv.FLAG_ONE_SCALE),
         "d_norot": dec(kv.FLAG_NO_ROTATE),
     }
+
+    def timed(fn):
+        fn(L - 1)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(L):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / L
+
     times = {k: [] for k in variants}
     for _ in range(rounds):
         for k, fn in variants.items():
@@ -396,26 +476,41 @@ def ablations(kv, torch, stream, x_pair, q, cache_pair, ws, out, length, iters, 
     return {
         "quantize_us": {f"iters_{iters}": round(t["q_full"], 2), "iters_0": round(t["q_none"], 2),
                         "no_rotate": round(t["q_norot"], 2),
+                        "no_rotate_iters_0": round(t["q_norot_none"], 2),
                         "balancing_share": round((t["q_full"] - t["q_none"]) / t["q_full"], 4)},
         "decode_us": {"two_scales": round(t["d_two"], 2), "one_scale": round(t["d_one"], 2),
                       "no_rotate": round(t["d_norot"], 2),
                       "second_scale_overhead": round((t["d_two"] - t["d_one"]) / t["d_one"], 4)},
-        "note": f"layer 0, K tensor for quantize; HIP events over {reps} launches after one "
-                f"warm launch; variants timed in turn, median of {rounds} rounds",
+        "regime": f"HBM: each of the {L} launches per timing reads another layer's input or "
+                  f"cache (none fits in the {MALL_BYTES >> 20} MB memory-side cache)",
+        "note": f"K tensor for quantize; HIP events over {L} launches after one warm launch; "
+                f"variants timed in turn, median of {rounds} rounds",
     }
 
 
-def steady_graph_timing(kv, torch, args, caches, news, qs, out, ws, L, B, T):
+def build_steady_caches(kv, kvgen, torch, wl, caches, iters, dev):
+    """Quantize the steady-state workload's cache once (outside timing), one
+    layer's bf16 K or V at a time, so its 34 GB of input never coexist."""
+    for layer, (kc, vc) in enumerate(caches):
+        for kind, c in ((kvgen.K, kc), (kvgen.V, vc)):
+            x = kvgen.kv_tensor(wl.seed, layer, kind, wl.batch, wl.kv_heads, wl.tokens,
+                                wl.sigma, device=dev)
+            kv.quantize(x, c, iters=iters)
+            del x
+    torch.cuda.synchronize()
+
+
+def steady_graph_timing(kv, torch, warmup, steps, caches, news, qs, out, ws, L, B, T):
     """Steady-state decoding timed on HIP-graph replays (torch.cuda.CUDAGraph).
 
     G_step holds one step: for every layer, append K and V at pos, decode over
     lens; then pos and lens advance by one, so each replay is the next step.
     G_dec holds the L decodes alone and G_app the 2 L appends alone (at a fixed
     position, so replaying them rewrites the same slots); their replays give
-    the per-launch times. The positions continue from the eager warmup steps.
+    the per-launch times. The positions continue from `warmup` eager steps.
     Returns (ms per step, us per append, us per decode)."""
     dev = out.device
-    pos = torch.full((B,), T + args.warmup, dtype=torch.int32, device=dev)
+    pos = torch.full((B,), T + warmup, dtype=torch.int32, device=dev)
     lens = pos + 1
     torch.cuda.synchronize()
 
@@ -455,38 +550,139 @@ def steady_graph_timing(kv, torch, args, caches, news, qs, out, ws, L, B, T):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n  # ms per replay
 
-    log(f"[bench] timing {args.steps} steps (HIP graph replays)")
-    ms_step = timed(g_step, args.steps)
-    reps = max(args.steps, 10)
+    log(f"[bench] timing {steps} steps (HIP graph replays)")
+    ms_step = timed(g_step, steps)
+    reps = max(steps, 10)
     d_us = timed(g_dec, reps) * 1e3 / L
     a_us = timed(g_app, reps) * 1e3 / (2 * L)
     return ms_step, a_us, d_us
 
 
-def cpu_baseline(args, wl, xs, news, qs, steady, unit, bf16_bytes_step, cap):
+def steady_workload(kv, kvgen, torch, wl, args, dev):
+    """Sub-result: the Llama-3-8B-shaped steady-state decode (32 layers, batch
+    32, 8192-token cache, one appended token per sequence and layer per
+    step), graph-timed as in --workload 3."""
+    L, B, Hkv, Hq, T = wl.layers, wl.batch, wl.kv_heads, wl.q_heads, wl.tokens
+    cap = T + CHUNK
+    log(f"[bench] sub-workload {wl.name}: building the cache ...")
+    caches = [(kv.Cache.empty(B, Hkv, cap, kv.K, device=dev),
+               kv.Cache.empty(B, Hkv, cap, kv.V, device=dev)) for _ in range(L)]
+    build_steady_caches(kv, kvgen, torch, wl, caches, args.iters, dev)
+    news = [(kvgen.new_tokens(wl.seed, layer, kvgen.K, B, Hkv, wl.sigma, device=dev),
+             kvgen.new_tokens(wl.seed, layer, kvgen.V, B, Hkv, wl.sigma, device=dev))
+            for layer in range(L)]
+    qs = [kvgen.queries(wl.seed, layer, B, Hq, device=dev) for layer in range(L)]
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    ws = kv.decode_workspace(B, Hq, cap, device=dev)
+    warm, steps = 2, 10
+    for i in range(warm):
+        pos = torch.full((B,), T + i, dtype=torch.int32, device=dev)
+        for layer in range(L):
+            kv.append(news[layer][0], pos, caches[layer][0])
+            kv.append(news[layer][1], pos, caches[layer][1])
+            kv.decode_attn(qs[layer], caches[layer][0], caches[layer][1], pos + 1, out=out,
+                           workspace=ws)
+    torch.cuda.synchronize()
+    ms_step, a_us, d_us = steady_graph_timing(kv, torch, warm, steps, caches, news, qs, out, ws,
+                                              L, B, T)
+    nb = decode_bytes(T + warm + steps + 1, B, Hkv, Hq)
+    res = {"config": {"layers": L, "batch": B, "kv_heads": Hkv, "q_heads": Hq, "tokens": T,
+                      "step": "append K, V + decode per layer (HIP graph replays)"},
+           "step_ms": round(ms_step, 4), "step_tokens_per_s": round(B / (ms_step / 1e3), 1),
+           "decode_tokens_per_s": round(B / (L * d_us / 1e3), 1),
+           "decode_us_per_launch": round(d_us, 2), "append_us_per_launch": round(a_us, 2),
+           "decode": hbm_entry(nb, d_us)}
+    del caches, news, qs, out, ws
+    return res
+
+
+def stress_workload(kv, kvgen, torch, wl, args, dev, stream):
+    """Sub-result: the long-horizon stress shape (1 layer, batch 64, 131072
+    tokens quantized in 128-token chunks, token scales lognormal(0, 1)):
+    quantize K and V, append one token, decode over the whole cache."""
+    B, Hkv, Hq, T = wl.batch, wl.kv_heads, wl.q_heads, wl.tokens
+    cap = T + CHUNK
+    log(f"[bench] sub-workload {wl.name}: generating inputs ...")
+    xk = kvgen.kv_tensor(wl.seed, 0, kvgen.K, B, Hkv, T, wl.sigma, device=dev)
+    xv = kvgen.kv_tensor(wl.seed, 0, kvgen.V, B, Hkv, T, wl.sigma, device=dev)
+    kc = kv.Cache.empty(B, Hkv, cap, kv.K, device=dev)
+    vc = kv.Cache.empty(B, Hkv, cap, kv.V, device=dev)
+    nk = kvgen.new_tokens(wl.seed, 0, kvgen.K, B, Hkv, wl.sigma, device=dev)
+    nv = kvgen.new_tokens(wl.seed, 0, kvgen.V, B, Hkv, wl.sigma, device=dev)
+    q = kvgen.queries(wl.seed, 0, B, Hq, device=dev)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    ws = kv.decode_workspace(B, Hq, cap, device=dev)
+    pos = torch.full((B,), T, dtype=torch.int32, device=dev)
+    lens = pos + 1
+    quant = [lambda: kv.quantize(xk, kc, iters=args.iters, stream=stream),
+             lambda: kv.quantize(xv, vc, iters=args.iters, stream=stream)]
+    for f in quant:
+        f()
+    kv.append(nk, pos, kc, stream=stream)
+    kv.append(nv, pos, vc, stream=stream)
+    kv.decode_attn(q, kc, vc, lens, out=out, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    q_us = timed_events(torch, stream, quant * 3)
+    d_us = timed_events(torch, stream, [lambda: kv.decode_attn(q, kc, vc, lens, out=out,
+                                                               workspace=ws, stream=stream)] * 10)
+    elts = B * Hkv * T * D
+    qm, dm = sum(q_us) / len(q_us), sum(d_us) / len(d_us)
+    res = {"config": {"layers": 1, "batch": B, "kv_heads": Hkv, "q_heads": Hq, "tokens": T,
+                      "token_scale_sigma": wl.sigma},
+           "quantize_us_per_launch": round(qm, 2),
+           "quantize": hbm_entry(QUANT_BYTES_PER_ELT_BF16 * elts, qm),
+           "decode_us_per_launch": round(dm, 2),
+           "decode_tokens_per_s": round(B / (dm * 1e-6), 1),
+           "decode": hbm_entry(decode_bytes(T + 1, B, Hkv, Hq), dm),
+           "note": "HIP events; quantize mean of 6 launches (K, V alternating), decode mean of "
+                   "10 calls over a 5.4 GB cache"}
+    del xk, xv, kc, vc, nk, nv, q, out, ws
+    return res
+
+
+def cpu_sample(args, wl, xs, news, qs):
+    """Host copies of the (layer 0, sequence, kv-head) slices the CPU baseline
+    runs: whole slices of the step, drawn with a fixed seed."""
+    import numpy as np
+    threads = cpu_threads()
+    n = args.cpu_slices or 2 * threads
+    B, Hkv, Hq = wl.batch, wl.kv_heads, wl.q_heads
+    G = Hq // Hkv
+    rng = np.random.default_rng(0)
+    pairs = [(int(rng.integers(B)), int(rng.integers(Hkv))) for _ in range(n + 1)]
+    inputs = []
+    for b, g in pairs:
+        inputs.append(tuple(t.double().cpu().numpy() for t in (
+            xs[0][0][b:b + 1, g:g + 1], xs[0][1][b:b + 1, g:g + 1],
+            news[0][0][b:b + 1, g:g + 1], news[0][1][b:b + 1, g:g + 1],
+            qs[0][b:b + 1, g * G:(g + 1) * G])))
+    return inputs
+
+
+def cpu_threads() -> int:
+    """Host threads for the oracle: every CPU this process may run on, up to
+    the box's share for one GPU."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    return max(1, min(HOST_THREAD_CAP, avail))
+
+
+def cpu_baseline(args, wl, inputs, unit, bf16_bytes_step, cap):
     """The oracle (fp64 C, unmodified) timed on this host's cores on a bounded
     sample of the same step: whole (layer 0, sequence b, kv-head g) slices --
     quantize all chunks of K and V, append the new token, decode the group's
-    query heads -- run one slice per thread, then scaled to the full step."""
+    query heads -- one slice per thread at a time, then scaled to the full
+    step. One more slice runs alone on one thread for the one-core figure."""
     import numpy as np
 
     import oracle
 
     oracle.lib()
-    threads = max(1, min(16, os.cpu_count() or 1))
-    n = args.cpu_slices or 2 * threads
-    B, Hkv, Hq, T = wl.batch, wl.kv_heads, wl.q_heads, wl.tokens
-    G = Hq // Hkv
-    rng = np.random.default_rng(0)
-    pairs = [(int(rng.integers(B)), int(rng.integers(Hkv))) for _ in range(n)]
-    inputs = []
-    for b, g in pairs:
-        xk = xs[0][0][b:b + 1, g:g + 1].double().cpu().numpy()
-        xv = xs[0][1][b:b + 1, g:g + 1].double().cpu().numpy()
-        nk = news[0][0][b:b + 1, g:g + 1].double().cpu().numpy()
-        nv = news[0][1][b:b + 1, g:g + 1].double().cpu().numpy()
-        q = qs[0][b:b + 1, g * G:(g + 1) * G].double().cpu().numpy()
-        inputs.append((xk, xv, nk, nv, q))
+    threads = cpu_threads()
+    T = wl.tokens
+    G = wl.q_heads // wl.kv_heads
 
     def one(item):
         xk, xv, nk, nv, q = item
@@ -501,7 +697,8 @@ def cpu_baseline(args, wl, xs, news, qs, steady, unit, bf16_bytes_step, cap):
             outs.append((codes, rp, c))
         oracle.decode_attn(q, *outs[0], *outs[1], [T + 1])
 
-    work = list(inputs)
+    work = list(inputs[:-1])
+    n = len(work)
     lock = threading.Lock()
 
     def worker():
@@ -520,19 +717,31 @@ def cpu_baseline(args, wl, xs, news, qs, steady, unit, bf16_bytes_step, cap):
     for t in ts:
         t.join()
     wall = time.perf_counter() - t0
-    slices_per_step = wl.layers * B * Hkv
-    step_s = wall * slices_per_step / n
-    if steady:
-        value = B / step_s
-    else:
-        value = bf16_bytes_step / step_s / 1e9
-    return {"value": round(value, 6), "unit": unit, "cores": threads, "kind": "oracle",
-            "wall_s": round(wall, 2),
+    log("[bench] cpu baseline: one slice on one thread ...")
+    t1 = time.perf_counter()
+    one(inputs[-1])
+    wall1 = time.perf_counter() - t1
+    slices_per_step = wl.layers * wl.batch * wl.kv_heads
+
+    def value(step_s):
+        return round(bf16_bytes_step / step_s / 1e9, 6)
+
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
+    return {"value": value(wall * slices_per_step / n), "unit": unit, "cores": threads,
+            "kind": "oracle", "wall_s": round(wall, 2),
+            "host_cpus": os.cpu_count(), "affinity_cpus": affinity,
+            "one_core": {"value": value(wall1 * slices_per_step), "wall_s": round(wall1, 2),
+                         "sample": "1 slice on 1 thread, scaled by "
+                                   f"{slices_per_step} to the full step"},
             "sample": f"{n} whole (layer 0, seq, kv-head) slices of the step "
                       f"(quantize {2 * T // CHUNK} chunks of K+V incl. the oracle's "
                       f"O(D^2) rotation, append 1 token each, decode {G} query heads over "
-                      f"{T + 1} tokens), {threads} threads, scaled by "
-                      f"{slices_per_step}/{n} to the full step"}
+                      f"{T + 1} tokens), {threads} threads (the host's CPUs available to this "
+                      f"process, at most {HOST_THREAD_CAP}: the box's share for one GPU), "
+                      f"scaled by {slices_per_step}/{n} to the full step"}
 
 
 if __name__ == "__main__":

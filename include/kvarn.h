@@ -110,9 +110,10 @@ typedef struct {
 } kvarn_cache;
 
 /*
- * kvarn_quantize -- quantize whole 128-token chunks of K or V into a cache
- * (abstract: Hadamard rotation followed by dual-scaling variance
- * normalization across both axes, 2-bit; "How It Works", items 1 and 2).
+ * kvarn_quantize -- quantize whole 128-token chunks of K or V into a cache:
+ * rotate each token along the channels, balance the block's token and
+ * channel scales, store 2-bit codes (abstract, codewithpapers.app record;
+ * rndamp article on KVarN, "How It Works", items 1 and 2).
  *
  * For every (b, h) and every chunk of x's tokens [0, tokens):
  *   y  = x_chunk . H_128 / sqrt(128)                 (rotation per token)

@@ -99,9 +99,27 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
 
 
-def _stream(stream) -> int | None:
+def _on_device(what: str, *tensors) -> torch.device:
+    """Every tensor argument must live on one GPU: the kernels dereference
+    their data pointers on the device, so a host tensor would be read as a
+    device address."""
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            where = t.device if isinstance(t, torch.Tensor) else type(t).__name__
+            raise ValueError(f"{what}: every tensor argument must be on the GPU (got {where})")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{what}: tensor arguments on different devices ({dev}, {t.device})")
+    return dev
+
+
+def _stream(stream, device=None) -> int | None:
     if stream is None:
-        return torch.cuda.current_stream().cuda_stream
+        return torch.cuda.current_stream(device).cuda_stream
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
     return int(stream)
@@ -143,9 +161,26 @@ class Cache:
         return self.row_scale.shape[2]
 
     def desc(self) -> CacheDesc:
+        """The kvarn_cache descriptor, after checking dtypes, shapes and
+        placement against the layout the kernels index."""
         for t in (self.codes, self.row_scale, self.col_scale):
             if not t.is_contiguous():
                 raise ValueError("cache tensors must be contiguous")
+        if self.codes.dtype != torch.uint8 or self.row_scale.dtype != torch.float32 or \
+                self.col_scale.dtype != torch.float32:
+            raise ValueError("cache tensors must be uint8 codes and fp32 scales")
+        if self.codes.dim() != 4 or self.row_scale.dim() != 3 or self.col_scale.dim() != 4:
+            raise ValueError("cache tensors must be codes [B,H,cap/128,4096], row_scale "
+                             "[B,H,cap], col_scale [B,H,cap/128,128]")
+        B, H, nch = self.codes.shape[:3]
+        if self.codes.shape[3] != CHUNK_BYTES or \
+                tuple(self.row_scale.shape) != (B, H, nch * CHUNK) or \
+                tuple(self.col_scale.shape) != (B, H, nch, HEAD_DIM):
+            raise ValueError("cache tensors must be codes [B,H,cap/128,4096], row_scale "
+                             "[B,H,cap], col_scale [B,H,cap/128,128] with one B, H and cap")
+        if self.kind not in (K, V):
+            raise ValueError("cache kind must be K or V")
+        _on_device("cache", self.codes, self.row_scale, self.col_scale)
         return CacheDesc(self.codes.data_ptr(), self.row_scale.data_ptr(),
                          self.col_scale.data_ptr(), self.batch, self.kv_heads,
                          self.capacity, self.kind)
@@ -160,9 +195,10 @@ def quantize(x: torch.Tensor, cache: Cache, token_offset: int = 0, iters: int = 
     if x.shape[0] != cache.batch or x.shape[1] != cache.kv_heads:
         raise ValueError("x batch/heads differ from the cache")
     d = cache.desc()
+    dev = _on_device("quantize", x, cache.codes)
     st = load().kvarn_quantize_ex(x.data_ptr(), _dtype_code(x), x.stride(0), x.stride(1),
                                   x.stride(2), x.shape[2], token_offset, iters, flags,
-                                  ctypes.byref(d), _stream(stream))
+                                  ctypes.byref(d), _stream(stream, dev))
     _raise(st, "kvarn_quantize")
 
 
@@ -173,11 +209,13 @@ def append(x: torch.Tensor, positions: torch.Tensor, cache: Cache, stream=None,
     if x.dim() != 3 or tuple(x.shape) != (cache.batch, cache.kv_heads, HEAD_DIM) or \
             not x.is_contiguous():
         raise ValueError("x must be contiguous [B, H, 128] matching the cache")
-    if positions.dtype != torch.int32 or positions.numel() != cache.batch:
-        raise ValueError("positions must be int32 [B]")
+    if positions.dtype != torch.int32 or positions.numel() != cache.batch or \
+            not positions.is_contiguous():
+        raise ValueError("positions must be contiguous int32 [B]")
     d = cache.desc()
+    dev = _on_device("append", x, positions, cache.codes)
     st = load().kvarn_append_ex(x.data_ptr(), _dtype_code(x), positions.data_ptr(), flags,
-                                ctypes.byref(d), _stream(stream))
+                                ctypes.byref(d), _stream(stream, dev))
     _raise(st, "kvarn_append")
 
 
@@ -194,15 +232,17 @@ def append_rebalance(x: torch.Tensor, positions: torch.Tensor, cache: Cache,
     if x.dim() != 3 or tuple(x.shape) != (cache.batch, cache.kv_heads, HEAD_DIM) or \
             not x.is_contiguous():
         raise ValueError("x must be contiguous [B, H, 128] matching the cache")
-    if positions.dtype != torch.int32 or positions.numel() != cache.batch:
-        raise ValueError("positions must be int32 [B]")
+    if positions.dtype != torch.int32 or positions.numel() != cache.batch or \
+            not positions.is_contiguous():
+        raise ValueError("positions must be contiguous int32 [B]")
     if tuple(window.shape) != (cache.batch, cache.kv_heads, CHUNK, HEAD_DIM) or \
             window.dtype != x.dtype or not window.is_contiguous():
         raise ValueError("window must be contiguous [B, H, 128, 128] of x's dtype")
     d = cache.desc()
+    dev = _on_device("append_rebalance", x, positions, window, cache.codes)
     st = load().kvarn_append_rebalance(x.data_ptr(), _dtype_code(x), positions.data_ptr(),
                                        window.data_ptr(), iters, flags, ctypes.byref(d),
-                                       _stream(stream))
+                                       _stream(stream, dev))
     _raise(st, "kvarn_append_rebalance")
 
 
@@ -224,21 +264,30 @@ def decode_attn(q: torch.Tensor, k: Cache, v: Cache, seq_lens: torch.Tensor,
     FLAG_ONE_SCALE."""
     if q.dim() != 3 or q.shape[2] != HEAD_DIM or not q.is_contiguous():
         raise ValueError("q must be contiguous [B, Hq, 128]")
-    if seq_lens.dtype != torch.int32 or seq_lens.numel() != k.batch:
-        raise ValueError("seq_lens must be int32 [B]")
+    if q.shape[0] != k.batch:
+        raise ValueError("q's batch differs from the caches'")
+    if seq_lens.dtype != torch.int32 or seq_lens.numel() != k.batch or \
+            not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be contiguous int32 [B]")
     B, Hq = q.shape[0], q.shape[1]
+    if out is not None and (out.dtype != torch.float32 or not out.is_contiguous() or
+                            tuple(out.shape) != (B, Hq, HEAD_DIM)):
+        raise ValueError("out must be contiguous fp32 [B, Hq, 128]")
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    kd, vd = k.desc(), v.desc()
+    dev = _on_device("decode_attn", q, seq_lens, out, workspace, k.codes, v.codes)
     if out is None:
-        out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=dev)
     if workspace is None:
-        workspace = decode_workspace(B, Hq, k.capacity, q.device)
+        workspace = decode_workspace(B, Hq, k.capacity, dev)
     if softmax_scale is None:
         softmax_scale = HEAD_DIM ** -0.5
-    kd, vd = k.desc(), v.desc()
     st = load().kvarn_decode_attn_ex(q.data_ptr(), _dtype_code(q), Hq, ctypes.byref(kd),
                                      ctypes.byref(vd), seq_lens.data_ptr(), softmax_scale,
                                      flags, out.data_ptr(), n_split, workspace.data_ptr(),
                                      workspace.numel() * workspace.element_size(),
-                                     _stream(stream))
+                                     _stream(stream, dev))
     _raise(st, "kvarn_decode_attn")
     return out
 
@@ -255,13 +304,18 @@ def token_error(x: torch.Tensor, cache: Cache, token_offset: int = 0, stream=Non
     if x.shape[0] != cache.batch or x.shape[1] != cache.kv_heads:
         raise ValueError("x batch/heads differ from the cache")
     shape = (x.shape[0], x.shape[1], x.shape[2])
-    if ratio is None:
-        ratio = torch.empty(shape, dtype=torch.float32, device=x.device)
-    if cosine is None:
-        cosine = torch.empty(shape, dtype=torch.float32, device=x.device)
+    for name, t in (("ratio", ratio), ("cosine", cosine)):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or
+                              tuple(t.shape) != shape):
+            raise ValueError(f"{name} must be contiguous fp32 [B, H, T] = {list(shape)}")
     d = cache.desc()
+    dev = _on_device("token_error", x, ratio, cosine, cache.codes)
+    if ratio is None:
+        ratio = torch.empty(shape, dtype=torch.float32, device=dev)
+    if cosine is None:
+        cosine = torch.empty(shape, dtype=torch.float32, device=dev)
     st = load().kvarn_token_error(x.data_ptr(), _dtype_code(x), x.stride(0), x.stride(1),
                                   x.stride(2), x.shape[2], token_offset, flags, ctypes.byref(d),
-                                  ratio.data_ptr(), cosine.data_ptr(), _stream(stream))
+                                  ratio.data_ptr(), cosine.data_ptr(), _stream(stream, dev))
     _raise(st, "kvarn_token_error")
     return ratio, cosine

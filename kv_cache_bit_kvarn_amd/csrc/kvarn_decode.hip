@@ -642,21 +642,22 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 
 }  // namespace
 
-// SIMDs of the current device (CUs x 4), queried once per device.
-static int device_simds() {
+// Compute units of the current device, queried once per device (an MI355X
+// has 256; that count is assumed if the query fails).
+int device_cus() {
   static std::atomic<int> cache[64];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1024;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
   int v = cache[dev].load(std::memory_order_relaxed);
   if (v > 0) return v;
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus <= 0)
     cus = 256;
-  v = 4 * cus;
-  cache[dev].store(v, std::memory_order_relaxed);
-  return v;
+  cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
 }
+static int device_simds() { return 4 * device_cus(); }
 
 // Splits per (sequence, kv-head, head group): about two single-wave
 // workgroups per SIMD in one round. Fewer leave SIMDs without a second wave

@@ -109,12 +109,8 @@ __global__ __launch_bounds__(64 * kWaves) void token_error_kernel(DiagArgs a) {
 hipError_t launch_token_error(const DiagArgs &a, hipStream_t s) {
   const int64_t total = (int64_t)a.batch * a.heads * a.tokens;
   if (total == 0) return hipSuccess;
-  int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
   const int64_t want = (total + kWaves - 1) / kWaves;
-  const int64_t cap = 8LL * (cus > 0 ? cus : 1);
+  const int64_t cap = 8LL * device_cus();
   const dim3 grid((unsigned)(want < cap ? want : cap));
   const bool rot = !(a.flags & KVARN_FLAG_NO_ROTATE);
   if (a.dtype == KVARN_DT_F32) {

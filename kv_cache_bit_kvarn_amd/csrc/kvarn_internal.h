@@ -57,7 +57,15 @@ __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u 
 struct FastDiv {
   uint32_t d, m, s;
 };
-FastDiv make_fastdiv(uint32_t d);
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  FastDiv f;
+  f.d = d;
+  f.s = 31 + l;
+  f.m = (uint32_t)(((1ull << f.s) + d - 1) / d);
+  return f;
+}
 __device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
   return (uint32_t)(((uint64_t)n * f.m) >> f.s);
 }
@@ -103,6 +111,7 @@ struct DecodeArgs {
   float *partial;  // [batch][q_heads][n_split][2 + D]
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+int device_cus();  // compute units of the current device, cached per device
 int decode_auto_splits(int batch, int kv_heads, int q_heads, int capacity);
 
 }  // namespace kvarn

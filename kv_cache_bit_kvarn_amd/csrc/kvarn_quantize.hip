@@ -58,16 +58,6 @@
 
 namespace kvarn {
 
-FastDiv make_fastdiv(uint32_t d) {
-  uint32_t l = 0;
-  while ((1ull << l) < d) ++l;
-  FastDiv f;
-  f.d = d;
-  f.s = 31 + l;
-  f.m = (uint32_t)(((1ull << f.s) + d - 1) / d);
-  return f;
-}
-
 namespace {
 
 constexpr int kThreads = 512;
@@ -669,13 +659,9 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
 
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t s) {
   if (a.nblocks == 0) return hipSuccess;
-  int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
   // two resident workgroups per CU (register-limited); each walks blocks
   // strided by the grid
-  const uint32_t resident = 2u * (uint32_t)(cus > 0 ? cus : 1);
+  const uint32_t resident = 2u * (uint32_t)device_cus();
   const uint32_t blocks = a.nblocks < resident ? a.nblocks : resident;
   const bool rot = !(a.flags & KVARN_FLAG_NO_ROTATE);
 #define KVARN_LAUNCH_QUANT(F32, ROT, POS) \

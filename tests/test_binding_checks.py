@@ -1,0 +1,72 @@
+"""The Python binding's argument checks, which need no GPU: host tensors,
+mismatched shapes and wrong output buffers are refused with ValueError before
+any pointer reaches the library (the kernels would otherwise read or write a
+host address or out of bounds)."""
+import pytest
+import torch
+
+import kv_cache_bit_kvarn_amd as kv
+
+
+def _cache(kind=kv.K, B=2, H=2, cap=256):
+    return kv.Cache.empty(B, H, cap, kind, device="cpu")
+
+
+def test_host_cache_refused():
+    c = _cache()
+    with pytest.raises(ValueError, match="GPU"):
+        c.desc()
+
+
+def test_cache_layout_checked():
+    c = _cache()
+    bad = kv.Cache(c.codes, c.row_scale[:, :, :128].contiguous(), c.col_scale, kv.K)
+    with pytest.raises(ValueError, match="row_scale"):
+        bad.desc()
+    bad = kv.Cache(c.codes, c.row_scale, c.col_scale.double(), kv.K)
+    with pytest.raises(ValueError, match="fp32"):
+        bad.desc()
+    bad = kv.Cache(c.codes, c.row_scale, c.col_scale, 5)
+    with pytest.raises(ValueError, match="kind"):
+        bad.desc()
+
+
+def test_quantize_host_tensors_refused():
+    x = torch.zeros((2, 2, 256, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        kv.quantize(x, _cache())
+
+
+def test_append_host_positions_refused():
+    x = torch.zeros((2, 2, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        kv.append(x, torch.zeros(2, dtype=torch.int32), _cache())
+    with pytest.raises(ValueError, match="int32"):
+        kv.append(x, torch.zeros(2, dtype=torch.int64), _cache())
+
+
+def test_decode_checks():
+    k, v = _cache(kv.K), _cache(kv.V)
+    q = torch.zeros((2, 8, 128), dtype=torch.bfloat16)
+    lens = torch.ones(2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="batch"):
+        kv.decode_attn(torch.zeros((3, 8, 128), dtype=torch.bfloat16), k, v, lens)
+    with pytest.raises(ValueError, match="out"):
+        kv.decode_attn(q, k, v, lens, out=torch.zeros((2, 8, 64), dtype=torch.float32))
+    with pytest.raises(ValueError, match="out"):
+        kv.decode_attn(q, k, v, lens, out=torch.zeros((2, 8, 128), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="out"):
+        kv.decode_attn(q, k, v, lens, out=torch.zeros((2, 128, 8)).transpose(1, 2))
+    with pytest.raises(ValueError, match="seq_lens"):
+        kv.decode_attn(q, k, v, torch.ones(3, dtype=torch.int32))
+    with pytest.raises(ValueError, match="GPU"):
+        kv.decode_attn(q, k, v, lens)
+
+
+def test_token_error_output_shapes():
+    c = _cache()
+    x = torch.zeros((2, 2, 256, 128), dtype=torch.float32)
+    with pytest.raises(ValueError, match="ratio"):
+        kv.token_error(x, c, ratio=torch.zeros((2, 2, 128)))
+    with pytest.raises(ValueError, match="cosine"):
+        kv.token_error(x, c, cosine=torch.zeros((2, 2, 256), dtype=torch.float64))

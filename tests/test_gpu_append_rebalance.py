@@ -24,7 +24,11 @@ def _unpacked(oracle, cache, kind):
             cache.row_scale.double().cpu().numpy(), cache.col_scale.double().cpu().numpy())
 
 
-def _run(kvarn, kind, dtype, B=3, H=2, cap=256):
+def _run(kvarn, kind, dtype, B=3, H=2, cap=256, oracle=None, flags=0):
+    """With KVARN_FLAG_NO_ROTATE the tokens are handed over rotated (rounded to
+    `dtype` after an fp64 rotation), and `hist` keeps the oracle input that
+    reproduces exactly what the GPU read: the scaled rotation is its own
+    inverse."""
     cache = kvarn.Cache.empty(B, H, cap, kind, device="cuda")
     plain = kvarn.Cache.empty(B, H, cap, kind, device="cuda")
     window = kvarn.append_window(B, H, dtype=dtype)
@@ -32,7 +36,12 @@ def _run(kvarn, kind, dtype, B=3, H=2, cap=256):
     hist = {}          # (b, position) -> token [H, D] (fp64 copy of what the GPU read)
     for step in range(STEPS):
         x = kvgen.new_tokens(61, 0, kind, B, H, 0.5, step=step, dtype=dtype, device="cuda")
-        xs = x.double().cpu().numpy()
+        if flags & kvarn.FLAG_NO_ROTATE:
+            xr = oracle.rotate(x.double().cpu().numpy())
+            x = torch.from_numpy(xr).to(dtype).cuda()
+            xs = oracle.rotate(x.double().cpu().numpy())
+        else:
+            xs = x.double().cpu().numpy()
         pos = np.full(B, -1, np.int32)
         for b in range(B):
             if step not in SKIPS[b]:
@@ -40,16 +49,18 @@ def _run(kvarn, kind, dtype, B=3, H=2, cap=256):
                 hist[(b, count[b])] = xs[b]
                 count[b] += 1
         p = torch.from_numpy(pos).cuda()
-        kvarn.append_rebalance(x, p, cache, window)
-        kvarn.append(x, p, plain)
+        kvarn.append_rebalance(x, p, cache, window, flags=flags)
+        kvarn.append(x, p, plain, flags=flags)
     torch.cuda.synchronize()
     return cache, plain, hist, count
 
 
 @pytest.mark.parametrize("kind", [kvgen.K, kvgen.V])
-@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_rebalance_at_close(kvarn, oracle, kind, dtype):
-    cache, plain, hist, count = _run(kvarn, kind, dtype)
+@pytest.mark.parametrize("dtype,no_rotate", [(torch.float32, False), (torch.bfloat16, False),
+                                             (torch.bfloat16, True)])
+def test_rebalance_at_close(kvarn, oracle, kind, dtype, no_rotate):
+    flags = kvarn.FLAG_NO_ROTATE if no_rotate else 0
+    cache, plain, hist, count = _run(kvarn, kind, dtype, oracle=oracle, flags=flags)
     assert count == [150, 140, 110]
     codes, rp, c = _unpacked(oracle, cache, kind)
     pc, prp, pcs = _unpacked(oracle, plain, kind)
@@ -77,14 +88,15 @@ def test_rebalance_at_close(kvarn, oracle, kind, dtype):
                     u = y / (rp1[0, h, 128 + i] * c1[0, h, 1])
                     assert oracle.boundary_mask(u)[mism[h, i]].all()
         # error of the closed chunk: re-balanced vs frozen column scales
-        x_t = torch.from_numpy(xs[None]).to(dtype).cuda()
+        x_t = torch.from_numpy(oracle.rotate(xs[None]) if no_rotate else xs[None]).to(dtype).cuda()
         sub = lambda cc: kvarn.Cache(cc.codes[b:b + 1], cc.row_scale[b:b + 1],  # noqa: E731
                                      cc.col_scale[b:b + 1], kind)
-        r1, q1 = kvarn.token_error(x_t, sub(cache))
-        r0, q0 = kvarn.token_error(x_t, sub(plain))
+        r1, q1 = kvarn.token_error(x_t, sub(cache), flags=flags)
+        r0, q0 = kvarn.token_error(x_t, sub(plain), flags=flags)
         e1 = float(((r1 - 1) ** 2 + 2 * r1 * (1 - q1)).mean())
         e0 = float(((r0 - 1) ** 2 + 2 * r0 * (1 - q0)).mean())
-        log(f"[test] rebalance kind={kind} {dtype} b={b}: {st}; relative squared error "
+        log(f"[test] rebalance kind={kind} {dtype} no_rotate={no_rotate} b={b}: {st}; "
+            f"relative squared error "
             f"re-balanced {e1:.5f}, frozen c (SC-11) {e0:.5f}")
     # sequence 2 never filled a chunk: identical to the plain append
     assert np.array_equal(codes[2], pc[2])

@@ -73,6 +73,69 @@ def test_append_no_rotate(kvarn, oracle, kind):
     assert not mism.any()
 
 
+def _rotated_bf16(oracle, x):
+    """x . H_128 / sqrt(128) in fp64, rounded to bf16: what a model with the
+    rotation absorbed into its weights hands over. Returned with the oracle
+    input that reproduces exactly those values: the scaled rotation is its
+    own inverse, so rotate(xr) rotated again is xr up to fp64 rounding."""
+    xr = torch.from_numpy(oracle.rotate(x.double().cpu().numpy())).to(torch.bfloat16)
+    return xr, oracle.rotate(xr.double().numpy())
+
+
+@pytest.mark.parametrize("kind", [kvgen.K, kvgen.V])
+@pytest.mark.parametrize("iters", [4, 0])
+def test_quantize_no_rotate_bf16(kvarn, oracle, kind, iters):
+    """bf16 pre-rotated K/V with the rotation skipped (the identity-tile MFMAs
+    and the first row step without the factor 128) against the oracle fed the
+    exact values the GPU read."""
+    x = kvgen.kv_tensor(51, 0, kind, 2, 3, 384, 0.5, dtype=torch.float32)
+    xr, x_eq = _rotated_bf16(oracle, x)
+    cache = kvarn.Cache.empty(2, 3, 384, kind, device="cuda")
+    kvarn.quantize(xr.cuda(), cache, iters=iters, flags=kvarn.FLAG_NO_ROTATE)
+    torch.cuda.synchronize()
+    ora = oracle.quantize_tensor(x_eq, iters=iters)
+    g = oracle.unpack(cache.codes.cpu().numpy(), kind=kind)
+    st = assert_quant_parity(oracle, ora, g, cache.row_scale.cpu().numpy(),
+                             cache.col_scale.cpu().numpy(), "no-rotate bf16")
+    log(f"[test] quantize no-rotate bf16 kind={kind} iters={iters}: {st}")
+
+
+@pytest.mark.parametrize("kind", [kvgen.K, kvgen.V])
+def test_append_no_rotate_bf16(kvarn, oracle, kind):
+    """bf16 pre-rotated tokens appended with the rotation skipped: opening
+    chunk 1 (column scales copied from chunk 0) and inside it."""
+    B, H, cap = 2, 2, 256
+    ck, rk, colk = kvgen.random_cache(52 + kind, B, H, cap)
+    cache = kvarn.Cache(ck.cuda(), rk.cuda(), colk.cuda(), kind)
+    codes = oracle.unpack(ck.numpy(), kind=kind)
+    rp, c = rk.double().numpy().copy(), colk.double().numpy().copy()
+    ys = {}
+    for step, p in enumerate((128, 129, 133)):
+        x = kvgen.new_tokens(53, 0, kind, B, H, 0.5, step=step, dtype=torch.float32)
+        xr, x_eq = _rotated_bf16(oracle, x)
+        ys[p] = xr.double().numpy()
+        pos = torch.full((B,), p, dtype=torch.int32)
+        kvarn.append(xr.cuda(), pos.cuda(), cache, flags=kvarn.FLAG_NO_ROTATE)
+        oracle.append(x_eq, pos.numpy(), codes, rp, c)
+    torch.cuda.synchronize()
+    g = oracle.unpack(cache.codes.cpu().numpy(), kind=kind)
+    np.testing.assert_allclose(cache.row_scale.cpu().numpy()[:, :, 128:134],
+                               rp[:, :, 128:134], rtol=SCALE_RTOL, atol=0)
+    np.testing.assert_allclose(cache.col_scale.cpu().numpy(), c, rtol=SCALE_RTOL, atol=0)
+    mism = g != codes
+    for p in (128, 129, 133):
+        for b in range(B):
+            for h in range(H):
+                if mism[b, h, p].any():
+                    u = ys[p][b, h] / (rp[b, h, p] * c[b, h, 1])
+                    assert oracle.boundary_mask(u)[mism[b, h, p]].all()
+    mism[:, :, [128, 129, 133]] = False
+    if kind == kvgen.V:
+        assert np.all(g[:, :, [130, 131]] == 0)
+        mism[:, :, [130, 131]] = False
+    assert not mism.any()
+
+
 def _random_caches(kv, B, Hkv, cap, seed):
     ck, rk, colk = kvgen.random_cache(seed, B, Hkv, cap)
     cv, rv, colv = kvgen.random_cache(seed + 1000, B, Hkv, cap)
