@@ -589,7 +589,7 @@ def steady_workload(kv, kvgen, torch, wl, args, dev):
     res = {"config": {"layers": L, "batch": B, "kv_heads": Hkv, "q_heads": Hq, "tokens": T,
                       "step": "append K, V + decode per layer (HIP graph replays)"},
            "step_ms": round(ms_step, 4), "step_tokens_per_s": round(B / (ms_step / 1e3), 1),
-           "decode_tokens_per_s": round(B / (L * d_us / 1e3), 1),
+           "decode_tokens_per_s": round(B / (L * d_us * 1e-6), 1),
            "decode_us_per_launch": round(d_us, 2), "append_us_per_launch": round(a_us, 2),
            "decode": hbm_entry(nb, d_us)}
     del caches, news, qs, out, ws
