@@ -252,6 +252,31 @@ int kvarn_decode_attn_ex(const void *q, int32_t q_dtype, int32_t q_heads,
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * kvarn_decode_attn_noalloc -- kvarn_decode_attn_ex without a workspace
+ * argument and without any allocation, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. The split partial results go to a device array
+ * inside the library, KVARN_NOALLOC_SCRATCH_BYTES per GPU, held by each GPU
+ * the library runs on until the process ends.
+ *
+ * Same arguments, results and kernels as kvarn_decode_attn_ex. The partials
+ * of one call take batch * q_heads * splits * 130 * 4 bytes, splits being
+ * n_split (clamped to [1, capacity/128]) or the library's choice for
+ * n_split == 0; a call that needs more than KVARN_NOALLOC_SCRATCH_BYTES
+ * returns KVARN_ERR_WORKSPACE and enqueues nothing. The work runs on the
+ * current device, which must be the device of `stream`.
+ * Every call on one GPU shares that GPU's array: two calls that may overlap
+ * in time on one GPU (different streams, different host threads) race and
+ * must be ordered by the caller.
+ */
+enum { KVARN_NOALLOC_SCRATCH_BYTES = 16 << 20 };
+int kvarn_decode_attn_noalloc(const void *q, int32_t q_dtype, int32_t q_heads,
+                              const kvarn_cache *k, const kvarn_cache *v,
+                              const int32_t *seq_lens, float softmax_scale,
+                              uint32_t flags, float *out, int32_t n_split,
+                              void *stream);
+
+/*
  * kvarn_token_error -- per-token magnitude and direction of the cache's
  * reconstruction against the original K or V (rndamp article on KVarN,
  * "The Problem": the error of K is one of token magnitude rather than of

@@ -29,7 +29,9 @@ K, V = 0, 1
 
 EXPORTED = ("kvarn_quantize", "kvarn_quantize_ex", "kvarn_append", "kvarn_append_ex",
             "kvarn_decode_workspace_bytes", "kvarn_decode_attn", "kvarn_decode_attn_ex",
-            "kvarn_append_rebalance", "kvarn_token_error", "kvarn_status_string")
+            "kvarn_decode_attn_noalloc", "kvarn_append_rebalance", "kvarn_token_error",
+            "kvarn_status_string")
+NOALLOC_SCRATCH_BYTES = 16 << 20   # KVARN_NOALLOC_SCRATCH_BYTES
 
 
 class KvarnError(RuntimeError):
@@ -77,6 +79,9 @@ def load(path: str | None = None):
     L.kvarn_decode_attn_ex.argtypes = [vp, i32, i32, cd, cd, vp, ctypes.c_float, u32, vp, i32,
                                        vp, ctypes.c_size_t, vp]
     L.kvarn_decode_attn_ex.restype = ctypes.c_int
+    L.kvarn_decode_attn_noalloc.argtypes = [vp, i32, i32, cd, cd, vp, ctypes.c_float, u32, vp,
+                                            i32, vp]
+    L.kvarn_decode_attn_noalloc.restype = ctypes.c_int
     L.kvarn_append_rebalance.argtypes = [vp, i32, vp, vp, i32, u32, cd, vp]
     L.kvarn_append_rebalance.restype = ctypes.c_int
     L.kvarn_token_error.argtypes = [vp, i32, i64, i64, i64, i32, i32, u32, cd, vp, vp, vp]
@@ -289,6 +294,35 @@ def decode_attn(q: torch.Tensor, k: Cache, v: Cache, seq_lens: torch.Tensor,
                                      workspace.numel() * workspace.element_size(),
                                      _stream(stream, dev))
     _raise(st, "kvarn_decode_attn")
+    return out
+
+
+def decode_attn_noalloc(q: torch.Tensor, k: Cache, v: Cache, seq_lens: torch.Tensor,
+                        out: torch.Tensor, softmax_scale: float | None = None, n_split: int = 0,
+                        stream=None, flags: int = 0) -> torch.Tensor:
+    """decode_attn without a workspace: the library keeps the split partials
+    in its own fixed device array (NOALLOC_SCRATCH_BYTES per GPU) and the call
+    allocates nothing, so `out` must be given. Calls that may overlap in time
+    on one GPU race on that array."""
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM or not q.is_contiguous():
+        raise ValueError("q must be contiguous [B, Hq, 128]")
+    if q.shape[0] != k.batch:
+        raise ValueError("q's batch differs from the caches'")
+    if seq_lens.dtype != torch.int32 or seq_lens.numel() != k.batch or \
+            not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be contiguous int32 [B]")
+    B, Hq = q.shape[0], q.shape[1]
+    if out.dtype != torch.float32 or not out.is_contiguous() or \
+            tuple(out.shape) != (B, Hq, HEAD_DIM):
+        raise ValueError("out must be contiguous fp32 [B, Hq, 128]")
+    kd, vd = k.desc(), v.desc()
+    dev = _on_device("decode_attn_noalloc", q, seq_lens, out, k.codes, v.codes)
+    if softmax_scale is None:
+        softmax_scale = HEAD_DIM ** -0.5
+    st = load().kvarn_decode_attn_noalloc(q.data_ptr(), _dtype_code(q), Hq, ctypes.byref(kd),
+                                          ctypes.byref(vd), seq_lens.data_ptr(), softmax_scale,
+                                          flags, out.data_ptr(), n_split, _stream(stream, dev))
+    _raise(st, "kvarn_decode_attn_noalloc")
     return out
 
 

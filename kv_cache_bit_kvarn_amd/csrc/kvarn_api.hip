@@ -30,6 +30,65 @@ int dtype_size(int32_t dtype) {
 
 int from_hip(hipError_t e) { return e == hipSuccess ? KVARN_OK : KVARN_ERR_HIP; }
 
+// Checks shared by the decode entry points (everything but the workspace).
+int check_decode(const void *q, int32_t q_dtype, int32_t q_heads, const kvarn_cache *k,
+                 const kvarn_cache *v, const int32_t *seq_lens, float softmax_scale,
+                 uint32_t flags, const float *out, int32_t n_split) {
+  if (flags & ~(uint32_t)(KVARN_FLAG_NO_ROTATE | KVARN_FLAG_ONE_SCALE)) return KVARN_ERR_FLAGS;
+  if (!q || !seq_lens || !out) return KVARN_ERR_NULL;
+  int st = check_cache(k);
+  if (st != KVARN_OK) return st;
+  st = check_cache(v);
+  if (st != KVARN_OK) return st;
+  if (k->kind != KVARN_K || v->kind != KVARN_V) return KVARN_ERR_DTYPE;
+  if (!dtype_size(q_dtype)) return KVARN_ERR_DTYPE;
+  if (k->batch != v->batch || k->kv_heads != v->kv_heads || k->capacity != v->capacity)
+    return KVARN_ERR_SHAPE;
+  if (q_heads <= 0 || k->kv_heads <= 0 || q_heads % k->kv_heads) return KVARN_ERR_SHAPE;
+  if (q_heads / k->kv_heads > GQA_MAX) return KVARN_ERR_SHAPE;
+  if (k->capacity <= 0 || k->batch > 65535 || k->kv_heads > 65535 || q_heads > 65535)
+    return KVARN_ERR_SHAPE;
+  if (!(softmax_scale == softmax_scale)) return KVARN_ERR_SHAPE;  // NaN
+  if (!aligned16(q) || !aligned16(out)) return KVARN_ERR_ALIGN;
+  if (n_split < 0) return KVARN_ERR_SHAPE;
+  return KVARN_OK;
+}
+
+// Split count of a call with valid arguments (HIP may be queried).
+int decode_splits(int32_t q_heads, const kvarn_cache *k, int32_t n_split) {
+  const int nch = k->capacity / T;
+  int ns = n_split == 0 ? decode_auto_splits(k->batch, k->kv_heads, q_heads, k->capacity) : n_split;
+  if (ns > nch) ns = nch;
+  if (ns < 1) ns = 1;
+  return ns;
+}
+
+DecodeArgs decode_args(const void *q, int32_t q_dtype, int32_t q_heads, const kvarn_cache *k,
+                       const kvarn_cache *v, const int32_t *seq_lens, float softmax_scale,
+                       uint32_t flags, float *out, int ns, void *partial) {
+  DecodeArgs a;
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.batch = k->batch;
+  a.q_heads = q_heads;
+  a.kv_heads = k->kv_heads;
+  a.capacity = k->capacity;
+  a.n_split = ns;
+  a.k_codes = k->codes;
+  a.v_codes = v->codes;
+  a.k_row = k->row_scale;
+  a.k_col = k->col_scale;
+  a.v_row = v->row_scale;
+  a.v_col = v->col_scale;
+  a.lens = seq_lens;
+  a.scale = softmax_scale;
+  a.flags = flags;
+  a.out = out;
+  a.partial = static_cast<float *>(partial);
+  return a;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -216,52 +275,35 @@ int kvarn_decode_attn_ex(const void *q, int32_t q_dtype, int32_t q_heads, const 
                          const kvarn_cache *v, const int32_t *seq_lens, float softmax_scale,
                          uint32_t flags, float *out, int32_t n_split, void *workspace,
                          size_t workspace_bytes, void *stream) {
-  if (flags & ~(uint32_t)(KVARN_FLAG_NO_ROTATE | KVARN_FLAG_ONE_SCALE)) return KVARN_ERR_FLAGS;
-  if (!q || !seq_lens || !out) return KVARN_ERR_NULL;
-  int st = check_cache(k);
+  int st = check_decode(q, q_dtype, q_heads, k, v, seq_lens, softmax_scale, flags, out, n_split);
   if (st != KVARN_OK) return st;
-  st = check_cache(v);
-  if (st != KVARN_OK) return st;
-  if (k->kind != KVARN_K || v->kind != KVARN_V) return KVARN_ERR_DTYPE;
-  if (!dtype_size(q_dtype)) return KVARN_ERR_DTYPE;
-  if (k->batch != v->batch || k->kv_heads != v->kv_heads || k->capacity != v->capacity)
-    return KVARN_ERR_SHAPE;
-  if (q_heads <= 0 || k->kv_heads <= 0 || q_heads % k->kv_heads) return KVARN_ERR_SHAPE;
-  if (q_heads / k->kv_heads > GQA_MAX) return KVARN_ERR_SHAPE;
-  if (k->capacity <= 0 || k->batch > 65535 || k->kv_heads > 65535 || q_heads > 65535)
-    return KVARN_ERR_SHAPE;
-  if (!(softmax_scale == softmax_scale)) return KVARN_ERR_SHAPE;  // NaN
-  if (!aligned16(q) || !aligned16(out)) return KVARN_ERR_ALIGN;
-  if (n_split < 0) return KVARN_ERR_SHAPE;
   if (k->batch == 0) return KVARN_OK;
   const size_t need = kvarn_decode_workspace_bytes(k->batch, q_heads, k->capacity);
   if (!workspace) return KVARN_ERR_NULL;
   if (workspace_bytes < need) return KVARN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return KVARN_ERR_ALIGN;
   // arguments are valid: from here on HIP may be queried
-  const int nch = k->capacity / T;
-  int ns = n_split == 0 ? decode_auto_splits(k->batch, k->kv_heads, q_heads, k->capacity) : n_split;
-  if (ns > nch) ns = nch;
-  if (ns < 1) ns = 1;
-  DecodeArgs a;
-  a.q = q;
-  a.q_dtype = q_dtype;
-  a.batch = k->batch;
-  a.q_heads = q_heads;
-  a.kv_heads = k->kv_heads;
-  a.capacity = k->capacity;
-  a.n_split = ns;
-  a.k_codes = k->codes;
-  a.v_codes = v->codes;
-  a.k_row = k->row_scale;
-  a.k_col = k->col_scale;
-  a.v_row = v->row_scale;
-  a.v_col = v->col_scale;
-  a.lens = seq_lens;
-  a.scale = softmax_scale;
-  a.flags = flags;
-  a.out = out;
-  a.partial = static_cast<float *>(workspace);
+  const int ns = decode_splits(q_heads, k, n_split);
+  const DecodeArgs a = decode_args(q, q_dtype, q_heads, k, v, seq_lens, softmax_scale, flags,
+                                   out, ns, workspace);
+  return from_hip(launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+int kvarn_decode_attn_noalloc(const void *q, int32_t q_dtype, int32_t q_heads,
+                              const kvarn_cache *k, const kvarn_cache *v,
+                              const int32_t *seq_lens, float softmax_scale, uint32_t flags,
+                              float *out, int32_t n_split, void *stream) {
+  int st = check_decode(q, q_dtype, q_heads, k, v, seq_lens, softmax_scale, flags, out, n_split);
+  if (st != KVARN_OK) return st;
+  if (k->batch == 0) return KVARN_OK;
+  const int ns = decode_splits(q_heads, k, n_split);
+  const size_t need = (size_t)k->batch * q_heads * (size_t)ns * (2 + D) * sizeof(float);
+  if (need > (size_t)KVARN_NOALLOC_SCRATCH_BYTES) return KVARN_ERR_WORKSPACE;
+  hipError_t e = hipSuccess;
+  void *partial = noalloc_scratch(&e);
+  if (!partial) return from_hip(e);
+  const DecodeArgs a = decode_args(q, q_dtype, q_heads, k, v, seq_lens, softmax_scale, flags,
+                                   out, ns, partial);
   return from_hip(launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 

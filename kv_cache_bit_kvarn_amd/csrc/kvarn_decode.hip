@@ -35,6 +35,7 @@
 // decode_combine: grid (q_heads, batch): log-sum-exp merge of the partials
 // (m, l, acc[128]), then the inverse rotation.
 #include <atomic>
+#include <mutex>
 
 #include "kvarn_internal.h"
 
@@ -641,6 +642,35 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 }
 
 }  // namespace
+
+// The split partials of kvarn_decode_attn_noalloc. In host code `scratch`
+// names a host-side stand-in, not device memory: kernels get the address that
+// hipGetSymbolAddress returns for the current device (each GPU holds its own
+// copy), never the array's name.
+static __device__ __align__(256) uint8_t scratch[KVARN_NOALLOC_SCRATCH_BYTES];
+
+void *noalloc_scratch(hipError_t *err) {
+  static std::mutex mu;
+  static void *addr[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess && (dev < 0 || dev >= 64)) e = hipErrorInvalidDevice;
+  if (e != hipSuccess) {
+    *err = e;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
 
 // Compute units of the current device, queried once per device (an MI355X
 // has 256; that count is assumed if the query fails).

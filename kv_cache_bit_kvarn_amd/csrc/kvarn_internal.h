@@ -112,6 +112,10 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 int device_cus();  // compute units of the current device, cached per device
+// Device address of the current device's copy of the library's fixed decode
+// scratch array (KVARN_NOALLOC_SCRATCH_BYTES), taken once per device; nullptr
+// with *err set when the query fails.
+void *noalloc_scratch(hipError_t *err);
 int decode_auto_splits(int batch, int kv_heads, int q_heads, int capacity);
 
 }  // namespace kvarn

@@ -43,6 +43,11 @@ hipError_t launch_token_error(const DiagArgs &a, hipStream_t) {
   return g_result;
 }
 int decode_auto_splits(int, int, int, int capacity) { return capacity / T; }
+static int g_scratch_queries = 0;
+void *noalloc_scratch(hipError_t *) {
+  ++g_scratch_queries;
+  return reinterpret_cast<void *>(0xC0000);
+}
 
 }  // namespace kvarn
 
@@ -199,6 +204,28 @@ static void check_decode() {
   CHECK(g_decode.n_split == 3);
 }
 
+static void check_decode_noalloc() {
+  kvarn_cache k = cache(2, 4, 1024, KVARN_K), v = cache(2, 4, 1024, KVARN_V);
+  const int32_t *lens = static_cast<int32_t *>(P(0x50000));
+  float *out = static_cast<float *>(P(0x80000));
+  g_calls = 0;
+  g_scratch_queries = 0;
+  CHECK(kvarn_decode_attn_noalloc(nullptr, KVARN_DT_BF16, 16, &k, &v, lens, 0.1f, 0u, out, 0,
+                                  nullptr) == KVARN_ERR_NULL);
+  CHECK(kvarn_decode_attn_noalloc(P(0x40000), KVARN_DT_BF16, 14, &k, &v, lens, 0.1f, 0u, out, 0,
+                                  nullptr) == KVARN_ERR_SHAPE);
+  // partials beyond the fixed array: 64 sequences x 64 query heads x 64 splits x 520 B
+  kvarn_cache kb = cache(64, 8, 128 * 1024, KVARN_K), vb = cache(64, 8, 128 * 1024, KVARN_V);
+  CHECK(kvarn_decode_attn_noalloc(P(0x40000), KVARN_DT_BF16, 64, &kb, &vb, lens, 0.1f, 0u, out,
+                                  64, nullptr) == KVARN_ERR_WORKSPACE);
+  CHECK(g_calls == 0 && g_scratch_queries == 0);
+  CHECK(kvarn_decode_attn_noalloc(P(0x40000), KVARN_DT_BF16, 16, &k, &v, lens, 0.5f,
+                                  KVARN_FLAG_ONE_SCALE, out, 0, nullptr) == KVARN_OK);
+  CHECK(g_calls == 1 && g_scratch_queries == 1);
+  CHECK(g_decode.partial == P(0xC0000) && g_decode.n_split == 8 && g_decode.scale == 0.5f);
+  CHECK(g_decode.flags == KVARN_FLAG_ONE_SCALE);
+}
+
 static void check_token_error() {
   kvarn_cache c = cache(2, 2, 256, KVARN_K);
   float *r = static_cast<float *>(P(0xA0000)), *q = static_cast<float *>(P(0xB0000));
@@ -229,6 +256,7 @@ int main() {
   check_quantize();
   check_append();
   check_decode();
+  check_decode_noalloc();
   check_token_error();
   check_status_strings();
   if (failures) {
