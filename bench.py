@@ -106,11 +106,11 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "quantize_block_kernel<bf16>": ["kv_cache_bit_kvarn_amd/csrc/kvarn_quantize.hip",
                                     "kv_cache_bit_kvarn_amd/csrc/kvarn_internal.h"],
-    "decode_split_kernel + decode_combine_kernel": [
+    "decode_kernel": [
         "kv_cache_bit_kvarn_amd/csrc/kvarn_decode.hip",
         "kv_cache_bit_kvarn_amd/csrc/kvarn_internal.h"],
 }
-DECODE_KERNELS = "decode_split_kernel + decode_combine_kernel"
+DECODE_KERNELS = "decode_kernel"
 
 
 def sources_digest(kernel: str) -> str:

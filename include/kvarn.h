@@ -38,7 +38,8 @@ extern "C" {
 enum {
     KVARN_HEAD_DIM = 128,   /* channels per head (power of two for the rotation) */
     KVARN_CHUNK = 128,      /* tokens per quantization block */
-    KVARN_CHUNK_BYTES = 4096 /* packed 2-bit codes of one 128 x 128 block */
+    KVARN_CHUNK_BYTES = 4096, /* packed 2-bit codes of one 128 x 128 block */
+    KVARN_DECODE_WAVES = 4    /* decode splits per workgroup */
 };
 
 typedef enum {
@@ -209,8 +210,9 @@ int kvarn_append_rebalance(const void *x, int32_t dtype,
 
 /*
  * kvarn_decode_workspace_bytes -- (host only) bytes of device workspace that
- * kvarn_decode_attn needs for these sizes (split-KV partial results). Returns
- * 0 for invalid sizes.
+ * kvarn_decode_attn needs for these sizes: one int32 counter per (sequence,
+ * query head) rounded up to 256 bytes, then the split-KV partial results of
+ * the largest split count the capacity allows. Returns 0 for invalid sizes.
  */
 size_t kvarn_decode_workspace_bytes(int32_t batch, int32_t q_heads,
                                     int32_t capacity);
@@ -234,9 +236,15 @@ size_t kvarn_decode_workspace_bytes(int32_t batch, int32_t q_heads,
  * seq_lens   (device) int32 [batch].
  * out        (device) fp32 [batch][q_heads][128], original basis.
  * n_split    number of token splits per (b, kv-head); 0 lets the library
- *            choose. Clamped to [1, capacity/128].
+ *            choose. Rounded up to a multiple of KVARN_DECODE_WAVES (the
+ *            splits of one workgroup) and clamped to [KVARN_DECODE_WAVES,
+ *            capacity/128 rounded up to that multiple]. Each sequence's used
+ *            chunks are spread evenly over the splits.
  * workspace  (device) at least kvarn_decode_workspace_bytes(batch, q_heads,
- *            capacity) bytes, 16-byte aligned; contents are scratch.
+ *            capacity) bytes, 16-byte aligned. Its leading counter bytes must
+ *            be zero before the first call (a zero-filled allocation); every
+ *            call leaves them zero again, the rest is scratch. Calls that
+ *            share a workspace must not overlap in time.
  */
 int kvarn_decode_attn(const void *q, int32_t q_dtype, int32_t q_heads,
                       const kvarn_cache *k, const kvarn_cache *v,

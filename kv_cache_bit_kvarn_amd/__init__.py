@@ -256,8 +256,10 @@ def decode_workspace_bytes(batch: int, q_heads: int, capacity: int) -> int:
 
 
 def decode_workspace(batch: int, q_heads: int, capacity: int, device="cuda") -> torch.Tensor:
+    """A decode workspace, zero-filled: its leading counters must be zero
+    before the first call, and every call leaves them zero."""
     n = decode_workspace_bytes(batch, q_heads, capacity)
-    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+    return torch.zeros(max(n, 16), dtype=torch.uint8, device=device)
 
 
 def decode_attn(q: torch.Tensor, k: Cache, v: Cache, seq_lens: torch.Tensor,

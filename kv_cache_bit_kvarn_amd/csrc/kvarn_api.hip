@@ -54,18 +54,21 @@ int check_decode(const void *q, int32_t q_dtype, int32_t q_heads, const kvarn_ca
   return KVARN_OK;
 }
 
-// Split count of a call with valid arguments (HIP may be queried).
-int decode_splits(int32_t q_heads, const kvarn_cache *k, int32_t n_split) {
-  const int nch = k->capacity / T;
-  int ns = n_split == 0 ? decode_auto_splits(k->batch, k->kv_heads, q_heads, k->capacity) : n_split;
-  if (ns > nch) ns = nch;
-  if (ns < 1) ns = 1;
-  return ns;
+// Workgroups per row of a call with valid arguments (HIP may be queried):
+// n_split splits rounded up to whole workgroups, at most one split per chunk
+// of capacity (rounded up to a workgroup), or the library's choice for 0.
+int decode_wgs(int32_t q_heads, const kvarn_cache *k, int32_t n_split) {
+  const int max_wg = decode_max_wgs(k->capacity);
+  int nw = n_split == 0 ? decode_auto_wgs(k->batch, k->kv_heads, q_heads, k->capacity)
+                        : (int)(((int64_t)n_split + KVARN_DECODE_WAVES - 1) / KVARN_DECODE_WAVES);
+  if (nw > max_wg) nw = max_wg;
+  if (nw < 1) nw = 1;
+  return nw;
 }
 
 DecodeArgs decode_args(const void *q, int32_t q_dtype, int32_t q_heads, const kvarn_cache *k,
                        const kvarn_cache *v, const int32_t *seq_lens, float softmax_scale,
-                       uint32_t flags, float *out, int ns, void *partial) {
+                       uint32_t flags, float *out, int n_wg, void *workspace) {
   DecodeArgs a;
   a.q = q;
   a.q_dtype = q_dtype;
@@ -73,7 +76,7 @@ DecodeArgs decode_args(const void *q, int32_t q_dtype, int32_t q_heads, const kv
   a.q_heads = q_heads;
   a.kv_heads = k->kv_heads;
   a.capacity = k->capacity;
-  a.n_split = ns;
+  a.n_wg = n_wg;
   a.k_codes = k->codes;
   a.v_codes = v->codes;
   a.k_row = k->row_scale;
@@ -84,7 +87,9 @@ DecodeArgs decode_args(const void *q, int32_t q_dtype, int32_t q_heads, const kv
   a.scale = softmax_scale;
   a.flags = flags;
   a.out = out;
-  a.partial = static_cast<float *>(partial);
+  a.counters = static_cast<int32_t *>(workspace);
+  a.partial = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                        decode_counter_bytes(k->batch, q_heads));
   return a;
 }
 
@@ -268,7 +273,8 @@ int kvarn_token_error(const void *x, int32_t dtype, int64_t stride_b, int64_t st
 
 size_t kvarn_decode_workspace_bytes(int32_t batch, int32_t q_heads, int32_t capacity) {
   if (batch < 0 || q_heads < 0 || capacity < 0 || capacity % T) return 0;
-  return (size_t)batch * q_heads * (size_t)(capacity / T) * (2 + D) * sizeof(float);
+  return decode_counter_bytes(batch, q_heads) +
+         decode_partial_bytes(batch, q_heads, decode_max_wgs(capacity));
 }
 
 int kvarn_decode_attn_ex(const void *q, int32_t q_dtype, int32_t q_heads, const kvarn_cache *k,
@@ -283,9 +289,9 @@ int kvarn_decode_attn_ex(const void *q, int32_t q_dtype, int32_t q_heads, const 
   if (workspace_bytes < need) return KVARN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return KVARN_ERR_ALIGN;
   // arguments are valid: from here on HIP may be queried
-  const int ns = decode_splits(q_heads, k, n_split);
+  const int nw = decode_wgs(q_heads, k, n_split);
   const DecodeArgs a = decode_args(q, q_dtype, q_heads, k, v, seq_lens, softmax_scale, flags,
-                                   out, ns, workspace);
+                                   out, nw, workspace);
   return from_hip(launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -296,14 +302,15 @@ int kvarn_decode_attn_noalloc(const void *q, int32_t q_dtype, int32_t q_heads,
   int st = check_decode(q, q_dtype, q_heads, k, v, seq_lens, softmax_scale, flags, out, n_split);
   if (st != KVARN_OK) return st;
   if (k->batch == 0) return KVARN_OK;
-  const int ns = decode_splits(q_heads, k, n_split);
-  const size_t need = (size_t)k->batch * q_heads * (size_t)ns * (2 + D) * sizeof(float);
+  const int nw = decode_wgs(q_heads, k, n_split);
+  const size_t need = decode_counter_bytes(k->batch, q_heads) +
+                      decode_partial_bytes(k->batch, q_heads, nw);
   if (need > (size_t)KVARN_NOALLOC_SCRATCH_BYTES) return KVARN_ERR_WORKSPACE;
   hipError_t e = hipSuccess;
-  void *partial = noalloc_scratch(&e);
-  if (!partial) return from_hip(e);
+  void *scratch = noalloc_scratch(&e);
+  if (!scratch) return from_hip(e);
   const DecodeArgs a = decode_args(q, q_dtype, q_heads, k, v, seq_lens, softmax_scale, flags,
-                                   out, ns, partial);
+                                   out, nw, scratch);
   return from_hip(launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -47,7 +47,8 @@ typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int HG = 4;                       // query heads per workgroup
+constexpr int HG = 4;                       // query heads per wave (and per workgroup)
+constexpr int kDecWaves = KVARN_DECODE_WAVES;  // waves (splits) per workgroup
 constexpr uint32_t kFieldMask = 0x33333333u;  // low 2 bits of every 4-bit field
 constexpr uint32_t kFp4Neg3Half = 0xBBBBBBBBu;  // e2m1 -1.5 in every field
 
@@ -422,27 +423,109 @@ __device__ __forceinline__ void process_chunk(DecSmem &sm, SplitState &st, const
   }
 }
 
+// Last step for one query head, by one wave: lane l holds channels 2 l and
+// 2 l + 1 of the merged numerator (x0, x1) and every lane the denominator L;
+// out = (x / L) H_128 / sqrt(128), or x / L when the rotation is absorbed.
+// The inverse rotation regroups the channels so that lane l holds channels
+// l and l + 64 (bit 6 in the lane, bits 0..5 across lanes) and runs the
+// butterflies on lane exchanges.
+template <bool kRotate>
+__device__ __forceinline__ void finalize_head(float x0, float x1, float L, int lane, float *out) {
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  x0 *= inv;
+  x1 *= inv;
+  if constexpr (kRotate) {
+    const float e0 = __shfl(x0, lane >> 1, 64), o0 = __shfl(x1, lane >> 1, 64);
+    const float e1 = __shfl(x0, 32 + (lane >> 1), 64), o1 = __shfl(x1, 32 + (lane >> 1), 64);
+    float y0 = (lane & 1) ? o0 : e0;  // channel lane
+    float y1 = (lane & 1) ? o1 : e1;  // channel lane + 64
+    {
+      const float s0 = y0 + y1, d0 = y0 - y1;
+      y0 = s0;
+      y1 = d0;
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const float p0 = __shfl_xor(y0, m, 64), p1 = __shfl_xor(y1, m, 64);
+      const bool upper = (lane & m) != 0;
+      y0 = upper ? p0 - y0 : y0 + p0;
+      y1 = upper ? p1 - y1 : y1 + p1;
+    }
+    out[lane] = y0 * kInvSqrtD;
+    out[lane + 64] = y1 * kInvSqrtD;
+  } else {
+    *reinterpret_cast<f32x2 *>(out + 2 * lane) = f32x2{x0, x1};
+  }
+}
+
+// Accesses to memory shared by the workgroups of one launch, coherent across
+// the XCDs (agent scope; the device emits them with the system-coherence bit
+// and no cache maintenance).
+__device__ __forceinline__ void coherent_store(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void coherent_store2(float *p, f32x2 v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t *>(p), __builtin_bit_cast(uint64_t, v),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x2 coherent_load2(const float *p) {
+  return __builtin_bit_cast(
+      f32x2, __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// The four waves' results of a workgroup, merged in LDS.
+struct MergeSmem {
+  float m[kDecWaves][HG];
+  float l[kDecWaves][HG];
+  alignas(16) float acc[kDecWaves][HG][D];
+  int last;
+};
+
 // kRotate = false: the query comes rotated (rotation absorbed into the model's
 // weights); kTwoScales = false: column scales taken as 1 (ablation).
+//
+// One workgroup = four waves = four consecutive splits of one (sequence,
+// kv-head, head group). A sequence's used chunks are spread evenly over the
+// n_wg * 4 splits of its row (counts differ by at most one; splits past its
+// length get none). After the chunk loop the four waves merge their
+// (m, l, acc) in LDS, and wave h then carries head h0 + h: with one
+// workgroup per row it writes the output directly; otherwise it writes the
+// workgroup's partial, and the workgroup that finishes last (a counter per
+// row in the workspace, reset by that workgroup) merges the row's partials
+// and writes the output, so no second launch is needed.
 template <bool kRotate, bool kTwoScales>
-__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
-  __shared__ DecSmem sm;
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeArgs a) {
+  __shared__ DecSmem sms[kDecWaves];
+  __shared__ MergeSmem mg;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  DecSmem &sm = sms[wv];
   const int G = a.q_heads / a.kv_heads;
   const int n_hg = (G + HG - 1) / HG;
-  const int split = blockIdx.x % a.n_split, hg = blockIdx.x / a.n_split;
+  const int wgs = blockIdx.x % a.n_wg, hg = blockIdx.x / a.n_wg;
   const int g = blockIdx.y, b = blockIdx.z;
   const int h0 = hg * HG, nh = min(HG, G - h0);  // query heads g * G + h0 + [0, nh)
   const int nch = a.capacity / T;
   const int len = a.lens[b];
   const bool valid = len >= 1 && len <= a.capacity;
   const int used = valid ? (len + T - 1) / T : 0;
-  const int per = (nch + a.n_split - 1) / a.n_split;
-  const int c0 = split * per;
+  const int n_split = a.n_wg * kDecWaves, split = wgs * kDecWaves + wv;
+#ifdef KVARN_DECODE_CAPACITY_RANGES
+  const int per = (nch + n_split - 1) / n_split;
+  const int c0 = min(split * per, used);
   const int c1 = min(c0 + per, used);
+#else
+  const int c0 = (int)((int64_t)split * used / n_split);
+  const int c1 = (int)((int64_t)(split + 1) * used / n_split);
+#endif
   const int64_t bg = (int64_t)b * a.kv_heads + g;
   const int64_t qh0 = (int64_t)b * a.q_heads + (int64_t)g * G + h0;
-  (void)n_hg;
+  const int64_t row = bg * n_hg + hg;  // counter index
 
   // ---- query: lane (slot n, head hl) keeps the channels of its slot,
   // slot_elem(n, j) = c0 + (n & 1) + 2 j, and rotates them in registers: bits
@@ -534,111 +617,97 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     cur = nxt;
   }
 
-  // ---- partial results (m, l, acc) of head h0 + (lane >> 4) for this split ----
-  const int h = lane >> 4, n = lane & 15;
-  const float lsum = group_sum<16>(st.l_run);
-  if (h < nh) {
-    float *pp = a.partial + ((qh0 + h) * a.n_split + split) * (2 + D);
+  // ---- the four waves' (m, l, acc) meet in LDS; wave h then merges head h ----
+  {
+    const int h = lane >> 4, n = lane & 15;
+    const float lsum = group_sum<16>(st.l_run);
     if (n == 0) {
-      pp[0] = st.m_run;
-      pp[1] = lsum;
+      mg.m[wv][h] = st.m_run;
+      mg.l[wv][h] = lsum;
     }
     // 2: the code operand carries c/2
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) pp[2 + 16 * ct + n] = 2.f * st.acc[ct];
+    for (int ct = 0; ct < 8; ++ct) mg.acc[wv][h][16 * ct + n] = 2.f * st.acc[ct];
   }
-}
-
-// Log-sum-exp merge of the split partials of one (sequence, query head), then
-// the inverse rotation. 256 threads; the splits are taken in rounds of 32:
-// all loads of a round are issued together (thread s < 32 reads split s's
-// (m, l); wave w reads two channels per lane of splits w, w + 4, ...), the
-// round is merged into a running maximum, and the four waves' sums meet in
-// LDS. Wave 0 then rotates the 128 channels back in registers (channel bit 6
-// in the lane, bits 0..5 across lanes).
-template <bool kRotate>
-__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
-  constexpr int RS = 32;  // splits per round
-  __shared__ float wgt[RS];
-  __shared__ float red[4];
-  __shared__ f32x2 part[4][64];
-  const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
-  const int lane = t & 63, wv = t >> 6;
-  constexpr int ROW = 2 + D;
-  const float *pp = a.partial + ((int64_t)b * a.q_heads + h) * a.n_split * ROW;
-  f32x2 num = {0.f, 0.f};
-  float den = 0.f, m_run = -INFINITY;
-  for (int base = 0; base < a.n_split; base += RS) {
-    const int cnt = min(RS, a.n_split - base);
-    float ms = -INFINITY, ls = 0.f;
-    if (t < cnt) {
-      ms = pp[(int64_t)(base + t) * ROW];
-      ls = pp[(int64_t)(base + t) * ROW + 1];
-    }
-    f32x2 v[RS / 4];
-#pragma unroll
-    for (int i = 0; i < RS / 4; ++i) {
-      const int q = wv + 4 * i;
-      v[i] = q < cnt ? *reinterpret_cast<const f32x2 *>(pp + (int64_t)(base + q) * ROW + 2 + 2 * lane)
-                     : f32x2{0.f, 0.f};
-    }
-    // round maximum: threads 0..31 hold the round's split maxima (wave 0)
-    float mx = group_max<16>(ms);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    __syncthreads();  // the previous round's readers of wgt and red are done
-    if (t == 0) red[0] = mx;
-    __syncthreads();
-    const float m_new = fmaxf(m_run, red[0]);
-    if (m_new != -INFINITY) {
-      const float rescale = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
-      const float w = ms == -INFINITY ? 0.f : exp2f(ms - m_new);
-      if (t < RS) wgt[t] = w;
-      __syncthreads();
-      num *= rescale;
-      den = den * rescale + w * ls;
-#pragma unroll
-      for (int i = 0; i < RS / 4; ++i) num += wgt[wv + 4 * i] * v[i];
-      m_run = m_new;
-    }
-  }
-  // denominators live in wave 0's first 32 lanes (one per split slot)
-  den = group_sum<16>(den);
-  den += __shfl_xor(den, 16, 64);
-  den += __shfl_xor(den, 32, 64);
   __syncthreads();
-  if (t == 0) red[1] = den;
-  part[wv][lane] = num;
-  __syncthreads();
-  if (wv == 0) {
-    const float L = red[1];
-    const f32x2 sum = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
-    // channels 2 lane and 2 lane + 1 -> lane holds channels lane and lane + 64
-    float x0 = L > 0.f ? sum[0] / L : 0.f, x1 = L > 0.f ? sum[1] / L : 0.f;
-    float *out = a.out + ((int64_t)b * a.q_heads + h) * D;
-    if constexpr (kRotate) {
-      // regroup: lane l needs channels l and l + 64; channel c sits in lane c / 2
-      const float e0 = __shfl(x0, lane >> 1, 64), o0 = __shfl(x1, lane >> 1, 64);
-      const float e1 = __shfl(x0, 32 + (lane >> 1), 64), o1 = __shfl(x1, 32 + (lane >> 1), 64);
-      float y0 = (lane & 1) ? o0 : e0;  // channel lane
-      float y1 = (lane & 1) ? o1 : e1;  // channel lane + 64
-      {
-        const float s0 = y0 + y1, d0 = y0 - y1;
-        y0 = s0;
-        y1 = d0;
-      }
+  const int hh = wv;  // the head this wave merges (wave-uniform)
+  float M = -INFINITY, L = 0.f;
+  f32x2 x = {0.f, 0.f};
+  if (hh < nh) {
 #pragma unroll
-      for (int m = 1; m < 64; m <<= 1) {
-        const float p0 = __shfl_xor(y0, m, 64), p1 = __shfl_xor(y1, m, 64);
-        const bool upper = (lane & m) != 0;
-        y0 = upper ? p0 - y0 : y0 + p0;
-        y1 = upper ? p1 - y1 : y1 + p1;
-      }
-      out[lane] = y0 * kInvSqrtD;
-      out[lane + 64] = y1 * kInvSqrtD;
-    } else {
-      *reinterpret_cast<f32x2 *>(out + 2 * lane) = f32x2{x0, x1};
+    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, mg.m[w][hh]);
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float mw = mg.m[w][hh];
+      // the running maxima are whole numbers (log2 units): exact powers of two
+      const float e = mw == -INFINITY ? 0.f : exp2f(mw - M);
+      L = fmaf(e, mg.l[w][hh], L);
+      x += e * *reinterpret_cast<const f32x2 *>(&mg.acc[w][hh][2 * lane]);
     }
   }
+  if (a.n_wg == 1) {
+    if (hh < nh) finalize_head<kRotate>(x[0], x[1], L, lane, a.out + (qh0 + hh) * D);
+    return;
+  }
+  // The workgroup that finishes its row last merges it. The partials and the
+  // counter are the only memory shared between workgroups; they are written
+  // and read coherently across the XCDs' separate L2 caches (agent-scope
+  // accesses), each thread's partial stores complete before the count is
+  // taken, and the last workgroup reads them after it. (A full agent-scope
+  // fence would write back and invalidate the whole L2 of the XCD in every
+  // workgroup, which costs more than the merge.)
+  if (hh < nh) {
+    float *pp = a.partial + ((qh0 + hh) * a.n_wg + wgs) * (2 + D);
+    if (lane == 0) {
+      coherent_store(pp, M);
+      coherent_store(pp + 1, L);
+    }
+    coherent_store2(pp + 2 + 2 * lane, x);
+  }
+  __builtin_amdgcn_s_waitcnt(kVmcntZero);
+  __syncthreads();
+  if (tid == 0)
+    mg.last = __hip_atomic_fetch_add(a.counters + row, 1, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT) == a.n_wg - 1;
+  __syncthreads();
+  if (!mg.last) return;
+  if (hh < nh) {
+    // the row's partials in rounds of 8, all loads of a round issued before
+    // any is used, merged into a running (M, L, x) by log-sum-exp
+    const float *pp = a.partial + (qh0 + hh) * a.n_wg * (2 + D);
+    constexpr int R = 8;
+    M = -INFINITY;
+    L = 0.f;
+    x = f32x2{0.f, 0.f};
+    for (int i0 = 0; i0 < a.n_wg; i0 += R) {
+      float mi[R], li[R];
+      f32x2 xi[R];
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        const float *pi = pp + (i0 + j) * (2 + D);
+        const bool in = i0 + j < a.n_wg;
+        mi[j] = in ? coherent_load(pi) : -INFINITY;
+        li[j] = in ? coherent_load(pi + 1) : 0.f;
+        xi[j] = in ? coherent_load2(pi + 2 + 2 * lane) : f32x2{0.f, 0.f};
+      }
+      float mn = M;
+#pragma unroll
+      for (int j = 0; j < R; ++j) mn = fmaxf(mn, mi[j]);
+      const float sc = M == -INFINITY ? 0.f : exp2f(M - mn);
+      L *= sc;
+      x *= sc;
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        const float e = mi[j] == -INFINITY ? 0.f : exp2f(mi[j] - mn);
+        L = fmaf(e, li[j], L);
+        x += e * xi[j];
+      }
+      M = mn;
+    }
+    finalize_head<kRotate>(x[0], x[1], L, lane, a.out + (qh0 + hh) * D);
+  }
+  if (tid == 0)  // ready for the next call
+    __hip_atomic_store(a.counters + row, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
@@ -689,18 +758,21 @@ int device_cus() {
 }
 static int device_simds() { return 4 * device_cus(); }
 
-// Splits per (sequence, kv-head, head group): about two single-wave
-// workgroups per SIMD in one round. Fewer leave SIMDs without a second wave
-// to overlap with; more add per-workgroup set-up and merge work (and a second
-// round) for no gain (measured on the 8 x 8 x 32768 and 32 x 8 x 8192 caches).
-int decode_auto_splits(int batch, int kv_heads, int q_heads, int capacity) {
-  const int nch = capacity / T;
-  if (batch <= 0 || kv_heads <= 0 || q_heads <= 0 || nch <= 0) return 1;
+// Workgroups per (sequence, kv-head, head group): about kWavesPerSimd waves
+// per SIMD in one round (four-wave workgroups, one split per wave; the
+// kernel's registers allow three waves per SIMD).
+#ifndef KVARN_DECODE_WAVES_PER_SIMD
+#define KVARN_DECODE_WAVES_PER_SIMD 3
+#endif
+constexpr int kWavesPerSimd = KVARN_DECODE_WAVES_PER_SIMD;
+int decode_auto_wgs(int batch, int kv_heads, int q_heads, int capacity) {
+  const int max_wg = decode_max_wgs(capacity);
+  if (batch <= 0 || kv_heads <= 0 || q_heads <= 0 || max_wg <= 0) return 1;
   const int G = q_heads / kv_heads;
-  const int64_t pairs = (int64_t)batch * kv_heads * ((G + HG - 1) / HG);
-  const int64_t target = 2 * (int64_t)device_simds();
-  int64_t s = (target + pairs / 2) / pairs;
-  if (s > nch) s = nch;
+  const int64_t rows = (int64_t)batch * kv_heads * ((G + HG - 1) / HG);
+  const int64_t target = (int64_t)kWavesPerSimd * device_simds() / kDecWaves;
+  int64_t s = (target + rows / 2) / rows;
+  if (s > max_wg) s = max_wg;
   if (s < 1) s = 1;
   return (int)s;
 }
@@ -709,22 +781,16 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
   if (a.batch == 0 || a.q_heads == 0) return hipSuccess;
   const int G = a.q_heads / a.kv_heads;
   const int n_hg = (G + HG - 1) / HG;
-  const dim3 grid(a.n_split * n_hg, a.kv_heads, a.batch);
+  const dim3 grid(a.n_wg * n_hg, a.kv_heads, a.batch), block(64 * kDecWaves);
   const bool rot = !(a.flags & KVARN_FLAG_NO_ROTATE), two = !(a.flags & KVARN_FLAG_ONE_SCALE);
   if (rot && two)
-    hipLaunchKernelGGL((decode_split_kernel<true, true>), grid, dim3(64), 0, s, a);
+    hipLaunchKernelGGL((decode_kernel<true, true>), grid, block, 0, s, a);
   else if (rot)
-    hipLaunchKernelGGL((decode_split_kernel<true, false>), grid, dim3(64), 0, s, a);
+    hipLaunchKernelGGL((decode_kernel<true, false>), grid, block, 0, s, a);
   else if (two)
-    hipLaunchKernelGGL((decode_split_kernel<false, true>), grid, dim3(64), 0, s, a);
+    hipLaunchKernelGGL((decode_kernel<false, true>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((decode_split_kernel<false, false>), grid, dim3(64), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (rot)
-    hipLaunchKernelGGL((decode_combine_kernel<true>), dim3(a.q_heads, a.batch), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((decode_combine_kernel<false>), dim3(a.q_heads, a.batch), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_kernel<false, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 

@@ -101,14 +101,16 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t s);
 
 struct DecodeArgs {
   const void *q;
-  int q_dtype, batch, q_heads, kv_heads, capacity, n_split;
+  int q_dtype, batch, q_heads, kv_heads, capacity;
+  int n_wg;        // workgroups (of KVARN_DECODE_WAVES splits) per (sequence, kv-head, head group)
   uint32_t flags;  // KVARN_FLAG_NO_ROTATE, KVARN_FLAG_ONE_SCALE
   const uint8_t *k_codes, *v_codes;
   const float *k_row, *k_col, *v_row, *v_col;
   const int32_t *lens;
   float scale;
   float *out;
-  float *partial;  // [batch][q_heads][n_split][2 + D]
+  int32_t *counters;  // one per (sequence, kv-head, head group); zero between calls
+  float *partial;     // [batch][q_heads][n_wg][2 + D]
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 int device_cus();  // compute units of the current device, cached per device
@@ -116,6 +118,18 @@ int device_cus();  // compute units of the current device, cached per device
 // scratch array (KVARN_NOALLOC_SCRATCH_BYTES), taken once per device; nullptr
 // with *err set when the query fails.
 void *noalloc_scratch(hipError_t *err);
-int decode_auto_splits(int batch, int kv_heads, int q_heads, int capacity);
+// the most workgroups per row that still give every split a chunk
+inline int decode_max_wgs(int capacity) {
+  return (capacity / T + KVARN_DECODE_WAVES - 1) / KVARN_DECODE_WAVES;
+}
+int decode_auto_wgs(int batch, int kv_heads, int q_heads, int capacity);
+// Workspace layout: counters (batch * q_heads int32, rounded up to 256 bytes;
+// q_heads bounds the number of (kv-head, head group) rows), then the partials.
+inline size_t decode_counter_bytes(int32_t batch, int32_t q_heads) {
+  return ((size_t)batch * q_heads * sizeof(int32_t) + 255) / 256 * 256;
+}
+inline size_t decode_partial_bytes(int32_t batch, int32_t q_heads, int n_wg) {
+  return (size_t)batch * q_heads * (size_t)n_wg * (2 + D) * sizeof(float);
+}
 
 }  // namespace kvarn

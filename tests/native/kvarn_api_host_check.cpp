@@ -42,7 +42,7 @@ hipError_t launch_token_error(const DiagArgs &a, hipStream_t) {
   ++g_calls;
   return g_result;
 }
-int decode_auto_splits(int, int, int, int capacity) { return capacity / T; }
+int decode_auto_wgs(int, int, int, int capacity) { return decode_max_wgs(capacity); }
 static int g_scratch_queries = 0;
 void *noalloc_scratch(hipError_t *) {
   ++g_scratch_queries;
@@ -167,7 +167,8 @@ static void check_decode() {
   const int32_t *lens = static_cast<int32_t *>(P(0x50000));
   float *out = static_cast<float *>(P(0x80000));
   const size_t need = kvarn_decode_workspace_bytes(2, 16, 1024);
-  CHECK(need == (size_t)2 * 16 * 8 * 130 * 4);
+  // 2 x 16 counters (256 bytes), then 2 workgroups of partials per row
+  CHECK(need == 256 + (size_t)2 * 16 * 2 * 130 * 4);
   CHECK(kvarn_decode_workspace_bytes(2, 16, 1000) == 0);
   CHECK(kvarn_decode_workspace_bytes(-1, 16, 1024) == 0);
   void *ws = P(0x90000);
@@ -195,13 +196,14 @@ static void check_decode() {
   CHECK(g_calls == 0);
   CHECK(kvarn_decode_attn(P(0x40000), KVARN_DT_F32, 16, &k, &v, lens, 0.25f, out, 100, ws, need, nullptr) ==
         KVARN_OK);
-  CHECK(g_decode.n_split == 8);  // clamped to the chunk count
+  CHECK(g_decode.n_wg == 2);  // 100 splits: 25 workgroups, clamped to 8 chunks / 4
   CHECK(g_decode.q_heads == 16 && g_decode.kv_heads == 4 && g_decode.batch == 2);
   CHECK(g_decode.k_codes == k.codes && g_decode.v_codes == v.codes && g_decode.scale == 0.25f);
-  CHECK(g_decode.partial == ws && g_decode.out == out && g_decode.q_dtype == KVARN_DT_F32);
+  CHECK(g_decode.counters == ws && g_decode.out == out && g_decode.q_dtype == KVARN_DT_F32);
+  CHECK((char *)g_decode.partial == (char *)ws + 256);
   CHECK(kvarn_decode_attn(P(0x40000), KVARN_DT_BF16, 16, &k, &v, lens, 0.25f, out, 3, ws, need, nullptr) ==
         KVARN_OK);
-  CHECK(g_decode.n_split == 3);
+  CHECK(g_decode.n_wg == 1);
 }
 
 static void check_decode_noalloc() {
@@ -214,7 +216,7 @@ static void check_decode_noalloc() {
                                   nullptr) == KVARN_ERR_NULL);
   CHECK(kvarn_decode_attn_noalloc(P(0x40000), KVARN_DT_BF16, 14, &k, &v, lens, 0.1f, 0u, out, 0,
                                   nullptr) == KVARN_ERR_SHAPE);
-  // partials beyond the fixed array: 64 sequences x 64 query heads x 64 splits x 520 B
+  // partials beyond the fixed array: 64 sequences x 64 query heads x 16 workgroups x 520 B
   kvarn_cache kb = cache(64, 8, 128 * 1024, KVARN_K), vb = cache(64, 8, 128 * 1024, KVARN_V);
   CHECK(kvarn_decode_attn_noalloc(P(0x40000), KVARN_DT_BF16, 64, &kb, &vb, lens, 0.1f, 0u, out,
                                   64, nullptr) == KVARN_ERR_WORKSPACE);
@@ -222,7 +224,8 @@ static void check_decode_noalloc() {
   CHECK(kvarn_decode_attn_noalloc(P(0x40000), KVARN_DT_BF16, 16, &k, &v, lens, 0.5f,
                                   KVARN_FLAG_ONE_SCALE, out, 0, nullptr) == KVARN_OK);
   CHECK(g_calls == 1 && g_scratch_queries == 1);
-  CHECK(g_decode.partial == P(0xC0000) && g_decode.n_split == 8 && g_decode.scale == 0.5f);
+  CHECK((void *)g_decode.counters == P(0xC0000) && g_decode.n_wg == 2 && g_decode.scale == 0.5f);
+  CHECK((char *)g_decode.partial == (char *)P(0xC0000) + 256);
   CHECK(g_decode.flags == KVARN_FLAG_ONE_SCALE);
 }
 

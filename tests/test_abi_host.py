@@ -92,8 +92,11 @@ def test_append_validation(lib):
 
 
 def test_workspace_bytes(lib):
-    assert lib.kvarn_decode_workspace_bytes(8, 32, 32768) == 8 * 32 * 256 * 130 * 4
-    assert lib.kvarn_decode_workspace_bytes(1, 4, 256) == 1 * 4 * 2 * 130 * 4
+    # one int32 counter per (sequence, query head) rounded up to 256 bytes, then
+    # the partials of ceil(chunks / 4) four-split workgroups per row
+    assert lib.kvarn_decode_workspace_bytes(8, 32, 32768) == 1024 + 8 * 32 * 64 * 130 * 4
+    assert lib.kvarn_decode_workspace_bytes(1, 4, 256) == 256 + 1 * 4 * 1 * 130 * 4
+    assert lib.kvarn_decode_workspace_bytes(1, 4, 640) == 256 + 1 * 4 * 2 * 130 * 4
     assert lib.kvarn_decode_workspace_bytes(1, 4, 100) == 0
     assert lib.kvarn_decode_workspace_bytes(-1, 4, 256) == 0
 

@@ -137,3 +137,23 @@ def test_pipeline_qwen_layer_sampled_heads(kvarn, oracle):
         err = rel_l2(out[:, 4 * g:4 * g + 4].cpu().numpy(), want)
         log(f"[test] qwen layer kv-head {g}: rel L2 {err:.3e}")
         assert err <= ATTN_RL2
+
+
+def test_decode_last_workgroup_merge_resets_counters(kvarn, oracle):
+    """Many workgroups per row: the workgroup that finishes a row last merges
+    its partials (here 20 per row); it leaves the row's counter at zero, so a
+    second call on the same workspace gives the same output."""
+    B, Hkv, G, cap = 2, 2, 8, 128 * 80
+    kc, vc, hk, hv = _random_caches(kvarn, B, Hkv, cap, seed=77)
+    q = kvgen.queries(78, 0, B, Hkv * G, dtype=torch.bfloat16)
+    lens = [cap, 5000]
+    L = torch.tensor(lens, dtype=torch.int32).cuda()
+    ws = kvarn.decode_workspace(B, Hkv * G, cap)
+    a = kvarn.decode_attn(q.cuda(), kc, vc, L, n_split=80, workspace=ws).clone()
+    b = kvarn.decode_attn(q.cuda(), kc, vc, L, n_split=80, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert int(ws[:B * Hkv * G * 4].view(torch.int32).abs().sum()) == 0
+    err = rel_l2(a.cpu().numpy(), _oracle_on(oracle, q, hk, hv, lens))
+    log(f"[test] decode 20 workgroups per row: rel L2 {err:.3e}")
+    assert err <= ATTN_RL2
