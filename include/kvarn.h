@@ -23,7 +23,9 @@
  *  - Arguments are validated on the host before any HIP call. On a validation
  *    error the call returns a negative kvarn_status and enqueues nothing.
  *    A failed launch returns KVARN_ERR_HIP.
- *  - head_dim is fixed at 128 and the chunk (block) length at 128 tokens.
+ *  - The chunk (block) length is 128 tokens. head_dim is 128, 64 or 256 (a
+ *    field of the cache descriptor); 128 runs the tuned kernels, 64 and 256
+ *    run generic kernels that compute the same quantities.
  */
 #ifndef KVARN_H
 #define KVARN_H
@@ -82,23 +84,26 @@ typedef enum { KVARN_K = 0, KVARN_V = 1 } kvarn_kind;
 
 /*
  * One K or V cache of one layer. All three arrays are (device) memory owned
- * by the caller; capacity % 128 == 0; every pointer 16-byte aligned.
+ * by the caller; capacity % 128 == 0; every pointer 16-byte aligned. D is
+ * head_dim (0 stands for 128; 64, 128 and 256 are supported).
  *
- * codes      [batch][kv_heads][capacity/128][4096] bytes. Four 2-bit codes
- *            per byte, lowest bits first. Within a 128-token chunk:
- *              K: token t owns bytes [32 t, 32 t + 32); channel j sits in
- *                 byte 32 t + j/4 at bits 2 (j % 4);
+ * codes      [batch][kv_heads][capacity/128][32 D] bytes (4096 for D = 128).
+ *            Four 2-bit codes per byte, lowest bits first. Within a
+ *            128-token chunk:
+ *              K: token t owns bytes [D/4 t, D/4 (t + 1)); channel j sits in
+ *                 byte D/4 t + j/4 at bits 2 (j % 4);
  *              V: channel j owns bytes [32 j, 32 j + 32); token t sits in
  *                 byte 32 j + t/4 at bits 2 (t % 4).
  *            Code q in {0,1,2,3} stands for the level (q - 1.5).
  * row_scale  [batch][kv_heads][capacity] fp32: per-token scale r'_t.
- * col_scale  [batch][kv_heads][capacity/128][128] fp32: per-chunk, per-channel
+ * col_scale  [batch][kv_heads][capacity/128][D] fp32: per-chunk, per-channel
  *            scale c_j.
  * The stored value is reconstructed in the rotated basis as
  *   y_hat[t][j] = (code[t][j] - 1.5) * row_scale[t] * col_scale[t/128][j]
- * and in the original basis as y_hat . H_128 / sqrt(128), H_128 the
- * Sylvester-order Hadamard matrix (the "two scales" of the rndamp article's
- * "Numbers" section).
+ * and in the original basis as y_hat . H_D / sqrt(D), H_D the Sylvester-order
+ * Hadamard matrix (the "two scales" of the rndamp article's "Numbers"
+ * section). The calls below are written for D = 128; for another D read D
+ * wherever 128 stands for the channel count.
  */
 typedef struct {
     uint8_t *codes;
@@ -107,7 +112,8 @@ typedef struct {
     int32_t batch;
     int32_t kv_heads;
     int32_t capacity;
-    int32_t kind; /* kvarn_kind */
+    int32_t kind;     /* kvarn_kind */
+    int32_t head_dim; /* D: 0 (= 128), 64, 128 or 256 */
 } kvarn_cache;
 
 /*
@@ -216,6 +222,10 @@ int kvarn_append_rebalance(const void *x, int32_t dtype,
  */
 size_t kvarn_decode_workspace_bytes(int32_t batch, int32_t q_heads,
                                     int32_t capacity);
+/* The same for caches of head size head_dim (64, 128 or 256); 0 for invalid
+ * sizes. kvarn_decode_workspace_bytes is this with head_dim 128. */
+size_t kvarn_decode_workspace_bytes_ex(int32_t batch, int32_t q_heads,
+                                       int32_t capacity, int32_t head_dim);
 
 /*
  * kvarn_decode_attn -- one decoding step of grouped-query attention over the
@@ -240,8 +250,8 @@ size_t kvarn_decode_workspace_bytes(int32_t batch, int32_t q_heads,
  *            splits of one workgroup) and clamped to [KVARN_DECODE_WAVES,
  *            capacity/128 rounded up to that multiple]. Each sequence's used
  *            chunks are spread evenly over the splits.
- * workspace  (device) at least kvarn_decode_workspace_bytes(batch, q_heads,
- *            capacity) bytes, 16-byte aligned. Its leading counter bytes must
+ * workspace  (device) at least kvarn_decode_workspace_bytes_ex(batch,
+ *            q_heads, capacity, head_dim) bytes, 16-byte aligned. Its leading counter bytes must
  *            be zero before the first call (a zero-filled allocation); every
  *            call leaves them zero again, the rest is scratch. Calls that
  *            share a workspace must not overlap in time.
@@ -267,15 +277,17 @@ int kvarn_decode_attn_ex(const void *q, int32_t q_dtype, int32_t q_heads,
  * inside the library, KVARN_NOALLOC_SCRATCH_BYTES per GPU, held by each GPU
  * the library runs on until the process ends.
  *
- * Same arguments, results and kernels as kvarn_decode_attn_ex. The partials
- * of one call take batch * q_heads * splits * 130 * 4 bytes, splits being
- * n_split (clamped to [1, capacity/128]) or the library's choice for
- * n_split == 0; a call that needs more than KVARN_NOALLOC_SCRATCH_BYTES
- * returns KVARN_ERR_WORKSPACE and enqueues nothing. The work runs on the
- * current device, which must be the device of `stream`.
- * Every call on one GPU shares that GPU's array: two calls that may overlap
- * in time on one GPU (different streams, different host threads) race and
- * must be ordered by the caller.
+ * Same arguments, results and kernels as kvarn_decode_attn_ex. A call uses
+ * the counters (batch * q_heads * 4 bytes rounded up to 256) and the
+ * partials of its workgroups, batch * q_heads * W * (2 + D) * 4 bytes with
+ * W = n_split / KVARN_DECODE_WAVES rounded up (clamped as for
+ * kvarn_decode_attn) or the library's choice for n_split == 0; a call that
+ * needs more than KVARN_NOALLOC_SCRATCH_BYTES returns KVARN_ERR_WORKSPACE and
+ * enqueues nothing. The array starts zeroed and every call leaves its
+ * counters zero. The work runs on the current device, which must be the
+ * device of `stream`. Every call on one GPU shares that GPU's array: two
+ * calls that may overlap in time on one GPU (different streams, different
+ * host threads) race and must be ordered by the caller.
  */
 enum { KVARN_NOALLOC_SCRATCH_BYTES = 16 << 20 };
 int kvarn_decode_attn_noalloc(const void *q, int32_t q_dtype, int32_t q_heads,

@@ -17,8 +17,9 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvarn.so")
 
 HEAD_DIM = 128
+HEAD_DIMS = (64, 128, 256)   # supported head sizes (128: the tuned kernels)
 CHUNK = 128
-CHUNK_BYTES = 4096
+CHUNK_BYTES = 4096           # packed codes of one chunk at head size 128 (32 x head_dim)
 
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_CAPACITY, ERR_WORKSPACE, ERR_HIP = (
     0, -1, -2, -3, -4, -5, -6, -7)
@@ -28,7 +29,8 @@ DT_BF16, DT_F32 = 0, 1
 K, V = 0, 1
 
 EXPORTED = ("kvarn_quantize", "kvarn_quantize_ex", "kvarn_append", "kvarn_append_ex",
-            "kvarn_decode_workspace_bytes", "kvarn_decode_attn", "kvarn_decode_attn_ex",
+            "kvarn_decode_workspace_bytes", "kvarn_decode_workspace_bytes_ex",
+            "kvarn_decode_attn", "kvarn_decode_attn_ex",
             "kvarn_decode_attn_noalloc", "kvarn_append_rebalance", "kvarn_token_error",
             "kvarn_status_string")
 NOALLOC_SCRATCH_BYTES = 16 << 20   # KVARN_NOALLOC_SCRATCH_BYTES
@@ -44,7 +46,7 @@ class CacheDesc(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("row_scale", ctypes.c_void_p),
                 ("col_scale", ctypes.c_void_p), ("batch", ctypes.c_int32),
                 ("kv_heads", ctypes.c_int32), ("capacity", ctypes.c_int32),
-                ("kind", ctypes.c_int32)]
+                ("kind", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
 
 
 _lib = None
@@ -68,6 +70,8 @@ def load(path: str | None = None):
     L.kvarn_append.restype = ctypes.c_int
     L.kvarn_decode_workspace_bytes.argtypes = [i32, i32, i32]
     L.kvarn_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.kvarn_decode_workspace_bytes_ex.argtypes = [i32, i32, i32, i32]
+    L.kvarn_decode_workspace_bytes_ex.restype = ctypes.c_size_t
     L.kvarn_decode_attn.argtypes = [vp, i32, i32, cd, cd, vp, ctypes.c_float, vp, i32,
                                     vp, ctypes.c_size_t, vp]
     L.kvarn_decode_attn.restype = ctypes.c_int
@@ -137,20 +141,21 @@ def _raise(st: int, what: str):
 
 @dataclass
 class Cache:
-    """One layer's K or V cache: device tensors in the layout of kvarn.h."""
-    codes: torch.Tensor      # uint8 [B, H, cap/128, 4096]
+    """One layer's K or V cache: device tensors in the layout of kvarn.h
+    (D = head_dim: 64, 128 or 256)."""
+    codes: torch.Tensor      # uint8 [B, H, cap/128, 32 D]
     row_scale: torch.Tensor  # f32 [B, H, cap]
-    col_scale: torch.Tensor  # f32 [B, H, cap/128, 128]
+    col_scale: torch.Tensor  # f32 [B, H, cap/128, D]
     kind: int
 
     @staticmethod
     def empty(batch: int, kv_heads: int, capacity: int, kind: int, device="cuda",
-              zero: bool = True) -> "Cache":
+              zero: bool = True, head_dim: int = HEAD_DIM) -> "Cache":
         nch = capacity // CHUNK
         f = torch.zeros if zero else torch.empty
-        return Cache(f((batch, kv_heads, nch, CHUNK_BYTES), dtype=torch.uint8, device=device),
+        return Cache(f((batch, kv_heads, nch, 32 * head_dim), dtype=torch.uint8, device=device),
                      f((batch, kv_heads, capacity), dtype=torch.float32, device=device),
-                     f((batch, kv_heads, nch, HEAD_DIM), dtype=torch.float32, device=device),
+                     f((batch, kv_heads, nch, head_dim), dtype=torch.float32, device=device),
                      kind)
 
     @property
@@ -165,6 +170,10 @@ class Cache:
     def capacity(self):
         return self.row_scale.shape[2]
 
+    @property
+    def head_dim(self):
+        return self.col_scale.shape[3] if self.col_scale.dim() == 4 else HEAD_DIM
+
     def desc(self) -> CacheDesc:
         """The kvarn_cache descriptor, after checking dtypes, shapes and
         placement against the layout the kernels index."""
@@ -175,28 +184,32 @@ class Cache:
                 self.col_scale.dtype != torch.float32:
             raise ValueError("cache tensors must be uint8 codes and fp32 scales")
         if self.codes.dim() != 4 or self.row_scale.dim() != 3 or self.col_scale.dim() != 4:
-            raise ValueError("cache tensors must be codes [B,H,cap/128,4096], row_scale "
-                             "[B,H,cap], col_scale [B,H,cap/128,128]")
+            raise ValueError("cache tensors must be codes [B,H,cap/128,32 D], row_scale "
+                             "[B,H,cap], col_scale [B,H,cap/128,D]")
         B, H, nch = self.codes.shape[:3]
-        if self.codes.shape[3] != CHUNK_BYTES or \
+        D = self.col_scale.shape[3]
+        if D not in HEAD_DIMS:
+            raise ValueError(f"head_dim {D} not supported (64, 128 or 256)")
+        if self.codes.shape[3] != 32 * D or \
                 tuple(self.row_scale.shape) != (B, H, nch * CHUNK) or \
-                tuple(self.col_scale.shape) != (B, H, nch, HEAD_DIM):
-            raise ValueError("cache tensors must be codes [B,H,cap/128,4096], row_scale "
-                             "[B,H,cap], col_scale [B,H,cap/128,128] with one B, H and cap")
+                tuple(self.col_scale.shape) != (B, H, nch, D):
+            raise ValueError("cache tensors must be codes [B,H,cap/128,32 D], row_scale "
+                             "[B,H,cap], col_scale [B,H,cap/128,D] with one B, H, cap and D")
         if self.kind not in (K, V):
             raise ValueError("cache kind must be K or V")
         _on_device("cache", self.codes, self.row_scale, self.col_scale)
         return CacheDesc(self.codes.data_ptr(), self.row_scale.data_ptr(),
                          self.col_scale.data_ptr(), self.batch, self.kv_heads,
-                         self.capacity, self.kind)
+                         self.capacity, self.kind, self.head_dim)
 
 
 def quantize(x: torch.Tensor, cache: Cache, token_offset: int = 0, iters: int = 4,
              stream=None, flags: int = 0) -> None:
-    """x [B, H, tokens, 128] (bf16/fp32, channels contiguous) -> cache slots
+    """x [B, H, tokens, D] (bf16/fp32, channels contiguous) -> cache slots
     [token_offset, token_offset + tokens). flags: FLAG_NO_ROTATE."""
-    if x.dim() != 4 or x.shape[3] != HEAD_DIM or x.stride(3) != 1:
-        raise ValueError("x must be [B, H, T, 128] with contiguous channels")
+    if x.dim() != 4 or x.shape[3] != cache.head_dim or x.stride(3) != 1:
+        raise ValueError("x must be [B, H, T, D] with contiguous channels, D the cache's "
+                         "head_dim")
     if x.shape[0] != cache.batch or x.shape[1] != cache.kv_heads:
         raise ValueError("x batch/heads differ from the cache")
     d = cache.desc()
@@ -209,11 +222,11 @@ def quantize(x: torch.Tensor, cache: Cache, token_offset: int = 0, iters: int = 
 
 def append(x: torch.Tensor, positions: torch.Tensor, cache: Cache, stream=None,
            flags: int = 0) -> None:
-    """x [B, H, 128] new tokens at positions [B] (int32, device). flags:
+    """x [B, H, D] new tokens at positions [B] (int32, device). flags:
     FLAG_NO_ROTATE."""
-    if x.dim() != 3 or tuple(x.shape) != (cache.batch, cache.kv_heads, HEAD_DIM) or \
+    if x.dim() != 3 or tuple(x.shape) != (cache.batch, cache.kv_heads, cache.head_dim) or \
             not x.is_contiguous():
-        raise ValueError("x must be contiguous [B, H, 128] matching the cache")
+        raise ValueError("x must be contiguous [B, H, D] matching the cache")
     if positions.dtype != torch.int32 or positions.numel() != cache.batch or \
             not positions.is_contiguous():
         raise ValueError("positions must be contiguous int32 [B]")
@@ -224,9 +237,10 @@ def append(x: torch.Tensor, positions: torch.Tensor, cache: Cache, stream=None,
     _raise(st, "kvarn_append")
 
 
-def append_window(batch: int, kv_heads: int, dtype=torch.bfloat16, device="cuda") -> torch.Tensor:
-    """A window for append_rebalance: [batch, kv_heads, 128, 128]."""
-    return torch.zeros((batch, kv_heads, CHUNK, HEAD_DIM), dtype=dtype, device=device)
+def append_window(batch: int, kv_heads: int, dtype=torch.bfloat16, device="cuda",
+                  head_dim: int = HEAD_DIM) -> torch.Tensor:
+    """A window for append_rebalance: [batch, kv_heads, 128, head_dim]."""
+    return torch.zeros((batch, kv_heads, CHUNK, head_dim), dtype=dtype, device=device)
 
 
 def append_rebalance(x: torch.Tensor, positions: torch.Tensor, cache: Cache,
@@ -234,15 +248,15 @@ def append_rebalance(x: torch.Tensor, positions: torch.Tensor, cache: Cache,
     """append, plus the chunk re-quantized from `window` (same dtype as x,
     [B, H, 128, 128], kept by the caller) when a token fills it. flags:
     FLAG_NO_ROTATE."""
-    if x.dim() != 3 or tuple(x.shape) != (cache.batch, cache.kv_heads, HEAD_DIM) or \
+    if x.dim() != 3 or tuple(x.shape) != (cache.batch, cache.kv_heads, cache.head_dim) or \
             not x.is_contiguous():
-        raise ValueError("x must be contiguous [B, H, 128] matching the cache")
+        raise ValueError("x must be contiguous [B, H, D] matching the cache")
     if positions.dtype != torch.int32 or positions.numel() != cache.batch or \
             not positions.is_contiguous():
         raise ValueError("positions must be contiguous int32 [B]")
-    if tuple(window.shape) != (cache.batch, cache.kv_heads, CHUNK, HEAD_DIM) or \
+    if tuple(window.shape) != (cache.batch, cache.kv_heads, CHUNK, cache.head_dim) or \
             window.dtype != x.dtype or not window.is_contiguous():
-        raise ValueError("window must be contiguous [B, H, 128, 128] of x's dtype")
+        raise ValueError("window must be contiguous [B, H, 128, D] of x's dtype")
     d = cache.desc()
     dev = _on_device("append_rebalance", x, positions, window, cache.codes)
     st = load().kvarn_append_rebalance(x.data_ptr(), _dtype_code(x), positions.data_ptr(),
@@ -251,45 +265,55 @@ def append_rebalance(x: torch.Tensor, positions: torch.Tensor, cache: Cache,
     _raise(st, "kvarn_append_rebalance")
 
 
-def decode_workspace_bytes(batch: int, q_heads: int, capacity: int) -> int:
-    return int(load().kvarn_decode_workspace_bytes(batch, q_heads, capacity))
+def decode_workspace_bytes(batch: int, q_heads: int, capacity: int,
+                           head_dim: int = HEAD_DIM) -> int:
+    return int(load().kvarn_decode_workspace_bytes_ex(batch, q_heads, capacity, head_dim))
 
 
-def decode_workspace(batch: int, q_heads: int, capacity: int, device="cuda") -> torch.Tensor:
+def decode_workspace(batch: int, q_heads: int, capacity: int, device="cuda",
+                     head_dim: int = HEAD_DIM) -> torch.Tensor:
     """A decode workspace, zero-filled: its leading counters must be zero
     before the first call, and every call leaves them zero."""
-    n = decode_workspace_bytes(batch, q_heads, capacity)
+    n = decode_workspace_bytes(batch, q_heads, capacity, head_dim)
     return torch.zeros(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def _decode_checks(what, q, k, v, seq_lens, out):
+    D = k.head_dim
+    if v.head_dim != D:
+        raise ValueError(f"{what}: K and V caches differ in head_dim")
+    if q.dim() != 3 or q.shape[2] != D or not q.is_contiguous():
+        raise ValueError(f"{what}: q must be contiguous [B, Hq, D], D the caches' head_dim")
+    if q.shape[0] != k.batch:
+        raise ValueError(f"{what}: q's batch differs from the caches'")
+    if seq_lens.dtype != torch.int32 or seq_lens.numel() != k.batch or \
+            not seq_lens.is_contiguous():
+        raise ValueError(f"{what}: seq_lens must be contiguous int32 [B]")
+    if out is not None and (out.dtype != torch.float32 or not out.is_contiguous() or
+                            tuple(out.shape) != (q.shape[0], q.shape[1], D)):
+        raise ValueError(f"{what}: out must be contiguous fp32 [B, Hq, D]")
+    return D
 
 
 def decode_attn(q: torch.Tensor, k: Cache, v: Cache, seq_lens: torch.Tensor,
                 out: torch.Tensor | None = None, softmax_scale: float | None = None,
                 n_split: int = 0, workspace: torch.Tensor | None = None,
                 stream=None, flags: int = 0) -> torch.Tensor:
-    """q [B, Hq, 128] -> out fp32 [B, Hq, 128] (original basis; with
+    """q [B, Hq, D] -> out fp32 [B, Hq, D] (original basis; with
     FLAG_NO_ROTATE q and out are in the rotated basis). flags: FLAG_NO_ROTATE,
     FLAG_ONE_SCALE."""
-    if q.dim() != 3 or q.shape[2] != HEAD_DIM or not q.is_contiguous():
-        raise ValueError("q must be contiguous [B, Hq, 128]")
-    if q.shape[0] != k.batch:
-        raise ValueError("q's batch differs from the caches'")
-    if seq_lens.dtype != torch.int32 or seq_lens.numel() != k.batch or \
-            not seq_lens.is_contiguous():
-        raise ValueError("seq_lens must be contiguous int32 [B]")
-    B, Hq = q.shape[0], q.shape[1]
-    if out is not None and (out.dtype != torch.float32 or not out.is_contiguous() or
-                            tuple(out.shape) != (B, Hq, HEAD_DIM)):
-        raise ValueError("out must be contiguous fp32 [B, Hq, 128]")
+    D = _decode_checks("decode_attn", q, k, v, seq_lens, out)
     if workspace is not None and not workspace.is_contiguous():
         raise ValueError("workspace must be contiguous")
+    B, Hq = q.shape[0], q.shape[1]
     kd, vd = k.desc(), v.desc()
     dev = _on_device("decode_attn", q, seq_lens, out, workspace, k.codes, v.codes)
     if out is None:
-        out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=dev)
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
     if workspace is None:
-        workspace = decode_workspace(B, Hq, k.capacity, dev)
+        workspace = decode_workspace(B, Hq, k.capacity, dev, head_dim=D)
     if softmax_scale is None:
-        softmax_scale = HEAD_DIM ** -0.5
+        softmax_scale = D ** -0.5
     st = load().kvarn_decode_attn_ex(q.data_ptr(), _dtype_code(q), Hq, ctypes.byref(kd),
                                      ctypes.byref(vd), seq_lens.data_ptr(), softmax_scale,
                                      flags, out.data_ptr(), n_split, workspace.data_ptr(),
@@ -306,21 +330,14 @@ def decode_attn_noalloc(q: torch.Tensor, k: Cache, v: Cache, seq_lens: torch.Ten
     in its own fixed device array (NOALLOC_SCRATCH_BYTES per GPU) and the call
     allocates nothing, so `out` must be given. Calls that may overlap in time
     on one GPU race on that array."""
-    if q.dim() != 3 or q.shape[2] != HEAD_DIM or not q.is_contiguous():
-        raise ValueError("q must be contiguous [B, Hq, 128]")
-    if q.shape[0] != k.batch:
-        raise ValueError("q's batch differs from the caches'")
-    if seq_lens.dtype != torch.int32 or seq_lens.numel() != k.batch or \
-            not seq_lens.is_contiguous():
-        raise ValueError("seq_lens must be contiguous int32 [B]")
-    B, Hq = q.shape[0], q.shape[1]
-    if out.dtype != torch.float32 or not out.is_contiguous() or \
-            tuple(out.shape) != (B, Hq, HEAD_DIM):
-        raise ValueError("out must be contiguous fp32 [B, Hq, 128]")
+    if out is None:
+        raise ValueError("decode_attn_noalloc: out must be given")
+    D = _decode_checks("decode_attn_noalloc", q, k, v, seq_lens, out)
+    Hq = q.shape[1]
     kd, vd = k.desc(), v.desc()
     dev = _on_device("decode_attn_noalloc", q, seq_lens, out, k.codes, v.codes)
     if softmax_scale is None:
-        softmax_scale = HEAD_DIM ** -0.5
+        softmax_scale = D ** -0.5
     st = load().kvarn_decode_attn_noalloc(q.data_ptr(), _dtype_code(q), Hq, ctypes.byref(kd),
                                           ctypes.byref(vd), seq_lens.data_ptr(), softmax_scale,
                                           flags, out.data_ptr(), n_split, _stream(stream, dev))
@@ -333,10 +350,11 @@ def token_error(x: torch.Tensor, cache: Cache, token_offset: int = 0, stream=Non
                 cosine: torch.Tensor | None = None):
     """Per-token ||x_hat|| / ||x|| and cos(x_hat, x) of the cache's
     reconstruction of slots [token_offset, token_offset + T) against
-    x [B, H, T, 128] (bf16/fp32, channels contiguous). Returns (ratio,
+    x [B, H, T, D] (bf16/fp32, channels contiguous). Returns (ratio,
     cosine), fp32 [B, H, T]. flags: FLAG_NO_ROTATE (x already rotated)."""
-    if x.dim() != 4 or x.shape[3] != HEAD_DIM or x.stride(3) != 1:
-        raise ValueError("x must be [B, H, T, 128] with contiguous channels")
+    if x.dim() != 4 or x.shape[3] != cache.head_dim or x.stride(3) != 1:
+        raise ValueError("x must be [B, H, T, D] with contiguous channels, D the cache's "
+                         "head_dim")
     if x.shape[0] != cache.batch or x.shape[1] != cache.kv_heads:
         raise ValueError("x batch/heads differ from the cache")
     shape = (x.shape[0], x.shape[1], x.shape[2])

@@ -11,12 +11,17 @@ namespace {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// head_dim of a cache (0 stands for 128)
+int cache_dim(const kvarn_cache *c) { return c->head_dim == 0 ? D : c->head_dim; }
+bool dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
+
 int check_cache(const kvarn_cache *c) {
   if (!c) return KVARN_ERR_NULL;
   if (!c->codes || !c->row_scale || !c->col_scale) return KVARN_ERR_NULL;
   if (c->kind != KVARN_K && c->kind != KVARN_V) return KVARN_ERR_DTYPE;
   if (c->batch < 0 || c->kv_heads < 0 || c->capacity < 0 || c->capacity % T != 0)
     return KVARN_ERR_SHAPE;
+  if (!dim_ok(cache_dim(c))) return KVARN_ERR_SHAPE;
   if (!aligned16(c->codes) || !aligned16(c->row_scale) || !aligned16(c->col_scale))
     return KVARN_ERR_ALIGN;
   return KVARN_OK;
@@ -30,6 +35,10 @@ int dtype_size(int32_t dtype) {
 
 int from_hip(hipError_t e) { return e == hipSuccess ? KVARN_OK : KVARN_ERR_HIP; }
 
+hipError_t run_decode(const DecodeArgs &a, hipStream_t s) {
+  return a.head_dim == D ? launch_decode(a, s) : launch_decode_generic(a, s);
+}
+
 // Checks shared by the decode entry points (everything but the workspace).
 int check_decode(const void *q, int32_t q_dtype, int32_t q_heads, const kvarn_cache *k,
                  const kvarn_cache *v, const int32_t *seq_lens, float softmax_scale,
@@ -42,7 +51,8 @@ int check_decode(const void *q, int32_t q_dtype, int32_t q_heads, const kvarn_ca
   if (st != KVARN_OK) return st;
   if (k->kind != KVARN_K || v->kind != KVARN_V) return KVARN_ERR_DTYPE;
   if (!dtype_size(q_dtype)) return KVARN_ERR_DTYPE;
-  if (k->batch != v->batch || k->kv_heads != v->kv_heads || k->capacity != v->capacity)
+  if (k->batch != v->batch || k->kv_heads != v->kv_heads || k->capacity != v->capacity ||
+      cache_dim(k) != cache_dim(v))
     return KVARN_ERR_SHAPE;
   if (q_heads <= 0 || k->kv_heads <= 0 || q_heads % k->kv_heads) return KVARN_ERR_SHAPE;
   if (q_heads / k->kv_heads > GQA_MAX) return KVARN_ERR_SHAPE;
@@ -76,6 +86,7 @@ DecodeArgs decode_args(const void *q, int32_t q_dtype, int32_t q_heads, const kv
   a.q_heads = q_heads;
   a.kv_heads = k->kv_heads;
   a.capacity = k->capacity;
+  a.head_dim = cache_dim(k);
   a.n_wg = n_wg;
   a.k_codes = k->codes;
   a.v_codes = v->codes;
@@ -110,7 +121,7 @@ int kvarn_quantize_ex(const void *x, int32_t dtype, int64_t stride_b, int64_t st
   if (!esz) return KVARN_ERR_DTYPE;
   if (tokens < 0 || token_offset < 0 || tokens % T || token_offset % T) return KVARN_ERR_SHAPE;
   if (iters < 0 || iters > 64) return KVARN_ERR_SHAPE;
-  if (stride_b < 0 || stride_h < 0 || stride_t < D) return KVARN_ERR_SHAPE;
+  if (stride_b < 0 || stride_h < 0 || stride_t < cache_dim(dst)) return KVARN_ERR_SHAPE;
   if ((int64_t)tokens + token_offset > dst->capacity) return KVARN_ERR_CAPACITY;
   if (!aligned16(x) || (stride_b * esz) % 16 || (stride_h * esz) % 16 || (stride_t * esz) % 16)
     return KVARN_ERR_ALIGN;
@@ -138,7 +149,9 @@ int kvarn_quantize_ex(const void *x, int32_t dtype, int64_t stride_b, int64_t st
   a.row_scale = dst->row_scale;
   a.col_scale = dst->col_scale;
   a.pos = nullptr;
-  return from_hip(launch_quantize(a, static_cast<hipStream_t>(stream)));
+  a.head_dim = cache_dim(dst);
+  return from_hip(a.head_dim == D ? launch_quantize(a, static_cast<hipStream_t>(stream))
+                                  : launch_quantize_generic(a, static_cast<hipStream_t>(stream)));
 }
 
 int kvarn_quantize(const void *x, int32_t dtype, int64_t stride_b, int64_t stride_h,
@@ -171,7 +184,9 @@ int kvarn_append_ex(const void *x, int32_t dtype, const int32_t *positions, uint
   a.row_scale = dst->row_scale;
   a.col_scale = dst->col_scale;
   a.window = nullptr;
-  return from_hip(launch_append(a, static_cast<hipStream_t>(stream)));
+  a.head_dim = cache_dim(dst);
+  return from_hip(a.head_dim == D ? launch_append(a, static_cast<hipStream_t>(stream))
+                                  : launch_append_generic(a, static_cast<hipStream_t>(stream)));
 }
 
 int kvarn_append(const void *x, int32_t dtype, const int32_t *positions,
@@ -205,15 +220,17 @@ int kvarn_append_rebalance(const void *x, int32_t dtype, const int32_t *position
   p.row_scale = dst->row_scale;
   p.col_scale = dst->col_scale;
   p.window = window;
-  st = from_hip(launch_append(p, s));
+  p.head_dim = cache_dim(dst);
+  st = from_hip(p.head_dim == D ? launch_append(p, s) : launch_append_generic(p, s));
   if (st != KVARN_OK) return st;
   // the chunks just filled, quantized again from the window
   QuantArgs a;
   a.x = window;
   a.dtype = dtype;
-  a.sh = (int64_t)T * D;
+  a.head_dim = p.head_dim;
+  a.sh = (int64_t)T * a.head_dim;
   a.sb = a.sh * dst->kv_heads;
-  a.st = D;
+  a.st = a.head_dim;
   a.batch = dst->batch;
   a.heads = dst->kv_heads;
   a.chunks = 1;
@@ -229,7 +246,7 @@ int kvarn_append_rebalance(const void *x, int32_t dtype, const int32_t *position
   a.row_scale = dst->row_scale;
   a.col_scale = dst->col_scale;
   a.pos = positions;
-  return from_hip(launch_quantize(a, s));
+  return from_hip(a.head_dim == D ? launch_quantize(a, s) : launch_quantize_generic(a, s));
 }
 
 int kvarn_token_error(const void *x, int32_t dtype, int64_t stride_b, int64_t stride_h,
@@ -243,7 +260,7 @@ int kvarn_token_error(const void *x, int32_t dtype, int64_t stride_b, int64_t st
   if (!x || !ratio || !cosine) return KVARN_ERR_NULL;
   const int esz = dtype_size(dtype);
   if (!esz) return KVARN_ERR_DTYPE;
-  if (stride_b < 0 || stride_h < 0 || stride_t < D) return KVARN_ERR_SHAPE;
+  if (stride_b < 0 || stride_h < 0 || stride_t < cache_dim(cache)) return KVARN_ERR_SHAPE;
   if ((int64_t)tokens + token_offset > cache->capacity) return KVARN_ERR_CAPACITY;
   if (!aligned16(x) || (stride_b * esz) % 16 || (stride_h * esz) % 16 || (stride_t * esz) % 16)
     return KVARN_ERR_ALIGN;
@@ -268,13 +285,20 @@ int kvarn_token_error(const void *x, int32_t dtype, int64_t stride_b, int64_t st
   a.col_scale = cache->col_scale;
   a.ratio = ratio;
   a.cosine = cosine;
-  return from_hip(launch_token_error(a, static_cast<hipStream_t>(stream)));
+  a.head_dim = cache_dim(cache);
+  return from_hip(a.head_dim == D ? launch_token_error(a, static_cast<hipStream_t>(stream))
+                                  : launch_token_error_generic(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t kvarn_decode_workspace_bytes_ex(int32_t batch, int32_t q_heads, int32_t capacity,
+                                       int32_t head_dim) {
+  if (batch < 0 || q_heads < 0 || capacity < 0 || capacity % T || !dim_ok(head_dim)) return 0;
+  return decode_counter_bytes(batch, q_heads) +
+         decode_partial_bytes(batch, q_heads, decode_max_wgs(capacity), head_dim);
 }
 
 size_t kvarn_decode_workspace_bytes(int32_t batch, int32_t q_heads, int32_t capacity) {
-  if (batch < 0 || q_heads < 0 || capacity < 0 || capacity % T) return 0;
-  return decode_counter_bytes(batch, q_heads) +
-         decode_partial_bytes(batch, q_heads, decode_max_wgs(capacity));
+  return kvarn_decode_workspace_bytes_ex(batch, q_heads, capacity, D);
 }
 
 int kvarn_decode_attn_ex(const void *q, int32_t q_dtype, int32_t q_heads, const kvarn_cache *k,
@@ -284,7 +308,8 @@ int kvarn_decode_attn_ex(const void *q, int32_t q_dtype, int32_t q_heads, const 
   int st = check_decode(q, q_dtype, q_heads, k, v, seq_lens, softmax_scale, flags, out, n_split);
   if (st != KVARN_OK) return st;
   if (k->batch == 0) return KVARN_OK;
-  const size_t need = kvarn_decode_workspace_bytes(k->batch, q_heads, k->capacity);
+  const size_t need =
+      kvarn_decode_workspace_bytes_ex(k->batch, q_heads, k->capacity, cache_dim(k));
   if (!workspace) return KVARN_ERR_NULL;
   if (workspace_bytes < need) return KVARN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return KVARN_ERR_ALIGN;
@@ -292,7 +317,7 @@ int kvarn_decode_attn_ex(const void *q, int32_t q_dtype, int32_t q_heads, const 
   const int nw = decode_wgs(q_heads, k, n_split);
   const DecodeArgs a = decode_args(q, q_dtype, q_heads, k, v, seq_lens, softmax_scale, flags,
                                    out, nw, workspace);
-  return from_hip(launch_decode(a, static_cast<hipStream_t>(stream)));
+  return from_hip(run_decode(a, static_cast<hipStream_t>(stream)));
 }
 
 int kvarn_decode_attn_noalloc(const void *q, int32_t q_dtype, int32_t q_heads,
@@ -304,14 +329,14 @@ int kvarn_decode_attn_noalloc(const void *q, int32_t q_dtype, int32_t q_heads,
   if (k->batch == 0) return KVARN_OK;
   const int nw = decode_wgs(q_heads, k, n_split);
   const size_t need = decode_counter_bytes(k->batch, q_heads) +
-                      decode_partial_bytes(k->batch, q_heads, nw);
+                      decode_partial_bytes(k->batch, q_heads, nw, cache_dim(k));
   if (need > (size_t)KVARN_NOALLOC_SCRATCH_BYTES) return KVARN_ERR_WORKSPACE;
   hipError_t e = hipSuccess;
   void *scratch = noalloc_scratch(&e);
   if (!scratch) return from_hip(e);
   const DecodeArgs a = decode_args(q, q_dtype, q_heads, k, v, seq_lens, softmax_scale, flags,
                                    out, nw, scratch);
-  return from_hip(launch_decode(a, static_cast<hipStream_t>(stream)));
+  return from_hip(run_decode(a, static_cast<hipStream_t>(stream)));
 }
 
 int kvarn_decode_attn(const void *q, int32_t q_dtype, int32_t q_heads, const kvarn_cache *k,

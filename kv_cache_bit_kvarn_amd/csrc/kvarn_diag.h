@@ -8,6 +8,7 @@ namespace kvarn {
 struct DiagArgs {
   const void *x;
   int dtype;
+  int head_dim;
   int64_t sb, sh, st;
   int batch, heads, tokens, token_offset, capacity, kind;
   uint32_t flags;  // KVARN_FLAG_NO_ROTATE
@@ -16,5 +17,6 @@ struct DiagArgs {
   float *ratio, *cosine;
 };
 hipError_t launch_token_error(const DiagArgs &a, hipStream_t s);
+hipError_t launch_token_error_generic(const DiagArgs &a, hipStream_t s);  // head_dim 64, 256
 
 }  // namespace kvarn

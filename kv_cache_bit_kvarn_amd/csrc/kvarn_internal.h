@@ -73,6 +73,7 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
 struct QuantArgs {
   const void *x;
   int dtype;
+  int head_dim;         // channels per head (128: the tuned kernel; 64, 256: generic)
   int64_t sb, sh, st;
   int batch, heads, chunks, chunk0, iters, capacity, kind;
   uint32_t flags;       // KVARN_FLAG_NO_ROTATE
@@ -89,6 +90,7 @@ hipError_t launch_quantize(const QuantArgs &a, hipStream_t s);
 struct AppendArgs {
   const void *x;
   int dtype;
+  int head_dim;
   const int32_t *pos;
   int batch, heads, capacity, kind;
   uint32_t flags;  // KVARN_FLAG_NO_ROTATE
@@ -102,6 +104,7 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t s);
 struct DecodeArgs {
   const void *q;
   int q_dtype, batch, q_heads, kv_heads, capacity;
+  int head_dim;
   int n_wg;        // workgroups (of KVARN_DECODE_WAVES splits) per (sequence, kv-head, head group)
   uint32_t flags;  // KVARN_FLAG_NO_ROTATE, KVARN_FLAG_ONE_SCALE
   const uint8_t *k_codes, *v_codes;
@@ -128,8 +131,13 @@ int decode_auto_wgs(int batch, int kv_heads, int q_heads, int capacity);
 inline size_t decode_counter_bytes(int32_t batch, int32_t q_heads) {
   return ((size_t)batch * q_heads * sizeof(int32_t) + 255) / 256 * 256;
 }
-inline size_t decode_partial_bytes(int32_t batch, int32_t q_heads, int n_wg) {
-  return (size_t)batch * q_heads * (size_t)n_wg * (2 + D) * sizeof(float);
+inline size_t decode_partial_bytes(int32_t batch, int32_t q_heads, int n_wg, int head_dim) {
+  return (size_t)batch * q_heads * (size_t)n_wg * (2 + head_dim) * sizeof(float);
 }
+
+// Head sizes other than 128 (kvarn_generic.hip): same arguments, head_dim 64 or 256.
+hipError_t launch_quantize_generic(const QuantArgs &a, hipStream_t s);
+hipError_t launch_append_generic(const AppendArgs &a, hipStream_t s);
+hipError_t launch_decode_generic(const DecodeArgs &a, hipStream_t s);
 
 }  // namespace kvarn

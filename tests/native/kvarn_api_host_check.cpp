@@ -42,6 +42,25 @@ hipError_t launch_token_error(const DiagArgs &a, hipStream_t) {
   ++g_calls;
   return g_result;
 }
+// the kernels for head sizes 64 and 256 record into the same slots and count
+// separately, so the dispatch by head size is checked too
+static int g_generic = 0;
+hipError_t launch_quantize_generic(const QuantArgs &a, hipStream_t s) {
+  ++g_generic;
+  return launch_quantize(a, s);
+}
+hipError_t launch_append_generic(const AppendArgs &a, hipStream_t s) {
+  ++g_generic;
+  return launch_append(a, s);
+}
+hipError_t launch_decode_generic(const DecodeArgs &a, hipStream_t s) {
+  ++g_generic;
+  return launch_decode(a, s);
+}
+hipError_t launch_token_error_generic(const DiagArgs &a, hipStream_t s) {
+  ++g_generic;
+  return launch_token_error(a, s);
+}
 int decode_auto_wgs(int, int, int, int capacity) { return decode_max_wgs(capacity); }
 static int g_scratch_queries = 0;
 void *noalloc_scratch(hipError_t *) {
@@ -67,7 +86,7 @@ static int failures = 0;
 static void *P(uintptr_t a) { return reinterpret_cast<void *>(a); }
 
 static kvarn_cache cache(int batch = 2, int heads = 4, int cap = 512, int kind = KVARN_K) {
-  kvarn_cache c;
+  kvarn_cache c{};
   c.codes = static_cast<uint8_t *>(P(0x10000));
   c.row_scale = static_cast<float *>(P(0x20000));
   c.col_scale = static_cast<float *>(P(0x30000));
@@ -247,6 +266,46 @@ static void check_token_error() {
   CHECK(g_diag.tokens == 10 && g_diag.token_offset == 3 && g_diag.flags == 1u);
 }
 
+static void check_head_dim() {
+  g_calls = g_generic = 0;
+  kvarn_cache c = cache(2, 2, 256, KVARN_K);
+  c.head_dim = 96;
+  CHECK(kvarn_quantize(P(0x40000), KVARN_DT_BF16, 0, 0, 128, 256, 0, 4, &c, nullptr) == KVARN_ERR_SHAPE);
+  c.head_dim = 256;
+  // a token row narrower than the head
+  CHECK(kvarn_quantize(P(0x40000), KVARN_DT_BF16, 2 * 256 * 256, 256 * 256, 128, 256, 0, 4, &c, nullptr) ==
+        KVARN_ERR_SHAPE);
+  CHECK(g_calls == 0);
+  g_nquant = 0;
+  CHECK(kvarn_quantize(P(0x40000), KVARN_DT_BF16, 2 * 256 * 256, 256 * 256, 256, 256, 0, 4, &c, nullptr) ==
+        KVARN_OK);
+  CHECK(g_generic == 1 && g_quant[0].head_dim == 256);
+  CHECK(kvarn_append(P(0x40000), KVARN_DT_BF16, static_cast<int32_t *>(P(0x50000)), &c, nullptr) == KVARN_OK);
+  CHECK(g_generic == 2 && g_append.head_dim == 256);
+  float *r = static_cast<float *>(P(0xA0000)), *q = static_cast<float *>(P(0xB0000));
+  CHECK(kvarn_token_error(P(0x40000), KVARN_DT_BF16, 2 * 256 * 256, 256 * 256, 256, 10, 0, 0u, &c, r, q,
+                          nullptr) == KVARN_OK);
+  CHECK(g_generic == 3 && g_diag.head_dim == 256);
+  // decode: K and V must share the head size, and partials are sized by it
+  kvarn_cache k = cache(2, 4, 1024, KVARN_K), v = cache(2, 4, 1024, KVARN_V);
+  k.head_dim = v.head_dim = 64;
+  const size_t need = kvarn_decode_workspace_bytes_ex(2, 16, 1024, 64);
+  CHECK(need == 256 + (size_t)2 * 16 * 2 * (64 + 2) * 4);
+  CHECK(kvarn_decode_workspace_bytes_ex(2, 16, 1024, 96) == 0);
+  CHECK(kvarn_decode_workspace_bytes_ex(2, 16, 1024, 128) == kvarn_decode_workspace_bytes(2, 16, 1024));
+  const int32_t *lens = static_cast<int32_t *>(P(0x50000));
+  float *out = static_cast<float *>(P(0x80000));
+  v.head_dim = 256;
+  CHECK(kvarn_decode_attn(P(0x40000), KVARN_DT_BF16, 16, &k, &v, lens, 0.1f, out, 0, P(0x90000), need,
+                          nullptr) == KVARN_ERR_SHAPE);
+  v.head_dim = 64;
+  CHECK(kvarn_decode_attn(P(0x40000), KVARN_DT_BF16, 16, &k, &v, lens, 0.1f, out, 0, P(0x90000), need - 1,
+                          nullptr) == KVARN_ERR_WORKSPACE);
+  CHECK(kvarn_decode_attn(P(0x40000), KVARN_DT_BF16, 16, &k, &v, lens, 0.1f, out, 0, P(0x90000), need,
+                          nullptr) == KVARN_OK);
+  CHECK(g_generic == 4 && g_decode.head_dim == 64 && g_decode.n_wg == 2);
+}
+
 static void check_status_strings() {
   for (int s = -9; s <= 1; ++s) {
     const char *t = kvarn_status_string(s);
@@ -261,6 +320,7 @@ int main() {
   check_decode();
   check_decode_noalloc();
   check_token_error();
+  check_head_dim();
   check_status_strings();
   if (failures) {
     fprintf(stderr, "%d checks failed\n", failures);

@@ -70,3 +70,18 @@ def test_token_error_output_shapes():
         kv.token_error(x, c, ratio=torch.zeros((2, 2, 128)))
     with pytest.raises(ValueError, match="cosine"):
         kv.token_error(x, c, cosine=torch.zeros((2, 2, 256), dtype=torch.float64))
+
+
+def test_cache_head_dim_checked():
+    c = kv.Cache.empty(1, 1, 128, kv.K, device="cpu", head_dim=256)
+    assert c.head_dim == 256 and c.codes.shape[3] == 32 * 256
+    bad = kv.Cache.empty(1, 1, 128, kv.K, device="cpu", head_dim=96)
+    with pytest.raises(ValueError, match="head_dim"):
+        bad.desc()
+    with pytest.raises(ValueError, match="D"):
+        kv.quantize(torch.zeros((1, 1, 128, 128)), c)
+    k2 = kv.Cache.empty(1, 1, 128, kv.K, device="cpu", head_dim=64)
+    v2 = kv.Cache.empty(1, 1, 128, kv.V, device="cpu", head_dim=256)
+    with pytest.raises(ValueError, match="head_dim"):
+        kv.decode_attn(torch.zeros((1, 4, 64), dtype=torch.bfloat16), k2, v2,
+                       torch.ones(1, dtype=torch.int32))
