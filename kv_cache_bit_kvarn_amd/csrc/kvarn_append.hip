@@ -13,7 +13,10 @@
 namespace kvarn {
 namespace {
 
-__device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+__device__ __forceinline__ uint32_t or_quad(uint32_t c) {
+  c |= __float_as_uint(lane_xor<1>(__uint_as_float(c)));
+  return c | __float_as_uint(lane_xor<2>(__uint_as_float(c)));
+}
 
 // kRotate = false: the token is already rotated (rotation absorbed into the
 // model's weights).
@@ -55,7 +58,7 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
     y1 = d;
 #pragma unroll
     for (int bit = 1; bit < 64; bit <<= 1) {
-      const float p0 = shfl_xor(y0, bit), p1 = shfl_xor(y1, bit);
+      const float p0 = lane_xor(y0, bit), p1 = lane_xor(y1, bit);
       const bool hi = (lane & bit) != 0;
       y0 = hi ? p0 - y0 : y0 + p0;
       y1 = hi ? p1 - y1 : y1 + p1;
@@ -81,7 +84,7 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
   const float z0 = y0 * (1.f / c0), z1 = y1 * (1.f / c1);
   float m = fmaxf(fabsf(z0), fabsf(z1));
 #pragma unroll
-  for (int bit = 1; bit < 64; bit <<= 1) m = fmaxf(m, shfl_xor(m, bit));
+  for (int bit = 1; bit < 64; bit <<= 1) m = fmaxf(m, lane_xor(m, bit));
   if (lane == 0)
     a.row_scale[(int64_t)bh * a.capacity + pos] = m * (kRotate ? kRangeFromUnscaled : kRangeFromRotated);
   const float qs = m > 0.f ? 2.f / m : 0.f;
@@ -90,30 +93,29 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
 
   uint8_t *cb = a.codes + ((int64_t)bh * nch + k) * CHUNK_BYTES;
   if (a.kind == KVARN_K) {
-    // token row: channel j -> byte j/4, bits 2 (j % 4). Lane l gathers the
-    // four codes of channels 4l..4l+3 (l < 16) or 64 + 4(l-16).. (l < 32).
-    const int src = 4 * (lane & 15);
-    uint32_t byte = 0;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint32_t v0 = (uint32_t)__shfl((int)q0, src + r, 64);
-      const uint32_t v1 = (uint32_t)__shfl((int)q1, src + r, 64);
-      byte |= ((lane < 16) ? v0 : v1) << (2 * r);
+    // token row: channel j -> byte j/4, bits 2 (j % 4). The four lanes of
+    // quad j hold channels 4 j .. 4 j + 3 (and 64 + the same): their codes
+    // meet by ORs across the quad.
+    const int sh = 2 * (lane & 3);
+    const uint32_t b0 = or_quad(q0 << sh), b1 = or_quad(q1 << sh);
+    if ((lane & 3) == 0) {
+      cb[slot * 32 + (lane >> 2)] = (uint8_t)b0;
+      cb[slot * 32 + 16 + (lane >> 2)] = (uint8_t)b1;
     }
-    if (lane < 32) cb[slot * 32 + lane] = (uint8_t)byte;
   } else {
-    // channel row j: token slot s -> byte s/4, bits 2 (s % 4)
-    const int sh = 2 * (slot & 3);
-    uint8_t *p0 = cb + lane * 32 + (slot >> 2);
-    uint8_t *p1 = cb + (lane + 64) * 32 + (slot >> 2);
-    if (sh == 0) {
-      *p0 = (uint8_t)q0;
-      *p1 = (uint8_t)q1;
-    } else {
-      const uint32_t keep = ~(3u << sh) & 0xFFu;
-      *p0 = (uint8_t)((*p0 & keep) | (q0 << sh));
-      *p1 = (uint8_t)((*p1 & keep) | (q1 << sh));
-    }
+    // channel row j: token slot s -> byte s/4, bits 2 (s % 4). The field is
+    // cleared and set by two atomics on its 32-bit word, which need no
+    // read of the byte first (the other tokens of the word are kept); a
+    // token that starts a byte clears the byte's three later fields too.
+    const int byte = slot >> 2;
+    const int shift = 8 * (byte & 3) + 2 * (slot & 3);
+    const uint32_t field = ((slot & 3) == 0 ? 0xFFu : 3u) << shift;
+    uint32_t *w0 = reinterpret_cast<uint32_t *>(cb + lane * 32 + (byte & ~3));
+    uint32_t *w1 = reinterpret_cast<uint32_t *>(cb + (lane + 64) * 32 + (byte & ~3));
+    __hip_atomic_fetch_and(w0, ~field, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_and(w1, ~field, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_or(w0, q0 << shift, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_or(w1, q1 << shift, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

@@ -426,36 +426,26 @@ __device__ __forceinline__ void process_chunk(DecSmem &sm, SplitState &st, const
 // Last step for one query head, by one wave: lane l holds channels 2 l and
 // 2 l + 1 of the merged numerator (x0, x1) and every lane the denominator L;
 // out = (x / L) H_128 / sqrt(128), or x / L when the rotation is absorbed.
-// The inverse rotation regroups the channels so that lane l holds channels
-// l and l + 64 (bit 6 in the lane, bits 0..5 across lanes) and runs the
-// butterflies on lane exchanges.
+// Channel bit 0 is the register, bits 1..6 are lane bits 0..5: the first
+// butterfly stage is in registers, the other six exchange lanes.
 template <bool kRotate>
 __device__ __forceinline__ void finalize_head(float x0, float x1, float L, int lane, float *out) {
   const float inv = L > 0.f ? 1.f / L : 0.f;
   x0 *= inv;
   x1 *= inv;
   if constexpr (kRotate) {
-    const float e0 = __shfl(x0, lane >> 1, 64), o0 = __shfl(x1, lane >> 1, 64);
-    const float e1 = __shfl(x0, 32 + (lane >> 1), 64), o1 = __shfl(x1, 32 + (lane >> 1), 64);
-    float y0 = (lane & 1) ? o0 : e0;  // channel lane
-    float y1 = (lane & 1) ? o1 : e1;  // channel lane + 64
-    {
-      const float s0 = y0 + y1, d0 = y0 - y1;
-      y0 = s0;
-      y1 = d0;
-    }
+    float y0 = x0 + x1, y1 = x0 - x1;
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) {
-      const float p0 = __shfl_xor(y0, m, 64), p1 = __shfl_xor(y1, m, 64);
+      const float p0 = lane_xor(y0, m), p1 = lane_xor(y1, m);
       const bool upper = (lane & m) != 0;
       y0 = upper ? p0 - y0 : y0 + p0;
       y1 = upper ? p1 - y1 : y1 + p1;
     }
-    out[lane] = y0 * kInvSqrtD;
-    out[lane + 64] = y1 * kInvSqrtD;
-  } else {
-    *reinterpret_cast<f32x2 *>(out + 2 * lane) = f32x2{x0, x1};
+    x0 = y0 * kInvSqrtD;
+    x1 = y1 * kInvSqrtD;
   }
+  *reinterpret_cast<f32x2 *>(out + 2 * lane) = f32x2{x0, x1};
 }
 
 // Accesses to memory shared by the workgroups of one launch, coherent across
@@ -577,7 +567,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeArgs a) {
       const bool upper = (n_l & m) != 0;
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
-        const float p = __shfl_xor(qr[jj], m, 64);
+        const float p = lane_xor(qr[jj], m);
         qr[jj] = upper ? p - qr[jj] : qr[jj] + p;
       }
     }

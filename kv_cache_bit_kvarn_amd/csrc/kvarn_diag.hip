@@ -19,7 +19,7 @@ constexpr int kWaves = 4;  // waves per workgroup
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
+  for (int m = 1; m < 64; m <<= 1) v += lane_xor(v, m);
   return v;
 }
 
@@ -53,7 +53,7 @@ __global__ __launch_bounds__(64 * kWaves) void token_error_kernel(DiagArgs a) {
       y1 = d;
 #pragma unroll
       for (int m = 1; m < 64; m <<= 1) {
-        const float p0 = __shfl_xor(y0, m, 64), p1 = __shfl_xor(y1, m, 64);
+        const float p0 = lane_xor(y0, m), p1 = lane_xor(y1, m);
         const bool upper = lane & m;
         y0 = upper ? p0 - y0 : y0 + p0;
         y1 = upper ? p1 - y1 : y1 + p1;

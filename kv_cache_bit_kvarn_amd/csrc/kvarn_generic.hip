@@ -35,12 +35,12 @@ static_assert(inv_sqrt_d(64) * 8.f == 1.f && inv_sqrt_d(256) * 16.f == 1.f, "1/s
 
 __device__ __forceinline__ float wsum(float v) {
 #pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
+  for (int m = 1; m < 64; m <<= 1) v += lane_xor(v, m);
   return v;
 }
 __device__ __forceinline__ float wmax(float v) {
 #pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, lane_xor(v, m));
   return v;
 }
 
@@ -62,7 +62,7 @@ __device__ __forceinline__ void fwht_wave(float (&v)[KD], int lane) {
     const bool up = (lane & m) != 0;
 #pragma unroll
     for (int k = 0; k < KD; ++k) {
-      const float p = __shfl_xor(v[k], m, 64);
+      const float p = lane_xor(v[k], m);
       v[k] = up ? p - v[k] : v[k] + p;
     }
   }

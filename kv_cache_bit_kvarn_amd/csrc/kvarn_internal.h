@@ -26,15 +26,51 @@ constexpr float kInvSqrtD = 0.088388347648318447f;  // 1/sqrt(128)
 constexpr float kRangeFromRotated = 0.5f;
 
 // ---- cross-lane helpers (DPP on gfx950, wave64) -------------------------
-__device__ __forceinline__ float dpp_xor1(float v) {
-  // quad_perm [1,0,3,2]: lane i reads lane i^1
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+// The value that lane (l ^ M) of the wave holds, for M = 1, 2, 4, 8, 16, 32,
+// by VALU lane exchanges: quad permutes (M = 1, 2), a quad reversal followed
+// by a half-row mirror (M = 4: lane i reads (i ^ 7) ^ 3 = i ^ 4), a rotation
+// by 8 within the 16-lane row (M = 8), and the row-pair and half-wave swaps
+// (M = 16, 32). A lane shuffle (ds_bpermute) is an LDS round trip instead,
+// several times slower in a dependent chain.
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+  const int x = __float_as_int(v);
+  if constexpr (M == 1) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+  } else if constexpr (M == 2) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
+  } else if constexpr (M == 4) {
+    const int r = __builtin_amdgcn_mov_dpp(x, 0x1B, 0xF, 0xF, false);        // quad_perm [3,2,1,0]
+    return __int_as_float(__builtin_amdgcn_mov_dpp(r, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  } else if constexpr (M == 8) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false));  // row_ror:8
+  } else if constexpr (M == 16) {
+    const auto s = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+    return __uint_as_float(((threadIdx.x >> 4) & 1) ? s[0] : s[1]);
+  } else {
+    static_assert(M == 32, "lane_xor: M is a power of two below 64");
+    const auto s = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+    return __uint_as_float(((threadIdx.x >> 5) & 1) ? s[0] : s[1]);
+  }
+}
+// The same for an M known after unrolling.
+__device__ __forceinline__ float lane_xor(float v, int m) {
+  switch (m) {
+    case 1: return lane_xor<1>(v);
+    case 2: return lane_xor<2>(v);
+    case 4: return lane_xor<4>(v);
+    case 8: return lane_xor<8>(v);
+    case 16: return lane_xor<16>(v);
+    default: return lane_xor<32>(v);
+  }
 }
 
-// s_waitcnt operand on gfx9: vmcnt(0), expcnt and lgkmcnt left at their maxima
-constexpr int kVmcntZero = (0x7 << 4) | (0xF << 8);
-// vmcnt(2), expcnt and lgkmcnt left at their maxima
-constexpr int kVmcntTwo = 2 | (0x7 << 4) | (0xF << 8);
+// s_waitcnt operand on gfx9 that waits until at most n vector-memory
+// operations of the wave are outstanding (vmcnt bits 3:0 and 15:14), with
+// expcnt and lgkmcnt left at their maxima
+constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+constexpr int kVmcntZero = waitcnt_vm(0);
+static_assert(kVmcntZero == ((0x7 << 4) | (0xF << 8)), "vmcnt(0) encoding");
 
 // Workgroup barrier for LDS traffic only: the wave's LDS accesses complete
 // (lgkmcnt(0)), then s_barrier. Unlike __syncthreads() it does not wait for

@@ -65,6 +65,14 @@ constexpr int kWaves = kThreads / 64;
 constexpr int CPT = 32;                        // values per lane: 4 tokens x 8 channels
 constexpr float kGrid = 1.9999980926513672f;  // 2 (1 - 2^-20)
 constexpr float kTiny = 1.17549435e-38f;       // smallest normal fp32
+// Global stores each wave issues per block after it prefetches the block
+// after next into LDS (section 4: column scales, row scales, codes). The
+// prefetch wait leaves all but one of them outstanding, so one store fewer
+// than counted here (a compiler-merged or removed store) still waits for
+// the prefetch; more stores only wait less long.
+constexpr int kStoresAfterPrefetch = 3;
+constexpr int kPrefetchLanded = waitcnt_vm(kStoresAfterPrefetch - 1);
+static_assert(kStoresAfterPrefetch >= 2 && kStoresAfterPrefetch - 1 < 64, "prefetch wait count");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -405,13 +413,13 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
         // next block's input from the LDS slice into xn, then the block after
         // it into the slice: in flight during this whole block and the next
         // one's rotation (the LDS-only barriers below do not wait for it).
-        // The slice's load was issued one block ago; every block issues at
-        // least two stores after it (its codes and its row scales, or it
-        // waits for everything when it skips), and vector memory counts
-        // retire in order, so vmcnt(2) means the load has landed while the
-        // last block's stores may still be in flight. The slice is the wave's
-        // own: LDS ordering within the wave is all that is needed after that.
-        __builtin_amdgcn_s_waitcnt(kVmcntTwo);
+        // The slice's load was issued one block ago and was followed by that
+        // block's kStoresAfterPrefetch stores (a skipped block waits for
+        // everything instead); vector-memory operations retire in order, so
+        // kPrefetchLanded means the load has landed while the last block's
+        // stores may still be in flight. The slice is the wave's own: LDS
+        // ordering within the wave is all that is needed after that.
+        __builtin_amdgcn_s_waitcnt(kPrefetchLanded);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) xn[kk] = sm.xin[wv][kk][lane];
         __builtin_amdgcn_s_waitcnt((0x7 << 4) | 0xF | (0x3 << 14));  // lgkmcnt(0): reads done
@@ -536,7 +544,11 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
     }
 
     // ---- 4. range step and codes --------------------------------------------
-    if ((lane & 3) == 0)  // wave wv holds the column scales of channels 16 wv + [0, 16)
+    // The three global stores below (column scales, row scales, codes) are
+    // issued by every wave of every block that is not skipped, each with
+    // active lanes in every wave: they are the kStoresAfterPrefetch that the
+    // prefetch wait counts on.
+    if ((lane & 3) == 0)  // store 1 of 3; wave wv holds the column scales of channels 16 wv + [0, 16)
       a.col_scale[(bh * nch + chunk) * D + 16 * wv + ((tid & 63) >> 2)] = cm;
     float mx[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -547,7 +559,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
         mx[r] = fmaxf(mx[r], fabsf(y[4 * nt + r]));
       }
     const float m = row_reduce4<true>(mx, n);  // token 4 g + tsel(n)
-    if (n < 4) {  // lane t % 16 < 4 of row (t / 16) % 4: token 4 (t / 16) + tsel(t) of the block
+    if (n < 4) {  // store 2 of 3; lane t % 16 < 4 of row (t / 16) % 4: token 4 (t / 16) + tsel(t)
       const int t = tid;
       a.row_scale[bh * a.capacity + (int64_t)chunk * T + 4 * (t >> 4) + tsel(t)] = m * range_factor;
     }
@@ -595,7 +607,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
       const u32x2 pk = {__builtin_amdgcn_perm(t23, t01, 0x05040100u),
                         __builtin_amdgcn_perm(t23, t01, 0x07060302u)};
       // tokens 16 wv + 4 g + [0, 4) are 128 contiguous bytes from (16 wv + 4 g) * 32
-      *reinterpret_cast<u32x2 *>(cbase + 8 * (t & 511)) = pk;
+      *reinterpret_cast<u32x2 *>(cbase + 8 * (t & 511)) = pk;  // store 3 of 3 (K)
     } else {
       // Byte j of p0 (p1) is the V byte of channel 16 j + n (16 (4 + j) + n),
       // tokens 16 wv + 4 g + [0, 4) (byte column 4 wv + g of the channel
@@ -647,7 +659,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
       const int u = tid;
       const uint32_t *src = vs + VST_ROW * (u >> 2) + 2 * (u & 3);
       const u32x2 word = {src[0], src[1]};
-      *reinterpret_cast<u32x2 *>(cbase + 8 * u) = word;
+      *reinterpret_cast<u32x2 *>(cbase + 8 * u) = word;  // store 3 of 3 (V)
     }
   }
   // the last prefetch into the LDS slice lands before the workgroup (and its
