@@ -42,10 +42,13 @@ D, CHUNK = 128, 128
 # codes, 4 B row scale per 128 channels, 4 B column scale per 128 tokens
 QUANT_BYTES_PER_ELT_BF16 = 2.0 + 0.25 + 4.0 / 128 + 4.0 / 128
 # MI355X fp32 vector peak, published: 256 CUs x 4 SIMDs x 32 lanes per clock
-# x 2 flop per FMA x 2.4 GHz = 157.3 TFLOP/s. Plain (non-packed) v_fmac_f32
-# reaches most of it: a throughput probe of independent FMAs measured
-# 120 TFLOP/s (DPP-sourced FMAs: 68-70).
+# x 2 flop per FMA x 2.4 GHz = 157.3 TFLOP/s, which counts packed (two-wide)
+# fp32 instructions. The kernels here are built without packed fp32 (it is
+# switched off in the build), and a throughput probe measures a wave64
+# non-packed fp32 instruction (fma, mul, add, DPP-sourced add, cvt_pk_u8)
+# at 4.2 cycles of its SIMD, i.e. 16 lanes per clock: 78.6 TFLOP/s for FMAs.
 VALU_F32_PEAK_TFLOPS = 256 * 4 * 32 * 2 * 2.4e9 / 1e12
+VALU_F32_NONPACKED_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 # the machine's CPU share for one GPU: worker pools stay within it
 HOST_THREAD_CAP = 16
 
@@ -374,7 +377,10 @@ def quant_roofline(qbytes, elts, q_us, iters, wl_name):
     t_alu = q_flop / (VALU_F32_PEAK_TFLOPS * 1e12)
     alu = {"achieved": round(q_tflops, 2), "peak": round(VALU_F32_PEAK_TFLOPS, 2),
            "unit": "TFLOP/s", "frac": round(q_tflops / VALU_F32_PEAK_TFLOPS, 4),
-           "flop_per_element": quant_flop_per_elt(iters)}
+           "flop_per_element": quant_flop_per_elt(iters),
+           "peak_nonpacked": round(VALU_F32_NONPACKED_TFLOPS, 2),
+           "frac_nonpacked": round(q_tflops / VALU_F32_NONPACKED_TFLOPS, 4),
+           "ideal_us_nonpacked": round(q_flop / (VALU_F32_NONPACKED_TFLOPS * 1e12) * 1e6, 2)}
     hbm = {"achieved": round(q_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
            "frac": round(q_gbps / HBM_PEAK_GBPS, 4)}
     bound, main, other = ("hbm", hbm, alu) if t_hbm >= t_alu else ("alu", alu, dict(hbm))
