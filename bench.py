@@ -358,6 +358,8 @@ def main():
         sub = kvgen.WORKLOADS[4]
         res["workloads"][sub.name] = stress_workload(kv, kvgen, torch, sub, args, dev, stream)
         torch.cuda.empty_cache()
+        res["next_rows"] = next_rows_workload(kv, kvgen, torch, args, dev, stream)
+        torch.cuda.empty_cache()
     if cpu_inputs is not None:
         res["cpu_baseline"] = cpu_baseline(args, wl, cpu_inputs, res["unit"], bf16_bytes_step,
                                            cap)
@@ -643,6 +645,120 @@ def stress_workload(kv, kvgen, torch, wl, args, dev, stream):
            "note": "HIP events; quantize mean of 6 launches (K, V alternating), decode mean of "
                    "10 calls over a 5.4 GB cache"}
     del xk, xv, kc, vc, nk, nv, q, out, ws
+    return res
+
+
+def graph_us(torch, fn, reps: int = 5) -> float:
+    """Microseconds of one replay of a HIP graph holding fn's launches: the
+    median of `reps` timed replays after one untimed replay."""
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    g.replay()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        g.replay()
+        b.record(st)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3)
+    del g
+    return sorted(ts)[reps // 2]
+
+
+def next_rows_workload(kv, kvgen, torch, args, dev, stream):
+    """Sub-result: the rows built beyond the hot path, measured to the same
+    bar as the path itself.
+    - append_rebalance (the append that re-quantizes a chunk when it fills) at
+      the Llama-3-8B layer shape (32 sequences, 8 kv-heads): 128 steps of K and
+      V appends filling one chunk, captured in a HIP graph, against the same
+      steps with the plain append; the difference over the two chunk closes is
+      the cost of re-quantizing a full chunk of 256 (sequence, kv-head) blocks.
+    - head sizes 64 and 256 (generic kernels) at the Qwen3-4B layer shape
+      (8 sequences, 8 kv-heads, 32 query heads, 32768 tokens): quantize of bf16
+      K over 4 layers' inputs and decode over 4 layers' caches, each cycled so
+      that nothing is served from the memory-side cache; HIP events, 12 launches
+      after a warm one, median of 3 rounds."""
+    res = {}
+    B, H = 32, 8
+    kc = kv.Cache.empty(B, H, 2 * CHUNK, kv.K, device=dev)
+    vc = kv.Cache.empty(B, H, 2 * CHUNK, kv.V, device=dev)
+    wk, wv = kv.append_window(B, H, device=dev), kv.append_window(B, H, device=dev)
+    toks = [(kvgen.new_tokens(11, 0, kvgen.K, B, H, 0.5, step=t, device=dev),
+             kvgen.new_tokens(11, 0, kvgen.V, B, H, 0.5, step=t, device=dev)) for t in range(CHUNK)]
+    poss = [torch.full((B,), t, dtype=torch.int32, device=dev) for t in range(CHUNK)]
+
+    def fill(rebalance: bool):
+        for t in range(CHUNK):
+            if rebalance:
+                kv.append_rebalance(toks[t][0], poss[t], kc, wk, iters=args.iters)
+                kv.append_rebalance(toks[t][1], poss[t], vc, wv, iters=args.iters)
+            else:
+                kv.append(toks[t][0], poss[t], kc)
+                kv.append(toks[t][1], poss[t], vc)
+
+    t_re = graph_us(torch, lambda: fill(True))
+    t_plain = graph_us(torch, lambda: fill(False))
+    res["append_rebalance"] = {
+        "config": {"batch": B, "kv_heads": H, "tokens_appended": CHUNK},
+        "us_per_call": round(t_re / (2 * CHUNK), 2),
+        "plain_append_us_per_call": round(t_plain / (2 * CHUNK), 2),
+        "extra_us_per_128_steps": round(t_re - t_plain, 2),
+        "note": "HIP-graph replays of 128 steps (K and V); each append_rebalance call is an "
+                "append plus a launch of the chunk re-quantizer, whose workgroups leave at "
+                "once except at the step that closes the chunk (the extra time covers those "
+                "launches and the two closes)"}
+    del kc, vc, wk, wv, toks, poss
+    torch.cuda.empty_cache()
+
+    B, H, Hq, T, L = 8, 8, 32, 32768, 4
+    for dh in (64, 256):
+        log(f"[bench] head size {dh}: generating inputs ...")
+        xs = [kvgen.kv_tensor(5, l, kvgen.K, B, H, T, 0.5, device=dev, head_dim=dh)
+              for l in range(L)]
+        qcs = [kv.Cache.empty(B, H, T, kv.K, device=dev, head_dim=dh) for _ in range(L)]
+        caches = []
+        for l in range(L):
+            pair = []
+            for kind in (kv.K, kv.V):
+                x = kvgen.kv_tensor(5, l, kind, B, H, T, 0.5, device=dev, head_dim=dh)
+                c = kv.Cache.empty(B, H, T + CHUNK, kind, device=dev, head_dim=dh)
+                kv.quantize(x, c, iters=args.iters, stream=stream)
+                del x
+                pair.append(c)
+            caches.append(pair)
+        q = [kvgen.queries(5, l, B, Hq, device=dev, head_dim=dh) for l in range(L)]
+        out = torch.empty((B, Hq, dh), dtype=torch.float32, device=dev)
+        ws = kv.decode_workspace(B, Hq, T + CHUNK, device=dev, head_dim=dh)
+        lens = torch.full((B,), T + 1, dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()
+        qf = [lambda i=i: kv.quantize(xs[i % L], qcs[i % L], iters=args.iters, stream=stream)
+              for i in range(12)]
+        df = [lambda i=i: kv.decode_attn(q[i % L], caches[i % L][0], caches[i % L][1], lens,
+                                         out=out, workspace=ws, stream=stream) for i in range(12)]
+        qm, dm = [], []
+        for _ in range(3):
+            qf[0]()
+            qu = timed_events(torch, stream, qf)
+            df[0]()
+            du = timed_events(torch, stream, df)
+            qm.append(sum(qu) / len(qu))
+            dm.append(sum(du) / len(du))
+        qm, dm = sorted(qm)[1], sorted(dm)[1]
+        elts = B * H * T * dh
+        qbytes = (2.0 + 0.25 + 4.0 / dh + 4.0 / CHUNK) * elts
+        dbytes = (dh / 2 + 8 + dh / 16) * (T + 1) * B * H + B * Hq * dh * 6
+        res[f"head_dim_{dh}"] = {
+            "config": {"batch": B, "kv_heads": H, "q_heads": Hq, "tokens": T, "head_dim": dh},
+            "quantize_us_per_launch": round(qm, 2), "quantize": hbm_entry(qbytes, qm),
+            "decode_us_per_launch": round(dm, 2), "decode": hbm_entry(dbytes, dm),
+            "note": "generic kernels (correctness paths, not tuned)"}
+        del xs, qcs, caches, q, out, ws
+        torch.cuda.empty_cache()
     return res
 
 

@@ -328,6 +328,18 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
   // 1/2 of the range step, or the 1/2 alone for pre-rotated input
   const float range_factor = kRotate ? kRangeFromUnscaled : kRangeFromRotated;
 
+  // Positions mode runs after every append, and a chunk closes on one step in
+  // 128: a workgroup none of whose blocks closes leaves before it loads
+  // anything (the loop below skips the non-closing blocks of the others).
+  if constexpr (kPositions) {
+    bool any = false;
+    for (uint32_t b0 = blockIdx.x; b0 < a.nblocks; b0 += gridDim.x) {
+      const int pos = a.pos[split_block(a, b0).b];
+      any |= pos >= 0 && pos < a.capacity && pos % T == T - 1;
+    }
+    if (!any) return;  // uniform over the workgroup
+  }
+
   // the lane's two rotation operands live in LDS (registers are held by y,
   // P and the next block's input through the balancing)
   if (tid < 64) {
