@@ -264,21 +264,73 @@ def main():
                                                   news, qs, out, ws, L, B, T)
         q_us = None
     else:
-        log(f"[bench] timing {args.steps} steps")
+        # The quantize launches run eagerly (each keeps the GPU busy far longer
+        # than its launch takes). The append + decode phase, whose launches are
+        # shorter than the host's cost per call, runs as one captured HIP graph,
+        # so that the step is not timed waiting for the host; graphs of the
+        # decodes alone and the appends alone give their per-launch times.
+        pos_g = torch.full((B,), T, dtype=torch.int32, device=dev)
+        lens_g = pos_g + 1
+
+        def appends():
+            for layer in range(L):
+                kc, vc = caches[layer]
+                kv.append(news[layer][0], pos_g, kc)
+                kv.append(news[layer][1], pos_g, vc)
+
+        def decodes(layer=None):
+            for la in (range(L) if layer is None else [layer]):
+                kc, vc = caches[la]
+                kv.decode_attn(qs[la], kc, vc, lens_g, out=out, workspace=ws)
+
+        def phase2():
+            for layer in range(L):
+                kc, vc = caches[layer]
+                kv.append(news[layer][0], pos_g, kc)
+                kv.append(news[layer][1], pos_g, vc)
+                decodes(layer)
+
+        torch.cuda.synchronize()
+        graphs = {}
+        for name, fn in (("step", phase2), ("decode", decodes), ("append", appends)):
+            graphs[name] = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graphs[name]):
+                fn()
+        graphs["step"].replay()
+        torch.cuda.synchronize()
+
+        log(f"[bench] timing {args.steps} steps (append + decode as HIP graph replays)")
         start, end = ev(), ev()
         torch.cuda.synchronize()
         start.record(stream)
         for i in range(args.steps):
-            step(args.warmup + i, rec)
+            for layer in range(L):
+                for x, c in ((xs[layer][0], caches[layer][0]), (xs[layer][1], caches[layer][1])):
+                    a, b_ = ev(), ev()
+                    a.record(stream)
+                    kv.quantize(x, c, iters=args.iters, stream=stream)
+                    b_.record(stream)
+                    rec["quantize"].append((a, b_))
+            graphs["step"].replay()
         end.record(stream)
         torch.cuda.synchronize()
         ms_step = start.elapsed_time(end) / args.steps
 
-        def avg_us(name):
-            v = [a.elapsed_time(b_) * 1e3 for a, b_ in rec[name]]
-            return (sum(v) / len(v)) if v else None
+        def replay_us(g, n):
+            a, b_ = ev(), ev()
+            torch.cuda.synchronize()
+            a.record(stream)
+            for _ in range(n):
+                g.replay()
+            b_.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b_) * 1e3 / n
 
-        q_us, a_us, d_us = avg_us("quantize"), avg_us("append"), avg_us("decode")
+        v = [a.elapsed_time(b_) * 1e3 for a, b_ in rec["quantize"]]
+        q_us = sum(v) / len(v)
+        d_us = replay_us(graphs["decode"], max(args.steps, 5)) / L
+        a_us = replay_us(graphs["append"], max(args.steps, 5)) / (2 * L)
+        del graphs
     elts_per_quant = B * Hkv * T * D
     q_launches = 0 if steady else 2 * L
     bf16_bytes_step = q_launches * elts_per_quant * 2
@@ -299,7 +351,8 @@ def main():
                    "balancing_iters": args.iters, "input_dtype": "bf16",
                    "token_scale_sigma": wl.sigma,
                    "step": "append+decode per layer" if steady else
-                           "quantize K,V of every layer, then append + decode per layer"},
+                           "quantize K,V of every layer, then append + decode per layer "
+                           "(the append + decode phase as one HIP graph replay)"},
     }
     dec = {"tokens_per_s": round(B / (decode_ms_step / 1e3), 1),
            "us_per_launch": round(d_us, 2), "launches_per_step": L,
@@ -342,6 +395,11 @@ def main():
     cpu_inputs = None
     if not args.no_cpu_baseline and not steady:
         cpu_inputs = cpu_sample(args, wl, xs, news, qs)
+    if not steady:
+        res["host_us_per_call"] = host_cost(
+            kv, torch, stream, xs[0][0], caches[0], news[0][0], qs[0], out, ws,
+            torch.full((B,), T + 1, dtype=torch.int32, device=dev),
+            torch.full((B,), T, dtype=torch.int32, device=dev))
     if not args.no_ablations and not steady:
         res["ablations"] = ablations(kv, torch, stream, xs, qs, caches, ws, out, T + 1,
                                      args.iters)
@@ -645,6 +703,44 @@ def stress_workload(kv, kvgen, torch, wl, args, dev, stream):
            "note": "HIP events; quantize mean of 6 launches (K, V alternating), decode mean of "
                    "10 calls over a 5.4 GB cache"}
     del xk, xv, kc, vc, nk, nv, q, out, ws
+    return res
+
+
+def host_cost(kv, torch, stream, x, cache_pair, new_tok, q, out, ws, lens, pos, n: int = 200):
+    """Host microseconds per call, enqueue only: wall time of n back-to-back
+    calls with no synchronization inside (the GPU work queues up behind
+    them), for the Python binding's quantize, append and decode, and for
+    decode through the C ABI directly with its arguments marshalled once
+    (the library's own host share)."""
+    import ctypes
+    kc, vc = cache_pair
+    lib = kv.load()
+    kd, vd = kc.desc(), vc.desc()
+    sh = stream.cuda_stream
+    raw = (q.data_ptr(), kv._dtype_code(q), q.shape[1], ctypes.byref(kd), ctypes.byref(vd),
+           lens.data_ptr(), q.shape[2] ** -0.5, 0, out.data_ptr(), 0, ws.data_ptr(),
+           ws.numel() * ws.element_size(), sh)
+    calls = {
+        "quantize_binding": lambda: kv.quantize(x, kc, stream=stream),
+        "append_binding": lambda: kv.append(new_tok, pos, kc, stream=stream),
+        "decode_binding": lambda: kv.decode_attn(q, kc, vc, lens, out=out, workspace=ws,
+                                                 stream=stream),
+        "decode_c_abi": lambda: lib.kvarn_decode_attn_ex(*raw),
+    }
+    res = {}
+    for name, fn in calls.items():
+        reps = 8 if name.startswith("quantize") else n
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        t1 = time.perf_counter()
+        torch.cuda.synchronize()
+        res[name] = round((t1 - t0) / reps * 1e6, 2)
+    res["note"] = ("host wall time per enqueued call, no synchronization inside the loop; "
+                   "decode_c_abi calls kvarn_decode_attn_ex through ctypes with prebuilt "
+                   "arguments")
     return res
 
 
