@@ -505,14 +505,8 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeArgs a) {
   const bool valid = len >= 1 && len <= a.capacity;
   const int used = valid ? (len + T - 1) / T : 0;
   const int n_split = a.n_wg * kDecWaves, split = wgs * kDecWaves + wv;
-#ifdef KVARN_DECODE_CAPACITY_RANGES
-  const int per = (nch + n_split - 1) / n_split;
-  const int c0 = min(split * per, used);
-  const int c1 = min(c0 + per, used);
-#else
   const int c0 = (int)((int64_t)split * used / n_split);
   const int c1 = (int)((int64_t)(split + 1) * used / n_split);
-#endif
   const int64_t bg = (int64_t)b * a.kv_heads + g;
   const int64_t qh0 = (int64_t)b * a.q_heads + (int64_t)g * G + h0;
   const int64_t row = bg * n_hg + hg;  // counter index
@@ -751,10 +745,7 @@ static int device_simds() { return 4 * device_cus(); }
 // Workgroups per (sequence, kv-head, head group): about kWavesPerSimd waves
 // per SIMD in one round (four-wave workgroups, one split per wave; the
 // kernel's registers allow three waves per SIMD).
-#ifndef KVARN_DECODE_WAVES_PER_SIMD
-#define KVARN_DECODE_WAVES_PER_SIMD 3
-#endif
-constexpr int kWavesPerSimd = KVARN_DECODE_WAVES_PER_SIMD;
+constexpr int kWavesPerSimd = 3;
 int decode_auto_wgs(int batch, int kv_heads, int q_heads, int capacity) {
   const int max_wg = decode_max_wgs(capacity);
   if (batch <= 0 || kv_heads <= 0 || q_heads <= 0 || max_wg <= 0) return 1;
