@@ -35,9 +35,7 @@ int dtype_size(int32_t dtype) {
 
 int from_hip(hipError_t e) { return e == hipSuccess ? KVARN_OK : KVARN_ERR_HIP; }
 
-hipError_t run_decode(const DecodeArgs &a, hipStream_t s) {
-  return a.head_dim == D ? launch_decode(a, s) : launch_decode_generic(a, s);
-}
+hipError_t run_decode(const DecodeArgs &a, hipStream_t s) { return launch_decode(a, s); }
 
 // Checks shared by the decode entry points (everything but the workspace).
 int check_decode(const void *q, int32_t q_dtype, int32_t q_heads, const kvarn_cache *k,
@@ -69,7 +67,8 @@ int check_decode(const void *q, int32_t q_dtype, int32_t q_heads, const kvarn_ca
 // of capacity (rounded up to a workgroup), or the library's choice for 0.
 int decode_wgs(int32_t q_heads, const kvarn_cache *k, int32_t n_split) {
   const int max_wg = decode_max_wgs(k->capacity);
-  int nw = n_split == 0 ? decode_auto_wgs(k->batch, k->kv_heads, q_heads, k->capacity)
+  int nw = n_split == 0 ? decode_auto_wgs(k->batch, k->kv_heads, q_heads, k->capacity,
+                                                         cache_dim(k))
                         : (int)(((int64_t)n_split + KVARN_DECODE_WAVES - 1) / KVARN_DECODE_WAVES);
   if (nw > max_wg) nw = max_wg;
   if (nw < 1) nw = 1;

@@ -1,22 +1,24 @@
 // Decode attention over the 2-bit KVarN cache on gfx950, both scales fused
 // into the dequantization (rndamp article on KVarN, "Numbers").
 //
-// Rotated-domain evaluation. With H = H_128 / sqrt(128) (symmetric,
-// orthogonal) the cache stores y_hat = x_hat H, so
+// Rotated-domain evaluation. With H = H_D / sqrt(D) (symmetric, orthogonal)
+// the cache stores y_hat = x_hat H, so
 //   <q, x_hat_t>      = <q H, y_hat_t>
 //                     = r'_t * sum_j (qH)_j c_j (code_tj - 1.5)
 //   sum_t p_t x_hat_t = ( sum_t p_t y_hat_t ) H
 //                     = ( c_j * sum_t (p_t r'_t)(code_tj - 1.5) )_j  H.
-// The query is rotated once per workgroup, the column scale of K is folded
-// into the rotated query per chunk, the row scale of K into each score, the
-// row scale of V into each probability, and the column scale of V into the
+// The query is rotated once per wave, the column scale of K is folded into
+// the rotated query per chunk, the row scale of K into each score, the row
+// scale of V into each probability, and the column scale of V into the
 // output; the output is rotated back after the split-KV merge.
 //
-// decode_split: grid (n_split * head_groups, kv_heads, batch), one wave64 per
-// workgroup serving up to 4 query heads of one kv-head over its range of
-// 128-token chunks with an online softmax; the next chunk's codes and scales
-// are loaded while the current one is computed. Both products run on
-// v_mfma_scale_f32_16x16x128_f8f6f4, the cache codes being its fp4 operand:
+// One launch, grid (n_wg * head_groups, kv_heads, batch): a workgroup is four
+// waves, each a split serving up to 4 query heads of one kv-head over its
+// range of 128-token chunks with an online softmax; the next chunk's codes
+// and scales are loaded while the current one is computed. The waves merge
+// in LDS, and the last workgroup of a row merges the row's partials (no
+// second launch). Both products run on v_mfma_scale_f32_16x16x128_f8f6f4,
+// the cache codes being its fp4 operand:
 //  * a 2-bit code c in the low bits of a 4-bit field is the e2m1 number c/2,
 //    so w & 0x33333333 and (w >> 2) & 0x33333333 turn a code word into two
 //    operand registers (16 codes for 3 instructions), and c/2 - 3/4 is half
@@ -32,8 +34,9 @@
 //    is undone by the MFMA's per-row E8M0 scale;
 //  * the level offset is one MFMA per chunk against a constant -1.5 operand
 //    at scale 2^-1, added to each head's term sum.
-// decode_combine: grid (q_heads, batch): log-sum-exp merge of the partials
-// (m, l, acc[128]), then the inverse rotation.
+// Head sizes 64, 128 and 256 share the kernel: the QK contraction runs over
+// 128-channel halves (a 64-channel head fills half of one, the rest of both
+// operands zero) and PV over D / 16 channel tiles.
 #include <atomic>
 #include <mutex>
 
@@ -81,8 +84,6 @@ __host__ __device__ constexpr int elem_j(int x) { return (x >> 1) & 7; }
 // padding after every 4 slots, so 16-byte reads by 8 lanes hit distinct banks.
 __host__ __device__ constexpr int slot_base(int s) { return 8 * s + 4 * (s >> 2); }
 __host__ __device__ constexpr int elem_pos(int x) { return slot_base(elem_slot(x)) + elem_j(x); }
-// c_V: channel c is read by the lanes of output column c % 16, tile c / 16
-__host__ __device__ constexpr int cv_pos(int c) { return slot_base(c & 15) + (c >> 4); }
 constexpr int SLOT_ARRAY = 8 * 16 + 4 * 4;
 constexpr int OP_ROW = 36;  // dwords per operand row: 4 lane groups x 8 + 4 padding
 
@@ -170,10 +171,11 @@ __device__ __forceinline__ int row_scale_byte(int sigma, int lane) {
   return 127 - s;
 }
 
-// decode_split's workgroup is one wave, and the LDS accesses of one wave are
-// performed in program order: a cross-lane exchange through LDS then needs
-// only a wavefront-scope fence (which keeps the compiler from reordering the
-// accesses), not a barrier or a wait for the writes to complete.
+// Each wave exchanges values between its lanes through LDS of its own, and
+// the LDS accesses of one wave are performed in program order: such an
+// exchange needs only a wavefront-scope fence (which keeps the compiler from
+// reordering the accesses), not a barrier or a wait for the writes to
+// complete.
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -209,20 +211,47 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Sizes of the kernel for head size DD (64, 128 or 256). The QK contraction
+// runs over 128-channel halves (one MFMA each: DD = 256 has two; DD = 64 uses
+// the first 64 channels of one, the rest of its operands zero); PV writes
+// 16-channel output tiles.
+template <int DD>
+struct Dims {
+  static_assert(DD == 64 || DD == 128 || DD == 256, "head size");
+  static constexpr int NQ = DD > 128 ? 2 : 1;  // QK halves
+  static constexpr int NCT = DD / 16;          // PV output tiles
+  static constexpr int KROW = DD / 4;          // bytes of a K token row
+  static constexpr int CB = T * DD / 4;        // code bytes of a chunk
+  static constexpr int CPL = DD / 64;          // column scales (and output channels) per lane
+  static constexpr int CV_ARRAY = NCT * 16 + 16;
+};
+// c_V in LDS: channel c is read by the lanes of output column c % 16, tile
+// c / 16; NCT floats per column and 4 floats of padding after every 4
+// columns (for NCT = 8 this is slot_base, as for the other scale arrays)
+__host__ __device__ constexpr int cv_base(int nct, int s) { return nct * s + 4 * (s >> 2); }
+static_assert(cv_base(8, 5) == slot_base(5) && cv_base(8, 12) == slot_base(12), "c_V layout");
+// 1/sqrt(DD): the unscaled rotation's factor
+__host__ __device__ constexpr float inv_sqrt_dd(int dd) {
+  return dd == 64 ? 0.125f : dd == 256 ? 0.0625f : kInvSqrtD;
+}
+
+template <int DD>
 struct DecSmem {
-  alignas(16) float ck[SLOT_ARRAY];     // c_K, elem_pos order
-  alignas(16) float cv[SLOT_ARRAY];     // c_V, cv_pos order
-  alignas(16) float rk[SLOT_ARRAY];     // r'_K, elem_pos order
-  alignas(16) float rv[SLOT_ARRAY];     // r'_V, elem_pos order
-  alignas(16) uint32_t aq[16][OP_ROW];  // QK fp8 operand, row 4 h + k = term k of head h
-  alignas(16) uint32_t ap[16][OP_ROW];  // PV fp8 operand, rows 4 h + 3 stay zero
+  alignas(16) float ck[Dims<DD>::NQ][SLOT_ARRAY];  // c_K per half, elem_pos order
+  alignas(16) float cv[Dims<DD>::CV_ARRAY];        // c_V, cv_base order
+  alignas(16) float rk[SLOT_ARRAY];                // r'_K, elem_pos order
+  alignas(16) float rv[SLOT_ARRAY];                // r'_V, elem_pos order
+  alignas(16) uint32_t aq[Dims<DD>::NQ][16][OP_ROW];  // QK fp8 operand per half, row 4 h + k
+  alignas(16) uint32_t ap[16][OP_ROW];             // PV fp8 operand, rows 4 h + 3 stay zero
 };
 
 // Codes and scales of one chunk, in the lane's operand order.
+template <int DD>
 struct ChunkRegs {
-  u32x2 k[8];  // K bytes [8 g, 8 g + 8) of token slot_elem(n, tau)
-  u32x2 v[8];  // V bytes [8 g, 8 g + 8) of channel 16 ct + n
-  u32x2 ck, cv, rk, rv;  // scales of elements 2 lane, 2 lane + 1
+  u32x2 k[Dims<DD>::NQ][8];  // K bytes [8 g, 8 g + 8) of half hf of token slot_elem(n, tau)
+  u32x2 v[Dims<DD>::NCT];    // V bytes [8 g, 8 g + 8) of channel 16 ct + n
+  float ck[Dims<DD>::CPL], cv[Dims<DD>::CPL];  // column scales of channels CPL lane + i
+  u32x2 rk, rv;              // row scales of tokens 2 lane, 2 lane + 1
 };
 
 // The cache is streamed once per decode step: non-temporal loads, which keep
@@ -232,37 +261,62 @@ __device__ __forceinline__ V stream_load(const void *p) {
   return __builtin_nontemporal_load(reinterpret_cast<const V *>(p));
 }
 
-template <bool kTwoScales>
+template <int N>
+__device__ __forceinline__ void load_floats(const float *p, float (&out)[N]) {
+  if constexpr (N == 1) {
+    out[0] = stream_load<float>(p);
+  } else if constexpr (N == 2) {
+    const u32x2 u = stream_load<u32x2>(p);
+    out[0] = __uint_as_float(u[0]);
+    out[1] = __uint_as_float(u[1]);
+  } else {
+    static_assert(N == 4, "column scales per lane");
+    const u32x4 u = stream_load<u32x4>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(u[i]);
+  }
+}
+
+template <int DD, bool kTwoScales>
 __device__ __forceinline__ void load_chunk(const DecodeArgs &a, int64_t bg, int64_t nchunks,
-                                           int k, int lane, ChunkRegs &r) {
+                                           int k, int lane, ChunkRegs<DD> &r) {
+  using Dm = Dims<DD>;
   const int64_t chunk = bg * nchunks + k;
   const int n = lane & 15, g = lane >> 4;
-  const uint8_t *kc = a.k_codes + chunk * CHUNK_BYTES + 32 * slot_elem(n, 0) + 8 * g;
-  const uint8_t *vc = a.v_codes + chunk * CHUNK_BYTES + 32 * n + 8 * g;
+  // a 64-channel token row is 16 bytes: lane groups 2 and 3 hold no codes
+  const bool k_in = DD >= 128 || g < 2;
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    r.k[t] = stream_load<u32x2>(kc + 64 * t);   // token + 2 t
-    r.v[t] = stream_load<u32x2>(vc + 512 * t);  // channel + 16 t
+  for (int hf = 0; hf < Dm::NQ; ++hf) {
+    const uint8_t *kc =
+        a.k_codes + chunk * Dm::CB + Dm::KROW * slot_elem(n, 0) + 32 * hf + 8 * g;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)  // token + 2 t
+      r.k[hf][t] = k_in ? stream_load<u32x2>(kc + 2 * Dm::KROW * t) : u32x2{0u, 0u};
   }
+  const uint8_t *vc = a.v_codes + chunk * Dm::CB + 32 * n + 8 * g;
+#pragma unroll
+  for (int ct = 0; ct < Dm::NCT; ++ct) r.v[ct] = stream_load<u32x2>(vc + 512 * ct);  // channel + 16 ct
   if constexpr (kTwoScales) {
-    r.ck = stream_load<u32x2>(a.k_col + chunk * D + 2 * lane);
-    r.cv = stream_load<u32x2>(a.v_col + chunk * D + 2 * lane);
+    load_floats<Dm::CPL>(a.k_col + chunk * DD + Dm::CPL * lane, r.ck);
+    load_floats<Dm::CPL>(a.v_col + chunk * DD + Dm::CPL * lane, r.cv);
   }
   const int64_t row = bg * (int64_t)a.capacity + (int64_t)k * T + 2 * lane;
   r.rk = stream_load<u32x2>(a.k_row + row);
   r.rv = stream_load<u32x2>(a.v_row + row);
 }
 
+template <int DD>
 struct SplitState {
-  float qv[8];     // query (rotated, scaled) at the channels of this lane's slot
-  float acc[8];    // PV accumulators: head lane >> 4, channel 16 ct + (lane & 15)
+  float qv[Dims<DD>::NQ][8];  // query (rotated, scaled) at the channels of this lane's slot
+  float acc[Dims<DD>::NCT];   // PV accumulators: head lane >> 4, channel 16 ct + (lane & 15)
   float m_run, l_run;
 };
 
 // The QK operand from this lane's 8 values x of head lane >> 4, slot
 // lane & 15: per-head range scale, 4 fp8 terms written to rows 4 h + k of
-// sm.aq. Returns this lane's E8M0 row-scale byte for the operand it reads.
-__device__ __forceinline__ int build_qk_operand(DecSmem &sm, float (&x)[8], int lane) {
+// `rows`. Returns this lane's E8M0 row-scale byte for the operand it reads.
+__device__ __forceinline__ int build_qk_operand(uint32_t (&rows)[16][OP_ROW], float (&x)[8],
+                                                int lane) {
   const int n = lane & 15, h = lane >> 4;
   float mx = 0.f;
 #pragma unroll
@@ -274,7 +328,7 @@ __device__ __forceinline__ int build_qk_operand(DecSmem &sm, float (&x)[8], int 
   u32x2 t[4];
   fp8_terms<4>(x, t);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x2 *>(&sm.aq[4 * h + k][2 * n]) = t[k];
+  for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x2 *>(&rows[4 * h + k][2 * n]) = t[k];
   return row_scale_byte(sig, lane);
 }
 
@@ -286,25 +340,30 @@ __device__ __forceinline__ u32x8 read_operand(const uint32_t (&rows)[16][OP_ROW]
 }
 
 // kTwoScales = false: the column scales are taken as 1 (one-scale ablation);
-// the QK operand (aq_fixed, sa_fixed) is then the same for every chunk.
-template <bool kTwoScales>
-__device__ __forceinline__ void process_chunk(DecSmem &sm, SplitState &st, const ChunkRegs &cur,
-                                              int nvalid, int lane, const u32x8 &aq_fixed,
-                                              int sa_fixed) {
+// the QK operands (aq_fixed, sa_fixed) are then the same for every chunk.
+template <int DD, bool kTwoScales>
+__device__ __forceinline__ void process_chunk(DecSmem<DD> &sm, SplitState<DD> &st,
+                                              const ChunkRegs<DD> &cur, int nvalid, int lane,
+                                              const u32x8 (&aq_fixed)[Dims<DD>::NQ],
+                                              const int (&sa_fixed)[Dims<DD>::NQ]) {
+  using Dm = Dims<DD>;
+  constexpr int NQ = Dm::NQ, NCT = Dm::NCT;
   const int n = lane & 15, h = lane >> 4;
   const int sb = slot_base(n);
 
   // ---- scales to LDS ----
   wave_lds_sync();  // after the previous chunk's readers
   {
-    const int e = 2 * lane;
-    const int pe = elem_pos(e), pc = cv_pos(e);  // element e + 1 sits 8 further on
     if constexpr (kTwoScales) {
-      sm.ck[pe] = __uint_as_float(cur.ck[0]);
-      sm.ck[pe + 8] = __uint_as_float(cur.ck[1]);
-      sm.cv[pc] = __uint_as_float(cur.cv[0]);
-      sm.cv[pc + 8] = __uint_as_float(cur.cv[1]);
+#pragma unroll
+      for (int i = 0; i < Dm::CPL; ++i) {
+        const int e = Dm::CPL * lane + i;  // channel
+        sm.ck[e >> 7][elem_pos(e & 127)] = cur.ck[i];
+        sm.cv[cv_base(NCT, e & 15) + (e >> 4)] = cur.cv[i];
+      }
     }
+    const int e = 2 * lane;  // token; token e + 1 sits 8 further on
+    const int pe = elem_pos(e);
     sm.rk[pe] = __uint_as_float(cur.rk[0]);
     sm.rk[pe + 8] = __uint_as_float(cur.rk[1]);
     sm.rv[pe] = __uint_as_float(cur.rv[0]);
@@ -312,31 +371,45 @@ __device__ __forceinline__ void process_chunk(DecSmem &sm, SplitState &st, const
   }
   wave_lds_sync();
 
-  // ---- QK operand: head h, slot n: x = q * c_K * 2^sigma_h as 4 fp8 terms ----
-  int sa_q = sa_fixed;
-  u32x8 aq = aq_fixed;
-  if constexpr (kTwoScales) {
-    const f32x4 c0 = *reinterpret_cast<const f32x4 *>(&sm.ck[sb]);
-    const f32x4 c1 = *reinterpret_cast<const f32x4 *>(&sm.ck[sb + 4]);
-    float x[8];
+  // ---- QK operands: head h, slot n: x = q * c_K * 2^sigma_h as 4 fp8 terms ----
+  int sa_q[NQ];
+  u32x8 aq[NQ];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = st.qv[j] * (j < 4 ? c0[j] : c1[j - 4]);
-    sa_q = build_qk_operand(sm, x, lane);
+  for (int hf = 0; hf < NQ; ++hf) {
+    sa_q[hf] = sa_fixed[hf];
+    aq[hf] = aq_fixed[hf];
+  }
+  if constexpr (kTwoScales) {
+#pragma unroll
+    for (int hf = 0; hf < NQ; ++hf) {
+      const f32x4 c0 = *reinterpret_cast<const f32x4 *>(&sm.ck[hf][sb]);
+      const f32x4 c1 = *reinterpret_cast<const f32x4 *>(&sm.ck[hf][sb + 4]);
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = st.qv[hf][j] * (j < 4 ? c0[j] : c1[j - 4]);
+      sa_q[hf] = build_qk_operand(sm.aq[hf], x, lane);
+    }
     wave_lds_sync();
-    aq = read_operand(sm.aq, lane);
+#pragma unroll
+    for (int hf = 0; hf < NQ; ++hf) aq[hf] = read_operand(sm.aq[hf], lane);
   }
 
   // ---- QK^T: 8 token tiles; the four terms of head h land in d[0..3] ----
   float s[8];
   {
-    // all nine products are independent: issue them back to back and sum the
-    // terms afterwards, so the MFMA latency is paid once; the level offset of
-    // head h (the same for every token) is added after the term sum
+    // all products are independent of each other's results except the
+    // halves' accumulation: issue them back to back and sum the terms
+    // afterwards, so the MFMA latency is paid once; the level offset of head
+    // h (the same for every token) is added after the term sum
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     f32x4 d[8];
 #pragma unroll
-    for (int tau = 0; tau < 8; ++tau) d[tau] = mfma_f8f4(aq, code_operand(cur.k[tau]), zero, sa_q);
-    const f32x4 off = level_offset(aq, sa_q);
+    for (int tau = 0; tau < 8; ++tau) {
+      d[tau] = mfma_f8f4(aq[0], code_operand(cur.k[0][tau]), zero, sa_q[0]);
+      if constexpr (NQ == 2) d[tau] = mfma_f8f4(aq[1], code_operand(cur.k[1][tau]), d[tau], sa_q[1]);
+    }
+    f32x4 off = level_offset(aq[0], sa_q[0]);
+    if constexpr (NQ == 2) off += level_offset(aq[1], sa_q[1]);
     const float off_h = (off[0] + off[1]) + (off[2] + off[3]);
 #pragma unroll
     for (int tau = 0; tau < 8; ++tau)
@@ -394,58 +467,82 @@ __device__ __forceinline__ void process_chunk(DecSmem &sm, SplitState &st, const
     // when it moved for some head
     if (__builtin_amdgcn_ballot_w64(al != 1.f)) {
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct) st.acc[ct] *= al;
+      for (int ct = 0; ct < NCT; ++ct) st.acc[ct] *= al;
     }
     const int sa_p = row_scale_byte(sig, lane);
     wave_lds_sync();
 
-    // ---- PV: 8 channel tiles ----
+    // ---- PV: NCT channel tiles ----
     const u32x8 ap = read_operand(sm.ap, lane);
-    f32x4 cv0 = {1.f, 1.f, 1.f, 1.f}, cv1 = cv0;
+    float cvs[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) cvs[ct] = 1.f;
     if constexpr (kTwoScales) {
-      cv0 = *reinterpret_cast<const f32x4 *>(&sm.cv[sb]);
-      cv1 = *reinterpret_cast<const f32x4 *>(&sm.cv[sb + 4]);
+#pragma unroll
+      for (int c4 = 0; c4 < NCT / 4; ++c4) {
+        const f32x4 cv4 = *reinterpret_cast<const f32x4 *>(&sm.cv[cv_base(NCT, n) + 4 * c4]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cvs[4 * c4 + i] = cv4[i];
+      }
     }
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    f32x4 d[8];
+    f32x4 d[NCT];
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) d[ct] = mfma_f8f4(ap, code_operand(cur.v[ct]), zero, sa_p);
+    for (int ct = 0; ct < NCT; ++ct) d[ct] = mfma_f8f4(ap, code_operand(cur.v[ct]), zero, sa_p);
     const f32x4 off = level_offset(ap, sa_p);
     const float off_h = (off[0] + off[1]) + off[2];  // row 4 h + 3 is zero
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) {
+    for (int ct = 0; ct < NCT; ++ct) {
       const float dv = ((d[ct][0] + d[ct][1]) + d[ct][2]) + off_h;
       if constexpr (kTwoScales)
-        st.acc[ct] = fmaf(ct < 4 ? cv0[ct] : cv1[ct - 4], dv, st.acc[ct]);
+        st.acc[ct] = fmaf(cvs[ct], dv, st.acc[ct]);
       else
         st.acc[ct] += dv;
     }
   }
 }
 
-// Last step for one query head, by one wave: lane l holds channels 2 l and
-// 2 l + 1 of the merged numerator (x0, x1) and every lane the denominator L;
-// out = (x / L) H_128 / sqrt(128), or x / L when the rotation is absorbed.
-// Channel bit 0 is the register, bits 1..6 are lane bits 0..5: the first
-// butterfly stage is in registers, the other six exchange lanes.
-template <bool kRotate>
-__device__ __forceinline__ void finalize_head(float x0, float x1, float L, int lane, float *out) {
+// Last step for one query head, by one wave: lane l holds channels CPL l + i
+// of the merged numerator x and every lane the denominator L;
+// out = (x / L) H_DD / sqrt(DD), or x / L when the rotation is absorbed.
+// The channel bits below CPL are the register index, the others lane bits:
+// those butterfly stages are in registers, the rest exchange lanes.
+template <int DD, bool kRotate>
+__device__ __forceinline__ void finalize_head(float (&x)[Dims<DD>::CPL], float L, int lane,
+                                              float *out) {
+  constexpr int CPL = Dims<DD>::CPL;
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  x0 *= inv;
-  x1 *= inv;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) x[i] *= inv;
   if constexpr (kRotate) {
-    float y0 = x0 + x1, y1 = x0 - x1;
+#pragma unroll
+    for (int len = 1; len < CPL; len <<= 1)
+#pragma unroll
+      for (int i = 0; i < CPL; ++i)
+        if ((i & len) == 0) {
+          const float u = x[i], v = x[i + len];
+          x[i] = u + v;
+          x[i + len] = u - v;
+        }
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) {
-      const float p0 = lane_xor(y0, m), p1 = lane_xor(y1, m);
       const bool upper = (lane & m) != 0;
-      y0 = upper ? p0 - y0 : y0 + p0;
-      y1 = upper ? p1 - y1 : y1 + p1;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const float p = lane_xor(x[i], m);
+        x[i] = upper ? p - x[i] : x[i] + p;
+      }
     }
-    x0 = y0 * kInvSqrtD;
-    x1 = y1 * kInvSqrtD;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) x[i] *= inv_sqrt_dd(DD);
   }
-  *reinterpret_cast<f32x2 *>(out + 2 * lane) = f32x2{x0, x1};
+  if constexpr (CPL == 1) {
+    out[lane] = x[0];
+  } else if constexpr (CPL == 2) {
+    *reinterpret_cast<f32x2 *>(out + 2 * lane) = f32x2{x[0], x[1]};
+  } else {
+    *reinterpret_cast<f32x4 *>(out + 4 * lane) = f32x4{x[0], x[1], x[2], x[3]};
+  }
 }
 
 // Accesses to memory shared by the workgroups of one launch, coherent across
@@ -466,14 +563,42 @@ __device__ __forceinline__ f32x2 coherent_load2(const float *p) {
       f32x2, __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT));
 }
+// N consecutive floats (N = 1, 2 or 4; 8-byte aligned for N > 1)
+template <int N>
+__device__ __forceinline__ void coherent_store_n(float *p, const float (&v)[N]) {
+  if constexpr (N == 1) {
+    coherent_store(p, v[0]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; i += 2) coherent_store2(p + i, f32x2{v[i], v[i + 1]});
+  }
+}
+template <int N>
+__device__ __forceinline__ void coherent_load_n(const float *p, float (&v)[N]) {
+  if constexpr (N == 1) {
+    v[0] = coherent_load(p);
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; i += 2) {
+      const f32x2 u = coherent_load2(p + i);
+      v[i] = u[0];
+      v[i + 1] = u[1];
+    }
+  }
+}
 
 // The four waves' results of a workgroup, merged in LDS.
+template <int DD>
 struct MergeSmem {
   float m[kDecWaves][HG];
   float l[kDecWaves][HG];
-  alignas(16) float acc[kDecWaves][HG][D];
+  alignas(16) float acc[kDecWaves][HG][DD];
   int last;
 };
+
+// Waves per SIMD the kernel's registers allow, by head size (the split count
+// targets that many).
+__host__ __device__ constexpr int decode_waves_per_simd(int dd) { return dd == 256 ? 2 : 3; }
 
 // kRotate = false: the query comes rotated (rotation absorbed into the model's
 // weights); kTwoScales = false: column scales taken as 1 (ablation).
@@ -487,14 +612,17 @@ struct MergeSmem {
 // workgroup's partial, and the workgroup that finishes last (a counter per
 // row in the workspace, reset by that workgroup) merges the row's partials
 // and writes the output, so no second launch is needed.
-template <bool kRotate, bool kTwoScales>
-__global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeArgs a) {
-  __shared__ DecSmem sms[kDecWaves];
-  __shared__ MergeSmem mg;
+template <int DD, bool kRotate, bool kTwoScales>
+__global__ __launch_bounds__(64 * kDecWaves, decode_waves_per_simd(DD)) void decode_kernel(
+    DecodeArgs a) {
+  using Dm = Dims<DD>;
+  constexpr int NQ = Dm::NQ, NCT = Dm::NCT, CPL = Dm::CPL;
+  __shared__ DecSmem<DD> sms[kDecWaves];
+  __shared__ MergeSmem<DD> mg;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  DecSmem &sm = sms[wv];
+  DecSmem<DD> &sm = sms[wv];
   const int G = a.q_heads / a.kv_heads;
   const int n_hg = (G + HG - 1) / HG;
   const int wgs = blockIdx.x % a.n_wg, hg = blockIdx.x / a.n_wg;
@@ -511,82 +639,118 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeArgs a) {
   const int64_t qh0 = (int64_t)b * a.q_heads + (int64_t)g * G + h0;
   const int64_t row = bg * n_hg + hg;  // counter index
 
-  // ---- query: lane (slot n, head hl) keeps the channels of its slot,
-  // slot_elem(n, j) = c0 + (n & 1) + 2 j, and rotates them in registers: bits
-  // 1..3 of the channel index are in the lane (j), bits 0, 6, 4 and 5 are lane
-  // bits 0..3 of the 16-lane row that holds the head. Softmax scale, log2(e),
-  // 1/sqrt(128) and the 2 of the half-level code values are folded in. The
-  // query loads go first and the first chunk's loads next, so that waiting for
-  // the query leaves the chunk in flight during the set-up ----
+  // ---- query: lane (slot n, head hl) keeps the channels of its slot in each
+  // 128-channel half hf, 128 hf + slot_elem(n, j) = 128 hf + c0 + (n & 1) + 2 j,
+  // and rotates them in registers: bits 1..3 of the channel index (j) and bit
+  // 7 (hf) are in the lane, bits 0, 6, 4 and 5 are lane bits 0..3 of the
+  // 16-lane row that holds the head (a 64-channel head has no bit 6: the
+  // lanes of its upper slots hold zeros). Softmax scale, log2(e), 1/sqrt(DD)
+  // and the 2 of the half-level code values are folded in. The query loads go
+  // first and the first chunk's loads next, so that waiting for the query
+  // leaves the chunk in flight during the set-up ----
   const int n_l = lane & 15, hl = lane >> 4;
   const int qc0 = slot_elem(n_l, 0) & ~1;  // 16-channel window holding the slot
-  const int64_t qrow = (qh0 + min(hl, nh - 1)) * D + qc0;
-  float qw[16];
-  if (a.q_dtype == KVARN_DT_F32) {
-    const f32x4 *qf = reinterpret_cast<const f32x4 *>(static_cast<const float *>(a.q) + qrow);
+  const bool q_in = qc0 < DD;
+  float qr[NQ][8];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const f32x4 v4 = qf[r];
-      qw[4 * r] = v4[0]; qw[4 * r + 1] = v4[1]; qw[4 * r + 2] = v4[2]; qw[4 * r + 3] = v4[3];
-    }
-  } else {
-    const u32x4 *qb = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.q) + qrow);
+  for (int hf = 0; hf < NQ; ++hf) {
+    const int64_t qrow = (qh0 + min(hl, nh - 1)) * DD + 128 * hf + qc0;
+    float qw[16];
+    if (!q_in) {
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const u32x4 u = qb[r];
+      for (int i = 0; i < 16; ++i) qw[i] = 0.f;
+    } else if (a.q_dtype == KVARN_DT_F32) {
+      const f32x4 *qf = reinterpret_cast<const f32x4 *>(static_cast<const float *>(a.q) + qrow);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qw[8 * r + 2 * e] = bf16_lo(u[e]);
-        qw[8 * r + 2 * e + 1] = bf16_hi(u[e]);
+      for (int r = 0; r < 4; ++r) {
+        const f32x4 v4 = qf[r];
+        qw[4 * r] = v4[0]; qw[4 * r + 1] = v4[1]; qw[4 * r + 2] = v4[2]; qw[4 * r + 3] = v4[3];
+      }
+    } else {
+      const u32x4 *qb = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.q) + qrow);
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const u32x4 u = qb[r];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qw[8 * r + 2 * e] = bf16_lo(u[e]);
+          qw[8 * r + 2 * e + 1] = bf16_hi(u[e]);
+        }
       }
     }
-  }
-  ChunkRegs cur, nxt;
-  if (c0 < c1) load_chunk<kTwoScales>(a, bg, nch, c0, lane, cur);
-  float qr[8];
 #pragma unroll
-  for (int jj = 0; jj < 8; ++jj) qr[jj] = hl < nh ? ((n_l & 1) ? qw[2 * jj + 1] : qw[2 * jj]) : 0.f;
+    for (int jj = 0; jj < 8; ++jj) qr[hf][jj] = hl < nh ? ((n_l & 1) ? qw[2 * jj + 1] : qw[2 * jj]) : 0.f;
+  }
+  ChunkRegs<DD> cur, nxt;
+  if (c0 < c1) load_chunk<DD, kTwoScales>(a, bg, nch, c0, lane, cur);
   if constexpr (kRotate) {
 #pragma unroll
-    for (int len = 1; len < 8; len <<= 1)
+    for (int hf = 0; hf < NQ; ++hf)
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj)
-        if ((jj & len) == 0) {
-          const float u = qr[jj], v = qr[jj + len];
-          qr[jj] = u + v;
-          qr[jj + len] = u - v;
-        }
+      for (int len2 = 1; len2 < 8; len2 <<= 1)
 #pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {
-      const bool upper = (n_l & m) != 0;
+        for (int jj = 0; jj < 8; ++jj)
+          if ((jj & len2) == 0) {
+            const float u = qr[hf][jj], v = qr[hf][jj + len2];
+            qr[hf][jj] = u + v;
+            qr[hf][jj + len2] = u - v;
+          }
+    if constexpr (NQ == 2) {  // channel bit 7
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
-        const float p = lane_xor(qr[jj], m);
-        qr[jj] = upper ? p - qr[jj] : qr[jj] + p;
+        const float u = qr[0][jj], v = qr[1][jj];
+        qr[0][jj] = u + v;
+        qr[1][jj] = u - v;
       }
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+      if (DD == 64 && m == 2) continue;  // channel bit 6
+      const bool upper = (n_l & m) != 0;
+#pragma unroll
+      for (int hf = 0; hf < NQ; ++hf)
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const float p = lane_xor(qr[hf][jj], m);
+          qr[hf][jj] = upper ? p - qr[hf][jj] : qr[hf][jj] + p;
+        }
     }
   }
   for (int idx = lane; idx < 16 * OP_ROW; idx += 64) (&sm.ap[0][0])[idx] = 0u;
-  SplitState st;
+  if constexpr (DD == 64) {  // c_K of the slots past channel 64: never written, read as 0
+    for (int idx = lane; idx < SLOT_ARRAY; idx += 64) sm.ck[0][idx] = 0.f;
+  }
+  SplitState<DD> st;
   {
-    // the unscaled rotation's 1/sqrt(128) applies only when it ran here
-    const float qs = 2.f * a.scale * kLog2e * (kRotate ? kInvSqrtD : 1.f);
+    // the unscaled rotation's 1/sqrt(DD) applies only when it ran here
+    const float qs = 2.f * a.scale * kLog2e * (kRotate ? inv_sqrt_dd(DD) : 1.f);
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) st.qv[jj] = qr[jj] * qs;
+    for (int hf = 0; hf < NQ; ++hf)
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) st.qv[hf][jj] = qr[hf][jj] * qs;
   }
-  // one scale: the QK operand does not change from chunk to chunk
-  u32x8 aq_fixed = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-  int sa_fixed = 127;
+  // one scale: the QK operands do not change from chunk to chunk
+  u32x8 aq_fixed[NQ];
+  int sa_fixed[NQ];
+#pragma unroll
+  for (int hf = 0; hf < NQ; ++hf) {
+    aq_fixed[hf] = u32x8{0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    sa_fixed[hf] = 127;
+  }
   if constexpr (!kTwoScales) {
-    float x[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = st.qv[j];
-    sa_fixed = build_qk_operand(sm, x, lane);
+    for (int hf = 0; hf < NQ; ++hf) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = st.qv[hf][j];
+      sa_fixed[hf] = build_qk_operand(sm.aq[hf], x, lane);
+    }
     wave_lds_sync();
-    aq_fixed = read_operand(sm.aq, lane);
+#pragma unroll
+    for (int hf = 0; hf < NQ; ++hf) aq_fixed[hf] = read_operand(sm.aq[hf], lane);
   }
 #pragma unroll
-  for (int ct = 0; ct < 8; ++ct) st.acc[ct] = 0.f;
+  for (int ct = 0; ct < NCT; ++ct) st.acc[ct] = 0.f;
   st.m_run = -INFINITY;
   st.l_run = 0.f;
 
@@ -596,8 +760,8 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeArgs a) {
   // loads it has just issued: the counter completes in order).
   __builtin_amdgcn_s_waitcnt(kVmcntZero);
   for (int k = c0; k < c1; ++k) {
-    if (k + 1 < c1) load_chunk<kTwoScales>(a, bg, nch, k + 1, lane, nxt);
-    process_chunk<kTwoScales>(sm, st, cur, min(len - k * T, T), lane, aq_fixed, sa_fixed);
+    if (k + 1 < c1) load_chunk<DD, kTwoScales>(a, bg, nch, k + 1, lane, nxt);
+    process_chunk<DD, kTwoScales>(sm, st, cur, min(len - k * T, T), lane, aq_fixed, sa_fixed);
     cur = nxt;
   }
 
@@ -611,12 +775,14 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeArgs a) {
     }
     // 2: the code operand carries c/2
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) mg.acc[wv][h][16 * ct + n] = 2.f * st.acc[ct];
+    for (int ct = 0; ct < NCT; ++ct) mg.acc[wv][h][16 * ct + n] = 2.f * st.acc[ct];
   }
   __syncthreads();
   const int hh = wv;  // the head this wave merges (wave-uniform)
   float M = -INFINITY, L = 0.f;
-  f32x2 x = {0.f, 0.f};
+  float x[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) x[i] = 0.f;
   if (hh < nh) {
 #pragma unroll
     for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, mg.m[w][hh]);
@@ -626,11 +792,12 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeArgs a) {
       // the running maxima are whole numbers (log2 units): exact powers of two
       const float e = mw == -INFINITY ? 0.f : exp2f(mw - M);
       L = fmaf(e, mg.l[w][hh], L);
-      x += e * *reinterpret_cast<const f32x2 *>(&mg.acc[w][hh][2 * lane]);
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) x[i] = fmaf(e, mg.acc[w][hh][CPL * lane + i], x[i]);
     }
   }
   if (a.n_wg == 1) {
-    if (hh < nh) finalize_head<kRotate>(x[0], x[1], L, lane, a.out + (qh0 + hh) * D);
+    if (hh < nh) finalize_head<DD, kRotate>(x, L, lane, a.out + (qh0 + hh) * DD);
     return;
   }
   // The workgroup that finishes its row last merges it. The partials and the
@@ -641,12 +808,12 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeArgs a) {
   // fence would write back and invalidate the whole L2 of the XCD in every
   // workgroup, which costs more than the merge.)
   if (hh < nh) {
-    float *pp = a.partial + ((qh0 + hh) * a.n_wg + wgs) * (2 + D);
+    float *pp = a.partial + ((qh0 + hh) * a.n_wg + wgs) * (2 + DD);
     if (lane == 0) {
       coherent_store(pp, M);
       coherent_store(pp + 1, L);
     }
-    coherent_store2(pp + 2 + 2 * lane, x);
+    coherent_store_n<CPL>(pp + 2 + CPL * lane, x);
   }
   __builtin_amdgcn_s_waitcnt(kVmcntZero);
   __syncthreads();
@@ -658,37 +825,44 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeArgs a) {
   if (hh < nh) {
     // the row's partials in rounds of 8, all loads of a round issued before
     // any is used, merged into a running (M, L, x) by log-sum-exp
-    const float *pp = a.partial + (qh0 + hh) * a.n_wg * (2 + D);
+    const float *pp = a.partial + (qh0 + hh) * a.n_wg * (2 + DD);
     constexpr int R = 8;
     M = -INFINITY;
     L = 0.f;
-    x = f32x2{0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) x[i] = 0.f;
     for (int i0 = 0; i0 < a.n_wg; i0 += R) {
-      float mi[R], li[R];
-      f32x2 xi[R];
+      float mi[R], li[R], xi[R][CPL];
 #pragma unroll
       for (int j = 0; j < R; ++j) {
-        const float *pi = pp + (i0 + j) * (2 + D);
+        const float *pi = pp + (i0 + j) * (2 + DD);
         const bool in = i0 + j < a.n_wg;
         mi[j] = in ? coherent_load(pi) : -INFINITY;
         li[j] = in ? coherent_load(pi + 1) : 0.f;
-        xi[j] = in ? coherent_load2(pi + 2 + 2 * lane) : f32x2{0.f, 0.f};
+        if (in) {
+          coherent_load_n<CPL>(pi + 2 + CPL * lane, xi[j]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < CPL; ++i) xi[j][i] = 0.f;
+        }
       }
       float mn = M;
 #pragma unroll
       for (int j = 0; j < R; ++j) mn = fmaxf(mn, mi[j]);
       const float sc = M == -INFINITY ? 0.f : exp2f(M - mn);
       L *= sc;
-      x *= sc;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) x[i] *= sc;
 #pragma unroll
       for (int j = 0; j < R; ++j) {
         const float e = mi[j] == -INFINITY ? 0.f : exp2f(mi[j] - mn);
         L = fmaf(e, li[j], L);
-        x += e * xi[j];
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) x[i] = fmaf(e, xi[j][i], x[i]);
       }
       M = mn;
     }
-    finalize_head<kRotate>(x[0], x[1], L, lane, a.out + (qh0 + hh) * D);
+    finalize_head<DD, kRotate>(x, L, lane, a.out + (qh0 + hh) * DD);
   }
   if (tid == 0)  // ready for the next call
     __hip_atomic_store(a.counters + row, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -742,37 +916,45 @@ int device_cus() {
 }
 static int device_simds() { return 4 * device_cus(); }
 
-// Workgroups per (sequence, kv-head, head group): about kWavesPerSimd waves
-// per SIMD in one round (four-wave workgroups, one split per wave; the
-// kernel's registers allow three waves per SIMD).
-constexpr int kWavesPerSimd = 3;
-int decode_auto_wgs(int batch, int kv_heads, int q_heads, int capacity) {
+// Workgroups per (sequence, kv-head, head group): about as many waves per
+// SIMD as the kernel's registers allow for the head size, in one round
+// (four-wave workgroups, one split per wave).
+int decode_auto_wgs(int batch, int kv_heads, int q_heads, int capacity, int head_dim) {
   const int max_wg = decode_max_wgs(capacity);
   if (batch <= 0 || kv_heads <= 0 || q_heads <= 0 || max_wg <= 0) return 1;
   const int G = q_heads / kv_heads;
   const int64_t rows = (int64_t)batch * kv_heads * ((G + HG - 1) / HG);
-  const int64_t target = (int64_t)kWavesPerSimd * device_simds() / kDecWaves;
+  const int64_t target = (int64_t)decode_waves_per_simd(head_dim) * device_simds() / kDecWaves;
   int64_t s = (target + rows / 2) / rows;
   if (s > max_wg) s = max_wg;
   if (s < 1) s = 1;
   return (int)s;
 }
 
-hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
+template <int DD>
+static hipError_t launch_decode_dd(const DecodeArgs &a, hipStream_t s) {
   if (a.batch == 0 || a.q_heads == 0) return hipSuccess;
   const int G = a.q_heads / a.kv_heads;
   const int n_hg = (G + HG - 1) / HG;
   const dim3 grid(a.n_wg * n_hg, a.kv_heads, a.batch), block(64 * kDecWaves);
   const bool rot = !(a.flags & KVARN_FLAG_NO_ROTATE), two = !(a.flags & KVARN_FLAG_ONE_SCALE);
   if (rot && two)
-    hipLaunchKernelGGL((decode_kernel<true, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((decode_kernel<DD, true, true>), grid, block, 0, s, a);
   else if (rot)
-    hipLaunchKernelGGL((decode_kernel<true, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((decode_kernel<DD, true, false>), grid, block, 0, s, a);
   else if (two)
-    hipLaunchKernelGGL((decode_kernel<false, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((decode_kernel<DD, false, true>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((decode_kernel<false, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((decode_kernel<DD, false, false>), grid, block, 0, s, a);
   return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
+  switch (a.head_dim) {
+    case 64: return launch_decode_dd<64>(a, s);
+    case 256: return launch_decode_dd<256>(a, s);
+    default: return launch_decode_dd<128>(a, s);
+  }
 }
 
 }  // namespace kvarn

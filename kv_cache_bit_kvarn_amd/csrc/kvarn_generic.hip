@@ -1,8 +1,9 @@
-// Head sizes other than 128 (64 and 256): the quantizer, the one-token append,
-// the decode attention and the per-token error diagnostic for a head_dim D
-// that is a multiple of 64 (rndamp article on KVarN, "How It Works", item 1:
-// the Hadamard transform acts on the channel dimension of whatever head size
-// the model has). The D = 128 calls run the tuned kernels of the other files;
+// Head sizes other than 128 (64 and 256): the quantizer, the one-token append
+// and the per-token error diagnostic for a head_dim D that is a multiple of
+// 64 (rndamp article on KVarN, "How It Works", item 1: the Hadamard transform
+// acts on the channel dimension of whatever head size the model has; the
+// decode attention serves every head size in its own file). The D = 128
+// calls run the tuned kernels of the other files;
 // these kernels compute the same quantities in plain fp32 vector code with a
 // simpler layout:
 //  * a wave holds whole tokens: lane l holds channels l + 64 k (k < D / 64),
@@ -11,11 +12,7 @@
 //    sum over a token's channels is an in-wave butterfly;
 //  * the quantizer's eight waves hold 16 tokens each (token wv + 8 s) and
 //    meet in LDS for the column sums (each wave adds up all D channels in
-//    the same order, so every wave holds identical column scales);
-//  * the decode step computes its scores with one lane per token and its
-//    value sums with one lane per channel, the operands shared through LDS,
-//    and merges splits as the D = 128 kernel does (four waves per workgroup,
-//    the last workgroup of a row merging the row's partials).
+//    the same order, so every wave holds identical column scales).
 // Row and column normalizations: with v_i = 1 / sum_j P_ij / c_j^2 the
 // column step's mean over the T tokens is c_j^2 = (D / T) sum_i P_ij v_i.
 #include "kvarn_diag.h"
@@ -23,7 +20,6 @@
 namespace kvarn {
 namespace {
 
-constexpr float kLog2eG = 1.4426950408889634f;
 constexpr float kTinyG = 1.17549435e-38f;   // smallest normal fp32
 constexpr float kGridG = 1.9999980926513672f;  // 2 (1 - 2^-20), as the D = 128 quantizer
 
@@ -367,257 +363,6 @@ __global__ __launch_bounds__(256) void token_error_generic_kernel(DiagArgs a) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// Decode attention for head size D. One workgroup = four waves = four splits
-// of one (sequence, kv-head, group of up to four query heads), as the D = 128
-// kernel, with the same split ranges and merge.
-constexpr int kGW = KVARN_DECODE_WAVES;
-constexpr int GH = 4;  // query heads per wave
-
-template <int D_>
-struct GenSmem {
-  float qc[kGW][GH][D_];  // per wave: rotated, scaled query times the chunk's c_K
-  float w[kGW][GH][T];    // per wave: p_t r'_V_t of the chunk
-  float mrg_m[kGW][GH], mrg_l[kGW][GH];
-  float mrg_acc[kGW][GH][D_];
-  int last;
-};
-
-__device__ __forceinline__ void store_coh(float *p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_coh(const float *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// out = (x / L) H_D / sqrt(D) over the wave's channels l + 64 k, or x / L
-template <int KD, bool kRotate>
-__device__ __forceinline__ void finalize_generic(float (&x)[KD], float L, int lane, float *out) {
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-#pragma unroll
-  for (int k = 0; k < KD; ++k) x[k] *= inv;
-  if constexpr (kRotate) {
-    fwht_wave<KD>(x, lane);
-#pragma unroll
-    for (int k = 0; k < KD; ++k) x[k] *= inv_sqrt_d(64 * KD);
-  }
-#pragma unroll
-  for (int k = 0; k < KD; ++k) out[lane + 64 * k] = x[k];
-}
-
-template <int D_, bool kRotate, bool kTwoScales>
-__global__ __launch_bounds__(64 * kGW) void decode_generic_kernel(DecodeArgs a) {
-  constexpr int KD = D_ / 64;
-  constexpr int CB = T * D_ / 4;  // code bytes per chunk
-  __shared__ GenSmem<D_> sm;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int G = a.q_heads / a.kv_heads;
-  const int n_hg = (G + GH - 1) / GH;
-  const int wgs = blockIdx.x % a.n_wg, hg = blockIdx.x / a.n_wg;
-  const int g = blockIdx.y, b = blockIdx.z;
-  const int h0 = hg * GH, nh = min(GH, G - h0);
-  const int nch = a.capacity / T;
-  const int len = a.lens[b];
-  const bool valid = len >= 1 && len <= a.capacity;
-  const int used = valid ? (len + T - 1) / T : 0;
-  const int n_split = a.n_wg * kGW, split = wgs * kGW + wv;
-  const int c0 = (int)((int64_t)split * used / n_split);
-  const int c1 = (int)((int64_t)(split + 1) * used / n_split);
-  const int64_t bg = (int64_t)b * a.kv_heads + g;
-  const int64_t qh0 = (int64_t)b * a.q_heads + (int64_t)g * G + h0;
-  const int64_t row = bg * n_hg + hg;
-
-  // rotated query of each head, times softmax scale and log2(e) (scores in
-  // log2 units), channels l + 64 k of the lane
-  const float qscale = a.scale * kLog2eG * (kRotate ? inv_sqrt_d(D_) : 1.f);
-  float qv[GH][KD];
-#pragma unroll
-  for (int h = 0; h < GH; ++h) {
-    const int64_t qo = (qh0 + min(h, nh - 1)) * D_;
-    if (a.q_dtype == KVARN_DT_F32)
-      load_row<KD, true>(a.q, qo, lane, qv[h]);
-    else
-      load_row<KD, false>(a.q, qo, lane, qv[h]);
-    if constexpr (kRotate) fwht_wave<KD>(qv[h], lane);
-#pragma unroll
-    for (int k = 0; k < KD; ++k) qv[h][k] = h < nh ? qv[h][k] * qscale : 0.f;
-  }
-  float acc[GH][KD], m_run[GH], l_run[GH];
-#pragma unroll
-  for (int h = 0; h < GH; ++h) {
-    m_run[h] = -INFINITY;
-    l_run[h] = 0.f;
-#pragma unroll
-    for (int k = 0; k < KD; ++k) acc[h][k] = 0.f;
-  }
-  float (*qc)[D_] = sm.qc[wv];
-  float (*wt)[T] = sm.w[wv];
-  for (int kc = c0; kc < c1; ++kc) {
-    const int64_t chunk = bg * nch + kc;
-    const int nvalid = min(len - kc * T, T);
-    // query times c_K into LDS, and the per-head sums of it (level offset)
-    float qsum[GH];
-#pragma unroll
-    for (int h = 0; h < GH; ++h) {
-      float e = 0.f;
-#pragma unroll
-      for (int k = 0; k < KD; ++k) {
-        const float ck = kTwoScales ? a.k_col[chunk * D_ + lane + 64 * k] : 1.f;
-        const float v = qv[h][k] * ck;
-        qc[h][lane + 64 * k] = v;
-        e += v;
-      }
-      qsum[h] = wsum(e);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // scores of tokens lane and lane + 64: r'_K sum_j qc_j (code_j - 1.5)
-    float s[GH][2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int t = lane + 64 * u;
-      const uint32_t *kr = reinterpret_cast<const uint32_t *>(a.k_codes + chunk * CB + t * (D_ / 4));
-      float dot[GH];
-#pragma unroll
-      for (int h = 0; h < GH; ++h) dot[h] = 0.f;
-      for (int wi = 0; wi < D_ / 16; ++wi) {
-        const uint32_t word = kr[wi];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float cv = (float)((word >> (2 * e)) & 3u);
-#pragma unroll
-          for (int h = 0; h < GH; ++h) dot[h] = fmaf(qc[h][16 * wi + e], cv, dot[h]);
-        }
-      }
-      const float rk = a.k_row[bg * (int64_t)a.capacity + (int64_t)kc * T + t];
-#pragma unroll
-      for (int h = 0; h < GH; ++h) s[h][u] = t < nvalid ? rk * (dot[h] - 1.5f * qsum[h]) : -INFINITY;
-    }
-    // online softmax per head; integer running maximum (log2 units) as the
-    // D = 128 kernel, so that split layouts differ by powers of two only
-    float wsm[GH];
-#pragma unroll
-    for (int h = 0; h < GH; ++h) {
-      const float mc = wmax(fmaxf(s[h][0], s[h][1]));
-      const float mn = fmaxf(m_run[h], ceilf(mc));
-      const float al = m_run[h] == -INFINITY ? 0.f : exp2f(m_run[h] - mn);
-      float ps = 0.f;
-      float wsum_h = 0.f;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int t = lane + 64 * u;
-        const float p = s[h][u] == -INFINITY ? 0.f : exp2f(s[h][u] - mn);
-        ps += p;
-        const float wv_ = p * a.v_row[bg * (int64_t)a.capacity + (int64_t)kc * T + t];
-        wt[h][t] = wv_;
-        wsum_h += wv_;
-      }
-      l_run[h] = l_run[h] * al + wsum(ps);
-      m_run[h] = mn;
-      wsm[h] = wsum(wsum_h);
-#pragma unroll
-      for (int k = 0; k < KD; ++k) acc[h][k] *= al;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // values: channel j = lane + 64 k, c_V_j sum_t w_t (code_tj - 1.5)
-#pragma unroll
-    for (int k = 0; k < KD; ++k) {
-      const int j = lane + 64 * k;
-      const uint32_t *vr = reinterpret_cast<const uint32_t *>(a.v_codes + chunk * CB + j * 32);
-      float dot[GH];
-#pragma unroll
-      for (int h = 0; h < GH; ++h) dot[h] = 0.f;
-      for (int wi = 0; wi < 8; ++wi) {
-        const uint32_t word = vr[wi];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float cv = (float)((word >> (2 * e)) & 3u);
-#pragma unroll
-          for (int h = 0; h < GH; ++h) dot[h] = fmaf(wt[h][16 * wi + e], cv, dot[h]);
-        }
-      }
-      const float cvs = kTwoScales ? a.v_col[chunk * D_ + j] : 1.f;
-#pragma unroll
-      for (int h = 0; h < GH; ++h) acc[h][k] = fmaf(cvs, dot[h] - 1.5f * wsm[h], acc[h][k]);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  }
-
-  // ---- the four waves meet in LDS; wave h then carries head h ----
-  if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < GH; ++h) {
-      sm.mrg_m[wv][h] = m_run[h];
-      sm.mrg_l[wv][h] = l_run[h];
-    }
-  }
-#pragma unroll
-  for (int h = 0; h < GH; ++h)
-#pragma unroll
-    for (int k = 0; k < KD; ++k) sm.mrg_acc[wv][h][lane + 64 * k] = acc[h][k];
-  __syncthreads();
-  const int hh = wv;
-  float M = -INFINITY, L = 0.f, x[KD];
-#pragma unroll
-  for (int k = 0; k < KD; ++k) x[k] = 0.f;
-  if (hh < nh) {
-#pragma unroll
-    for (int u = 0; u < kGW; ++u) M = fmaxf(M, sm.mrg_m[u][hh]);
-#pragma unroll
-    for (int u = 0; u < kGW; ++u) {
-      const float mu = sm.mrg_m[u][hh];
-      const float e = mu == -INFINITY ? 0.f : exp2f(mu - M);
-      L = fmaf(e, sm.mrg_l[u][hh], L);
-#pragma unroll
-      for (int k = 0; k < KD; ++k) x[k] = fmaf(e, sm.mrg_acc[u][hh][lane + 64 * k], x[k]);
-    }
-  }
-  if (a.n_wg == 1) {
-    if (hh < nh) finalize_generic<KD, kRotate>(x, L, lane, a.out + (qh0 + hh) * D_);
-    return;
-  }
-  if (hh < nh) {
-    float *pp = a.partial + ((qh0 + hh) * a.n_wg + wgs) * (2 + D_);
-    if (lane == 0) {
-      store_coh(pp, M);
-      store_coh(pp + 1, L);
-    }
-#pragma unroll
-    for (int k = 0; k < KD; ++k) store_coh(pp + 2 + lane + 64 * k, x[k]);
-  }
-  __builtin_amdgcn_s_waitcnt(kVmcntZero);
-  __syncthreads();
-  if (tid == 0)
-    sm.last = __hip_atomic_fetch_add(a.counters + row, 1, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT) == a.n_wg - 1;
-  __syncthreads();
-  if (!sm.last) return;
-  if (hh < nh) {
-    const float *pp = a.partial + (qh0 + hh) * a.n_wg * (2 + D_);
-    M = -INFINITY;
-    for (int i = 0; i < a.n_wg; ++i) M = fmaxf(M, load_coh(pp + i * (2 + D_)));
-    L = 0.f;
-#pragma unroll
-    for (int k = 0; k < KD; ++k) x[k] = 0.f;
-    for (int i = 0; i < a.n_wg; ++i) {
-      const float *pi = pp + i * (2 + D_);
-      const float mi = load_coh(pi);
-      const float e = mi == -INFINITY ? 0.f : exp2f(mi - M);
-      L = fmaf(e, load_coh(pi + 1), L);
-#pragma unroll
-      for (int k = 0; k < KD; ++k) x[k] = fmaf(e, load_coh(pi + 2 + lane + 64 * k), x[k]);
-    }
-    finalize_generic<KD, kRotate>(x, L, lane, a.out + (qh0 + hh) * D_);
-  }
-  if (tid == 0) __hip_atomic_store(a.counters + row, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 }  // namespace
 
 // ---- launchers -------------------------------------------------------------
@@ -682,28 +427,6 @@ hipError_t launch_token_error_generic(const DiagArgs &a, hipStream_t s) {
   if ((int64_t)a.batch * a.heads * a.tokens == 0) return hipSuccess;
   if (a.head_dim == 64) return launch_token_error_d<64>(a, s);
   if (a.head_dim == 256) return launch_token_error_d<256>(a, s);
-  return hipErrorInvalidValue;
-}
-
-template <int D_>
-static hipError_t launch_decode_d(const DecodeArgs &a, hipStream_t s) {
-  const int G = a.q_heads / a.kv_heads;
-  const int n_hg = (G + GH - 1) / GH;
-  const dim3 grid(a.n_wg * n_hg, a.kv_heads, a.batch), block(64 * kGW);
-  const bool rot = !(a.flags & KVARN_FLAG_NO_ROTATE), two = !(a.flags & KVARN_FLAG_ONE_SCALE);
-#define KVARN_DG(R, W) hipLaunchKernelGGL((decode_generic_kernel<D_, R, W>), grid, block, 0, s, a)
-  if (rot && two) KVARN_DG(true, true);
-  else if (rot) KVARN_DG(true, false);
-  else if (two) KVARN_DG(false, true);
-  else KVARN_DG(false, false);
-#undef KVARN_DG
-  return hipGetLastError();
-}
-
-hipError_t launch_decode_generic(const DecodeArgs &a, hipStream_t s) {
-  if (a.batch == 0 || a.q_heads == 0) return hipSuccess;
-  if (a.head_dim == 64) return launch_decode_d<64>(a, s);
-  if (a.head_dim == 256) return launch_decode_d<256>(a, s);
   return hipErrorInvalidValue;
 }
 

@@ -149,7 +149,7 @@ struct DecodeArgs {
   float scale;
   float *out;
   int32_t *counters;  // one per (sequence, kv-head, head group); zero between calls
-  float *partial;     // [batch][q_heads][n_wg][2 + D]
+  float *partial;     // [batch][q_heads][n_wg][2 + head_dim]
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 int device_cus();  // compute units of the current device, cached per device
@@ -161,7 +161,7 @@ void *noalloc_scratch(hipError_t *err);
 inline int decode_max_wgs(int capacity) {
   return (capacity / T + KVARN_DECODE_WAVES - 1) / KVARN_DECODE_WAVES;
 }
-int decode_auto_wgs(int batch, int kv_heads, int q_heads, int capacity);
+int decode_auto_wgs(int batch, int kv_heads, int q_heads, int capacity, int head_dim);
 // Workspace layout: counters (batch * q_heads int32, rounded up to 256 bytes;
 // q_heads bounds the number of (kv-head, head group) rows), then the partials.
 inline size_t decode_counter_bytes(int32_t batch, int32_t q_heads) {
@@ -172,8 +172,8 @@ inline size_t decode_partial_bytes(int32_t batch, int32_t q_heads, int n_wg, int
 }
 
 // Head sizes other than 128 (kvarn_generic.hip): same arguments, head_dim 64 or 256.
+// (Decode serves every head size in kvarn_decode.hip.)
 hipError_t launch_quantize_generic(const QuantArgs &a, hipStream_t s);
 hipError_t launch_append_generic(const AppendArgs &a, hipStream_t s);
-hipError_t launch_decode_generic(const DecodeArgs &a, hipStream_t s);
 
 }  // namespace kvarn
