@@ -59,9 +59,11 @@ def test_decode_splits_agree(kvarn):
 
 
 def test_decode_many_splits_merge_in_rounds(kvarn, oracle):
-    """More than 32 splits: the merge takes the partials in rounds of 32 with
-    a running maximum. Every split count agrees with one split, and with the
-    oracle, over a cache of 80 chunks with a ragged last chunk."""
+    """Many workgroups per row: the last one merges the row's partials in
+    rounds of 8 with a running maximum (n_split 33, 64, 80: 9, 16 and 20
+    workgroups, two and three rounds). Every split count agrees with one
+    split, and with the oracle, over a cache of 80 chunks with a ragged last
+    chunk."""
     cap = 80 * 128
     kc, vc, hk, hv = _random_caches(kvarn, 2, 1, cap, seed=5)
     q = kvgen.queries(14, 0, 2, 4, dtype=torch.bfloat16)

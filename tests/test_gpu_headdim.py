@@ -133,6 +133,8 @@ def _oracle_decode(oracle, q, hk, hv, lens, D, ones_c=False):
     (1, 2, 8, 256, [200], 0),
     (2, 3, 3, 640, [640, 255], 1),
     (2, 2, 4, 2560, [2560, 700], 20),  # five workgroups per row: the last one merges
+    (1, 4, 2, 1280, [1153], 0),
+    (2, 2, 4, 4224, [4097, 3000], 48),  # twelve workgroups per row: two merge rounds
 ])
 def test_decode_headdim(kvarn, oracle, D, B, Hkv, G, cap, lens, n_split):
     kc, vc, hk, hv = _caches(kvarn, B, Hkv, cap, D, seed=97 + B + G)
@@ -142,6 +144,26 @@ def test_decode_headdim(kvarn, oracle, D, B, Hkv, G, cap, lens, n_split):
     torch.cuda.synchronize()
     err = rel_l2(out.cpu().numpy(), _oracle_decode(oracle, q, hk, hv, lens, D))
     log(f"[test] decode D={D} B={B} Hkv={Hkv} G={G} cap={cap} n_split={n_split}: rel L2 {err:.3e}")
+    assert err <= ATTN_RL2
+
+
+@pytest.mark.parametrize("D", DIMS)
+def test_decode_headdim_splits_agree(kvarn, oracle, D):
+    """One workgroup per row and 3, 10 and 20 (the last workgroup merging the
+    row's partials in one, two and three rounds of 8) agree with each other
+    up to fp32 reassociation, and with the oracle, over 80 chunks with a
+    ragged last chunk."""
+    cap = 80 * 128
+    kc, vc, hk, hv = _caches(kvarn, 2, 1, cap, D, seed=123)
+    q = kvgen.queries(124, 0, 2, 4, dtype=torch.bfloat16, head_dim=D)
+    lens = [cap, cap - 77]
+    L = torch.tensor(lens, dtype=torch.int32).cuda()
+    outs = [kvarn.decode_attn(q.cuda(), kc, vc, L, n_split=n) for n in (1, 12, 40, 80)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert rel_l2(o.cpu().numpy(), outs[0].cpu().numpy()) < 1e-5
+    err = rel_l2(outs[3].cpu().numpy(), _oracle_decode(oracle, q, hk, hv, lens, D))
+    log(f"[test] decode D={D} split counts agree; 20 workgroups per row: rel L2 {err:.3e}")
     assert err <= ATTN_RL2
 
 
