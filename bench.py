@@ -775,8 +775,8 @@ def next_rows_workload(kv, kvgen, torch, args, dev, stream):
       steps with the plain append; the difference over the two chunk closes is
       the cost of re-quantizing a full chunk of 256 (sequence, kv-head) blocks.
     - head sizes 64 and 256 at the Qwen3-4B layer shape (8 sequences,
-      8 kv-heads, 32 query heads, 32768 tokens; quantize runs the generic
-      kernels, decode the matrix-core kernel every head size shares): quantize of bf16
+      8 kv-heads, 32 query heads, 32768 tokens; quantize and decode run the
+      kernels every head size shares): quantize of bf16
       K over 4 layers' inputs and decode over 4 layers' caches, each cycled so
       that nothing is served from the memory-side cache; HIP events, 12 launches
       after a warm one, median of 3 rounds."""
@@ -853,8 +853,7 @@ def next_rows_workload(kv, kvgen, torch, args, dev, stream):
             "config": {"batch": B, "kv_heads": H, "q_heads": Hq, "tokens": T, "head_dim": dh},
             "quantize_us_per_launch": round(qm, 2), "quantize": hbm_entry(qbytes, qm),
             "decode_us_per_launch": round(dm, 2), "decode": hbm_entry(dbytes, dm),
-            "note": "quantize: generic kernel (a correctness path, not tuned); "
-                    "decode: the matrix-core kernel shared by every head size"}
+            "note": "quantize and decode: the matrix-core kernels shared by every head size"}
         del xs, qcs, caches, q, out, ws
         torch.cuda.empty_cache()
     return res

@@ -149,8 +149,7 @@ int kvarn_quantize_ex(const void *x, int32_t dtype, int64_t stride_b, int64_t st
   a.col_scale = dst->col_scale;
   a.pos = nullptr;
   a.head_dim = cache_dim(dst);
-  return from_hip(a.head_dim == D ? launch_quantize(a, static_cast<hipStream_t>(stream))
-                                  : launch_quantize_generic(a, static_cast<hipStream_t>(stream)));
+  return from_hip(launch_quantize(a, static_cast<hipStream_t>(stream)));
 }
 
 int kvarn_quantize(const void *x, int32_t dtype, int64_t stride_b, int64_t stride_h,
@@ -245,7 +244,7 @@ int kvarn_append_rebalance(const void *x, int32_t dtype, const int32_t *position
   a.row_scale = dst->row_scale;
   a.col_scale = dst->col_scale;
   a.pos = positions;
-  return from_hip(a.head_dim == D ? launch_quantize(a, s) : launch_quantize_generic(a, s));
+  return from_hip(launch_quantize(a, s));
 }
 
 int kvarn_token_error(const void *x, int32_t dtype, int64_t stride_b, int64_t stride_h,

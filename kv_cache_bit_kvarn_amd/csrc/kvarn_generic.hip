@@ -1,27 +1,20 @@
-// Head sizes other than 128 (64 and 256): the quantizer, the one-token append
-// and the per-token error diagnostic for a head_dim D that is a multiple of
-// 64 (rndamp article on KVarN, "How It Works", item 1: the Hadamard transform
+// Head sizes other than 128 (64 and 256): the one-token append and the
+// per-token error diagnostic for a head_dim D that is a multiple of 64
+// (rndamp article on KVarN, "How It Works", item 1: the Hadamard transform
 // acts on the channel dimension of whatever head size the model has; the
-// decode attention serves every head size in its own file). The D = 128
-// calls run the tuned kernels of the other files;
-// these kernels compute the same quantities in plain fp32 vector code with a
-// simpler layout:
-//  * a wave holds whole tokens: lane l holds channels l + 64 k (k < D / 64),
-//    so the rotation of a token is an in-wave fast Walsh-Hadamard transform
-//    (channel bits 6 and up inside the lane, bits 0..5 across lanes), and a
-//    sum over a token's channels is an in-wave butterfly;
-//  * the quantizer's eight waves hold 16 tokens each (token wv + 8 s) and
-//    meet in LDS for the column sums (each wave adds up all D channels in
-//    the same order, so every wave holds identical column scales).
-// Row and column normalizations: with v_i = 1 / sum_j P_ij / c_j^2 the
-// column step's mean over the T tokens is c_j^2 = (D / T) sum_i P_ij v_i.
+// block quantizer and the decode attention serve every head size in their
+// own files, and the D = 128 append and diagnostic run the tuned kernels of
+// the other files). These kernels compute the same quantities in plain fp32
+// vector code with a simpler layout: a wave holds whole tokens, lane l
+// channels l + 64 k (k < D / 64), so the rotation of a token is an in-wave
+// fast Walsh-Hadamard transform (channel bits 6 and up inside the lane, bits
+// 0..5 across lanes), and a sum over a token's channels is an in-wave
+// butterfly.
 #include "kvarn_diag.h"
 
 namespace kvarn {
 namespace {
 
-constexpr float kTinyG = 1.17549435e-38f;   // smallest normal fp32
-constexpr float kGridG = 1.9999980926513672f;  // 2 (1 - 2^-20), as the D = 128 quantizer
 
 // 1/sqrt(D) for D a power of four (64, 256): an exact power of two
 __host__ __device__ constexpr float inv_sqrt_d(int d) {
@@ -73,153 +66,6 @@ __device__ __forceinline__ void load_row(const void *x, int64_t off, int lane, f
       v[k] = static_cast<const float *>(x)[off + lane + 64 * k];
     else
       v[k] = __uint_as_float((uint32_t) static_cast<const uint16_t *>(x)[off + lane + 64 * k] << 16);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Block quantizer for head size D (same steps and readings as the D = 128
-// kernel: rotation, `iters` sweeps of a row step then a column step from
-// c = 1, per-token range step r' = max_j |y_j| / c_j / 2, codes
-// floor(u + 2) on the 4-level grid).
-template <int D_, bool kF32, bool kRotate, bool kPositions>
-__global__ __launch_bounds__(512) void quantize_generic_kernel(QuantArgs a) {
-  constexpr int KD = D_ / 64, NW = 8, TW = T / NW;
-  __shared__ float cpart[2][NW][D_];
-  __shared__ uint32_t codes[T][D_ / 4];  // one byte per code, then packed
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t nch = a.capacity / T;
-  // the unscaled rotation's 1/sqrt(D) and the range step's 1/2
-  const float range_factor = kRotate ? 0.5f * inv_sqrt_d(D_) : 0.5f;
-  for (uint32_t blk = blockIdx.x; blk < a.nblocks; blk += gridDim.x) {
-    const uint32_t bh = fdiv(blk, a.div_chunks);
-    const uint32_t kc = blk - bh * (uint32_t)a.chunks;
-    const uint32_t b = fdiv(bh, a.div_heads), h = bh - b * (uint32_t)a.heads;
-    int chunk = a.chunk0 + (int)kc;
-    if constexpr (kPositions) {
-      const int pos = a.pos[b];
-      if (pos < 0 || pos >= a.capacity || pos % T != T - 1) continue;  // workgroup-uniform
-      chunk = pos / T;
-    }
-    const int64_t xb = (int64_t)b * a.sb + (int64_t)h * a.sh + (int64_t)kc * T * a.st;
-    float y[TW][KD], p[TW][KD];
-#pragma unroll
-    for (int s = 0; s < TW; ++s) {
-      load_row<KD, kF32>(a.x, xb + (int64_t)(wv + NW * s) * a.st, lane, y[s]);
-      if constexpr (kRotate) fwht_wave<KD>(y[s], lane);
-#pragma unroll
-      for (int k = 0; k < KD; ++k) p[s][k] = y[s][k] * y[s][k];
-    }
-    float cm[KD], w[KD];
-#pragma unroll
-    for (int k = 0; k < KD; ++k) {
-      cm[k] = 1.f;
-      w[k] = 1.f;
-    }
-    if (a.iters > 0) {
-      float v[TW];
-#pragma unroll
-      for (int s = 0; s < TW; ++s) {  // first row step, c = 1
-        float e = 0.f;
-#pragma unroll
-        for (int k = 0; k < KD; ++k) e += p[s][k];
-        v[s] = __builtin_amdgcn_rcpf(fmaxf(wsum(e), kTinyG));
-      }
-      for (int it = 0;; ++it) {
-        // column step: c_j^2 = (D / T) sum_i P_ij v_i; the eight waves' sums
-        // over their tokens meet in LDS (two buffers alternate by step, so
-        // one barrier per step orders both reuse and reads)
-        float (*cp)[D_] = cpart[it & 1];
-#pragma unroll
-        for (int k = 0; k < KD; ++k) {
-          float e = 0.f;
-#pragma unroll
-          for (int s = 0; s < TW; ++s) e = fmaf(p[s][k], v[s], e);
-          cp[wv][lane + 64 * k] = e;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < KD; ++k) {
-          float e = 0.f;
-#pragma unroll
-          for (int u = 0; u < NW; ++u) e += cp[u][lane + 64 * k];
-          cm[k] = e * ((float)D_ / (float)T);
-        }
-        if (it + 1 == a.iters) break;
-        // row step: v_i = 1 / sum_j P_ij / c_j^2
-#pragma unroll
-        for (int k = 0; k < KD; ++k) w[k] = __builtin_amdgcn_rcpf(fmaxf(cm[k], kTinyG));
-#pragma unroll
-        for (int s = 0; s < TW; ++s) {
-          float e = 0.f;
-#pragma unroll
-          for (int k = 0; k < KD; ++k) e = fmaf(p[s][k], w[k], e);
-          v[s] = __builtin_amdgcn_rcpf(fmaxf(wsum(e), kTinyG));
-        }
-      }
-      // c, and 1/c for the range step (a zero column keeps c = 1)
-#pragma unroll
-      for (int k = 0; k < KD; ++k) {
-        const bool pos_c = cm[k] > 0.f;
-        const float ic = pos_c ? __builtin_amdgcn_rsqf(cm[k]) : 1.f;
-        w[k] = ic;
-        cm[k] = pos_c ? cm[k] * ic : 1.f;
-      }
-    }
-    float *col = a.col_scale + ((int64_t)bh * nch + chunk) * D_;
-    if (wv == 0) {
-#pragma unroll
-      for (int k = 0; k < KD; ++k) col[lane + 64 * k] = cm[k];
-    }
-    // range step and codes: u = y / (r' c), code = floor(u + 2) through
-    // rounding of u (1 - 2^-20) + 1.5, as the D = 128 kernel decides it
-    uint8_t *cb8 = reinterpret_cast<uint8_t *>(&codes[0][0]);
-#pragma unroll
-    for (int s = 0; s < TW; ++s) {
-      float mx = 0.f;
-#pragma unroll
-      for (int k = 0; k < KD; ++k) {
-        y[s][k] *= w[k];
-        mx = fmaxf(mx, fabsf(y[s][k]));
-      }
-      mx = wmax(mx);
-      const int ti = wv + NW * s;
-      if (lane == 0) a.row_scale[(int64_t)bh * a.capacity + (int64_t)chunk * T + ti] = mx * range_factor;
-      const float q = mx > 0.f ? kGridG * __builtin_amdgcn_rcpf(mx) : 0.f;
-#pragma unroll
-      for (int k = 0; k < KD; ++k)
-        cb8[ti * D_ + lane + 64 * k] =
-            (uint8_t)__builtin_amdgcn_cvt_pk_u8_f32(fmaf(y[s][k], q, 1.5f), 0, 0u);
-    }
-    __syncthreads();
-    // pack: 32 D bytes per block, one 32-bit word per thread and round
-    uint32_t *dst = reinterpret_cast<uint32_t *>(a.codes + ((int64_t)bh * nch + chunk) * (T * D_ / 4));
-    for (int wi = tid; wi < T * D_ / 16; wi += 512) {
-      uint32_t word = 0;
-      if (a.kind == KVARN_K) {
-        // token-major: token t owns D/4 bytes; byte j/4 holds channels j..j+3
-        const int t = wi / (D_ / 16), jw = wi % (D_ / 16);  // bytes 4 jw .. of token t
-#pragma unroll
-        for (int by = 0; by < 4; ++by) {
-          const uint32_t c4 = codes[t][4 * jw + by];  // codes of channels 16 jw + 4 by + [0, 4)
-          const uint32_t packed = (c4 & 3u) | ((c4 >> 6) & 0xCu) | ((c4 >> 12) & 0x30u) |
-                                  ((c4 >> 18) & 0xC0u);
-          word |= packed << (8 * by);
-        }
-      } else {
-        // channel-major: channel j owns 32 bytes; byte t/4 holds tokens t..t+3
-        const int j = wi / 8, tw = wi % 8;  // bytes 4 tw .. of channel j: tokens 16 tw ..
-#pragma unroll
-        for (int by = 0; by < 4; ++by) {
-          uint32_t packed = 0;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) packed |= (uint32_t)cb8[(16 * tw + 4 * by + r) * D_ + j] << (2 * r);
-          word |= packed << (8 * by);
-        }
-      }
-      dst[wi] = word;
-    }
-    __syncthreads();  // the code area is rewritten by the next block
   }
 }
 
@@ -366,31 +212,6 @@ __global__ __launch_bounds__(256) void token_error_generic_kernel(DiagArgs a) {
 }  // namespace
 
 // ---- launchers -------------------------------------------------------------
-
-template <int D_>
-static hipError_t launch_quantize_d(const QuantArgs &a, hipStream_t s) {
-  const uint32_t resident = (uint32_t)device_cus();  // one 512-thread workgroup per CU
-  const uint32_t blocks = a.nblocks < resident ? a.nblocks : resident;
-  const bool rot = !(a.flags & KVARN_FLAG_NO_ROTATE), f32 = a.dtype == KVARN_DT_F32;
-#define KVARN_QG(F, R, P) \
-  hipLaunchKernelGGL((quantize_generic_kernel<D_, F, R, P>), dim3(blocks), dim3(512), 0, s, a)
-  if (a.pos) {
-    if (f32) { if (rot) KVARN_QG(true, true, true); else KVARN_QG(true, false, true); }
-    else { if (rot) KVARN_QG(false, true, true); else KVARN_QG(false, false, true); }
-  } else {
-    if (f32) { if (rot) KVARN_QG(true, true, false); else KVARN_QG(true, false, false); }
-    else { if (rot) KVARN_QG(false, true, false); else KVARN_QG(false, false, false); }
-  }
-#undef KVARN_QG
-  return hipGetLastError();
-}
-
-hipError_t launch_quantize_generic(const QuantArgs &a, hipStream_t s) {
-  if (a.nblocks == 0) return hipSuccess;
-  if (a.head_dim == 64) return launch_quantize_d<64>(a, s);
-  if (a.head_dim == 256) return launch_quantize_d<256>(a, s);
-  return hipErrorInvalidValue;
-}
 
 template <int D_>
 static hipError_t launch_append_d(const AppendArgs &a, hipStream_t s) {

@@ -109,7 +109,7 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
 struct QuantArgs {
   const void *x;
   int dtype;
-  int head_dim;         // channels per head (128: the tuned kernel; 64, 256: generic)
+  int head_dim;         // channels per head: 64, 128 or 256
   int64_t sb, sh, st;
   int batch, heads, chunks, chunk0, iters, capacity, kind;
   uint32_t flags;       // KVARN_FLAG_NO_ROTATE
@@ -172,8 +172,7 @@ inline size_t decode_partial_bytes(int32_t batch, int32_t q_heads, int n_wg, int
 }
 
 // Head sizes other than 128 (kvarn_generic.hip): same arguments, head_dim 64 or 256.
-// (Decode serves every head size in kvarn_decode.hip.)
-hipError_t launch_quantize_generic(const QuantArgs &a, hipStream_t s);
+// (The block quantizer and decode serve every head size in their own files.)
 hipError_t launch_append_generic(const AppendArgs &a, hipStream_t s);
 
 }  // namespace kvarn

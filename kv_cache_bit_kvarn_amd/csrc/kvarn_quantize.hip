@@ -1,51 +1,55 @@
 // Block quantizer of the KVarN method on gfx950.
 //
-// One workgroup (512 threads, 8 wave64) quantizes one 128-token x 128-channel
-// block of K or V (one layer, sequence, kv-head, chunk) at a time and walks
-// the blocks of the launch persistently (stride = grid), loading the next
-// block's bf16 input into registers while the current one is coded. Wave w
-// owns tokens [16 w, 16 w + 16).
-//   1. load: lane (m = lane % 16, g = lane / 16) reads four 16-byte pieces of
+// One workgroup (512 threads, 8 wave64) quantizes one 128-token x D-channel
+// block of K or V (one layer, sequence, kv-head, chunk; D = 64, 128 or 256)
+// at a time and walks the blocks of the launch persistently (stride = grid),
+// loading the next block's bf16 input into registers while the current one
+// is coded. Wave w owns tokens [16 w, 16 w + 16). NT = D / 16 is the number
+// of 16-channel output tiles, KK = D / 32 the number of 32-channel input
+// pieces.
+//   1. load: lane (m = lane % 16, g = lane / 16) reads KK 16-byte pieces of
 //      token 16 w + m (channels 32 kk + 8 g + [0, 8)), so one load instruction
 //      covers 64 contiguous bytes of each of 16 rows; the pieces are the A
 //      operands of the MFMAs;
 //   2. Hadamard rotation along channels (rndamp article on KVarN, "How It
 //      Works", item 1) as a dense product on the matrix cores:
-//      y = x H_128 with v_mfma_f32_16x16x32_bf16, 32 MFMAs per wave.
-//      Sylvester's H_128 has entry (-1)^popcount(i & j); split over the tile
+//      y = x H_D with v_mfma_f32_16x16x32_bf16, KK x NT MFMAs per wave.
+//      Sylvester's H_D has entry (-1)^popcount(i & j); split over the tile
 //      indices, each 32 x 16 tile (kk, nt) of it is a sign
 //      (-1)^popcount(kk & (nt/2)) times one of two lane-constant operands
-//      (nt % 2), the sign going onto the input piece. The result lands token
-//      by token: lane (n, g) holds tokens 16 w + 4 g + r (r < 4) of channels
-//      16 nt + n (nt < 8). bf16 inputs and +-1 are exact and the products
-//      accumulate in fp32; fp32 input is split exactly into three bf16 terms
-//      (three MFMAs per product). With the rotation absorbed into the
-//      weights, the MFMAs run on identity tiles (one per output tile), which
-//      copies x exactly;
+//      (nt % 2), whatever D is. The result lands token by token: lane (n, g)
+//      holds tokens 16 w + 4 g + r (r < 4) of channels 16 nt + n (nt < NT).
+//      bf16 inputs and +-1 are exact and the products accumulate in fp32;
+//      fp32 input is split exactly into three bf16 terms (three MFMAs per
+//      product). With the rotation absorbed into the weights, the MFMAs run
+//      on identity tiles (one per output tile), which copies x exactly;
 //   3. dual-scaling normalization ("How It Works", item 2; abstract: both
 //      axes of K and V): the squares P = y^2 stay in registers next to y.
-//      Row step: each lane weighs its 8 channels of each of its 4 tokens by
-//      1/c^2 (8 registers) and the 16 lanes of a row combine their sums
-//      (two lane-pair exchanges that halve the values, then two rotations),
-//      with no LDS and no barrier. Column step: each lane weighs its 4 tokens
-//      of each of its 8 channels by 1/r^2 and writes the 8 partial sums to
-//      LDS unreduced; after a barrier wave w adds up channels 16 w + [0, 16)
-//      only (lane l: channel 16 w + l / 4, 8 of its 32 partials, the quad's
-//      four lanes meeting by DPP adds), writes 1/c^2 to a shared 128-entry
-//      array and, after a second barrier, every lane reads the 8 values of
-//      its channels. (Each wave adding up all 128 channels itself would need
-//      one barrier less but three times the VALU instructions.)
+//      Row step: each lane weighs its NT channels of each of its 4 tokens by
+//      1/c^2 and the 16 lanes of a row combine their sums (two lane-pair
+//      exchanges that halve the values, then two rotations), with no LDS and
+//      no barrier. Column step: each lane weighs its 4 tokens of each of its
+//      NT channels by 1/r^2 and writes the NT partial sums to LDS unreduced;
+//      after a barrier wave w adds up channels (D/8) w + [0, D/8) only
+//      (512/D lanes per channel, each taking D/16 of its 32 partials, the
+//      lanes meeting by DPP adds), writes 1/c^2 to a shared D-entry array
+//      and, after a second barrier, every lane reads the NT values of its
+//      channels. (Each wave adding up all channels itself would need one
+//      barrier less but three times the VALU instructions.)
 //   4. per-token range step and 2-bit codes (v_cvt_pk_u8_f32): K codes of
 //      four adjacent channels (four adjacent lanes) merge by a shift and an
 //      OR across the quad, pass through a small per-wave LDS area and leave
-//      as 8 contiguous bytes per lane (a wave writes its 16 token rows as
-//      one 512-byte span); V codes of a lane's 4 tokens form a byte in the
+//      as D/16 contiguous bytes per lane (a wave writes its 16 token rows as
+//      one 4D-byte span); V codes of a lane's 4 tokens form a byte in the
 //      lane (shifts inside the bytes of words that each hold one token of
-//      four channel tiles), and a 4 x 4 byte transpose across the wave's rows
-//      (two permlane swaps) gives each lane two whole 4-byte words of channel
-//      rows.
-// The rotation is applied without its 1/sqrt(128) factor; that factor leaves
+//      four channel tiles), and 4 x 4 byte transposes across the wave's rows
+//      (two permlane swaps per pair of words) give each lane whole 4-byte
+//      words of channel rows.
+// The rotation is applied without its 1/sqrt(D) factor; that factor leaves
 // the column scales and codes unchanged and is folded into the row scale.
+// With D != 128 the row step's mean over D channels and the column step's
+// mean over 128 tokens no longer cancel: the column step carries D/128 (an
+// exact power of two here).
 //
 // Code decision: the oracle takes code = floor(u + 2), u = y/(r' c) in [-2, 2].
 // Here t = u * (1 - 2^-20) + 1.5 is rounded to nearest by v_cvt_pk_u8_f32;
@@ -62,7 +66,6 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-constexpr int CPT = 32;                        // values per lane: 4 tokens x 8 channels
 constexpr float kGrid = 1.9999980926513672f;  // 2 (1 - 2^-20)
 constexpr float kTiny = 1.17549435e-38f;       // smallest normal fp32
 // Global stores each wave issues per block after it prefetches the block
@@ -79,41 +82,65 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // LDS. On gfx950 a ds_write_b32 is served one half-wave per pass with the
 // dword address taken modulo 32 as its bank; a ds_read_b32 pair
 // (ds_read2st64) of consecutive lanes reads consecutive dwords. The areas
-// below are laid out for that model:
+// below are laid out for that model (for D = 128; the other head sizes use
+// the same strides):
 //  * cpart: the column step's partial sums, cp[nt] of lane l of wave u at
 //    cpart[CP_PLANE nt + CP_WAVE u + l]. A wave's write of one nt covers 64
-//    consecutive words; reading lane l of wave w takes plane w, channel
-//    16 w + l / 4 of waves 2 (l % 4) + s (s < 2) and rows r, at
-//    CP_PLANE w + CP_WAVE (2 (l % 4) + s) + 16 r + l / 4, and the 72-word
-//    wave stride puts the four lanes of a quad 144 words (16 banks) apart, so
-//    neither side has bank conflicts;
+//    consecutive words. Channel 16 nt + n has 32 partials (waves u, rows r)
+//    at CP_PLANE nt + CP_WAVE u + 16 r + n; wave w adds up channels
+//    (D/8) w + l / LPC (LPC = 512/D lanes each), lane l taking partials
+//    (l % LPC) 32/LPC + [0, 32/LPC) in (u, r) order. For D = 128 that is
+//    plane w, waves 2 (l % 4) + s (s < 2), and the 72-word wave stride puts
+//    the four lanes of a quad 144 words (16 banks) apart, so neither side
+//    has bank conflicts;
 //  * ctot: the per-channel result of a column step (1/c^2, and 1/c after the
-//    last one), written by the wave that reduced the channel and read by
+//    last one), written by the lanes that reduced the channel and read by
 //    every lane for channels 16 nt + n (the four lane rows of a wave read the
 //    same words);
-//  * kst[wave]: K code staging, rows of KST_ROW words per group of 4 tokens
-//    (word (token r, half k, quad q) at KST_ROW g + 8 r + 4 k + q; the
-//    36-word rows put the two 16-lane rows of a half-wave on disjoint
-//    banks);
+//  * kst[wave]: K code staging, rows of KST_ROW = 4 NT + 4 words per group
+//    of 4 tokens (word (token r, word k, quad q) at KST_ROW g + NT r + 4 k +
+//    q; for D = 128 the 36-word rows put the two 16-lane rows of a half-wave
+//    on disjoint banks);
 //  * vst[buffer]: V code staging, word (channel j, wave w) at VST_ROW j + w
 //    (9-word rows: the 32 channels of a half-wave's write fall on distinct
 //    banks); two buffers alternated by V block, so that one barrier per
 //    block orders the writes before the reads and the reads before the
 //    buffer's next writes.
-constexpr int KST_ROW = 36;
 constexpr int VST_ROW = 9;
 constexpr int CP_WAVE = 72;
 constexpr int CP_PLANE = kWaves * CP_WAVE;
+
+// Sizes of the kernel for head size DQ.
+template <int DQ>
+struct QDims {
+  static_assert(DQ == 64 || DQ == 128 || DQ == 256, "head size");
+  static constexpr int NT = DQ / 16;        // 16-channel output tiles
+  static constexpr int KK = DQ / 32;        // 32-channel input pieces (MFMA steps)
+  static constexpr int CPT = 4 * NT;        // values per lane: 4 tokens x NT channels
+  static constexpr int LPC = 512 / DQ;      // lanes per channel in the column-step sum
+  static constexpr int PPL = 32 / LPC;      // partial sums each of them adds
+  static constexpr int KST_ROW = 4 * NT + 4;  // K staging words per group of 4 tokens
+  static constexpr int CHUNK_CODE_BYTES = T * DQ / 4;
+};
+// Waves per SIMD the registers allow: two workgroups per CU for 64 and 128
+// channels, one for 256 (y and P alone take 128 registers there).
+__host__ __device__ constexpr int quant_waves_per_simd(int dq) { return dq == 256 ? 2 : 4; }
+// 1/sqrt(DQ)/2: the unscaled rotation's factor and the range step's 1/2
+__host__ __device__ constexpr float range_from_unscaled(int dq) {
+  return dq == 64 ? 0.0625f : dq == 256 ? 0.03125f : kRangeFromUnscaled;
+}
+
+template <int DQ>
 struct QuantSmem {
-  alignas(16) float cpart[8 * CP_PLANE];
-  alignas(16) float ctot[D];
-  alignas(16) uint32_t kst[kWaves][4 * KST_ROW];
-  alignas(16) uint32_t vst[2][D * VST_ROW];
+  alignas(16) float cpart[QDims<DQ>::NT * CP_PLANE];
+  alignas(16) float ctot[DQ];
+  alignas(16) uint32_t kst[kWaves][4 * QDims<DQ>::KST_ROW];
+  alignas(16) uint32_t vst[2][DQ * VST_ROW];
   alignas(16) u32x4 hop[4][64];  // rotation operands of each lane (2, 3: negated)
   // bf16 input two blocks ahead, streamed by the wave straight into its own
   // slice (piece kk of lane l at xin[wave][kk][l], the order the direct
   // global-to-LDS load writes in)
-  alignas(16) u32x4 xin[kWaves][4][64];
+  alignas(16) u32x4 xin[kWaves][QDims<DQ>::KK][64];
 };
 
 __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
@@ -221,21 +248,22 @@ __device__ __forceinline__ u32x4 identity_operand(int lane, int p) {
 }
 
 // acc[nt] += x (input channels 32 kk + [0, 32) of the wave's 16 tokens) times
-// tile (kk, nt) of the rotation. A Hadamard tile with a negative sign takes
-// the negated operand hp[2 + nt % 2] (kept in LDS next to the positive ones,
-// so that no sign flips cost vector instructions); the identity has one tile
-// per output tile, at kk = nt / 2.
-template <bool kRotate, int KK>
-__device__ __forceinline__ void rotate_step(f32x4 (&acc)[8], const u32x4 &x, const u32x4 (&hp)[4]) {
+// tile (kk, nt) of the rotation (kk a constant after unrolling). A Hadamard
+// tile with a negative sign takes the negated operand hp[2 + nt % 2] (kept in
+// LDS next to the positive ones, so that no sign flips cost vector
+// instructions); the identity has one tile per output tile, at kk = nt / 2.
+template <bool kRotate, int NT>
+__device__ __forceinline__ void rotate_step(f32x4 (&acc)[NT], const u32x4 &x, const u32x4 (&hp)[4],
+                                            int kk) {
   if constexpr (kRotate) {
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const bool neg = __builtin_popcount((nt >> 1) & KK) & 1;
+    for (int nt = 0; nt < NT; ++nt) {
+      const bool neg = __builtin_popcount((nt >> 1) & kk) & 1;
       acc[nt] = mfma_bf16(x, hp[(neg ? 2 : 0) + (nt & 1)], acc[nt]);
     }
   } else {
-    acc[2 * KK] = mfma_bf16(x, hp[0], acc[2 * KK]);
-    acc[2 * KK + 1] = mfma_bf16(x, hp[1], acc[2 * KK + 1]);
+    acc[2 * kk] = mfma_bf16(x, hp[0], acc[2 * kk]);
+    acc[2 * kk + 1] = mfma_bf16(x, hp[1], acc[2 * kk + 1]);
   }
 }
 
@@ -285,21 +313,23 @@ __device__ __forceinline__ const char *x_block_bf16(const QuantArgs &a, const Bl
 }
 
 // Piece kk of the lane's token row: channels 32 kk + 8 g + [0, 8).
+template <int KK>
 __device__ __forceinline__ void load_bf16_block(const QuantArgs &a, const BlockIdx &bi,
-                                                int64_t xlane, u32x4 (&xr)[4]) {
+                                                int64_t xlane, u32x4 (&xr)[KK]) {
   const u32x4 *src = reinterpret_cast<const u32x4 *>(x_block_bf16(a, bi, xlane));
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) xr[kk] = __builtin_nontemporal_load(src + 4 * kk);
+  for (int kk = 0; kk < KK; ++kk) xr[kk] = __builtin_nontemporal_load(src + 4 * kk);
 }
 
 // The same pieces as load_bf16_block, copied by the memory system straight
 // into the wave's LDS slice (global_load_lds_dwordx4: lane l's 16 bytes land
 // at slice[kk][l]); counted by vmcnt like any load.
+template <int KK>
 __device__ __forceinline__ void prefetch_bf16_block_lds(const QuantArgs &a, const BlockIdx &bi,
                                                         int64_t xlane, u32x4 (*slice)[64]) {
   const u32x4 *src = reinterpret_cast<const u32x4 *>(x_block_bf16(a, bi, xlane));
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
+  for (int kk = 0; kk < KK; ++kk)
     __builtin_amdgcn_global_load_lds(src + 4 * kk,
                                      (__attribute__((address_space(3))) void *)&slice[kk][0], 16, 0, 0);
 }
@@ -309,14 +339,53 @@ __device__ __forceinline__ void prefetch_bf16_block_lds(const QuantArgs &a, cons
 // quarter of the rate)
 __device__ __forceinline__ uint32_t bytes4(uint32_t b) { return __builtin_amdgcn_perm(0u, b, 0u); }
 
+// Pairwise sum of N values (N a power of two), halves first.
+template <int N>
+__device__ __forceinline__ float tree_sum(const float *q) {
+  if constexpr (N == 1) {
+    return q[0];
+  } else {
+    return tree_sum<N / 2>(q) + tree_sum<N / 2>(q + N / 2);
+  }
+}
+
+// V codes: lane g of the four rows (lanes 16 apart) holds words p0, p1 whose
+// byte j is the V byte of channel 16 j + n (16 (4 + j) + n) for byte column g.
+// Two 4 x 4 byte transposes across the rows: lane g ends with the words of
+// channels 16 g + n (o0) and 64 + 16 g + n (o1), byte g' from row g'. Rows g
+// and g ^ 2 (permlane32) trade the column pair the other keeps, then rows g
+// and g ^ 1 (permlane16) the column the other keeps.
+__device__ __forceinline__ void v_transpose(uint32_t p0, uint32_t p1, int t, uint32_t &o0,
+                                            uint32_t &o1) {
+  const uint32_t hi = (t >> 5) & 1, odd = (t >> 4) & 1;  // g / 2, g % 2
+  const uint32_t k1 = __builtin_amdgcn_perm(p1, p0, 0x05040100u + bytes4(2u * hi));
+  const uint32_t s1 = __builtin_amdgcn_perm(p1, p0, 0x07060302u - bytes4(2u * hi));
+  const auto x1 = __builtin_amdgcn_permlane32_swap(s1, s1, false, false);
+  const uint32_t r1 = hi ? x1[0] : x1[1];
+  const uint32_t k2 = __builtin_amdgcn_perm(r1, k1, 0x06040200u + bytes4(odd));
+  const uint32_t s2 = __builtin_amdgcn_perm(r1, k1, 0x07050301u - bytes4(odd));
+  const auto x2 = __builtin_amdgcn_permlane16_swap(s2, s2, false, false);
+  const uint32_t r2 = odd ? x2[0] : x2[1];
+  // byte rho of the word is row rho's byte: kept (rho = g: byte 0,
+  // rho = g ^ 2: byte 2) or received (rho = g ^ 1: byte 4, g ^ 3: byte 6),
+  // i.e. byte f(rho ^ g) with f = (0, 4, 2, 6)
+  const uint32_t sel =
+      __builtin_amdgcn_perm(0u, 0x06020400u, 0x03020100u ^ bytes4((uint32_t)((t >> 4) & 3)));
+  o0 = __builtin_amdgcn_perm(r2, k2, sel);
+  o1 = __builtin_amdgcn_perm(r2, k2, sel + 0x01010101u);
+}
+
 // kRotate = false: the input is already rotated (rotation absorbed into the
 // model's weights) and the MFMAs copy it through identity tiles.
 // kPositions: x is a one-chunk window per (b, h); block (b, h) re-quantizes
 // cache chunk pos[b] / 128 only when pos[b] % 128 == 127, i.e. when the token
 // just appended at pos[b] filled its chunk (kvarn_append_rebalance).
-template <bool kF32, bool kRotate, bool kPositions>
-__global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a) {
-  __shared__ QuantSmem sm;
+template <int DQ, bool kF32, bool kRotate, bool kPositions>
+__global__ __launch_bounds__(kThreads, quant_waves_per_simd(DQ)) void quantize_block_kernel(
+    QuantArgs a) {
+  using Q = QDims<DQ>;
+  constexpr int NT = Q::NT, KK = Q::KK, CPT = Q::CPT, LPC = Q::LPC, PPL = Q::PPL;
+  __shared__ QuantSmem<DQ> sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar LDS addresses
@@ -324,9 +393,11 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
   const int ti = 16 * wv + n;  // token whose input row the lane loads
   const int64_t xlane = 2 * (int64_t)ti * a.st + 16 * g;  // its bytes within a bf16 block
   const int64_t nch = a.capacity / T;
-  // r' from the running maximum: the unscaled rotation's 1/sqrt(128) and the
+  // the channel whose column-step sum this lane takes part in
+  const int ch = (DQ / 8) * wv + lane / LPC;
+  // r' from the running maximum: the unscaled rotation's 1/sqrt(D) and the
   // 1/2 of the range step, or the 1/2 alone for pre-rotated input
-  const float range_factor = kRotate ? kRangeFromUnscaled : kRangeFromRotated;
+  const float range_factor = kRotate ? range_from_unscaled(DQ) : kRangeFromRotated;
 
   // Positions mode runs after every append, and a chunk closes on one step in
   // 128: a workgroup none of whose blocks closes leaves before it loads
@@ -354,43 +425,39 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
 
   // bf16 input: the block being started is in xn (registers); the next one
   // is in the wave's LDS slice xin[wv] or on its way there
-  u32x4 xn[4];
+  u32x4 xn[KK];
   uint32_t blk = blockIdx.x;
   if constexpr (!kF32) {
     if (blk < a.nblocks) {
-      load_bf16_block(a, split_block(a, blk), xlane, xn);
-      prefetch_bf16_block_lds(a, split_block(a, min(blk + gridDim.x, a.nblocks - 1)), xlane,
-                              sm.xin[wv]);
+      load_bf16_block<KK>(a, split_block(a, blk), xlane, xn);
+      prefetch_bf16_block_lds<KK>(a, split_block(a, min(blk + gridDim.x, a.nblocks - 1)), xlane,
+                                  sm.xin[wv]);
     }
     // waited for here once, so that the loop head does not merge the first
     // loads into every block's wait
     __builtin_amdgcn_s_waitcnt(kVmcntZero);
   }
-  auto rotate_f32 = [&](const BlockIdx &bi, f32x4 (&acc)[8]) {  // three bf16 terms per piece
+  auto rotate_f32 = [&](const BlockIdx &bi, f32x4 (&acc)[NT]) {  // three bf16 terms per piece
     const u32x4 hp[4] = {sm.hop[0][lane], sm.hop[1][lane], sm.hop[2][lane], sm.hop[3][lane]};
     const f32x4 *src =
         reinterpret_cast<const f32x4 *>(static_cast<const float *>(a.x) + x_offset(a, bi, ti)) +
         2 * g;
-    f32x4 xv[8];
+    f32x4 xv[2 * KK];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) xv[q] = __builtin_nontemporal_load(src + 8 * (q >> 1) + (q & 1));
-#define KVARN_ROTATE_F32(KK)                                  \
-  {                                                           \
-    u32x4 th, tm, tl;                                         \
-    split_bf16x3(xv[2 * (KK)], xv[2 * (KK) + 1], th, tm, tl); \
-    rotate_step<kRotate, KK>(acc, tl, hp);                    \
-    rotate_step<kRotate, KK>(acc, tm, hp);                    \
-    rotate_step<kRotate, KK>(acc, th, hp);                    \
-  }
-    KVARN_ROTATE_F32(0) KVARN_ROTATE_F32(1) KVARN_ROTATE_F32(2) KVARN_ROTATE_F32(3)
-#undef KVARN_ROTATE_F32
+    for (int q = 0; q < 2 * KK; ++q) xv[q] = __builtin_nontemporal_load(src + 8 * (q >> 1) + (q & 1));
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 th, tm, tl;
+      split_bf16x3(xv[2 * kk], xv[2 * kk + 1], th, tm, tl);
+      rotate_step<kRotate, NT>(acc, tl, hp, kk);
+      rotate_step<kRotate, NT>(acc, tm, hp, kk);
+      rotate_step<kRotate, NT>(acc, th, hp, kk);
+    }
   };
-  auto rotate_bf16 = [&](const u32x4 (&x)[4], f32x4 (&acc)[8]) {
+  auto rotate_bf16 = [&](const u32x4 (&x)[KK], f32x4 (&acc)[NT]) {
     const u32x4 hp[4] = {sm.hop[0][lane], sm.hop[1][lane], sm.hop[2][lane], sm.hop[3][lane]};
-    rotate_step<kRotate, 0>(acc, x[0], hp);
-    rotate_step<kRotate, 1>(acc, x[1], hp);
-    rotate_step<kRotate, 2>(acc, x[2], hp);
-    rotate_step<kRotate, 3>(acc, x[3], hp);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) rotate_step<kRotate, NT>(acc, x[kk], hp, kk);
   };
 
   int vbuf = 0;  // V staging buffer of the next V block
@@ -410,18 +477,18 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
     float y[CPT], p[CPT];
     f32x4 gram = {0.f, 0.f, 0.f, 0.f};  // bf16: x x^T of the wave's 16 tokens
     {
-      f32x4 acc[8];
+      f32x4 acc[NT];
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
       if constexpr (kF32) {
         rotate_f32(bi, acc);
       } else {
         rotate_bf16(xn, acc);
-        // first row step by Parseval: sum_j y_j^2 = 128 sum_k x_k^2 (1 sum_k
+        // first row step by Parseval: sum_j y_j^2 = D sum_k x_k^2 (1 sum_k
         // x_k^2 without the rotation); the diagonal of x x^T, from the same
         // operand registers, lands in lane (n, g = n / 4), register n % 4
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) gram = mfma_bf16(xn[kk], xn[kk], gram);
+        for (int kk = 0; kk < KK; ++kk) gram = mfma_bf16(xn[kk], xn[kk], gram);
         // next block's input from the LDS slice into xn, then the block after
         // it into the slice: in flight during this whole block and the next
         // one's rotation (the LDS-only barriers below do not wait for it).
@@ -433,13 +500,13 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
         // ordering within the wave is all that is needed after that.
         __builtin_amdgcn_s_waitcnt(kPrefetchLanded);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) xn[kk] = sm.xin[wv][kk][lane];
+        for (int kk = 0; kk < KK; ++kk) xn[kk] = sm.xin[wv][kk][lane];
         __builtin_amdgcn_s_waitcnt((0x7 << 4) | 0xF | (0x3 << 14));  // lgkmcnt(0): reads done
         const uint32_t nb = min(blk + 2 * gridDim.x, a.nblocks - 1);
-        prefetch_bf16_block_lds(a, split_block(a, nb), xlane, sm.xin[wv]);
+        prefetch_bf16_block_lds<KK>(a, split_block(a, nb), xlane, sm.xin[wv]);
       }
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
+      for (int nt = 0; nt < NT; ++nt) {
         y[4 * nt + 0] = acc[nt].x; y[4 * nt + 1] = acc[nt].y;
         y[4 * nt + 2] = acc[nt].z; y[4 * nt + 3] = acc[nt].w;
       }
@@ -455,16 +522,15 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
     }
 
     // ---- 3. dual scaling ---------------------------------------------------
-    float w[8];                  // 1/c^2 of channels 16 nt + n; 1/c after the last column step
-    float cm = 1.f;  // c^2 of channel 16 wv + lane / 4 after a column step, then c
+    float w[NT];     // 1/c^2 of channels 16 nt + n; 1/c after the last column step
+    float cm = 1.f;  // c^2 of channel ch after a column step, then c
     if (a.iters > 0) {
-      // v_i = 1 / (T r_i^2) of the lane's tokens. With D = T the row step's
-      // 1/D and the column step's 1/T cancel: v_i = 1 / sum_j P_ij / c_j^2,
-      // and the column step's weighted sum is c_j^2 itself. A zero row or
+      // v_i = 1 / (D r_i^2) of the lane's tokens: v_i = 1 / sum_j P_ij / c_j^2,
+      // and the column step's c_j^2 = (1/T) sum_i P_ij / r_i^2 is
+      // (D/T) sum_i P_ij v_i (D/T = 1 for the square block). A zero row or
       // column (all its P are 0) takes the reciprocal of the smallest normal
       // number instead of 1: its products are 0 either way, and its stored
       // scales are set below.
-      static_assert(D == T, "the row and column normalizations cancel only for square blocks");
       float v[4];
       {
         // first row step (c = 1): v_i = 1 / sum_j P_ij
@@ -472,9 +538,12 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
         if constexpr (kF32) {
           float s[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            s[r] = ((p[r] + p[4 + r]) + (p[8 + r] + p[12 + r])) +
-                   ((p[16 + r] + p[20 + r]) + (p[24 + r] + p[28 + r]));
+          for (int r = 0; r < 4; ++r) {
+            float q[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) q[nt] = p[4 * nt + r];
+            s[r] = tree_sum<NT>(q);
+          }
           tot = row_reduce4<false>(s, n);
         } else {
           // token 4 g + tsel(n) sits in lane 16 g + 4 g + tsel(n), register tsel(n)
@@ -482,49 +551,51 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
           const float d = (r & 2) ? ((r & 1) ? gram.w : gram.z) : ((r & 1) ? gram.y : gram.x);
           const int t = tid;
           const int src = 20 * ((t >> 4) & 3) + tsel(t);
-          tot = (kRotate ? (float)D : 1.f) * __shfl(d, src, 64);
+          tot = (kRotate ? (float)DQ : 1.f) * __shfl(d, src, 64);
         }
         const float vt = rcp(fmaxf(tot, kTiny));
         v[0] = token_value<0>(vt); v[1] = token_value<1>(vt);
         v[2] = token_value<2>(vt); v[3] = token_value<3>(vt);
       }
       for (int it = 0;;) {
-        // column step: c_j^2 = (1/T) sum_i P_ij / r_i^2 = sum_i P_ij v_i. The
-        // lane's 8 partial sums (its 4 tokens of channels 16 nt + n) go to
-        // LDS; wave w then adds up channel 16 w + l / 4: lane l takes waves
-        // 2 (l % 4) and 2 (l % 4) + 1, all four rows, and the quad's four
-        // lanes meet by two DPP adds.
-        float cp[8];
+        // column step: the lane's NT partial sums (its 4 tokens of channels
+        // 16 nt + n) go to LDS; the LPC lanes of channel ch then add up its
+        // 32 partials, PPL each, and meet by DPP adds
+        float cp[NT];
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
+        for (int nt = 0; nt < NT; ++nt)
           cp[nt] = fmaf(p[4 * nt + 3], v[3],
                         fmaf(p[4 * nt + 2], v[2], fmaf(p[4 * nt + 1], v[1], p[4 * nt] * v[0])));
         {
           float *pw = sm.cpart + CP_WAVE * wv + lane;
 #pragma unroll
-          for (int nt = 0; nt < 8; ++nt) pw[CP_PLANE * nt] = cp[nt];
+          for (int nt = 0; nt < NT; ++nt) pw[CP_PLANE * nt] = cp[nt];
         }
         lds_barrier();
         {
-          const float *pr = sm.cpart + CP_PLANE * wv + 2 * CP_WAVE * (lane & 3) + (lane >> 2);
-          float q[8];
+          const float *pr = sm.cpart + CP_PLANE * (ch >> 4) + (ch & 15);
+          const int sub = lane % LPC;
+          float q[PPL];
 #pragma unroll
-          for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) q[4 * u + r] = pr[CP_WAVE * u + 16 * r];
-          cm = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+          for (int i = 0; i < PPL; ++i) {
+            const int gp = sub * PPL + i;  // partial (wave gp / 4, row gp % 4)
+            q[i] = pr[CP_WAVE * (gp >> 2) + 16 * (gp & 3)];
+          }
+          cm = tree_sum<PPL>(q);
           cm += dpp_f<kXor1>(cm);
-          cm += dpp_f<kXor2>(cm);
+          if constexpr (LPC >= 4) cm += dpp_f<kXor2>(cm);
+          if constexpr (LPC >= 8) cm += lane_xor<4>(cm);
+          if constexpr (DQ != T) cm *= (float)DQ / (float)T;  // a power of two
         }
         if (++it == a.iters) break;
-        // 1/c^2 of channel 16 wv + l / 4 (the four lanes of each channel write
-        // the same value), then every lane takes channels 16 nt + n
-        sm.ctot[16 * wv + (lane >> 2)] = rcp(fmaxf(cm, kTiny));
+        // 1/c^2 of channel ch (its LPC lanes write the same value), then
+        // every lane takes channels 16 nt + n
+        sm.ctot[ch] = rcp(fmaxf(cm, kTiny));
         lds_barrier();
         {
           const float *pg = sm.ctot + n;
 #pragma unroll
-          for (int nt = 0; nt < 8; ++nt) w[nt] = pg[16 * nt];
+          for (int nt = 0; nt < NT; ++nt) w[nt] = pg[16 * nt];
         }
         // row step: r_i^2 = (1/D) sum_j P_ij / c_j^2  ->  v_i = 1 / sum_j P_ij / c_j^2
         float s[4];
@@ -532,7 +603,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
         for (int r = 0; r < 4; ++r) {
           float e = p[r] * w[0];
 #pragma unroll
-          for (int nt = 1; nt < 8; ++nt) e = fmaf(p[4 * nt + r], w[nt], e);
+          for (int nt = 1; nt < NT; ++nt) e = fmaf(p[4 * nt + r], w[nt], e);
           s[r] = e;
         }
         const float tot = row_reduce4<false>(s, n);
@@ -540,19 +611,19 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
         v[0] = token_value<0>(vt); v[1] = token_value<1>(vt);
         v[2] = token_value<2>(vt); v[3] = token_value<3>(vt);
       }
-      // c and 1/c of channel 16 wv + l / 4 (a zero column keeps c = 1)
+      // c and 1/c of channel ch (a zero column keeps c = 1)
       const float ic = cm > 0.f ? __builtin_amdgcn_rsqf(cm) : 1.f;
       cm = cm > 0.f ? cm * ic : 1.f;  // c = c^2 / sqrt(c^2)
-      sm.ctot[16 * wv + (lane >> 2)] = ic;
+      sm.ctot[ch] = ic;
       lds_barrier();
       {
         const float *pg = sm.ctot + (tid & 15);
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) w[nt] = pg[16 * nt];
+        for (int nt = 0; nt < NT; ++nt) w[nt] = pg[16 * nt];
       }
     } else {
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) w[nt] = 1.f;
+      for (int nt = 0; nt < NT; ++nt) w[nt] = 1.f;
     }
 
     // ---- 4. range step and codes --------------------------------------------
@@ -560,11 +631,11 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
     // issued by every wave of every block that is not skipped, each with
     // active lanes in every wave: they are the kStoresAfterPrefetch that the
     // prefetch wait counts on.
-    if ((lane & 3) == 0)  // store 1 of 3; wave wv holds the column scales of channels 16 wv + [0, 16)
-      a.col_scale[(bh * nch + chunk) * D + 16 * wv + ((tid & 63) >> 2)] = cm;
+    if (lane % LPC == 0)  // store 1 of 3; wave wv holds the column scales of channels (D/8) wv + [0, D/8)
+      a.col_scale[(bh * nch + chunk) * DQ + ch] = cm;
     float mx[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         y[4 * nt + r] *= w[nt];
@@ -579,17 +650,17 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
     const float qs[4] = {token_value<0>(qt), token_value<1>(qt), token_value<2>(qt),
                          token_value<3>(qt)};
 
-    uint8_t *cbase = a.codes + (bh * nch + chunk) * CHUNK_BYTES;
+    uint8_t *cbase = a.codes + (bh * nch + chunk) * Q::CHUNK_CODE_BYTES;
     if (a.kind == KVARN_K) {
       // kw[r][k] byte i = code of token 4 g + r, channel 16 (4 k + i) + n;
       // shifted to bit 2 (n % 4) and ORed over the quad it becomes token-row
       // byte 16 k + 4 i + n / 4 (channels 4 (4 k + i) + n / 4 .. + 4)
-      uint32_t kw[4][2];
+      uint32_t kw[4][NT / 4];
       const int sh = 2 * (tid & 3);
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
+        for (int k = 0; k < NT / 4; ++k) {
           uint32_t c = 0;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
@@ -598,80 +669,101 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
           c |= dpp_u<kXor1>(c);
           kw[r][k] = c | dpp_u<kXor2>(c);
         }
-      // the four lanes of quad q hold the same words: each writes all eight
-      // (token r, half k) words of the quad (equal values to equal addresses)
+      // the four lanes of quad q hold the same words: each writes all of the
+      // quad's (token r, word k) words (equal values to equal addresses)
       const int t = tid;
       const int s = t & 3, q = (t >> 2) & 3;
-      uint32_t *ks = &sm.kst[wv][0] + KST_ROW * ((t >> 4) & 3);
+      uint32_t *ks = &sm.kst[wv][0] + Q::KST_ROW * ((t >> 4) & 3);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        ks[8 * r + q] = kw[r][0];
-        ks[8 * r + 4 + q] = kw[r][1];
-      }
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int k = 0; k < NT / 4; ++k) ks[NT * r + 4 * k + q] = kw[r][k];
       wave_lds_sync();
-      // lane n takes bytes [8 n, 8 n + 8) of the row of tokens 4 g .. 4 g + 3:
-      // token n / 4 (= q), half k = s / 2, bytes 2 (s % 2) and 2 (s % 2) + 1
-      // of the four quads' words
-      const u32x4 wq = *reinterpret_cast<const u32x4 *>(ks + 8 * q + 4 * (s >> 1));
-      const uint32_t sel = 0x05010400u + bytes4(2u * (uint32_t)(s & 1));
-      const uint32_t t01 = __builtin_amdgcn_perm(wq.y, wq.x, sel);
-      const uint32_t t23 = __builtin_amdgcn_perm(wq.w, wq.z, sel);
-      const u32x2 pk = {__builtin_amdgcn_perm(t23, t01, 0x05040100u),
-                        __builtin_amdgcn_perm(t23, t01, 0x07060302u)};
-      // tokens 16 wv + 4 g + [0, 4) are 128 contiguous bytes from (16 wv + 4 g) * 32
-      *reinterpret_cast<u32x2 *>(cbase + 8 * (t & 511)) = pk;  // store 3 of 3 (K)
+      // lane n stores bytes [NT s, NT s + NT) of the row of token 4 g + q:
+      // token-row bytes 16 k + 4 i + q' (quad q'), gathered from the four
+      // quads' words of (token q, word k); the wave's 16 token rows are one
+      // contiguous span, of which the lane's bytes start at (D/16) (t % 512)
+      if constexpr (DQ == 64) {  // k = 0, byte i = s of each word
+        const u32x4 wq = *reinterpret_cast<const u32x4 *>(ks + 4 * q);
+        const uint32_t sel = 0x0C0C0400u + 0x0101u * (uint32_t)s;  // bytes s, 4 + s, zero, zero
+        const uint32_t t01 = __builtin_amdgcn_perm(wq.y, wq.x, sel);
+        const uint32_t t23 = __builtin_amdgcn_perm(wq.w, wq.z, sel);
+        *reinterpret_cast<uint32_t *>(cbase + 4 * (t & 511)) =
+            __builtin_amdgcn_perm(t23, t01, 0x05040100u);  // store 3 of 3 (K)
+      } else if constexpr (DQ == 128) {  // k = s / 2, bytes i = 2 (s % 2) + [0, 2)
+        const u32x4 wq = *reinterpret_cast<const u32x4 *>(ks + 8 * q + 4 * (s >> 1));
+        const uint32_t sel = 0x05010400u + bytes4(2u * (uint32_t)(s & 1));
+        const uint32_t t01 = __builtin_amdgcn_perm(wq.y, wq.x, sel);
+        const uint32_t t23 = __builtin_amdgcn_perm(wq.w, wq.z, sel);
+        const u32x2 pk = {__builtin_amdgcn_perm(t23, t01, 0x05040100u),
+                          __builtin_amdgcn_perm(t23, t01, 0x07060302u)};
+        *reinterpret_cast<u32x2 *>(cbase + 8 * (t & 511)) = pk;  // store 3 of 3 (K)
+      } else {  // k = s, all four bytes of each word: a 4 x 4 byte transpose
+        const u32x4 wq = *reinterpret_cast<const u32x4 *>(ks + 16 * q + 4 * s);
+        const uint32_t a01 = __builtin_amdgcn_perm(wq.y, wq.x, 0x05010400u);  // x0 y0 x1 y1
+        const uint32_t b01 = __builtin_amdgcn_perm(wq.y, wq.x, 0x07030602u);  // x2 y2 x3 y3
+        const uint32_t a23 = __builtin_amdgcn_perm(wq.w, wq.z, 0x05010400u);
+        const uint32_t b23 = __builtin_amdgcn_perm(wq.w, wq.z, 0x07030602u);
+        const u32x4 pk = {__builtin_amdgcn_perm(a23, a01, 0x05040100u),
+                          __builtin_amdgcn_perm(a23, a01, 0x07060302u),
+                          __builtin_amdgcn_perm(b23, b01, 0x05040100u),
+                          __builtin_amdgcn_perm(b23, b01, 0x07060302u)};
+        *reinterpret_cast<u32x4 *>(cbase + 16 * (t & 511)) = pk;  // store 3 of 3 (K)
+      }
     } else {
-      // Byte j of p0 (p1) is the V byte of channel 16 j + n (16 (4 + j) + n),
-      // tokens 16 wv + 4 g + [0, 4) (byte column 4 wv + g of the channel
-      // row). The codes of token r of the four tiles are converted into the
-      // bytes of one word, and the four tokens' words meet by shifts of 2 r
-      // within the bytes (no field reaches the next byte).
-      uint32_t xa[4], xb[4];
+      // Byte j of pw[m] is the V byte of channel 16 (4 m + j) + n, tokens
+      // 16 wv + 4 g + [0, 4) (byte column 4 wv + g of the channel row). The
+      // codes of token r of four tiles are converted into the bytes of one
+      // word, and the four tokens' words meet by shifts of 2 r within the
+      // bytes (no field reaches the next byte).
+      uint32_t pw[NT / 4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        xa[r] = 0;
-        xb[r] = 0;
+      for (int m4 = 0; m4 < NT / 4; ++m4) {
+        uint32_t xr[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          xa[r] = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(y[4 * j + r], qs[r], 1.5f), j, xa[r]);
-          xb[r] = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(y[4 * (4 + j) + r], qs[r], 1.5f), j, xb[r]);
+        for (int r = 0; r < 4; ++r) {
+          xr[r] = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            xr[r] = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(y[4 * (4 * m4 + j) + r], qs[r], 1.5f), j,
+                                                   xr[r]);
+        }
+        pw[m4] = (xr[0] | (xr[1] << 2)) | ((xr[2] << 4) | (xr[3] << 6));
+      }
+      // lane g ends with the words of channels 16 g + n + 64 m (byte column
+      // 4 wv + [0, 4)), which go through LDS so that the block leaves as
+      // contiguous stores of D/16 bytes per thread
+      const int t = tid;
+      uint32_t *vs = &sm.vst[vbuf][0];
+      if constexpr (DQ == 64) {
+        uint32_t o0, o1;
+        v_transpose(pw[0], pw[0], t, o0, o1);  // the second word is unused
+        vs[VST_ROW * (t & 63) + (t >> 6)] = o0;
+      } else {
+#pragma unroll
+        for (int m2 = 0; m2 < NT / 8; ++m2) {
+          uint32_t o0, o1;
+          v_transpose(pw[2 * m2], pw[2 * m2 + 1], t, o0, o1);
+          vs[VST_ROW * ((t & 63) + 128 * m2) + (t >> 6)] = o0;
+          vs[VST_ROW * ((t & 63) + 128 * m2 + 64) + (t >> 6)] = o1;
         }
       }
-      const uint32_t p0 = (xa[0] | (xa[1] << 2)) | ((xa[2] << 4) | (xa[3] << 6));
-      const uint32_t p1 = (xb[0] | (xb[1] << 2)) | ((xb[2] << 4) | (xb[3] << 6));
-      // 4 x 4 byte transposes across the rows g (lanes 16 apart) of p0 and
-      // p1: lane g ends with the words of tiles g and 4 + g. Rows g and g ^ 2
-      // (permlane32) trade the column pair the other keeps, then rows g and
-      // g ^ 1 (permlane16) the column the other keeps.
-      const int t = tid;
-      const uint32_t hi = (t >> 5) & 1, odd = (t >> 4) & 1;  // g / 2, g % 2
-      const uint32_t k1 = __builtin_amdgcn_perm(p1, p0, 0x05040100u + bytes4(2u * hi));
-      const uint32_t s1 = __builtin_amdgcn_perm(p1, p0, 0x07060302u - bytes4(2u * hi));
-      const auto x1 = __builtin_amdgcn_permlane32_swap(s1, s1, false, false);
-      const uint32_t r1 = hi ? x1[0] : x1[1];
-      const uint32_t k2 = __builtin_amdgcn_perm(r1, k1, 0x06040200u + bytes4(odd));
-      const uint32_t s2 = __builtin_amdgcn_perm(r1, k1, 0x07050301u - bytes4(odd));
-      const auto x2 = __builtin_amdgcn_permlane16_swap(s2, s2, false, false);
-      const uint32_t r2 = odd ? x2[0] : x2[1];
-      // byte rho of the word is row rho's byte: kept (rho = g: byte 0,
-      // rho = g ^ 2: byte 2) or received (rho = g ^ 1: byte 4, g ^ 3: byte 6),
-      // i.e. byte f(rho ^ g) with f = (0, 4, 2, 6)
-      const uint32_t sel = __builtin_amdgcn_perm(
-          0u, 0x06020400u, 0x03020100u ^ bytes4((uint32_t)((t >> 4) & 3)));
-      // the words of channels 16 g + n (= t % 64) and 64 + 16 g + n, byte
-      // column 4 wv, go through LDS so that the block leaves as 4 KB of
-      // contiguous 8-byte stores
-      uint32_t *vs = &sm.vst[vbuf][0];
-      vs[VST_ROW * (t & 63) + (t >> 6)] = __builtin_amdgcn_perm(r2, k2, sel);
-      vs[VST_ROW * ((t & 63) + 64) + (t >> 6)] = __builtin_amdgcn_perm(r2, k2, sel + 0x01010101u);
       vbuf ^= 1;
       lds_barrier();
-      // thread u: channel u / 4, byte columns 8 (u % 4) + [0, 8) = the words
-      // of waves 2 (u % 4) and 2 (u % 4) + 1; channel row j starts at 32 j
+      // the channel row j (32 bytes: the words of waves 0..7) starts at 32 j;
+      // thread u stores bytes [(D/16) u, (D/16) (u + 1)) of the block's V codes
       const int u = tid;
-      const uint32_t *src = vs + VST_ROW * (u >> 2) + 2 * (u & 3);
-      const u32x2 word = {src[0], src[1]};
-      *reinterpret_cast<u32x2 *>(cbase + 8 * u) = word;  // store 3 of 3 (V)
+      if constexpr (DQ == 64) {  // channel u / 8, word of wave u % 8
+        *reinterpret_cast<uint32_t *>(cbase + 4 * u) = vs[VST_ROW * (u >> 3) + (u & 7)];  // store 3 of 3 (V)
+      } else if constexpr (DQ == 128) {  // channel u / 4, words of waves 2 (u % 4) + [0, 2)
+        const uint32_t *src = vs + VST_ROW * (u >> 2) + 2 * (u & 3);
+        const u32x2 word = {src[0], src[1]};
+        *reinterpret_cast<u32x2 *>(cbase + 8 * u) = word;  // store 3 of 3 (V)
+      } else {  // channel u / 2, words of waves 4 (u % 2) + [0, 4)
+        const uint32_t *src = vs + VST_ROW * (u >> 1) + 4 * (u & 1);
+        const u32x4 word = {src[0], src[1], src[2], src[3]};
+        *reinterpret_cast<u32x4 *>(cbase + 16 * u) = word;  // store 3 of 3 (V)
+      }
     }
   }
   // the last prefetch into the LDS slice lands before the workgroup (and its
@@ -681,15 +773,16 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_block_kernel(QuantArgs a
 
 }  // namespace
 
-hipError_t launch_quantize(const QuantArgs &a, hipStream_t s) {
-  if (a.nblocks == 0) return hipSuccess;
-  // two resident workgroups per CU (register-limited); each walks blocks
-  // strided by the grid
-  const uint32_t resident = 2u * (uint32_t)device_cus();
+template <int DQ>
+static hipError_t launch_quantize_dq(const QuantArgs &a, hipStream_t s) {
+  // resident workgroups per CU as the registers allow (quant_waves_per_simd
+  // x 4 SIMDs / 8 waves); each walks blocks strided by the grid
+  const uint32_t resident = (uint32_t)(quant_waves_per_simd(DQ) / 2) * (uint32_t)device_cus();
   const uint32_t blocks = a.nblocks < resident ? a.nblocks : resident;
   const bool rot = !(a.flags & KVARN_FLAG_NO_ROTATE);
-#define KVARN_LAUNCH_QUANT(F32, ROT, POS) \
-  hipLaunchKernelGGL((quantize_block_kernel<F32, ROT, POS>), dim3(blocks), dim3(kThreads), 0, s, a)
+#define KVARN_LAUNCH_QUANT(F32, ROT, POS)                                                   \
+  hipLaunchKernelGGL((quantize_block_kernel<DQ, F32, ROT, POS>), dim3(blocks), dim3(kThreads), 0, \
+                     s, a)
   if (a.pos) {
     if (a.dtype == KVARN_DT_F32) {
       if (rot) KVARN_LAUNCH_QUANT(true, true, true); else KVARN_LAUNCH_QUANT(true, false, true);
@@ -705,6 +798,15 @@ hipError_t launch_quantize(const QuantArgs &a, hipStream_t s) {
   }
 #undef KVARN_LAUNCH_QUANT
   return hipGetLastError();
+}
+
+hipError_t launch_quantize(const QuantArgs &a, hipStream_t s) {
+  if (a.nblocks == 0) return hipSuccess;
+  switch (a.head_dim) {
+    case 64: return launch_quantize_dq<64>(a, s);
+    case 256: return launch_quantize_dq<256>(a, s);
+    default: return launch_quantize_dq<128>(a, s);
+  }
 }
 
 }  // namespace kvarn
