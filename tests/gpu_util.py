@@ -44,8 +44,8 @@ def assert_quant_parity(oracle, ora, g_codes, g_rp, g_c, what=""):
 
 def cache_blocks(cache, kind, sel):
     """Selected blocks of a GPU cache as oracle-shaped arrays. sel: list of
-    (b, h, chunk). Returns codes [1, n, 128, 128] (unpacked by the oracle),
-    rp [1, n, 128], c [1, n, 1, 128]."""
+    (b, h, chunk). Returns codes [1, n, 128, D] (unpacked by the oracle),
+    rp [1, n, 128], c [1, n, 1, D] (D = the cache's head size)."""
     import oracle
     b = torch.tensor([s[0] for s in sel])
     h = torch.tensor([s[1] for s in sel])
@@ -55,17 +55,17 @@ def cache_blocks(cache, kind, sel):
     rows = cache.row_scale.view(cache.batch, cache.kv_heads, -1, 128)
     rp = rows[b.to(dev), h.to(dev), k.to(dev)].cpu().numpy()
     c = cache.col_scale[b.to(dev), h.to(dev), k.to(dev)].cpu().numpy()
-    codes = oracle.unpack(packed[None, :, None, :], kind=kind)
+    codes = oracle.unpack(packed[None, :, None, :], D=cache.head_dim, kind=kind)
     return codes, rp[None], c[None, :, None, :]
 
 
 def x_blocks(x, sel):
-    """Blocks of a [B, H, T, 128] tensor as an oracle input [1, n, 128, 128]."""
+    """Blocks of a [B, H, T, D] tensor as an oracle input [1, n, 128, D]."""
     dev = x.device
     b = torch.tensor([s[0] for s in sel], device=dev)
     h = torch.tensor([s[1] for s in sel], device=dev)
     k = torch.tensor([s[2] for s in sel], device=dev)
-    xs = x.view(x.shape[0], x.shape[1], -1, 128, 128)[b, h, k]
+    xs = x.view(x.shape[0], x.shape[1], -1, 128, x.shape[3])[b, h, k]
     return xs.double().cpu().numpy()[None]
 
 

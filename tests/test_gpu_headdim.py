@@ -9,7 +9,8 @@ import pytest
 import torch
 
 import kvgen
-from gpu_util import ATTN_RL2, SCALE_RTOL, assert_quant_parity, log, rel_l2
+from gpu_util import (ATTN_RL2, SCALE_RTOL, assert_quant_parity, cache_blocks, log, rel_l2,
+                      sample_blocks, x_blocks)
 
 pytestmark = pytest.mark.gpu
 
@@ -33,6 +34,25 @@ def test_quantize_headdim(kvarn, oracle, D, kind, dtype, iters):
                              cache.col_scale.cpu().numpy()[:, :, 1:], f"D={D}")
     assert np.all(cache.codes.cpu().numpy()[:, :, 0] == 0)  # chunk 0 untouched
     log(f"[test] quantize D={D} kind={kind} {dtype} iters={iters}: {st}")
+
+
+@pytest.mark.parametrize("D", DIMS)
+@pytest.mark.parametrize("kind", [kvgen.K, kvgen.V])
+def test_quantize_headdim_many_blocks(kvarn, oracle, D, kind):
+    """A launch of 2048 blocks (4 sequences x 8 kv-heads x 64 chunks, bf16):
+    every resident workgroup walks several blocks, so the two-deep prefetch,
+    the LDS input slice and the alternating V staging buffers all take part.
+    Sampled blocks, the first and the last, against the oracle."""
+    B, H, T = 4, 8, 8192
+    x = kvgen.kv_tensor(31 + D, 0, kind, B, H, T, 0.5, device="cuda", head_dim=D)
+    cache = kvarn.Cache.empty(B, H, T, kind, device="cuda", head_dim=D)
+    kvarn.quantize(x, cache)
+    torch.cuda.synchronize()
+    sel = sample_blocks(np.random.default_rng(D + kind), B, H, T // 128, 48,
+                        always=[(0, 0, 0), (B - 1, H - 1, T // 128 - 1)])
+    ora = oracle.quantize_tensor(x_blocks(x, sel), threads=8)
+    st = assert_quant_parity(oracle, ora, *cache_blocks(cache, kind, sel), f"many blocks D={D}")
+    log(f"[test] quantize D={D} kind={kind} 2048 blocks, {len(sel)} sampled: {st}")
 
 
 @pytest.mark.parametrize("D", DIMS)
