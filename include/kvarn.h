@@ -24,8 +24,10 @@
  *    error the call returns a negative kvarn_status and enqueues nothing.
  *    A failed launch returns KVARN_ERR_HIP.
  *  - The chunk (block) length is 128 tokens. head_dim is 128, 64 or 256 (a
- *    field of the cache descriptor); 128 runs the tuned kernels, 64 and 256
- *    run generic kernels that compute the same quantities.
+ *    field of the cache descriptor). The block quantizer and decode run the
+ *    same kernels for every head size; the one-token append and the token
+ *    error run simpler kernels for 64 and 256 that compute the same
+ *    quantities.
  */
 #ifndef KVARN_H
 #define KVARN_H
