@@ -546,7 +546,13 @@ def ablations(kv, torch, stream, xs, qs, caches, ws, out, length, iters, rounds=
                         "balancing_share": round((t["q_full"] - t["q_none"]) / t["q_full"], 4)},
         "decode_us": {"two_scales": round(t["d_two"], 2), "one_scale": round(t["d_one"], 2),
                       "no_rotate": round(t["d_norot"], 2),
-                      "second_scale_overhead": round((t["d_two"] - t["d_one"]) / t["d_one"], 4)},
+                      "second_scale_overhead": round((t["d_two"] - t["d_one"]) / t["d_one"], 4),
+                      # the column scales are 8 of the 80 bytes per cached token and
+                      # kv-head, which the one-scale variant does not read: the
+                      # overhead per byte read is what the fused scale costs beyond them
+                      "second_scale_extra_bytes": round(80 / 72 - 1, 4),
+                      "second_scale_overhead_per_byte": round(
+                          (t["d_two"] / 80) / (t["d_one"] / 72) - 1, 4)},
         "regime": f"HBM: each of the {L} launches per timing reads another layer's input or "
                   f"cache (none fits in the {MALL_BYTES >> 20} MB memory-side cache)",
         "note": f"K tensor for quantize; HIP events over {L} launches after one warm launch; "
