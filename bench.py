@@ -226,39 +226,27 @@ def main():
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
-    def step(i: int, rec: dict | None):
+    def step(i: int):
+        """One untimed (warmup) step, launched eagerly."""
         p = (T + i) if steady else T
         pos = torch.full((B,), p, dtype=torch.int32, device=dev)
         lens = torch.full((B,), p + 1, dtype=torch.int32, device=dev)
-
-        def launch(name, fn):
-            if rec is None:
-                fn()
-                return
-            a, b_ = ev(), ev()
-            a.record(stream)
-            fn()
-            b_.record(stream)
-            rec[name].append((a, b_))
-
         if not steady:
             for layer in range(L):
                 for x, c in ((xs[layer][0], caches[layer][0]), (xs[layer][1], caches[layer][1])):
-                    launch("quantize", lambda x=x, c=c: kv.quantize(x, c, iters=args.iters,
-                                                                    stream=stream))
+                    kv.quantize(x, c, iters=args.iters, stream=stream)
         for layer in range(L):
             kc, vc = caches[layer]
             for n, c in ((news[layer][0], kc), (news[layer][1], vc)):
-                launch("append", lambda n=n, c=c: kv.append(n, pos, c, stream=stream))
-            launch("decode", lambda kc=kc, vc=vc, layer=layer: kv.decode_attn(
-                qs[layer], kc, vc, lens, out=out, workspace=ws, stream=stream))
+                kv.append(n, pos, c, stream=stream)
+            kv.decode_attn(qs[layer], kc, vc, lens, out=out, workspace=ws, stream=stream)
 
     log(f"[bench] warmup {args.warmup} steps")
     for i in range(args.warmup):
-        step(i, None)
+        step(i)
     torch.cuda.synchronize()
 
-    rec = {"quantize": [], "append": [], "decode": []}
+    rec = {"quantize": []}
     if steady:
         ms_step, a_us, d_us = steady_graph_timing(kv, torch, args.warmup, args.steps, caches,
                                                   news, qs, out, ws, L, B, T)
