@@ -840,6 +840,17 @@ def next_rows_workload(kv, kvgen, torch, args, dev, stream):
             qm.append(sum(qu) / len(qu))
             dm.append(sum(du) / len(du))
         qm, dm = sorted(qm)[1], sorted(dm)[1]
+        # one-token appends of K and V, as in the step: graph replays of 72
+        # launches (the layers' appends nine times over; each rewrites the
+        # same slot), since each launch is shorter than the host's cost per
+        # call and a replay's own start-up is spread over as many launches as
+        # in the step
+        tok = [kvgen.new_tokens(5, l, kind, B, H, 0.5, device=dev, head_dim=dh)
+               for l in range(L) for kind in (kv.K, kv.V)]
+        pos = torch.full((B,), T, dtype=torch.int32, device=dev)
+        am = graph_us(torch, lambda: [kv.append(tok[2 * l + k], pos, caches[l][k])
+                                      for _ in range(9) for l in range(L)
+                                      for k in range(2)]) / (9 * 2 * L)
         elts = B * H * T * dh
         qbytes = (2.0 + 0.25 + 4.0 / dh + 4.0 / CHUNK) * elts
         dbytes = (dh / 2 + 8 + dh / 16) * (T + 1) * B * H + B * Hq * dh * 6
@@ -847,8 +858,10 @@ def next_rows_workload(kv, kvgen, torch, args, dev, stream):
             "config": {"batch": B, "kv_heads": H, "q_heads": Hq, "tokens": T, "head_dim": dh},
             "quantize_us_per_launch": round(qm, 2), "quantize": hbm_entry(qbytes, qm),
             "decode_us_per_launch": round(dm, 2), "decode": hbm_entry(dbytes, dm),
-            "note": "quantize and decode: the matrix-core kernels shared by every head size"}
-        del xs, qcs, caches, q, out, ws
+            "append_us_per_launch": round(am, 2),
+            "note": "quantize and decode: the matrix-core kernels shared by every head size; "
+                    "append: the generic one-token kernel (latency-bound, no bandwidth claim)"}
+        del xs, qcs, caches, q, out, ws, tok
         torch.cuda.empty_cache()
     return res
 

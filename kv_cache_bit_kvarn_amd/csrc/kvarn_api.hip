@@ -183,8 +183,7 @@ int kvarn_append_ex(const void *x, int32_t dtype, const int32_t *positions, uint
   a.col_scale = dst->col_scale;
   a.window = nullptr;
   a.head_dim = cache_dim(dst);
-  return from_hip(a.head_dim == D ? launch_append(a, static_cast<hipStream_t>(stream))
-                                  : launch_append_generic(a, static_cast<hipStream_t>(stream)));
+  return from_hip(launch_append(a, static_cast<hipStream_t>(stream)));
 }
 
 int kvarn_append(const void *x, int32_t dtype, const int32_t *positions,
@@ -219,7 +218,7 @@ int kvarn_append_rebalance(const void *x, int32_t dtype, const int32_t *position
   p.col_scale = dst->col_scale;
   p.window = window;
   p.head_dim = cache_dim(dst);
-  st = from_hip(p.head_dim == D ? launch_append(p, s) : launch_append_generic(p, s));
+  st = from_hip(launch_append(p, s));
   if (st != KVARN_OK) return st;
   // the chunks just filled, quantized again from the window
   QuantArgs a;
@@ -284,8 +283,7 @@ int kvarn_token_error(const void *x, int32_t dtype, int64_t stride_b, int64_t st
   a.ratio = ratio;
   a.cosine = cosine;
   a.head_dim = cache_dim(cache);
-  return from_hip(a.head_dim == D ? launch_token_error(a, static_cast<hipStream_t>(stream))
-                                  : launch_token_error_generic(a, static_cast<hipStream_t>(stream)));
+  return from_hip(launch_token_error(a, static_cast<hipStream_t>(stream)));
 }
 
 size_t kvarn_decode_workspace_bytes_ex(int32_t batch, int32_t q_heads, int32_t capacity,

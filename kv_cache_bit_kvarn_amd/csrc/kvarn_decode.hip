@@ -230,10 +230,6 @@ struct Dims {
 // columns (for NCT = 8 this is slot_base, as for the other scale arrays)
 __host__ __device__ constexpr int cv_base(int nct, int s) { return nct * s + 4 * (s >> 2); }
 static_assert(cv_base(8, 5) == slot_base(5) && cv_base(8, 12) == slot_base(12), "c_V layout");
-// 1/sqrt(DD): the unscaled rotation's factor
-__host__ __device__ constexpr float inv_sqrt_dd(int dd) {
-  return dd == 64 ? 0.125f : dd == 256 ? 0.0625f : kInvSqrtD;
-}
 
 template <int DD>
 struct DecSmem {
@@ -534,7 +530,7 @@ __device__ __forceinline__ void finalize_head(float (&x)[Dims<DD>::CPL], float L
       }
     }
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) x[i] *= inv_sqrt_dd(DD);
+    for (int i = 0; i < CPL; ++i) x[i] *= inv_sqrt_head(DD);
   }
   if constexpr (CPL == 1) {
     out[lane] = x[0];
@@ -723,7 +719,7 @@ __global__ __launch_bounds__(64 * kDecWaves, decode_waves_per_simd(DD)) void dec
   SplitState<DD> st;
   {
     // the unscaled rotation's 1/sqrt(DD) applies only when it ran here
-    const float qs = 2.f * a.scale * kLog2e * (kRotate ? inv_sqrt_dd(DD) : 1.f);
+    const float qs = 2.f * a.scale * kLog2e * (kRotate ? inv_sqrt_head(DD) : 1.f);
 #pragma unroll
     for (int hf = 0; hf < NQ; ++hf)
 #pragma unroll

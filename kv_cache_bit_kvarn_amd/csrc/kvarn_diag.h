@@ -17,6 +17,5 @@ struct DiagArgs {
   float *ratio, *cosine;
 };
 hipError_t launch_token_error(const DiagArgs &a, hipStream_t s);
-hipError_t launch_token_error_generic(const DiagArgs &a, hipStream_t s);  // head_dim 64, 256
 
 }  // namespace kvarn

@@ -17,11 +17,15 @@ constexpr int T = KVARN_CHUNK;         // tokens per block
 constexpr int CHUNK_BYTES = KVARN_CHUNK_BYTES;
 constexpr int GQA_MAX = 8;             // query heads per kv-head supported by decode
 
-// 1/sqrt(128)/2 = 2^-4.5: the rotation is applied unscaled on the device
-// (y' = sqrt(128) y); the range step r' = max|y/c|/2 then becomes
-// max|y'/c| * 2^-4.5, while c and every code are unchanged by that factor.
-constexpr float kRangeFromUnscaled = 0.044194173824159216f;
-constexpr float kInvSqrtD = 0.088388347648318447f;  // 1/sqrt(128)
+// 1/sqrt(d) for the head sizes served (64, 128, 256; exact powers of two for
+// 64 and 256). The rotation is applied unscaled on the device (y' = sqrt(d) y),
+// so the range step r' = max|y/c|/2 becomes max|y'/c| / sqrt(d) / 2, while c
+// and every code are unchanged by that factor.
+__host__ __device__ constexpr float inv_sqrt_head(int d) {
+  return d == 64 ? 0.125f : d == 256 ? 0.0625f : 0.088388347648318447f;
+}
+__host__ __device__ constexpr float range_from_unscaled(int d) { return 0.5f * inv_sqrt_head(d); }
+static_assert(range_from_unscaled(128) == 0.044194173824159216f, "2^-4.5");
 // r' = max|y/c|/2 for input that is already rotated (KVARN_FLAG_NO_ROTATE)
 constexpr float kRangeFromRotated = 0.5f;
 
@@ -171,8 +175,5 @@ inline size_t decode_partial_bytes(int32_t batch, int32_t q_heads, int n_wg, int
   return (size_t)batch * q_heads * (size_t)n_wg * (2 + head_dim) * sizeof(float);
 }
 
-// Head sizes other than 128 (kvarn_generic.hip): same arguments, head_dim 64 or 256.
-// (The block quantizer and decode serve every head size in their own files.)
-hipError_t launch_append_generic(const AppendArgs &a, hipStream_t s);
 
 }  // namespace kvarn

@@ -128,10 +128,6 @@ struct QDims {
 __host__ __device__ constexpr int quant_waves_per_simd(int dq) {
   return dq == 256 ? 2 : dq == 64 ? 6 : 4;
 }
-// 1/sqrt(DQ)/2: the unscaled rotation's factor and the range step's 1/2
-__host__ __device__ constexpr float range_from_unscaled(int dq) {
-  return dq == 64 ? 0.0625f : dq == 256 ? 0.03125f : kRangeFromUnscaled;
-}
 
 template <int DQ>
 struct QuantSmem {

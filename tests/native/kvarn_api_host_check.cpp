@@ -42,18 +42,6 @@ hipError_t launch_token_error(const DiagArgs &a, hipStream_t) {
   ++g_calls;
   return g_result;
 }
-// the append and diagnostic kernels for head sizes 64 and 256 record into
-// the same slots and count separately, so the dispatch by head size is
-// checked too (quantize and decode serve every head size with one launcher)
-static int g_generic = 0;
-hipError_t launch_append_generic(const AppendArgs &a, hipStream_t s) {
-  ++g_generic;
-  return launch_append(a, s);
-}
-hipError_t launch_token_error_generic(const DiagArgs &a, hipStream_t s) {
-  ++g_generic;
-  return launch_token_error(a, s);
-}
 int decode_auto_wgs(int, int, int, int capacity, int) { return decode_max_wgs(capacity); }
 static int g_scratch_queries = 0;
 void *noalloc_scratch(hipError_t *) {
@@ -260,7 +248,7 @@ static void check_token_error() {
 }
 
 static void check_head_dim() {
-  g_calls = g_generic = 0;
+  g_calls = 0;
   kvarn_cache c = cache(2, 2, 256, KVARN_K);
   c.head_dim = 96;
   CHECK(kvarn_quantize(P(0x40000), KVARN_DT_BF16, 0, 0, 128, 256, 0, 4, &c, nullptr) == KVARN_ERR_SHAPE);
@@ -272,13 +260,13 @@ static void check_head_dim() {
   g_nquant = 0;
   CHECK(kvarn_quantize(P(0x40000), KVARN_DT_BF16, 2 * 256 * 256, 256 * 256, 256, 256, 0, 4, &c, nullptr) ==
         KVARN_OK);
-  CHECK(g_generic == 0 && g_quant[0].head_dim == 256);
+  CHECK(g_quant[0].head_dim == 256);
   CHECK(kvarn_append(P(0x40000), KVARN_DT_BF16, static_cast<int32_t *>(P(0x50000)), &c, nullptr) == KVARN_OK);
-  CHECK(g_generic == 1 && g_append.head_dim == 256);
+  CHECK(g_append.head_dim == 256);
   float *r = static_cast<float *>(P(0xA0000)), *q = static_cast<float *>(P(0xB0000));
   CHECK(kvarn_token_error(P(0x40000), KVARN_DT_BF16, 2 * 256 * 256, 256 * 256, 256, 10, 0, 0u, &c, r, q,
                           nullptr) == KVARN_OK);
-  CHECK(g_generic == 2 && g_diag.head_dim == 256);
+  CHECK(g_diag.head_dim == 256);
   // decode: K and V must share the head size, and partials are sized by it
   kvarn_cache k = cache(2, 4, 1024, KVARN_K), v = cache(2, 4, 1024, KVARN_V);
   k.head_dim = v.head_dim = 64;
@@ -296,8 +284,7 @@ static void check_head_dim() {
                           nullptr) == KVARN_ERR_WORKSPACE);
   CHECK(kvarn_decode_attn(P(0x40000), KVARN_DT_BF16, 16, &k, &v, lens, 0.1f, out, 0, P(0x90000), need,
                           nullptr) == KVARN_OK);
-  // one decode kernel family serves every head size
-  CHECK(g_generic == 2 && g_decode.head_dim == 64 && g_decode.n_wg == 2);
+  CHECK(g_decode.head_dim == 64 && g_decode.n_wg == 2);
 }
 
 static void check_status_strings() {
