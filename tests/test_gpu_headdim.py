@@ -258,6 +258,51 @@ def test_token_error_headdim(kvarn, oracle, D):
                 np.testing.assert_allclose(g_c, c_o, rtol=0, atol=1e-5)
 
 
+def _token_errors(oracle, x, cache, kind, D, token_offset, tokens):
+    """The oracle's ratio and cosine of x [B,H,tokens,D] (host fp64) against
+    the cache's slots [token_offset, token_offset + tokens)."""
+    codes = oracle.unpack(cache.codes.cpu().numpy(), D=D, kind=kind)
+    rp, cs = cache.row_scale.double().cpu().numpy(), cache.col_scale.double().cpu().numpy()
+    B, H = x.shape[:2]
+    ratio, cosine = np.empty((B, H, tokens)), np.empty((B, H, tokens))
+    sl = slice(token_offset, token_offset + tokens)
+    for b in range(B):
+        for h in range(H):
+            xh = oracle.dequant(codes[b, h], rp[b, h], cs[b, h])[sl]
+            ratio[b, h], cosine[b, h] = oracle.token_error(x[b, h], xh)
+    return ratio, cosine
+
+
+@pytest.mark.parametrize("D", DIMS)
+@pytest.mark.parametrize("kind", [kvgen.K, kvgen.V])
+def test_token_error_headdim_bf16_ragged_no_rotate(kvarn, oracle, D, kind):
+    """bf16 input over all slots; fp32 strided input over the ragged slots
+    [77, 77 + 301) of a random cache; and pre-rotated input with the rotation
+    absorbed, which gives the unrotated numbers (the rotation keeps norms and
+    inner products)."""
+    B, H, T = 2, 2, 384
+    x = kvgen.kv_tensor(107, 0, kind, B, H, T, 0.5, dtype=torch.bfloat16, head_dim=D)
+    c = kvarn.Cache.empty(B, H, T, kind, device="cuda", head_dim=D)
+    kvarn.quantize(x.cuda(), c)
+    got = kvarn.token_error(x.cuda(), c)
+    xr = torch.from_numpy(oracle.rotate(x.double().numpy())).float().cuda()
+    got_r = kvarn.token_error(xr, c, flags=kvarn.FLAG_NO_ROTATE)
+    ck, rk, colk = kvgen.random_cache(108 + kind, B, H, 512, head_dim=D)
+    rc = kvarn.Cache(ck.cuda(), rk.cuda(), colk.cuda(), kind)
+    big = torch.randn(B, H, 320, D, generator=torch.Generator().manual_seed(109),
+                      dtype=torch.float32)
+    xs = big.cuda()[:, :, 5:306]
+    got_s = kvarn.token_error(xs, rc, token_offset=77)
+    torch.cuda.synchronize()
+    want = _token_errors(oracle, x.double().numpy(), c, kind, D, 0, T)
+    want_s = _token_errors(oracle, xs.double().cpu().numpy(), rc, kind, D, 77, 301)
+    for g, w, what in ((got, want, "bf16"), (got_r, want, "no-rotate"), (got_s, want_s, "ragged")):
+        gr, gc = (t.double().cpu().numpy() for t in g)
+        np.testing.assert_allclose(gr, w[0], rtol=1e-5, atol=0, err_msg=f"D={D} {what}: ratio")
+        np.testing.assert_allclose(gc, w[1], rtol=0, atol=1e-5, err_msg=f"D={D} {what}: cosine")
+    log(f"[test] token error D={D} kind={kind}: bf16, no-rotate and ragged range agree")
+
+
 def test_noalloc_headdim(kvarn):
     """The allocation-free decode at head size 256 equals the workspace call."""
     D, B, Hkv, G, cap = 256, 2, 2, 4, 1024
