@@ -66,9 +66,9 @@ typedef enum { KVARN_DT_BF16 = 0, KVARN_DT_F32 = 1 } kvarn_dtype;
  * KVARN_FLAG_NO_ROTATE  the rotation is absorbed into the model's weights
  *     (rndamp article on KVarN, "How It Works", item 1: the Hadamard transform
  *     can be folded into existing weights): quantize and append take K/V that
- *     are already rotated (x . H_128 / sqrt(128)) and skip the rotation;
- *     decode takes the rotated query q . H_128 / sqrt(128) and returns the
- *     output in the rotated basis (out . H_128 / sqrt(128) is the output in
+ *     are already rotated (x . H_D / sqrt(D), D = head_dim) and skip the
+ *     rotation; decode takes the rotated query q . H_D / sqrt(D) and returns
+ *     the output in the rotated basis (out . H_D / sqrt(D) is the output in
  *     the original basis).
  * KVARN_FLAG_ONE_SCALE  (decode only) ablation of the second scale: the
  *     column scales are treated as 1 and not read ("Numbers": two scales
@@ -125,7 +125,7 @@ typedef struct {
  * rndamp article on KVarN, "How It Works", items 1 and 2).
  *
  * For every (b, h) and every chunk of x's tokens [0, tokens):
- *   y  = x_chunk . H_128 / sqrt(128)                 (rotation per token)
+ *   y  = x_chunk . H_D / sqrt(D)                     (rotation per token)
  *   c  = 1; repeat `iters` times:                    (dual scaling)
  *          r_i^2 = mean_j y_ij^2 / c_j^2 ;  c_j^2 = mean_i y_ij^2 / r_i^2
  *   r'_i = max_j |y_ij| / c_j / 2                    (per-token range step)
@@ -133,15 +133,15 @@ typedef struct {
  * and store codes, r' and c at cache slots [token_offset, token_offset+tokens).
  * A zero token row stores r' = 0 and code 2; a zero column keeps c_j = 1.
  * Non-finite input gives unspecified codes and scales for its chunk.
- * The arithmetic is fp32 on the unscaled rotation (y sqrt(128)): a token's
- * energy 128 sum_j x_j^2 must stay below 2^127 (|x| below about 2^53). Over
+ * The arithmetic is fp32 on the unscaled rotation (y sqrt(D)): a token's
+ * energy D sum_j x_j^2 must stay below 2^127 (|x| below about 2^53). Over
  * that range, scaling x by 2^k scales r' by exactly 2^k and leaves codes and c
  * bit-identical, as long as the squared rotated values stay normal fp32
  * numbers. A nonzero token whose energy is below 2^-126 is weighted as if it
  * were 2^-126.
  *
  * x          (device) input, dtype `dtype`, logical shape
- *            [dst->batch][dst->kv_heads][tokens][128], element (b,h,t,j) at
+ *            [dst->batch][dst->kv_heads][tokens][D], element (b,h,t,j) at
  *            x + b*stride_b + h*stride_h + t*stride_t + j (strides in elements,
  *            channels contiguous). x must be 16-byte aligned and every stride
  *            a multiple of 16 bytes.
@@ -178,7 +178,7 @@ int kvarn_quantize_ex(const void *x, int32_t dtype, int64_t stride_b,
  * pos % 4 == 0 rewrites its whole byte (the three later token slots of that
  * byte become code 0); other tokens replace only their own 2 bits.
  *
- * x          (device) [batch][kv_heads][128], dtype `dtype`, contiguous,
+ * x          (device) [batch][kv_heads][D], dtype `dtype`, contiguous,
  *            16-byte aligned.
  * positions  (device) int32 [batch].
  */
@@ -203,7 +203,7 @@ int kvarn_append_ex(const void *x, int32_t dtype, const int32_t *positions,
  * tokens with `iters` iterations, replacing the chunk's codes, row scales and
  * column scales. Decode reads the cache as usual.
  *
- * window     (device) [batch][kv_heads][128][128] of `dtype`, 16-byte
+ * window     (device) [batch][kv_heads][128][D] of `dtype`, 16-byte
  *            aligned, caller-owned and kept between calls (no need to clear
  *            it). A chunk is re-quantized correctly only if all its 128
  *            tokens were appended through this call.
@@ -241,12 +241,12 @@ size_t kvarn_decode_workspace_bytes_ex(int32_t batch, int32_t q_heads,
  * (L_b = seq_lens[b]). A sequence with L_b outside [1, capacity] gets a zero
  * output row.
  *
- * q          (device) [batch][q_heads][128], dtype q_dtype, contiguous,
+ * q          (device) [batch][q_heads][D], dtype q_dtype, contiguous,
  *            unrotated (post positional encoding).
  * k, v       (host) descriptors of the K and V caches of one layer: same
- *            batch, kv_heads and capacity; kinds KVARN_K and KVARN_V.
+ *            batch, kv_heads, capacity and head_dim; kinds KVARN_K and KVARN_V.
  * seq_lens   (device) int32 [batch].
- * out        (device) fp32 [batch][q_heads][128], original basis.
+ * out        (device) fp32 [batch][q_heads][D], original basis.
  * n_split    number of token splits per (b, kv-head); 0 lets the library
  *            choose. Rounded up to a multiple of KVARN_DECODE_WAVES (the
  *            splits of one workgroup) and clamped to [KVARN_DECODE_WAVES,
@@ -314,7 +314,7 @@ int kvarn_decode_attn_noalloc(const void *q, int32_t q_dtype, int32_t q_heads,
  * are computed in the rotated one). Degenerate tokens: both zero -> (1, 1);
  * x_t zero only -> (+inf, 0); x_hat_t zero only -> (0, 0). Sums in fp32.
  *
- * x          (device) as for kvarn_quantize: [batch][kv_heads][tokens][128],
+ * x          (device) as for kvarn_quantize: [batch][kv_heads][tokens][D],
  *            dtype `dtype`, strides in elements, 16-byte aligned pointer and
  *            strides. With KVARN_FLAG_NO_ROTATE x is taken as already rotated.
  * tokens     any count >= 0 (0 is a no-op); token_offset >= 0;
