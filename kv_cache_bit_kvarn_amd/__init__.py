@@ -246,7 +246,7 @@ def append_window(batch: int, kv_heads: int, dtype=torch.bfloat16, device="cuda"
 def append_rebalance(x: torch.Tensor, positions: torch.Tensor, cache: Cache,
                      window: torch.Tensor, iters: int = 4, stream=None, flags: int = 0) -> None:
     """append, plus the chunk re-quantized from `window` (same dtype as x,
-    [B, H, 128, 128], kept by the caller) when a token fills it. flags:
+    [B, H, 128, D], kept by the caller) when a token fills it. flags:
     FLAG_NO_ROTATE."""
     if x.dim() != 3 or tuple(x.shape) != (cache.batch, cache.kv_heads, cache.head_dim) or \
             not x.is_contiguous():
