@@ -57,6 +57,30 @@ def test_quantize_headdim_many_blocks(kvarn, oracle, D, kind):
 
 @pytest.mark.parametrize("D", DIMS)
 @pytest.mark.parametrize("kind", [kvgen.K, kvgen.V])
+def test_quantize_headdim_strided_offset(kvarn, oracle, D, kind):
+    """x a strided view (token stride 2 D elements) written at token offset
+    256 of a larger cache; the slots before and after stay untouched."""
+    base = kvgen.kv_tensor(111 + D, 0, kind, 2, 3, 256, 0.5, dtype=torch.bfloat16,
+                           device="cuda", head_dim=D)
+    big = torch.zeros((2, 3, 256, 2 * D), dtype=torch.bfloat16, device="cuda")
+    big[..., D // 2:D // 2 + D] = base
+    x = big[..., D // 2:D // 2 + D]
+    assert x.stride(2) == 2 * D
+    cache = kvarn.Cache.empty(2, 3, 640, kind, device="cuda", head_dim=D)
+    kvarn.quantize(x, cache, token_offset=256, iters=4)
+    torch.cuda.synchronize()
+    ora = oracle.quantize_tensor(base.double().cpu().numpy())
+    g = oracle.unpack(cache.codes.cpu().numpy(), D=D, kind=kind)
+    assert_quant_parity(oracle, ora, g[:, :, 256:512], cache.row_scale[:, :, 256:512].cpu(),
+                        cache.col_scale[:, :, 2:4].cpu(), f"strided D={D}")
+    assert cache.codes[:, :, :2].count_nonzero() == 0
+    assert cache.codes[:, :, 4:].count_nonzero() == 0
+    assert cache.row_scale[:, :, :256].count_nonzero() == 0
+    assert cache.col_scale[:, :, 4:].count_nonzero() == 0
+
+
+@pytest.mark.parametrize("D", DIMS)
+@pytest.mark.parametrize("kind", [kvgen.K, kvgen.V])
 def test_quantize_headdim_no_rotate(kvarn, oracle, D, kind):
     """bf16 pre-rotated input with the rotation skipped, against the oracle fed
     the exact values the GPU read (the scaled rotation is its own inverse)."""
@@ -185,6 +209,21 @@ def test_decode_headdim_splits_agree(kvarn, oracle, D):
     err = rel_l2(outs[3].cpu().numpy(), _oracle_decode(oracle, q, hk, hv, lens, D))
     log(f"[test] decode D={D} split counts agree; 20 workgroups per row: rel L2 {err:.3e}")
     assert err <= ATTN_RL2
+
+
+@pytest.mark.parametrize("D", DIMS)
+def test_decode_headdim_invalid_lengths_give_zero(kvarn, oracle, D):
+    """Lengths 0 and capacity + 1 give zero rows; a valid length beside them
+    matches the oracle."""
+    kc, vc, hk, hv = _caches(kvarn, 3, 1, 256, D, seed=113)
+    q = kvgen.queries(114, 0, 3, 4, dtype=torch.bfloat16, head_dim=D)
+    lens = [0, 257, 10]
+    out = kvarn.decode_attn(q.cuda(), kc, vc, torch.tensor(lens, dtype=torch.int32).cuda())
+    torch.cuda.synchronize()
+    assert torch.all(out[0] == 0) and torch.all(out[1] == 0)
+    want = _oracle_decode(oracle, q[2:3], tuple(t[2:3] for t in hk), tuple(t[2:3] for t in hv),
+                          [10], D)
+    assert rel_l2(out[2:3].cpu().numpy(), want) <= ATTN_RL2
 
 
 @pytest.mark.parametrize("D", DIMS)
