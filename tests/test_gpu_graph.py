@@ -12,28 +12,31 @@ from gpu_util import log
 pytestmark = pytest.mark.gpu
 
 
-def test_graph_replays_match_eager(kvarn):
+@pytest.mark.parametrize("D", [128, 64, 256])
+def test_graph_replays_match_eager(kvarn, D):
     B, H, Hq, T, cap = 3, 2, 8, 384, 640
     dev = torch.device("cuda")
-    xk = kvgen.kv_tensor(31, 0, kvgen.K, B, H, T, 0.5, device=dev)
-    xv = kvgen.kv_tensor(31, 0, kvgen.V, B, H, T, 0.5, device=dev)
-    xq = kvgen.kv_tensor(32, 0, kvgen.K, B, H, 128, 0.5, device=dev)  # quantized in the step
+    xk = kvgen.kv_tensor(31, 0, kvgen.K, B, H, T, 0.5, device=dev, head_dim=D)
+    xv = kvgen.kv_tensor(31, 0, kvgen.V, B, H, T, 0.5, device=dev, head_dim=D)
+    xq = kvgen.kv_tensor(32, 0, kvgen.K, B, H, 128, 0.5, device=dev, head_dim=D)  # quantized in the step
     steps = 3
-    nks = [kvgen.new_tokens(33 + i, 0, kvgen.K, B, H, 0.5, device=dev) for i in range(steps)]
-    nvs = [kvgen.new_tokens(33 + i, 0, kvgen.V, B, H, 0.5, device=dev) for i in range(steps)]
-    qs = [kvgen.queries(40 + i, 0, B, Hq, device=dev) for i in range(steps)]
+    nks = [kvgen.new_tokens(33 + i, 0, kvgen.K, B, H, 0.5, device=dev, head_dim=D)
+           for i in range(steps)]
+    nvs = [kvgen.new_tokens(33 + i, 0, kvgen.V, B, H, 0.5, device=dev, head_dim=D)
+           for i in range(steps)]
+    qs = [kvgen.queries(40 + i, 0, B, Hq, device=dev, head_dim=D) for i in range(steps)]
 
     def fresh_caches():
-        kc = kvarn.Cache.empty(B, H, cap, kvarn.K, device=dev)
-        vc = kvarn.Cache.empty(B, H, cap, kvarn.V, device=dev)
+        kc = kvarn.Cache.empty(B, H, cap, kvarn.K, device=dev, head_dim=D)
+        vc = kvarn.Cache.empty(B, H, cap, kvarn.V, device=dev, head_dim=D)
         kvarn.quantize(xk, kc)
         kvarn.quantize(xv, vc)
         return kc, vc
 
     # eager reference: the three steps one after the other
     kc_e, vc_e = fresh_caches()
-    qc_e = kvarn.Cache.empty(B, H, 128, kvarn.K, device=dev)
-    ws_e = kvarn.decode_workspace(B, Hq, cap, device=dev)
+    qc_e = kvarn.Cache.empty(B, H, 128, kvarn.K, device=dev, head_dim=D)
+    ws_e = kvarn.decode_workspace(B, Hq, cap, device=dev, head_dim=D)
     outs_e, caches_e = [], []
     for i in range(steps):
         pos = torch.full((B,), T + i, dtype=torch.int32, device=dev)
@@ -47,12 +50,12 @@ def test_graph_replays_match_eager(kvarn):
 
     # the same step, captured once
     kc, vc = fresh_caches()
-    qc = kvarn.Cache.empty(B, H, 128, kvarn.K, device=dev)
-    ws = kvarn.decode_workspace(B, Hq, cap, device=dev)
+    qc = kvarn.Cache.empty(B, H, 128, kvarn.K, device=dev, head_dim=D)
+    ws = kvarn.decode_workspace(B, Hq, cap, device=dev, head_dim=D)
     nk, nv, q = nks[0].clone(), nvs[0].clone(), qs[0].clone()
     pos = torch.full((B,), T, dtype=torch.int32, device=dev)
     lens = pos + 1
-    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
