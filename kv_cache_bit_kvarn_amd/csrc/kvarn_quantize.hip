@@ -29,13 +29,15 @@
 //      1/c^2 and the 16 lanes of a row combine their sums (two lane-pair
 //      exchanges that halve the values, then two rotations), with no LDS and
 //      no barrier. Column step: each lane weighs its 4 tokens of each of its
-//      NT channels by 1/r^2 and writes the NT partial sums to LDS unreduced;
-//      after a barrier wave w adds up channels (D/8) w + [0, D/8) only
-//      (512/D lanes per channel, each taking D/16 of its 32 partials, the
-//      lanes meeting by DPP adds), writes 1/c^2 to a shared D-entry array
-//      and, after a second barrier, every lane reads the NT values of its
-//      channels. (Each wave adding up all channels itself would need one
-//      barrier less but three times the VALU instructions.)
+//      NT channels by 1/r^2, the four lane rows of the wave add up their
+//      sums by two lane-swap steps (each halving the values a lane holds),
+//      and the wave writes one partial per channel to LDS; after a barrier
+//      wave w adds up channels (D/8) w + [0, D/8) only (512/D lanes per
+//      channel, each taking D/64 of its 8 partials, the lanes meeting by DPP
+//      adds), writes 1/c^2 to a shared D-entry array and, after a second
+//      barrier, every lane reads the NT values of its channels. (Each wave
+//      adding up all channels itself would need one barrier less but three
+//      times the VALU instructions.)
 //   4. per-token range step and 2-bit codes (v_cvt_pk_u8_f32): K codes of
 //      four adjacent channels (four adjacent lanes) merge by a shift and an
 //      OR across the quad, pass through a small per-wave LDS area and leave
@@ -84,15 +86,15 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // (ds_read2st64) of consecutive lanes reads consecutive dwords. The areas
 // below are laid out for that model (for D = 128; the other head sizes use
 // the same strides):
-//  * cpart: the column step's partial sums, cp[nt] of lane l of wave u at
-//    cpart[CP_PLANE nt + CP_WAVE u + l]. A wave's write of one nt covers 64
-//    consecutive words. Channel 16 nt + n has 32 partials (waves u, rows r)
-//    at CP_PLANE nt + CP_WAVE u + 16 r + n; wave w adds up channels
-//    (D/8) w + l / LPC (LPC = 512/D lanes each), lane l taking partials
-//    (l % LPC) 32/LPC + [0, 32/LPC) in (u, r) order. For D = 128 that is
-//    plane w, waves 2 (l % 4) + s (s < 2), and the 72-word wave stride puts
-//    the four lanes of a quad 144 words (16 banks) apart, so neither side
-//    has bank conflicts;
+//  * cpart: the column step's partial sums, one per (wave u, channel c) at
+//    cpart[CP_WAVE u + cp_index(c)], written by lane row g of the wave for
+//    its channels [g D/4, (g + 1) D/4). Wave w adds up channels
+//    (D/8) w + l / LPC (LPC = 512/D lanes each), lane l taking waves
+//    (l % LPC) PPW + [0, PPW) (PPW = 8 / LPC). cp_index moves the D/4
+//    channels of lane row g by 16 g words (D = 128, 256), so that the two
+//    lane rows of a half-wave write distinct banks, and the wave strides
+//    (72, 200, 312 words) put the 64 reading lanes of a wave on distinct
+//    banks;
 //  * ctot: the per-channel result of a column step (1/c^2, and 1/c after the
 //    last one), written by the lanes that reduced the channel and read by
 //    every lane for channels 16 nt + n (the four lane rows of a wave read the
@@ -107,8 +109,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 //    block orders the writes before the reads and the reads before the
 //    buffer's next writes.
 constexpr int VST_ROW = 9;
-constexpr int CP_WAVE = 72;
-constexpr int CP_PLANE = kWaves * CP_WAVE;
 
 // Sizes of the kernel for head size DQ.
 template <int DQ>
@@ -118,10 +118,16 @@ struct QDims {
   static constexpr int KK = DQ / 32;        // 32-channel input pieces (MFMA steps)
   static constexpr int CPT = 4 * NT;        // values per lane: 4 tokens x NT channels
   static constexpr int LPC = 512 / DQ;      // lanes per channel in the column-step sum
-  static constexpr int PPL = 32 / LPC;      // partial sums each of them adds
+  static constexpr int PPW = 8 / LPC;       // partial sums (waves) each of them adds
+  static constexpr int CP_WAVE = DQ == 64 ? 72 : DQ == 128 ? 200 : 312;  // cpart wave stride
   static constexpr int KST_ROW = 4 * NT + 4;  // K staging words per group of 4 tokens
   static constexpr int CHUNK_CODE_BYTES = T * DQ / 4;
 };
+// cpart word of channel c within a wave's partials
+template <int DQ>
+__device__ __forceinline__ int cp_index(int c) {
+  return DQ == 64 ? c : c + 16 * (c / (DQ / 4));
+}
 // Waves per SIMD the registers allow: three workgroups per CU for 64
 // channels (at most 85 registers; 14% faster than two), two for 128, one
 // for 256 (y and P alone take 128 registers there).
@@ -131,7 +137,7 @@ __host__ __device__ constexpr int quant_waves_per_simd(int dq) {
 
 template <int DQ>
 struct QuantSmem {
-  alignas(16) float cpart[QDims<DQ>::NT * CP_PLANE];
+  alignas(16) float cpart[kWaves * QDims<DQ>::CP_WAVE];
   alignas(16) float ctot[DQ];
   alignas(16) uint32_t kst[kWaves][4 * QDims<DQ>::KST_ROW];
   alignas(16) uint32_t vst[2][DQ * VST_ROW];
@@ -143,6 +149,12 @@ struct QuantSmem {
 };
 
 __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+// 1 / max(x, smallest normal float) for x >= 0, the maximum taken on the bit
+// patterns (non-negative floats order as their patterns do as unsigned
+// integers), which needs no NaN canonicalization
+__device__ __forceinline__ float rcp_floor(float x) {
+  return __builtin_amdgcn_rcpf(__uint_as_float(max(__float_as_uint(x), __float_as_uint(kTiny))));
+}
 
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
@@ -383,7 +395,7 @@ template <int DQ, bool kF32, bool kRotate, bool kPositions>
 __global__ __launch_bounds__(kThreads, quant_waves_per_simd(DQ)) void quantize_block_kernel(
     QuantArgs a) {
   using Q = QDims<DQ>;
-  constexpr int NT = Q::NT, KK = Q::KK, CPT = Q::CPT, LPC = Q::LPC, PPL = Q::PPL;
+  constexpr int NT = Q::NT, KK = Q::KK, CPT = Q::CPT, LPC = Q::LPC, PPW = Q::PPW;
   __shared__ QuantSmem<DQ> sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -562,37 +574,50 @@ __global__ __launch_bounds__(kThreads, quant_waves_per_simd(DQ)) void quantize_b
           const int src = 20 * ((t >> 4) & 3) + tsel(t);
           tot = (kRotate ? (float)DQ : 1.f) * __shfl(d, src, 64);
         }
-        const float vt = rcp(fmaxf(tot, kTiny));
+        const float vt = rcp_floor(tot);
         v[0] = token_value<0>(vt); v[1] = token_value<1>(vt);
         v[2] = token_value<2>(vt); v[3] = token_value<3>(vt);
       }
       for (int it = 0;;) {
         __builtin_amdgcn_s_setprio(2);
         // column step: the lane's NT partial sums (its 4 tokens of channels
-        // 16 nt + n) go to LDS; the LPC lanes of channel ch then add up its
-        // 32 partials, PPL each, and meet by DPP adds
+        // 16 nt + n), added up over the wave's four lane rows, go to LDS;
+        // the LPC lanes of channel ch then add up its 8 partials (one per
+        // wave), PPW each, and meet by DPP adds
         float cp[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
           cp[nt] = fmaf(p[4 * nt + 3], v[3],
                         fmaf(p[4 * nt + 2], v[2], fmaf(p[4 * nt + 1], v[1], p[4 * nt] * v[0])));
         {
-          float *pw = sm.cpart + CP_WAVE * wv + lane;
+          // rows g and g ^ 2 (half-wave swap), then g and g ^ 1 (row swap):
+          // each swap hands over the half of the values the lane does not
+          // keep, so lane row g is left with channels 16 (g NT/4 + k) + n,
+          // k < NT/4, summed over the wave's 16 tokens
+          constexpr int NH = NT / 2, NQ = NT / 4;
+          float h[NH];
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) pw[CP_PLANE * nt] = cp[nt];
+          for (int j = 0; j < NH; ++j) {
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(cp[j]),
+                                                            __float_as_uint(cp[j + NH]), false, false);
+            h[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+          }
+          float *pw = sm.cpart + Q::CP_WAVE * wv;
+#pragma unroll
+          for (int k = 0; k < NQ; ++k) {
+            const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(h[k]),
+                                                            __float_as_uint(h[k + NQ]), false, false);
+            pw[cp_index<DQ>(16 * (g * NQ + k) + n)] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+          }
         }
         lds_barrier();
         __builtin_amdgcn_s_setprio(3);
         {
-          const float *pr = sm.cpart + CP_PLANE * (ch >> 4) + (ch & 15);
-          const int sub = lane % LPC;
-          float q[PPL];
+          const float *pr = sm.cpart + Q::CP_WAVE * ((lane % LPC) * PPW) + cp_index<DQ>(ch);
+          float q[PPW];
 #pragma unroll
-          for (int i = 0; i < PPL; ++i) {
-            const int gp = sub * PPL + i;  // partial (wave gp / 4, row gp % 4)
-            q[i] = pr[CP_WAVE * (gp >> 2) + 16 * (gp & 3)];
-          }
-          cm = tree_sum<PPL>(q);
+          for (int i = 0; i < PPW; ++i) q[i] = pr[Q::CP_WAVE * i];  // wave (lane % LPC) PPW + i
+          cm = tree_sum<PPW>(q);
           cm += dpp_f<kXor1>(cm);
           if constexpr (LPC >= 4) cm += dpp_f<kXor2>(cm);
           if constexpr (LPC >= 8) cm += lane_xor<4>(cm);
@@ -601,7 +626,7 @@ __global__ __launch_bounds__(kThreads, quant_waves_per_simd(DQ)) void quantize_b
         if (++it == a.iters) break;
         // 1/c^2 of channel ch (its LPC lanes write the same value), then
         // every lane takes channels 16 nt + n
-        sm.ctot[ch] = rcp(fmaxf(cm, kTiny));
+        sm.ctot[ch] = rcp_floor(cm);
         lds_barrier();
         {
           const float *pg = sm.ctot + n;
@@ -620,7 +645,7 @@ __global__ __launch_bounds__(kThreads, quant_waves_per_simd(DQ)) void quantize_b
         }
         __builtin_amdgcn_s_setprio(3);
         const float tot = row_reduce4<false>(s, n);
-        const float vt = rcp(fmaxf(tot, kTiny));
+        const float vt = rcp_floor(tot);
         v[0] = token_value<0>(vt); v[1] = token_value<1>(vt);
         v[2] = token_value<2>(vt); v[3] = token_value<3>(vt);
       }
