@@ -3,16 +3,16 @@
 
 One step = the whole path over one batch of synthetic input:
   quantize K and V of every layer (all 128-token chunks), then, layer by
-  layer, append one new token to K and V and run one decode-attention step
-  over the 2-bit cache.
+  layer, append one new token to K and V (one launch for both) and run one
+  decode-attention step over the 2-bit cache.
 Quantizing every layer before the first decode keeps each decode reading a
 cache that was written more than 256 MB earlier: the 256 MB memory-side cache
 (MALL) holds none of it, so every reported decode time is an HBM time.
 (The Llama-3-8B-shaped workload quantizes its cache once, before timing, and
 its step is append + decode per layer: steady-state decoding. Its step is
 captured once in a HIP graph and the replays are timed: the GPU work per
-layer (two appends, one decode) is shorter than the host's per-call launch
-overhead, so eager launches would leave the GPU waiting on the host.)
+layer (one K+V append, one decode) is shorter than the host's per-call
+launch overhead, so eager launches would leave the GPU waiting on the host.)
 
 Default workload: Qwen3-4B-shaped full cache (36 layers, batch 8, 8 kv-heads
 x 128, 32768 tokens, 32 query heads). The same JSON line also carries the
@@ -237,8 +237,7 @@ def main():
                     kv.quantize(x, c, iters=args.iters, stream=stream)
         for layer in range(L):
             kc, vc = caches[layer]
-            for n, c in ((news[layer][0], kc), (news[layer][1], vc)):
-                kv.append(n, pos, c, stream=stream)
+            kv.append_kv(news[layer][0], news[layer][1], pos, kc, vc, stream=stream)
             kv.decode_attn(qs[layer], kc, vc, lens, out=out, workspace=ws, stream=stream)
 
     log(f"[bench] warmup {args.warmup} steps")
@@ -263,8 +262,7 @@ def main():
         def appends():
             for layer in range(L):
                 kc, vc = caches[layer]
-                kv.append(news[layer][0], pos_g, kc)
-                kv.append(news[layer][1], pos_g, vc)
+                kv.append_kv(news[layer][0], news[layer][1], pos_g, kc, vc)
 
         def decodes(layer=None):
             for la in (range(L) if layer is None else [layer]):
@@ -274,8 +272,7 @@ def main():
         def phase2():
             for layer in range(L):
                 kc, vc = caches[layer]
-                kv.append(news[layer][0], pos_g, kc)
-                kv.append(news[layer][1], pos_g, vc)
+                kv.append_kv(news[layer][0], news[layer][1], pos_g, kc, vc)
                 decodes(layer)
 
         torch.cuda.synchronize()
@@ -317,7 +314,7 @@ def main():
         v = [a.elapsed_time(b_) * 1e3 for a, b_ in rec["quantize"]]
         q_us = sum(v) / len(v)
         d_us = replay_us(graphs["decode"], max(args.steps, 5)) / L
-        a_us = replay_us(graphs["append"], max(args.steps, 5)) / (2 * L)
+        a_us = replay_us(graphs["append"], max(args.steps, 5)) / L
         del graphs
     elts_per_quant = B * Hkv * T * D
     q_launches = 0 if steady else 2 * L
@@ -378,14 +375,15 @@ def main():
             "note": "context only, not a like-for-like comparison: here the whole 36-layer "
                     "cache of batch 8 x 32768 tokens is quantized in every step"}
     res["decode"] = dec
-    res["append"] = {"us_per_launch": round(a_us, 2), "launches_per_step": 2 * L}
+    res["append"] = {"us_per_launch": round(a_us, 2), "launches_per_step": L,
+                     "kernel": "append_kv_kernel: a layer's new K and V token in one launch"}
 
     cpu_inputs = None
     if not args.no_cpu_baseline and not steady:
         cpu_inputs = cpu_sample(args, wl, xs, news, qs)
     if not steady:
         res["host_us_per_call"] = host_cost(
-            kv, torch, stream, xs[0][0], caches[0], news[0][0], qs[0], out, ws,
+            kv, torch, stream, xs[0][0], caches[0], news[0], qs[0], out, ws,
             torch.full((B,), T + 1, dtype=torch.int32, device=dev),
             torch.full((B,), T, dtype=torch.int32, device=dev))
     if not args.no_ablations and not steady:
@@ -563,12 +561,13 @@ def build_steady_caches(kv, kvgen, torch, wl, caches, iters, dev):
 def steady_graph_timing(kv, torch, warmup, steps, caches, news, qs, out, ws, L, B, T):
     """Steady-state decoding timed on HIP-graph replays (torch.cuda.CUDAGraph).
 
-    G_step holds one step: for every layer, append K and V at pos, decode over
-    lens; then pos and lens advance by one, so each replay is the next step.
-    G_dec holds the L decodes alone and G_app the 2 L appends alone (at a fixed
-    position, so replaying them rewrites the same slots); their replays give
-    the per-launch times. The positions continue from `warmup` eager steps.
-    Returns (ms per step, us per append, us per decode)."""
+    G_step holds one step: for every layer, append K and V at pos (one
+    launch), decode over lens; then pos and lens advance by one, so each replay
+    is the next step. G_dec holds the L decodes alone and G_app the L appends
+    alone (at a fixed position, so replaying them rewrites the same slots);
+    their replays give the per-launch times. The positions continue from
+    `warmup` eager steps. Returns (ms per step, us per K+V append launch, us
+    per decode)."""
     dev = out.device
     pos = torch.full((B,), T + warmup, dtype=torch.int32, device=dev)
     lens = pos + 1
@@ -576,8 +575,7 @@ def steady_graph_timing(kv, torch, warmup, steps, caches, news, qs, out, ws, L, 
 
     def layer_appends(layer):
         kc, vc = caches[layer]
-        kv.append(news[layer][0], pos, kc)
-        kv.append(news[layer][1], pos, vc)
+        kv.append_kv(news[layer][0], news[layer][1], pos, kc, vc)
 
     def layer_decode(layer):
         kc, vc = caches[layer]
@@ -614,7 +612,7 @@ def steady_graph_timing(kv, torch, warmup, steps, caches, news, qs, out, ws, L, 
     ms_step = timed(g_step, steps)
     reps = max(steps, 10)
     d_us = timed(g_dec, reps) * 1e3 / L
-    a_us = timed(g_app, reps) * 1e3 / (2 * L)
+    a_us = timed(g_app, reps) * 1e3 / L
     return ms_step, a_us, d_us
 
 
@@ -638,8 +636,8 @@ def steady_workload(kv, kvgen, torch, wl, args, dev):
     for i in range(warm):
         pos = torch.full((B,), T + i, dtype=torch.int32, device=dev)
         for layer in range(L):
-            kv.append(news[layer][0], pos, caches[layer][0])
-            kv.append(news[layer][1], pos, caches[layer][1])
+            kv.append_kv(news[layer][0], news[layer][1], pos, caches[layer][0],
+                         caches[layer][1])
             kv.decode_attn(qs[layer], caches[layer][0], caches[layer][1], pos + 1, out=out,
                            workspace=ws)
     torch.cuda.synchronize()
@@ -647,10 +645,11 @@ def steady_workload(kv, kvgen, torch, wl, args, dev):
                                               L, B, T)
     nb = decode_bytes(T + warm + steps + 1, B, Hkv, Hq)
     res = {"config": {"layers": L, "batch": B, "kv_heads": Hkv, "q_heads": Hq, "tokens": T,
-                      "step": "append K, V + decode per layer (HIP graph replays)"},
+                      "step": "append K and V (one launch) + decode per layer (HIP graph "
+                              "replays)"},
            "step_ms": round(ms_step, 4), "step_tokens_per_s": round(B / (ms_step / 1e3), 1),
            "decode_tokens_per_s": round(B / (L * d_us * 1e-6), 1),
-           "decode_us_per_launch": round(d_us, 2), "append_us_per_launch": round(a_us, 2),
+           "decode_us_per_launch": round(d_us, 2), "append_kv_us_per_launch": round(a_us, 2),
            "decode": hbm_entry(nb, d_us)}
     del caches, news, qs, out, ws
     return res
@@ -678,8 +677,7 @@ def stress_workload(kv, kvgen, torch, wl, args, dev, stream):
              lambda: kv.quantize(xv, vc, iters=args.iters, stream=stream)]
     for f in quant:
         f()
-    kv.append(nk, pos, kc, stream=stream)
-    kv.append(nv, pos, vc, stream=stream)
+    kv.append_kv(nk, nv, pos, kc, vc, stream=stream)
     kv.decode_attn(q, kc, vc, lens, out=out, workspace=ws, stream=stream)
     torch.cuda.synchronize()
     q_us = timed_events(torch, stream, quant * 3)
@@ -700,14 +698,16 @@ def stress_workload(kv, kvgen, torch, wl, args, dev, stream):
     return res
 
 
-def host_cost(kv, torch, stream, x, cache_pair, new_tok, q, out, ws, lens, pos, n: int = 200):
+def host_cost(kv, torch, stream, x, cache_pair, new_toks, q, out, ws, lens, pos,
+              n: int = 200):
     """Host microseconds per call, enqueue only: wall time of n back-to-back
     calls with no synchronization inside (the GPU work queues up behind
-    them), for the Python binding's quantize, append and decode, and for
-    decode through the C ABI directly with its arguments marshalled once
-    (the library's own host share)."""
+    them), for the Python binding's quantize, append (one cache, and K and V
+    in one call) and decode, and for decode through the C ABI directly with
+    its arguments marshalled once (the library's own host share)."""
     import ctypes
     kc, vc = cache_pair
+    new_tok, new_tok_v = new_toks
     lib = kv.load()
     kd, vd = kc.desc(), vc.desc()
     sh = stream.cuda_stream
@@ -717,6 +717,7 @@ def host_cost(kv, torch, stream, x, cache_pair, new_tok, q, out, ws, lens, pos, 
     calls = {
         "quantize_binding": lambda: kv.quantize(x, kc, stream=stream),
         "append_binding": lambda: kv.append(new_tok, pos, kc, stream=stream),
+        "append_kv_binding": lambda: kv.append_kv(new_tok, new_tok_v, pos, kc, vc, stream=stream),
         "decode_binding": lambda: kv.decode_attn(q, kc, vc, lens, out=out, workspace=ws,
                                                  stream=stream),
         "decode_c_abi": lambda: lib.kvarn_decode_attn_ex(*raw),
@@ -840,17 +841,17 @@ def next_rows_workload(kv, kvgen, torch, args, dev, stream):
             qm.append(sum(qu) / len(qu))
             dm.append(sum(du) / len(du))
         qm, dm = sorted(qm)[1], sorted(dm)[1]
-        # one-token appends of K and V, as in the step: graph replays of 72
-        # launches (the layers' appends nine times over; each rewrites the
-        # same slot), since each launch is shorter than the host's cost per
-        # call and a replay's own start-up is spread over as many launches as
-        # in the step
+        # one-token appends of K and V in one launch, as in the step: graph
+        # replays of 36 launches (the layers' appends nine times over; each
+        # rewrites the same slots), since each launch is shorter than the
+        # host's cost per call and a replay's own start-up is spread over as
+        # many launches as in the step
         tok = [kvgen.new_tokens(5, l, kind, B, H, 0.5, device=dev, head_dim=dh)
                for l in range(L) for kind in (kv.K, kv.V)]
         pos = torch.full((B,), T, dtype=torch.int32, device=dev)
-        am = graph_us(torch, lambda: [kv.append(tok[2 * l + k], pos, caches[l][k])
-                                      for _ in range(9) for l in range(L)
-                                      for k in range(2)]) / (9 * 2 * L)
+        am = graph_us(torch, lambda: [kv.append_kv(tok[2 * l], tok[2 * l + 1], pos,
+                                                   caches[l][0], caches[l][1])
+                                      for _ in range(9) for l in range(L)]) / (9 * L)
         elts = B * H * T * dh
         qbytes = (2.0 + 0.25 + 4.0 / dh + 4.0 / CHUNK) * elts
         dbytes = (dh / 2 + 8 + dh / 16) * (T + 1) * B * H + B * Hq * dh * 6
@@ -858,9 +859,10 @@ def next_rows_workload(kv, kvgen, torch, args, dev, stream):
             "config": {"batch": B, "kv_heads": H, "q_heads": Hq, "tokens": T, "head_dim": dh},
             "quantize_us_per_launch": round(qm, 2), "quantize": hbm_entry(qbytes, qm),
             "decode_us_per_launch": round(dm, 2), "decode": hbm_entry(dbytes, dm),
-            "append_us_per_launch": round(am, 2),
+            "append_kv_us_per_launch": round(am, 2),
             "note": "quantize and decode: the matrix-core kernels shared by every head size; "
-                    "append: the generic one-token kernel (latency-bound, no bandwidth claim)"}
+                    "append: one launch for a layer's K and V token (latency-bound, no "
+                    "bandwidth claim)"}
         del xs, qcs, caches, q, out, ws, tok
         torch.cuda.empty_cache()
     return res

@@ -190,6 +190,25 @@ int kvarn_append_ex(const void *x, int32_t dtype, const int32_t *positions,
                     uint32_t flags, const kvarn_cache *dst, void *stream);
 
 /*
+ * kvarn_append_kv -- one decoding step's new K and V tokens in one launch
+ * (rndamp article, "The Problem": both caches grow by one token per step).
+ * The result is exactly that of kvarn_append_ex(xk, ..., k) followed by
+ * kvarn_append_ex(xv, ..., v): the two caches are disjoint, and each (b, h)
+ * of each cache is coded by one wave as there.
+ *
+ * xk, xv     (device) [batch][kv_heads][D] each, dtype `dtype`, contiguous,
+ *            16-byte aligned.
+ * positions  (device) int32 [batch], shared by both caches.
+ * flags      KVARN_FLAG_NO_ROTATE only.
+ * k, v       a K cache and a V cache of the same batch, kv_heads, capacity
+ *            and head size (else KVARN_ERR_DTYPE or KVARN_ERR_SHAPE).
+ * Errors as for kvarn_append; on error nothing is enqueued.
+ */
+int kvarn_append_kv(const void *xk, const void *xv, int32_t dtype,
+                    const int32_t *positions, uint32_t flags,
+                    const kvarn_cache *k, const kvarn_cache *v, void *stream);
+
+/*
  * kvarn_append_rebalance -- append with re-balancing at chunk close, the
  * alternative to kvarn_append's frozen column scales (the pages do not fix
  * how a new token enters the cache; the rndamp article's "The Problem" only

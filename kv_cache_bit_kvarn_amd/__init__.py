@@ -29,6 +29,7 @@ DT_BF16, DT_F32 = 0, 1
 K, V = 0, 1
 
 EXPORTED = ("kvarn_quantize", "kvarn_quantize_ex", "kvarn_append", "kvarn_append_ex",
+            "kvarn_append_kv",
             "kvarn_decode_workspace_bytes", "kvarn_decode_workspace_bytes_ex",
             "kvarn_decode_attn", "kvarn_decode_attn_ex",
             "kvarn_decode_attn_noalloc", "kvarn_append_rebalance", "kvarn_token_error",
@@ -80,6 +81,8 @@ def load(path: str | None = None):
     L.kvarn_quantize_ex.restype = ctypes.c_int
     L.kvarn_append_ex.argtypes = [vp, i32, vp, u32, cd, vp]
     L.kvarn_append_ex.restype = ctypes.c_int
+    L.kvarn_append_kv.argtypes = [vp, vp, i32, vp, u32, cd, cd, vp]
+    L.kvarn_append_kv.restype = ctypes.c_int
     L.kvarn_decode_attn_ex.argtypes = [vp, i32, i32, cd, cd, vp, ctypes.c_float, u32, vp, i32,
                                        vp, ctypes.c_size_t, vp]
     L.kvarn_decode_attn_ex.restype = ctypes.c_int
@@ -235,6 +238,33 @@ def append(x: torch.Tensor, positions: torch.Tensor, cache: Cache, stream=None,
     st = load().kvarn_append_ex(x.data_ptr(), _dtype_code(x), positions.data_ptr(), flags,
                                 ctypes.byref(d), _stream(stream, dev))
     _raise(st, "kvarn_append")
+
+
+def append_kv(xk: torch.Tensor, xv: torch.Tensor, positions: torch.Tensor, k: Cache, v: Cache,
+              stream=None, flags: int = 0) -> None:
+    """append(xk, positions, k) and append(xv, positions, v) in one launch:
+    xk, xv [B, H, D] of one dtype, k a K cache and v a V cache of one shape.
+    flags: FLAG_NO_ROTATE."""
+    if k.kind != K or v.kind != V:
+        raise ValueError("append_kv takes a K cache and a V cache")
+    if (k.batch, k.kv_heads, k.capacity, k.head_dim) != (v.batch, v.kv_heads, v.capacity,
+                                                          v.head_dim):
+        raise ValueError("append_kv: the K and V caches differ in shape")
+    for x in (xk, xv):
+        if x.dim() != 3 or tuple(x.shape) != (k.batch, k.kv_heads, k.head_dim) or \
+                not x.is_contiguous():
+            raise ValueError("xk and xv must be contiguous [B, H, D] matching the caches")
+    if xk.dtype != xv.dtype:
+        raise ValueError("xk and xv must have one dtype")
+    if positions.dtype != torch.int32 or positions.numel() != k.batch or \
+            not positions.is_contiguous():
+        raise ValueError("positions must be contiguous int32 [B]")
+    dk, dv = k.desc(), v.desc()
+    dev = _on_device("append_kv", xk, xv, positions, k.codes, v.codes)
+    st = load().kvarn_append_kv(xk.data_ptr(), xv.data_ptr(), _dtype_code(xk),
+                                positions.data_ptr(), flags, ctypes.byref(dk), ctypes.byref(dv),
+                                _stream(stream, dev))
+    _raise(st, "kvarn_append_kv")
 
 
 def append_window(batch: int, kv_heads: int, dtype=torch.bfloat16, device="cuda",

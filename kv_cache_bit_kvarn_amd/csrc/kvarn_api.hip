@@ -191,6 +191,43 @@ int kvarn_append(const void *x, int32_t dtype, const int32_t *positions,
   return kvarn_append_ex(x, dtype, positions, 0u, dst, stream);
 }
 
+int kvarn_append_kv(const void *xk, const void *xv, int32_t dtype, const int32_t *positions,
+                    uint32_t flags, const kvarn_cache *k, const kvarn_cache *v, void *stream) {
+  if (flags & ~(uint32_t)KVARN_FLAG_NO_ROTATE) return KVARN_ERR_FLAGS;
+  if (!xk || !xv || !positions) return KVARN_ERR_NULL;
+  int st = check_cache(k);
+  if (st != KVARN_OK) return st;
+  st = check_cache(v);
+  if (st != KVARN_OK) return st;
+  if (k->kind != KVARN_K || v->kind != KVARN_V) return KVARN_ERR_DTYPE;
+  if (!dtype_size(dtype)) return KVARN_ERR_DTYPE;
+  if (k->batch != v->batch || k->kv_heads != v->kv_heads || k->capacity != v->capacity ||
+      cache_dim(k) != cache_dim(v))
+    return KVARN_ERR_SHAPE;
+  if (!aligned16(xk) || !aligned16(xv)) return KVARN_ERR_ALIGN;
+  if ((int64_t)k->batch * k->kv_heads > INT_MAX) return KVARN_ERR_SHAPE;
+  if (k->batch == 0 || k->kv_heads == 0 || k->capacity == 0) return KVARN_OK;
+  AppendArgs a[2];
+  const kvarn_cache *c[2] = {k, v};
+  const void *x[2] = {xk, xv};
+  for (int i = 0; i < 2; ++i) {
+    a[i].x = x[i];
+    a[i].dtype = dtype;
+    a[i].pos = positions;
+    a[i].batch = c[i]->batch;
+    a[i].heads = c[i]->kv_heads;
+    a[i].capacity = c[i]->capacity;
+    a[i].kind = c[i]->kind;
+    a[i].flags = flags;
+    a[i].codes = c[i]->codes;
+    a[i].row_scale = c[i]->row_scale;
+    a[i].col_scale = c[i]->col_scale;
+    a[i].window = nullptr;
+    a[i].head_dim = cache_dim(c[i]);
+  }
+  return from_hip(launch_append_kv(a[0], a[1], static_cast<hipStream_t>(stream)));
+}
+
 int kvarn_append_rebalance(const void *x, int32_t dtype, const int32_t *positions, void *window,
                            int32_t iters, uint32_t flags, const kvarn_cache *dst, void *stream) {
   if (flags & ~(uint32_t)KVARN_FLAG_NO_ROTATE) return KVARN_ERR_FLAGS;

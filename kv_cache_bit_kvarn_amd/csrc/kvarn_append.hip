@@ -20,12 +20,11 @@ __device__ __forceinline__ uint32_t or_quad(uint32_t c) {
   return c | __float_as_uint(lane_xor<2>(__uint_as_float(c)));
 }
 
-// kRotate = false: the token is already rotated (rotation absorbed into the
-// model's weights).
+// One token of (sequence, kv-head) bh. kRotate = false: the token is already
+// rotated (rotation absorbed into the model's weights).
 template <int DA, bool kF32, bool kRotate>
-__global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
+__device__ __forceinline__ void append_token(const AppendArgs &a, int bh) {
   constexpr int KD = DA / 64;  // channels per lane
-  const int bh = blockIdx.x;
   const int b = bh / a.heads;
   const int lane = threadIdx.x;
   const int pos = a.pos[b];
@@ -136,6 +135,20 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
   }
 }
 
+template <int DA, bool kF32, bool kRotate>
+__global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
+  append_token<DA, kF32, kRotate>(a, blockIdx.x);
+}
+
+// K and V of the same step in one launch: blockIdx.y picks the cache.
+template <int DA, bool kF32, bool kRotate>
+__global__ __launch_bounds__(64) void append_kv_kernel(AppendArgs k, AppendArgs v) {
+  if (blockIdx.y == 0)
+    append_token<DA, kF32, kRotate>(k, blockIdx.x);
+  else
+    append_token<DA, kF32, kRotate>(v, blockIdx.x);
+}
+
 template <int DA>
 hipError_t launch_append_da(const AppendArgs &a, hipStream_t s) {
   const int blocks = a.batch * a.heads;
@@ -154,7 +167,34 @@ hipError_t launch_append_da(const AppendArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int DA>
+hipError_t launch_append_kv_da(const AppendArgs &k, const AppendArgs &v, hipStream_t s) {
+  const dim3 grid(k.batch * k.heads, 2);
+  const bool rot = !(k.flags & KVARN_FLAG_NO_ROTATE);
+  if (k.dtype == KVARN_DT_F32) {
+    if (rot)
+      hipLaunchKernelGGL((append_kv_kernel<DA, true, true>), grid, dim3(64), 0, s, k, v);
+    else
+      hipLaunchKernelGGL((append_kv_kernel<DA, true, false>), grid, dim3(64), 0, s, k, v);
+  } else {
+    if (rot)
+      hipLaunchKernelGGL((append_kv_kernel<DA, false, true>), grid, dim3(64), 0, s, k, v);
+    else
+      hipLaunchKernelGGL((append_kv_kernel<DA, false, false>), grid, dim3(64), 0, s, k, v);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_append_kv(const AppendArgs &k, const AppendArgs &v, hipStream_t s) {
+  if (k.batch * k.heads == 0) return hipSuccess;
+  switch (k.head_dim) {
+    case 64: return launch_append_kv_da<64>(k, v, s);
+    case 256: return launch_append_kv_da<256>(k, v, s);
+    default: return launch_append_kv_da<128>(k, v, s);
+  }
+}
 
 hipError_t launch_append(const AppendArgs &a, hipStream_t s) {
   if (a.batch * a.heads == 0) return hipSuccess;

@@ -140,6 +140,8 @@ struct AppendArgs {
                    // is also stored, as given, at slot pos % 128
 };
 hipError_t launch_append(const AppendArgs &a, hipStream_t s);
+// k and v: the same batch, heads, capacity, head size, dtype and flags
+hipError_t launch_append_kv(const AppendArgs &k, const AppendArgs &v, hipStream_t s);
 
 struct DecodeArgs {
   const void *q;

@@ -32,6 +32,13 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t) {
   ++g_calls;
   return g_result;
 }
+static AppendArgs g_append_kv[2];
+hipError_t launch_append_kv(const AppendArgs &k, const AppendArgs &v, hipStream_t) {
+  g_append_kv[0] = k;
+  g_append_kv[1] = v;
+  ++g_calls;
+  return g_result;
+}
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t) {
   g_decode = a;
   ++g_calls;
@@ -159,6 +166,29 @@ static void check_append() {
   const QuantArgs &a = g_quant[0];
   CHECK(a.pos == P(0x50000) && a.x == P(0x60000) && a.chunks == 1 && a.nblocks == 6u);
   CHECK(a.st == 128 && a.sh == 128 * 128 && a.sb == 2 * 128 * 128 && a.iters == 2);
+
+  // K and V in one launch
+  kvarn_cache k = cache(3, 2, 256, KVARN_K), v = c;
+  v.codes = static_cast<uint8_t *>(P(0x70000));
+  v.row_scale = static_cast<float *>(P(0x74000));
+  int32_t *pos = static_cast<int32_t *>(P(0x50000));
+  g_calls = 0;
+  CHECK(kvarn_append_kv(P(0x40000), nullptr, KVARN_DT_BF16, pos, 0u, &k, &v, nullptr) == KVARN_ERR_NULL);
+  CHECK(kvarn_append_kv(P(0x40000), P(0x48000), KVARN_DT_BF16, pos, 0u, &v, &k, nullptr) == KVARN_ERR_DTYPE);
+  kvarn_cache v2 = cache(3, 2, 512, KVARN_V);
+  CHECK(kvarn_append_kv(P(0x40000), P(0x48000), KVARN_DT_BF16, pos, 0u, &k, &v2, nullptr) == KVARN_ERR_SHAPE);
+  CHECK(kvarn_append_kv(P(0x40000), P(0x48000), KVARN_DT_BF16, pos, 2u, &k, &v, nullptr) == KVARN_ERR_FLAGS);
+  CHECK(g_calls == 0);
+  CHECK(kvarn_append_kv(P(0x40000), P(0x48000), KVARN_DT_F32, pos, KVARN_FLAG_NO_ROTATE, &k, &v, nullptr) ==
+        KVARN_OK);
+  CHECK(g_calls == 1);
+  CHECK(g_append_kv[0].x == P(0x40000) && g_append_kv[1].x == P(0x48000));
+  CHECK(g_append_kv[0].kind == KVARN_K && g_append_kv[1].kind == KVARN_V);
+  CHECK(g_append_kv[0].codes == k.codes && g_append_kv[1].codes == v.codes);
+  CHECK(g_append_kv[0].pos == pos && g_append_kv[1].pos == pos);
+  CHECK(g_append_kv[0].dtype == KVARN_DT_F32 && g_append_kv[1].flags == KVARN_FLAG_NO_ROTATE);
+  CHECK(g_append_kv[0].batch == 3 && g_append_kv[0].heads == 2 && g_append_kv[1].capacity == 256);
+  CHECK(g_append_kv[0].window == nullptr && g_append_kv[1].window == nullptr);
 }
 
 static void check_decode() {

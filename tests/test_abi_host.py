@@ -91,6 +91,28 @@ def test_append_validation(lib):
     assert lib.kvarn_append(A, 0, B, ctypes.byref(empty), None) == kv.OK
 
 
+def test_append_kv_validation(lib):
+    k, v = _cache(kind=kv.K), _cache(kind=kv.V)
+
+    def call(xk=A, xv=C, dtype=0, pos=B, flags=0, kc=k, vc=v):
+        return lib.kvarn_append_kv(xk, xv, dtype, pos, flags,
+                                   ctypes.byref(kc) if kc is not None else None,
+                                   ctypes.byref(vc) if vc is not None else None, None)
+    assert call(xk=None) == kv.ERR_NULL
+    assert call(xv=None) == kv.ERR_NULL
+    assert call(pos=None) == kv.ERR_NULL
+    assert call(kc=None) == kv.ERR_NULL
+    assert call(vc=None) == kv.ERR_NULL
+    assert call(flags=kv.FLAG_ONE_SCALE) == kv.ERR_FLAGS
+    assert call(dtype=3) == kv.ERR_DTYPE
+    assert call(kc=v) == kv.ERR_DTYPE                  # a V cache where K goes
+    assert call(vc=k) == kv.ERR_DTYPE
+    assert call(vc=_cache(kind=kv.V, cap=256)) == kv.ERR_SHAPE
+    assert call(vc=_cache(kind=kv.V, heads=2)) == kv.ERR_SHAPE
+    assert call(xv=C + 8) == kv.ERR_ALIGN
+    assert call(kc=_cache(kind=kv.K, batch=0), vc=_cache(kind=kv.V, batch=0)) == kv.OK
+
+
 def test_workspace_bytes(lib):
     # one int32 counter per (sequence, query head) rounded up to 256 bytes, then
     # the partials of ceil(chunks / 4) four-split workgroups per row

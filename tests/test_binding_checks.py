@@ -45,6 +45,24 @@ def test_append_host_positions_refused():
         kv.append(x, torch.zeros(2, dtype=torch.int64), _cache())
 
 
+def test_append_kv_checks():
+    k, v = _cache(kv.K), _cache(kv.V)
+    x = torch.zeros((2, 2, 128), dtype=torch.bfloat16)
+    pos = torch.zeros(2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="K cache and a V cache"):
+        kv.append_kv(x, x, pos, v, k)
+    with pytest.raises(ValueError, match="shape"):
+        kv.append_kv(x, x, pos, k, _cache(kv.V, cap=512))
+    with pytest.raises(ValueError, match="matching"):
+        kv.append_kv(x, torch.zeros((2, 2, 64), dtype=torch.bfloat16), pos, k, v)
+    with pytest.raises(ValueError, match="one dtype"):
+        kv.append_kv(x, x.float(), pos, k, v)
+    with pytest.raises(ValueError, match="int32"):
+        kv.append_kv(x, x, pos.long(), k, v)
+    with pytest.raises(ValueError, match="GPU"):       # host tensors and caches
+        kv.append_kv(x, x, pos, k, v)
+
+
 def test_decode_checks():
     k, v = _cache(kv.K), _cache(kv.V)
     q = torch.zeros((2, 8, 128), dtype=torch.bfloat16)

@@ -83,3 +83,33 @@ def test_append_after_quantize_pipeline(kvarn, oracle):
         u_all[:, :, p] = u
     mism = g_codes != o_codes
     assert not (mism & ~oracle.boundary_mask(u_all, U_TOL)).any()
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("dtype,flags", [(torch.bfloat16, 0), (torch.float32, 0),
+                                         (torch.bfloat16, 1)])
+def test_append_kv_equals_two_appends(kvarn, D, dtype, flags):
+    """kvarn_append_kv (K and V in one launch) leaves both caches bit for bit
+    as kvarn_append_ex on K and then on V does: chunk openings, tokens inside
+    and at the start of V bytes, and positions outside the cache (skipped)."""
+    B, H, cap = 7, 3, 512
+    pos = torch.tensor([0, 5, 128, 130, 383, 512, -1], dtype=torch.int32, device="cuda")
+    caches = []
+    for rep in range(2):
+        kv_pair = []
+        for kind in (kvgen.K, kvgen.V):
+            codes, row, col = kvgen.random_cache(31 + kind, B, H, cap, head_dim=D)
+            kv_pair.append(kvarn.Cache(codes.cuda(), row.cuda(), col.cuda(), kind))
+        caches.append(kv_pair)
+    xk = kvgen.new_tokens(5, 0, kvgen.K, B, H, 0.5, dtype=dtype, device="cuda", head_dim=D)
+    xv = kvgen.new_tokens(5, 0, kvgen.V, B, H, 0.5, dtype=dtype, device="cuda", head_dim=D)
+    (k1, v1), (k2, v2) = caches
+    kvarn.append(xk, pos, k1, flags=flags)
+    kvarn.append(xv, pos, v1, flags=flags)
+    kvarn.append_kv(xk, xv, pos, k2, v2, flags=flags)
+    torch.cuda.synchronize()
+    for a, b in ((k1, k2), (v1, v2)):
+        assert torch.equal(a.codes, b.codes)
+        assert torch.equal(a.row_scale, b.row_scale)
+        assert torch.equal(a.col_scale, b.col_scale)
+    log(f"[test] append_kv D={D} dtype={dtype} flags={flags} ok")
