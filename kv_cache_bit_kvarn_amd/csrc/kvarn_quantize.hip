@@ -204,6 +204,36 @@ __device__ __forceinline__ float token_value(float x) {
   return dpp_f<l * 0x55>(x);  // quad_perm [l, l, l, l]
 }
 
+// p[kOffset / 4] |= v on an LDS word, as a no-return LDS atomic. Written out because the
+// compiler's form waits for every outstanding vector-memory operation first
+// (it cannot tell the word from the LDS slice the input prefetch writes);
+// the word is in the K staging area, which no prefetch touches. The wait
+// for its completion is wave_lds_sync's lgkmcnt(0).
+template <int kOffset>  // bytes
+__device__ __forceinline__ void lds_or(uint32_t *p, uint32_t v) {
+  static_assert(kOffset >= 0 && kOffset < 65536, "ds offset field");
+  const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t *)p;
+  asm volatile("ds_or_b32 %0, %1 offset:%2" ::"v"(a), "v"(v), "i"(kOffset) : "memory");
+}
+
+// K codes of the lane's token R, channel tiles 4 K + [0, 4), as the bytes of
+// one word shifted to bit sh, ORed into staging word NT R + 4 K (for every R
+// and K from the given ones on).
+template <int DQ, int R, int K>
+__device__ __forceinline__ void k_code_words(const float *y, const float (&qs)[4], uint32_t *base,
+                                             int sh) {
+  constexpr int NT = DQ / 16;
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    c = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(y[4 * (4 * K + i) + R], qs[R], 1.5f), i, c);
+  lds_or<4 * (NT * R + 4 * K)>(base, c << sh);
+  if constexpr (K + 1 < NT / 4)
+    k_code_words<DQ, R, K + 1>(y, qs, base, sh);
+  else if constexpr (R + 1 < 4)
+    k_code_words<DQ, R + 1, 0>(y, qs, base, sh);
+}
+
 // LDS accesses of the wave complete and are visible to its other lanes.
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -691,32 +721,23 @@ __global__ __launch_bounds__(kThreads, quant_waves_per_simd(DQ)) void quantize_b
 
     uint8_t *cbase = a.codes + (bh * nch + chunk) * Q::CHUNK_CODE_BYTES;
     if (a.kind == KVARN_K) {
-      // kw[r][k] byte i = code of token 4 g + r, channel 16 (4 k + i) + n;
-      // shifted to bit 2 (n % 4) and ORed over the quad it becomes token-row
-      // byte 16 k + 4 i + n / 4 (channels 4 (4 k + i) + n / 4 .. + 4)
-      uint32_t kw[4][NT / 4];
-      const int sh = 2 * (tid & 3);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int k = 0; k < NT / 4; ++k) {
-          uint32_t c = 0;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            c = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(y[4 * (4 * k + i) + r], qs[r], 1.5f), i, c);
-          c <<= sh;
-          c |= dpp_u<kXor1>(c);
-          kw[r][k] = c | dpp_u<kXor2>(c);
-        }
-      // the four lanes of quad q hold the same words: each writes all of the
-      // quad's (token r, word k) words (equal values to equal addresses)
+      // word (r, k) of a lane: byte i = code of token 4 g + r, channel
+      // 16 (4 k + i) + n; shifted to bit 2 (n % 4) and ORed over the quad it
+      // becomes token-row byte 16 k + 4 i + n / 4 (channels 4 (4 k + i) +
+      // n / 4 .. + 4). The ORs are LDS atomics into the staging words, which
+      // the row's lanes clear first (a wave's LDS operations complete in
+      // order).
       const int t = tid;
       const int s = t & 3, q = (t >> 2) & 3;
       uint32_t *ks = &sm.kst[wv][0] + Q::KST_ROW * ((t >> 4) & 3);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int k = 0; k < NT / 4; ++k) ks[NT * r + 4 * k + q] = kw[r][k];
+      if constexpr (NT == 4) {
+        ks[n] = 0u;
+      } else if constexpr (NT == 8) {
+        *reinterpret_cast<u32x2 *>(ks + 2 * n) = u32x2{0u, 0u};
+      } else {
+        *reinterpret_cast<u32x4 *>(ks + 4 * n) = u32x4{0u, 0u, 0u, 0u};
+      }
+      k_code_words<DQ, 0, 0>(y, qs, ks + q, 2 * (tid & 3));
       wave_lds_sync();
       // lane n stores bytes [NT s, NT s + NT) of the row of token 4 g + q:
       // token-row bytes 16 k + 4 i + q' (quad q'), gathered from the four
