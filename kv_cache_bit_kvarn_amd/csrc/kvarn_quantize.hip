@@ -39,8 +39,8 @@
 //      adding up all channels itself would need one barrier less but three
 //      times the VALU instructions.)
 //   4. per-token range step and 2-bit codes (v_cvt_pk_u8_f32): K codes of
-//      four adjacent channels (four adjacent lanes) merge by a shift and an
-//      OR across the quad, pass through a small per-wave LDS area and leave
+//      four adjacent channels (four adjacent lanes) merge by a shift and
+//      LDS OR atomics into a small per-wave staging area and leave
 //      as D/16 contiguous bytes per lane (a wave writes its 16 token rows as
 //      one 4D-byte span); V codes of a lane's 4 tokens form a byte in the
 //      lane (shifts inside the bytes of words that each hold one token of
@@ -157,10 +157,6 @@ __device__ __forceinline__ float rcp_floor(float x) {
 }
 
 template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
-}
-template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
@@ -204,11 +200,11 @@ __device__ __forceinline__ float token_value(float x) {
   return dpp_f<l * 0x55>(x);  // quad_perm [l, l, l, l]
 }
 
-// p[kOffset / 4] |= v on an LDS word, as a no-return LDS atomic. Written out because the
-// compiler's form waits for every outstanding vector-memory operation first
-// (it cannot tell the word from the LDS slice the input prefetch writes);
-// the word is in the K staging area, which no prefetch touches. The wait
-// for its completion is wave_lds_sync's lgkmcnt(0).
+// p[kOffset / 4] |= v on an LDS word, as a no-return LDS atomic. Written
+// out because the compiler's form waits for every outstanding vector-memory
+// operation first (it cannot tell the word from the LDS slice the input
+// prefetch writes); the word is in the K staging area, which no prefetch
+// touches. The wait for its completion is wave_lds_sync's lgkmcnt(0).
 template <int kOffset>  // bytes
 __device__ __forceinline__ void lds_or(uint32_t *p, uint32_t v) {
   static_assert(kOffset >= 0 && kOffset < 65536, "ds offset field");
