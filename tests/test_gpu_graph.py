@@ -2,7 +2,9 @@
 serving loop's step -- quantize a chunk, append one token per sequence to K
 and V, one decode step, advance the positions -- replayed several times with
 eager work and synchronizations between the replays. Every replay must equal
-the same step run eagerly, bit for bit (same kernels on the same inputs)."""
+the same step run eagerly, bit for bit (same kernels on the same inputs; with
+`fused` the graph appends K and V in one launch, which codes them exactly as
+the two separate appends of the eager step do)."""
 import pytest
 import torch
 
@@ -12,8 +14,8 @@ from gpu_util import log
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("D", [128, 64, 256])
-def test_graph_replays_match_eager(kvarn, D):
+@pytest.mark.parametrize("D,fused", [(128, False), (64, False), (256, False), (128, True)])
+def test_graph_replays_match_eager(kvarn, D, fused):
     B, H, Hq, T, cap = 3, 2, 8, 384, 640
     dev = torch.device("cuda")
     xk = kvgen.kv_tensor(31, 0, kvgen.K, B, H, T, 0.5, device=dev, head_dim=D)
@@ -42,7 +44,7 @@ def test_graph_replays_match_eager(kvarn, D):
         pos = torch.full((B,), T + i, dtype=torch.int32, device=dev)
         lens = pos + 1
         kvarn.quantize(xq, qc_e)
-        kvarn.append(nks[i], pos, kc_e)
+        kvarn.append(nks[i], pos, kc_e)       # the eager reference appends K and V apart
         kvarn.append(nvs[i], pos, vc_e)
         outs_e.append(kvarn.decode_attn(qs[i], kc_e, vc_e, lens, workspace=ws_e).clone())
         caches_e.append([t.clone() for c in (kc_e, vc_e) for t in (c.codes, c.row_scale, c.col_scale)])
@@ -60,8 +62,11 @@ def test_graph_replays_match_eager(kvarn, D):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         kvarn.quantize(xq, qc)
-        kvarn.append(nk, pos, kc)
-        kvarn.append(nv, pos, vc)
+        if fused:
+            kvarn.append_kv(nk, nv, pos, kc, vc)
+        else:
+            kvarn.append(nk, pos, kc)
+            kvarn.append(nv, pos, vc)
         kvarn.decode_attn(q, kc, vc, lens, out=out, workspace=ws)
         pos.add_(1)
         lens.add_(1)
