@@ -270,7 +270,8 @@ size_t kvarn_decode_workspace_bytes_ex(int32_t batch, int32_t q_heads,
  *            choose. Rounded up to a multiple of KVARN_DECODE_WAVES (the
  *            splits of one workgroup) and clamped to [KVARN_DECODE_WAVES,
  *            capacity/128 rounded up to that multiple]. Each sequence's used
- *            chunks are spread evenly over the splits.
+ *            chunks are dealt round-robin over the splits (counts differ
+ *            by at most one).
  * workspace  (device) at least kvarn_decode_workspace_bytes_ex(batch,
  *            q_heads, capacity, head_dim) bytes, 16-byte aligned. Its leading counter bytes must
  *            be zero before the first call (a zero-filled allocation); every

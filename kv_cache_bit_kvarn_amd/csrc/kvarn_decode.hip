@@ -600,9 +600,11 @@ __host__ __device__ constexpr int decode_waves_per_simd(int dd) { return dd == 2
 // weights); kTwoScales = false: column scales taken as 1 (ablation).
 //
 // One workgroup = four waves = four consecutive splits of one (sequence,
-// kv-head, head group). A sequence's used chunks are spread evenly over the
-// n_wg * 4 splits of its row (counts differ by at most one; splits past its
-// length get none). After the chunk loop the four waves merge their
+// kv-head, head group). Split s of a row's n_wg * 4 takes the sequence's
+// used chunks s, s + n_wg * 4, s + 2 n_wg * 4, ... (counts differ by at
+// most one; splits past its length get none): the first chunk of a split
+// does not depend on the length, so its loads go out before the length has
+// arrived. After the chunk loop the four waves merge their
 // (m, l, acc) in LDS, and wave h then carries head h0 + h: with one
 // workgroup per row it writes the output directly; otherwise it writes the
 // workgroup's partial, and the workgroup that finishes last (a counter per
@@ -629,8 +631,6 @@ __global__ __launch_bounds__(64 * kDecWaves, decode_waves_per_simd(DD)) void dec
   const bool valid = len >= 1 && len <= a.capacity;
   const int used = valid ? (len + T - 1) / T : 0;
   const int n_split = a.n_wg * kDecWaves, split = wgs * kDecWaves + wv;
-  const int c0 = (int)((int64_t)split * used / n_split);
-  const int c1 = (int)((int64_t)(split + 1) * used / n_split);
   const int64_t bg = (int64_t)b * a.kv_heads + g;
   const int64_t qh0 = (int64_t)b * a.q_heads + (int64_t)g * G + h0;
   const int64_t row = bg * n_hg + hg;  // counter index
@@ -647,38 +647,52 @@ __global__ __launch_bounds__(64 * kDecWaves, decode_waves_per_simd(DD)) void dec
   const int n_l = lane & 15, hl = lane >> 4;
   const int qc0 = slot_elem(n_l, 0) & ~1;  // 16-channel window holding the slot
   const bool q_in = qc0 < DD;
+  // bf16 queries: the raw words first, then the first chunk, then the
+  // conversion, so that the wait for the query leaves the chunk in flight
+  // (vector-memory loads complete in order). fp32 queries (the small parity
+  // workload) are converted at once.
+  const bool q_f32 = a.q_dtype == KVARN_DT_F32;
   float qr[NQ][8];
+  u32x4 qb[NQ][2];
 #pragma unroll
   for (int hf = 0; hf < NQ; ++hf) {
     const int64_t qrow = (qh0 + min(hl, nh - 1)) * DD + 128 * hf + qc0;
-    float qw[16];
-    if (!q_in) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) qw[i] = 0.f;
-    } else if (a.q_dtype == KVARN_DT_F32) {
-      const f32x4 *qf = reinterpret_cast<const f32x4 *>(static_cast<const float *>(a.q) + qrow);
+    for (int jj = 0; jj < 8; ++jj) qr[hf][jj] = 0.f;
+    qb[hf][0] = qb[hf][1] = u32x4{0u, 0u, 0u, 0u};
+    if (q_in) {
+      if (q_f32) {
+        const f32x4 *qf = reinterpret_cast<const f32x4 *>(static_cast<const float *>(a.q) + qrow);
+        float qw[16];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const f32x4 v4 = qf[r];
-        qw[4 * r] = v4[0]; qw[4 * r + 1] = v4[1]; qw[4 * r + 2] = v4[2]; qw[4 * r + 3] = v4[3];
-      }
-    } else {
-      const u32x4 *qb = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.q) + qrow);
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const u32x4 u = qb[r];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          qw[8 * r + 2 * e] = bf16_lo(u[e]);
-          qw[8 * r + 2 * e + 1] = bf16_hi(u[e]);
+        for (int r = 0; r < 4; ++r) {
+          const f32x4 v4 = qf[r];
+          qw[4 * r] = v4[0]; qw[4 * r + 1] = v4[1]; qw[4 * r + 2] = v4[2]; qw[4 * r + 3] = v4[3];
         }
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+          qr[hf][jj] = hl < nh ? ((n_l & 1) ? qw[2 * jj + 1] : qw[2 * jj]) : 0.f;
+      } else {
+        const u32x4 *qp = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.q) + qrow);
+        qb[hf][0] = qp[0];
+        qb[hf][1] = qp[1];
       }
     }
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) qr[hf][jj] = hl < nh ? ((n_l & 1) ? qw[2 * jj + 1] : qw[2 * jj]) : 0.f;
   }
   ChunkRegs<DD> cur, nxt;
-  if (c0 < c1) load_chunk<DD, kTwoScales>(a, bg, nch, c0, lane, cur);
+  // chunk `split` is inside the cache (split < nch): loaded before the
+  // sequence length is known, and left unused when the length ends earlier
+  if (split < nch) load_chunk<DD, kTwoScales>(a, bg, nch, split, lane, cur);
+  if (!q_f32) {
+#pragma unroll
+    for (int hf = 0; hf < NQ; ++hf)
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        // channel qc0 + 2 jj + (n & 1): bf16 element (n & 1) of word jj
+        const uint32_t w = qb[hf][jj >> 2][jj & 3];
+        qr[hf][jj] = hl < nh ? ((n_l & 1) ? bf16_hi(w) : bf16_lo(w)) : 0.f;
+      }
+  }
   if constexpr (kRotate) {
 #pragma unroll
     for (int hf = 0; hf < NQ; ++hf)
@@ -755,8 +769,8 @@ __global__ __launch_bounds__(64 * kDecWaves, decode_waves_per_simd(DD)) void dec
   // load still pending on entry would make every iteration wait for the
   // loads it has just issued: the counter completes in order).
   __builtin_amdgcn_s_waitcnt(kVmcntZero);
-  for (int k = c0; k < c1; ++k) {
-    if (k + 1 < c1) load_chunk<DD, kTwoScales>(a, bg, nch, k + 1, lane, nxt);
+  for (int k = split; k < used; k += n_split) {
+    if (k + n_split < used) load_chunk<DD, kTwoScales>(a, bg, nch, k + n_split, lane, nxt);
     process_chunk<DD, kTwoScales>(sm, st, cur, min(len - k * T, T), lane, aq_fixed, sa_fixed);
     cur = nxt;
   }
