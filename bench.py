@@ -828,19 +828,22 @@ def next_rows_workload(kv, kvgen, torch, args, dev, stream):
         ws = kv.decode_workspace(B, Hq, T + CHUNK, device=dev, head_dim=dh)
         lens = torch.full((B,), T + 1, dtype=torch.int32, device=dev)
         torch.cuda.synchronize()
+        # as in the step: the quantizer with HIP events around each launch
+        # (median of three rounds of 12), decode as graph replays of 12 calls,
+        # since events around an eager decode call would also count the
+        # binding's host time (a call's host cost is close to a head-size-64
+        # decode's duration); layers cycled in both
         qf = [lambda i=i: kv.quantize(xs[i % L], qcs[i % L], iters=args.iters, stream=stream)
               for i in range(12)]
-        df = [lambda i=i: kv.decode_attn(q[i % L], caches[i % L][0], caches[i % L][1], lens,
-                                         out=out, workspace=ws, stream=stream) for i in range(12)]
-        qm, dm = [], []
+        qm = []
         for _ in range(3):
             qf[0]()
             qu = timed_events(torch, stream, qf)
-            df[0]()
-            du = timed_events(torch, stream, df)
             qm.append(sum(qu) / len(qu))
-            dm.append(sum(du) / len(du))
-        qm, dm = sorted(qm)[1], sorted(dm)[1]
+        qm = sorted(qm)[1]
+        dm = graph_us(torch, lambda: [kv.decode_attn(q[i % L], caches[i % L][0],
+                                                     caches[i % L][1], lens, out=out, workspace=ws)
+                                      for i in range(12)]) / 12
         # one-token appends of K and V in one launch, as in the step: graph
         # replays of 36 launches (the layers' appends nine times over; each
         # rewrites the same slots), since each launch is shorter than the
