@@ -833,10 +833,13 @@ __global__ __launch_bounds__(64 * kDecWaves, decode_waves_per_simd(DD)) void dec
   __syncthreads();
   if (!mg.last) return;
   if (hh < nh) {
-    // the row's partials in rounds of 8, all loads of a round issued before
-    // any is used, merged into a running (M, L, x) by log-sum-exp
+    // the row's partials in rounds of R, all loads of a round issued before
+    // any is used, merged into a running (M, L, x) by log-sum-exp; R covers
+    // the occupancy-derived workgroup count per row in one round (12 for head
+    // sizes 64 and 128 on 256 CUs, 8 for 256), so the merge waits for memory
+    // once
     const float *pp = a.partial + (qh0 + hh) * a.n_wg * (2 + DD);
-    constexpr int R = 8;
+    constexpr int R = DD == 256 ? 8 : 16;
     M = -INFINITY;
     L = 0.f;
 #pragma unroll

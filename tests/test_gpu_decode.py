@@ -60,16 +60,16 @@ def test_decode_splits_agree(kvarn):
 
 def test_decode_many_splits_merge_in_rounds(kvarn, oracle):
     """Many workgroups per row: the last one merges the row's partials in
-    rounds of 8 with a running maximum (n_split 33, 64, 80: 9, 16 and 20
-    workgroups, two and three rounds). Every split count agrees with one
-    split, and with the oracle, over a cache of 80 chunks with a ragged last
-    chunk."""
+    rounds of 16 with a running maximum (n_split 33, 64, 68, 80: 9, 16, 17
+    and 20 workgroups, one, one, two and two rounds, the second with one
+    and with four partials). Every split count agrees with one split, and
+    with the oracle, over a cache of 80 chunks with a ragged last chunk."""
     cap = 80 * 128
     kc, vc, hk, hv = _random_caches(kvarn, 2, 1, cap, seed=5)
     q = kvgen.queries(14, 0, 2, 4, dtype=torch.bfloat16)
     lens = [cap, cap - 77]
     L = torch.tensor(lens, dtype=torch.int32, device="cuda")
-    outs = [kvarn.decode_attn(q.cuda(), kc, vc, L, n_split=n) for n in (1, 33, 64, 80)]
+    outs = [kvarn.decode_attn(q.cuda(), kc, vc, L, n_split=n) for n in (1, 33, 64, 68, 80)]
     torch.cuda.synchronize()
     for o in outs[1:]:
         assert rel_l2(o.cpu().numpy(), outs[0].cpu().numpy()) < 1e-5
