@@ -649,48 +649,53 @@ __global__ __launch_bounds__(64 * kDecWaves, decode_waves_per_simd(DD)) void dec
   const bool q_in = qc0 < DD;
   // bf16 queries: the raw words first, then the first chunk, then the
   // conversion, so that the wait for the query leaves the chunk in flight
-  // (vector-memory loads complete in order). fp32 queries (the small parity
-  // workload) are converted at once.
+  // (vector-memory loads complete in order). Both loads are issued on every
+  // path, from clamped in-bounds addresses, with the unused values dropped
+  // afterwards: a load skipped on some path would leave the compiler unable
+  // to count the loads issued after the query's, and it would wait for all
+  // of them. fp32 queries (the small parity workload) are converted at once.
   const bool q_f32 = a.q_dtype == KVARN_DT_F32;
+  const bool q_use = q_in && hl < nh;
   float qr[NQ][8];
   u32x4 qb[NQ][2];
 #pragma unroll
   for (int hf = 0; hf < NQ; ++hf) {
-    const int64_t qrow = (qh0 + min(hl, nh - 1)) * DD + 128 * hf + qc0;
+    const int64_t qrow = (qh0 + min(hl, nh - 1)) * DD + 128 * hf + (q_in ? qc0 : 0);
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) qr[hf][jj] = 0.f;
     qb[hf][0] = qb[hf][1] = u32x4{0u, 0u, 0u, 0u};
-    if (q_in) {
-      if (q_f32) {
-        const f32x4 *qf = reinterpret_cast<const f32x4 *>(static_cast<const float *>(a.q) + qrow);
-        float qw[16];
+    if (!q_f32) {
+      const u32x4 *qp = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.q) + qrow);
+      qb[hf][0] = qp[0];
+      qb[hf][1] = qp[1];
+    } else if (q_in) {
+      const f32x4 *qf = reinterpret_cast<const f32x4 *>(static_cast<const float *>(a.q) + qrow);
+      float qw[16];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const f32x4 v4 = qf[r];
-          qw[4 * r] = v4[0]; qw[4 * r + 1] = v4[1]; qw[4 * r + 2] = v4[2]; qw[4 * r + 3] = v4[3];
-        }
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
-          qr[hf][jj] = hl < nh ? ((n_l & 1) ? qw[2 * jj + 1] : qw[2 * jj]) : 0.f;
-      } else {
-        const u32x4 *qp = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.q) + qrow);
-        qb[hf][0] = qp[0];
-        qb[hf][1] = qp[1];
+      for (int r = 0; r < 4; ++r) {
+        const f32x4 v4 = qf[r];
+        qw[4 * r] = v4[0]; qw[4 * r + 1] = v4[1]; qw[4 * r + 2] = v4[2]; qw[4 * r + 3] = v4[3];
       }
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj)
+        qr[hf][jj] = hl < nh ? ((n_l & 1) ? qw[2 * jj + 1] : qw[2 * jj]) : 0.f;
     }
   }
   ChunkRegs<DD> cur, nxt;
-  // chunk `split` is inside the cache (split < nch): loaded before the
-  // sequence length is known, and left unused when the length ends earlier
-  if (split < nch) load_chunk<DD, kTwoScales>(a, bg, nch, split, lane, cur);
+  // the split's first chunk, loaded before the sequence length is known;
+  // a split past the cache's chunks loads the last one (in bounds) and
+  // leaves it unused, as does one past the sequence's length
+  load_chunk<DD, kTwoScales>(a, bg, nch, min(split, nch - 1), lane, cur);
   if (!q_f32) {
+    // channel qc0 + 2 jj + (n & 1): bf16 element (n & 1) of word jj, moved
+    // to the high half by a shift of 16 or 0
+    const int q_sh = (n_l & 1) ? 0 : 16;
 #pragma unroll
     for (int hf = 0; hf < NQ; ++hf)
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
-        // channel qc0 + 2 jj + (n & 1): bf16 element (n & 1) of word jj
-        const uint32_t w = qb[hf][jj >> 2][jj & 3];
-        qr[hf][jj] = hl < nh ? ((n_l & 1) ? bf16_hi(w) : bf16_lo(w)) : 0.f;
+        const uint32_t w = (qb[hf][jj >> 2][jj & 3] << q_sh) & 0xFFFF0000u;
+        qr[hf][jj] = q_use ? __uint_as_float(w) : 0.f;
       }
   }
   if constexpr (kRotate) {
