@@ -178,7 +178,7 @@ def _oracle_decode(oracle, q, hk, hv, lens, D, ones_c=False):
     (2, 3, 3, 640, [640, 255], 1),
     (2, 2, 4, 2560, [2560, 700], 20),  # five workgroups per row: the last one merges
     (1, 4, 2, 1280, [1153], 0),
-    (2, 2, 4, 4224, [4097, 3000], 48),  # twelve workgroups per row: two merge rounds
+    (2, 2, 4, 4224, [4097, 3000], 48),  # twelve workgroups per row: one merge round (two at D = 256)
 ])
 def test_decode_headdim(kvarn, oracle, D, B, Hkv, G, cap, lens, n_split):
     kc, vc, hk, hv = _caches(kvarn, B, Hkv, cap, D, seed=97 + B + G)
@@ -194,9 +194,10 @@ def test_decode_headdim(kvarn, oracle, D, B, Hkv, G, cap, lens, n_split):
 @pytest.mark.parametrize("D", DIMS)
 def test_decode_headdim_splits_agree(kvarn, oracle, D):
     """One workgroup per row and 3, 10 and 20 (the last workgroup merging the
-    row's partials in one, two and three rounds of 8) agree with each other
-    up to fp32 reassociation, and with the oracle, over 80 chunks with a
-    ragged last chunk."""
+    row's partials in one, one and two rounds of 16 at head size 64, in one,
+    two and three rounds of 8 at 256) agree with each other up to fp32
+    reassociation, and with the oracle, over 80 chunks with a ragged last
+    chunk."""
     cap = 80 * 128
     kc, vc, hk, hv = _caches(kvarn, 2, 1, cap, D, seed=123)
     q = kvgen.queries(124, 0, 2, 4, dtype=torch.bfloat16, head_dim=D)
